@@ -1,0 +1,205 @@
+/*
+ * spec_verify.h — C ABI of the batched speculative-decoding verify step on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the verify half of one speculative step as defined in
+ *   [SB] "7.6 Speculative Decoding: Draft Models, Medusa, EAGLE & Lookahead"
+ *        (LLM stack book): sections "The rule", "The proof that this is exact",
+ *        "Extending to a chain of γ draft tokens", "A From-Scratch
+ *        Implementation" (apply_temperature, speculative_step), "Tree Attention"
+ *        and Exercise 5 (verify_tree_greedy);
+ *   [DM] "Speculative Decoding: Draft Models, EAGLE, and How to Actually Use
+ *        It": section "The Algorithm" (steps 1–4 and the k=4 worked example);
+ *   [SS] "Medusa, EAGLE and self-speculation": "Copying, verified against plain
+ *        greedy" (greedy argmax-match verification).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every array argument is a DEVICE pointer owned by the caller. The
+ *           library never allocates, frees or synchronizes; all work is enqueued
+ *           on `stream` (a hipStream_t, passed as void*; NULL = the null stream)
+ *           and the outputs are valid once the caller has synchronized with it.
+ * Logits.   Row-major. `dtype` (sv_dtype_t) covers every logits tensor of a
+ *           call. Consecutive rows are `row_stride` ELEMENTS apart (>= V); a
+ *           row of sequence b at position i starts at element
+ *           (b * rows_per_seq + i) * row_stride. Rows whose byte address is a
+ *           multiple of 16 take the vectorized path; others are read element by
+ *           element (correct, slower).
+ * Errors.   The return value reports host-side argument validation (done before
+ *           any HIP call, so nothing is enqueued on failure) and launch
+ *           failures (SV_ERR_HIP). Problems that only the device can see are
+ *           reported per sequence in the outputs (see each entry point).
+ * Workspace.Each call needs `workspace_bytes >= sv_workspace_bytes(...)` of
+ *           device memory, 256-byte aligned, that is ALL ZERO before the first
+ *           call (allocate it zeroed, or call sv_workspace_init once). Every
+ *           call returns it to all-zero before its last kernel ends, so it can
+ *           be reused by later calls of any size that fits. Two calls that use
+ *           one workspace must be ordered (same stream); overlapping calls on
+ *           one workspace race.
+ * Random.   Randomness is counter-based Philox4x32-10 (Salmon et al., SC'11)
+ *           with key = (seed low 32 bits, seed high 32 bits) and counter words
+ *           (c0, c1, c2, c3) = (c0, position, sequence b, 2*offset + stream):
+ *             stream 0, c0 = 0       : accept uniform of position i = word 0;
+ *             stream 1, c0 = v / 4   : Gumbel noise of vocab entry v = word v%4.
+ *           A word w maps to u = (w >> 8) * 2^-24 (accept test, u in [0,1)) or
+ *           to U = ((w >> 8) + 0.5) * 2^-24 in (0,1) and Gumbel noise
+ *           G = -ln(-ln U). Identical inputs, seed and offset give bitwise
+ *           identical outputs, whatever the grid size or run.
+ * Determinism of ties. Every argmax takes the LOWEST index among equal values.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 } sv_dtype_t;
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_NULL_ARG = 1,   /* a required pointer is NULL                         */
+  SV_ERR_BAD_SHAPE = 2,  /* B, gamma/N, V or max_depth out of range            */
+  SV_ERR_BAD_DTYPE = 3,  /* dtype is not an sv_dtype_t value                   */
+  SV_ERR_BAD_ARG = 4,    /* row stride < V, offset >= 2^31, misaligned workspace */
+  SV_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than sv_workspace_bytes  */
+  SV_ERR_HIP = 6         /* a HIP runtime call or kernel launch failed         */
+} sv_status_t;
+
+/* Limits checked on the host. */
+#define SV_MAX_GAMMA 16
+#define SV_MAX_TREE_NODES 1024
+#define SV_MAX_BATCH (1 << 20)
+
+/* Per-sequence device-detected error codes written to out_num_accepted[b]
+ * (chains) or out_path_len[b] (trees); the other outputs of b are then -1. */
+#define SV_SEQ_BAD_TOKEN (-1)       /* a drafted / node token outside [0, V)      */
+#define SV_SEQ_BAD_TEMPERATURE (-2) /* temperature < 0, NaN or infinite           */
+#define SV_SEQ_BAD_TREE (-3)        /* parents/depth do not describe a tree       */
+#define SV_SEQ_INTERNAL (-4)        /* a bounded device-side wait gave up         */
+
+/* Optional diagnostics of spec_verify_sample; the struct and each field may
+ * be NULL. All are device arrays of fp32. */
+typedef struct {
+  float* accept_prob;   /* [B, gamma]  a_{b,i} = min(1, p_i(x_i) / q_i(x_i)) for
+                         *             every i (not only up to the first
+                         *             rejection); greedy sequences: 1 if x_i
+                         *             equals the target argmax, else 0.        */
+  float* logz_target;   /* [B, gamma]  ln sum_v exp(l_{b,i,v} / T_b) of target
+                         *             rows 0..gamma-1; NaN for greedy sequences */
+  float* logz_draft;    /* [B, gamma]  the same for draft rows; NaN for greedy
+                         *             sequences and for the one-hot draft       */
+  float* residual_mass; /* [B]         beta = sum_v (p_v - q_v)_+ at the first
+                         *             rejected position (one-hot draft:
+                         *             1 - p(x)); NaN when the bonus token was
+                         *             drawn or the sequence is greedy           */
+} sv_diag_t;
+
+/* Bytes of workspace any entry point needs for B sequences of `rows` logit
+ * rows each (gamma + 1 for the chain entry points, N for the tree) over a
+ * vocabulary of V. Returns 0 for out-of-range arguments. */
+size_t sv_workspace_bytes(int32_t B, int32_t rows, int32_t V);
+
+/* Zero `workspace_bytes` bytes of `workspace` on `stream` (a fill kernel, not
+ * hipMemsetAsync). Needed once, before the first call, unless the memory was
+ * allocated zeroed. */
+sv_status_t sv_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. Never NULL. */
+const char* sv_status_string(sv_status_t status);
+
+/*
+ * spec_verify_sample — modified rejection sampling over a batch of chains.
+ * [SB] "The rule", "Extending to a chain of γ draft tokens", speculative_step;
+ * [DM] "The Algorithm" steps 2–4.
+ *
+ * For each sequence b with temperature T = temperature[b] > 0:
+ *   p_i = softmax(target row i / T), q_i = softmax(draft row i / T), i < gamma;
+ *   a_i = min(1, p_i(x_i) / q_i(x_i)), x_i = draft_ids[b, i];
+ *   accept x_i iff u_i < a_i (u_i from Philox stream 0 at position i);
+ *   n = index of the first rejected position (gamma if none);
+ *   if n < gamma: the correction token is drawn from (p_n - q_n)_+ normalized,
+ *                 by Gumbel-max over ln((p_n - q_n)_+) with stream-1 noise at
+ *                 position n;
+ *   else:         the bonus token is drawn from p_gamma = softmax(target row
+ *                 gamma / T) by Gumbel-max over l/T with stream-1 noise at
+ *                 position gamma.
+ *   If rounding leaves (p_n - q_n)_+ empty, the correction is drawn from p_n
+ *   instead (same noise). With draft_logits == NULL the draft is one-hot at x_i
+ *   ([SB] Exercise 4): a_i = p_i(x_i) and the residual is p_n without x_n.
+ * For T == 0 the sequence is verified greedily ([SB] "Extending to a chain of
+ * γ draft tokens", its temperature-0 paragraph): x_i is accepted iff it equals argmax_v of target row i (lowest index
+ * on ties); the correction is that argmax, the bonus the argmax of row gamma;
+ * draft logits and randomness are not used.
+ *
+ * target_logits  [B, gamma+1, V] rows, stride target_row_stride elements.
+ * draft_logits   [B, gamma, V] rows, stride draft_row_stride, or NULL.
+ * draft_ids      [B, gamma] int32.
+ * temperature    [B] fp32 (device).
+ * seed, offset   Philox key and per-step counter word (offset < 2^31).
+ * out_tokens     [B, gamma+1] int32: x_0 .. x_{n-1}, then the correction or
+ *                bonus token, then -1 padding.
+ * out_num_accepted [B] int32: n in [0, gamma], or an SV_SEQ_* code (< 0).
+ * diag           optional diagnostics (see sv_diag_t), may be NULL.
+ */
+sv_status_t spec_verify_sample(const void* target_logits, int64_t target_row_stride,
+                               const void* draft_logits, int64_t draft_row_stride,
+                               sv_dtype_t dtype, const int32_t* draft_ids,
+                               const float* temperature, int32_t B, int32_t gamma,
+                               int32_t V, uint64_t seed, uint64_t offset,
+                               int32_t* out_tokens, int32_t* out_num_accepted,
+                               const sv_diag_t* diag, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_greedy — argmax-match verification of a batch of chains.
+ * [SB] "Extending to a chain of γ draft tokens" (temperature 0); [SS]
+ * "Copying, verified against plain greedy" (speculative_greedy ; row j of the
+ * verify pass predicts the token after position j).
+ *
+ * g_i = argmax_v target[b, i, v] (lowest index on ties); x_i accepted iff
+ * x_i == g_i; n = first mismatch (gamma if none); emitted: x_0..x_{n-1}, then
+ * g_n (correction) or g_gamma (bonus). Same output layout as
+ * spec_verify_sample; out_num_accepted[b] = SV_SEQ_BAD_TOKEN for a drafted id
+ * outside [0, V).
+ */
+sv_status_t spec_verify_greedy(const void* target_logits, int64_t target_row_stride,
+                               sv_dtype_t dtype, const int32_t* draft_ids, int32_t B,
+                               int32_t gamma, int32_t V, int32_t* out_tokens,
+                               int32_t* out_num_accepted, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_tree — greedy verification of a token tree.
+ * [SB] "Tree Attention" (accept the longest surviving root-to-leaf path, bonus
+ * from the deepest accepted node) and Exercise 5 (verify_tree_greedy: a child
+ * is accepted iff its token equals the argmax of the target row of its parent).
+ *
+ * parents [N] int32 (device): parents[0] = -1, 0 <= parents[i] < i.
+ * depth   [N] int32 (device): depth[0] = 0, depth[i] = depth[parents[i]] + 1,
+ *         depth[i] <= max_depth.
+ * node_tokens [B, N] int32: node_tokens[b, 0] is the committed root (unused).
+ * target_logits [B, N, V]: row i predicts the token that follows node i.
+ * Rule: g_i = argmax of row i; node 0 is valid; node c > 0 is valid iff its
+ * parent is valid and node_tokens[b, c] == g_{parents[c]}. The accepted node is
+ * the deepest valid node (smallest index among equally deep ones); the path is
+ * its ancestors from the root, and the bonus token is its argmax.
+ * out_path     [B, max_depth+1] int32: node indices root first, -1 padded.
+ * out_path_len [B] int32: depth(accepted node) + 1, or an SV_SEQ_* code.
+ * out_bonus    [B] int32: bonus token, -1 on error.
+ */
+sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_stride,
+                             sv_dtype_t dtype, const int32_t* parents, const int32_t* depth,
+                             const int32_t* node_tokens, int32_t B, int32_t N, int32_t V,
+                             int32_t max_depth, int32_t* out_path, int32_t* out_path_len,
+                             int32_t* out_bonus, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,263 @@
+"""Seeded synthetic inputs of the verify step (host numpy arrays).
+
+This module only PRODUCES inputs: logits, drafted ids, temperatures and tree
+descriptions. It holds none of the verify arithmetic and is shared by the
+tests, the benchmark and the smoke check, which hand the same arrays to the GPU
+library and to the CPU oracle.
+
+The drafter is emulated: drafted ids are drawn from softmax(draft / T) of the
+stored (rounded) draft logits with numpy's own Gumbel-max draw, i.e. x ~ q as
+the drafting loop of "7.6 Speculative Decoding: Draft Models, Medusa, EAGLE &
+Lookahead" ("A From-Scratch Implementation", step 1) produces them; at T = 0
+the drafter proposes its argmax. bf16 logits are generated in fp32 and rounded
+to nearest-even; they are handed over as uint16 bit patterns.
+
+The five named workloads (``CONFIGS``) are:
+  chain_f32_small  B=1,   gamma=4, V=1000,   fp32, T=1.0
+  chain_bf16_peaked B=64, gamma=5, V=32000,  bf16, T=0.8, 5 boosted ids per row
+  chain_bf16_llama B=256, gamma=8, V=128256, bf16, T in {0, 0.7, 1.0}, Zipf boost
+  onehot_bf16_qwen B=512, gamma=6, V=152064, bf16, one-hot draft, T=1.0
+  tree_bf16_llama  B=32,  N=65 nodes (root + 4 + 16 + 44), V=128256, bf16, greedy
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+CONFIGS = ["chain_f32_small", "chain_bf16_peaked", "chain_bf16_llama", "onehot_bf16_qwen",
+           "tree_bf16_llama"]
+CONFIG_INDEX = {name: k for k, name in enumerate(CONFIGS)}
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    return ((bits + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 (exact)."""
+    return (np.ascontiguousarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def stored_values(a: np.ndarray) -> np.ndarray:
+    """The fp32 values of a stored logits array (float32 or bf16 bits)."""
+    return bf16_to_f32(a) if a.dtype == np.uint16 else a
+
+
+@dataclass
+class ChainInputs:
+    name: str
+    target: np.ndarray             # [B, gamma+1, V] float32 or uint16 (bf16 bits)
+    draft: np.ndarray | None       # [B, gamma, V] same dtype, or None (one-hot draft)
+    draft_ids: np.ndarray          # [B, gamma] int32
+    temperature: np.ndarray        # [B] float32
+    seed: int = 0
+    offset: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.draft_ids.shape[0]
+
+    @property
+    def gamma(self):
+        return self.draft_ids.shape[1]
+
+    @property
+    def V(self):
+        return self.target.shape[2]
+
+    @property
+    def is_bf16(self):
+        return self.target.dtype == np.uint16
+
+    def algorithmic_bytes(self) -> int:
+        """Every target row once, plus every draft row the verifier needs
+        (dense draft and T > 0)."""
+        es = self.target.itemsize
+        n = self.B * (self.gamma + 1) * self.V * es
+        if self.draft is not None:
+            n += int(np.count_nonzero(self.temperature > 0)) * self.gamma * self.V * es
+        return n
+
+
+@dataclass
+class TreeInputs:
+    name: str
+    target: np.ndarray        # [B, N, V]
+    parents: np.ndarray       # [N] int32
+    depth: np.ndarray         # [N] int32
+    node_tokens: np.ndarray   # [B, N] int32
+    max_depth: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.node_tokens.shape[0]
+
+    @property
+    def N(self):
+        return self.node_tokens.shape[1]
+
+    @property
+    def V(self):
+        return self.target.shape[2]
+
+    def algorithmic_bytes(self) -> int:
+        return self.B * self.N * self.V * self.target.itemsize
+
+
+def _seq_rng(seed: int, b: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, b])))
+
+
+def _parallel(fn, n, workers=None):
+    workers = workers or min(16, os.cpu_count() or 1)
+    if n <= 1 or workers <= 1:
+        for b in range(n):
+            fn(b)
+        return
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fn, range(n)))
+
+
+def _draw_from_logits(rng, logits_f32: np.ndarray, T: float) -> int:
+    """Emulated drafter: one draw from softmax(logits / T) (argmax at T = 0)."""
+    y = logits_f32.astype(np.float64)
+    if T == 0.0:
+        return int(np.argmax(y))
+    g = rng.gumbel(size=y.shape[0])
+    return int(np.argmax(y / T + g))
+
+
+def make_chain(name: str, B: int, gamma: int, V: int, *, bf16: bool, seed: int,
+               target_sigma: float, boost: str | None = None, n_boost: int = 0,
+               boost_value: float = 0.0, draft_scale: float = 1.0,
+               draft_sigma: float | tuple = 0.5, temperatures=(1.0,), one_hot: bool = False,
+               onehot_hit: float = 0.7, row_stride: int | None = None, workers=None) -> ChainInputs:
+    """Generic chain workload.
+
+    target = N(0, target_sigma^2) [+ boost]; draft = draft_scale * target[:, :gamma]
+    + N(0, sigma_b^2) with sigma_b fixed or drawn per sequence from a (lo, hi)
+    range; temperatures drawn per sequence uniformly from ``temperatures``;
+    one_hot: no draft logits, drafted id = target argmax w.p. onehot_hit else
+    uniform. ``row_stride`` > V pads every row (the padding holds large values
+    that must never be read).
+    """
+    S = row_stride or V
+    dt = np.uint16 if bf16 else np.float32
+    target = np.empty((B, gamma + 1, S), dt)
+    draft = None if one_hot else np.empty((B, gamma, S), dt)
+    ids = np.empty((B, gamma), np.int32)
+    temp = np.empty(B, np.float32)
+    sigmas = np.empty(B, np.float64)
+    logtab = np.log(np.arange(1, V + 1, dtype=np.float64)) if boost == "zipf" else None
+
+    def one(b):
+        rng = _seq_rng(seed, b)
+        T = float(temperatures[rng.integers(len(temperatures))]) if len(temperatures) > 1 else float(temperatures[0])
+        temp[b] = T
+        t = rng.standard_normal((gamma + 1, V), dtype=np.float32) * np.float32(target_sigma)
+        if boost == "zipf":
+            for r in range(gamma + 1):
+                rank0 = rng.permutation(V)  # rank - 1 of every vocab entry
+                t[r] -= (1.1 * logtab[rank0]).astype(np.float32)
+        elif boost == "peaks":
+            for r in range(gamma + 1):
+                hot = rng.choice(V, size=n_boost, replace=False)
+                t[r, hot] += np.float32(boost_value)
+        if S > V:
+            pad = np.full((gamma + 1, S - V), 1.0e4, np.float32)
+            t_store = np.concatenate([t, pad], axis=1)
+        else:
+            t_store = t
+        target[b] = round_bf16(t_store) if bf16 else t_store
+        t_vals = stored_values(target[b])[:, :V]
+        if one_hot:
+            for i in range(gamma):
+                if rng.random() < onehot_hit:
+                    ids[b, i] = int(np.argmax(t_vals[i]))
+                else:
+                    ids[b, i] = int(rng.integers(V))
+            sigmas[b] = np.nan
+            return
+        sig = float(rng.uniform(*draft_sigma)) if isinstance(draft_sigma, tuple) else float(draft_sigma)
+        sigmas[b] = sig
+        d = np.float32(draft_scale) * t[:gamma] + rng.standard_normal((gamma, V), dtype=np.float32) * np.float32(sig)
+        if S > V:
+            d = np.concatenate([d, np.full((gamma, S - V), 1.0e4, np.float32)], axis=1)
+        draft[b] = round_bf16(d) if bf16 else d
+        d_vals = stored_values(draft[b])[:, :V]
+        for i in range(gamma):
+            ids[b, i] = _draw_from_logits(rng, d_vals[i], T)
+
+    _parallel(one, B, workers)
+    inp = ChainInputs(name, target, draft, ids, temp, seed=0, offset=0,
+                      meta={"V": V, "row_stride": S, "draft_sigma": sigmas})
+    if S > V:
+        inp.meta["padded"] = True
+    return inp
+
+
+def _c5_tree():
+    """Root, 4 children, 16 grandchildren, then the first 44 great-grandchildren
+    in breadth-first order (branching 4, last level truncated)."""
+    parents = [-1] + [0] * 4 + [1 + (k - 5) // 4 for k in range(5, 21)] + [5 + (k - 21) // 4 for k in range(21, 65)]
+    depth = [0] + [1] * 4 + [2] * 16 + [3] * 44
+    return np.array(parents, np.int32), np.array(depth, np.int32)
+
+
+def make_tree(name: str, B: int, V: int, parents: np.ndarray, depth: np.ndarray, *, bf16: bool,
+              seed: int, target_sigma: float = 3.0, hit: float = 0.5, workers=None) -> TreeInputs:
+    N = len(parents)
+    dt = np.uint16 if bf16 else np.float32
+    target = np.empty((B, N, V), dt)
+    tokens = np.empty((B, N), np.int32)
+
+    def one(b):
+        rng = _seq_rng(seed, b)
+        t = rng.standard_normal((N, V), dtype=np.float32) * np.float32(target_sigma)
+        target[b] = round_bf16(t) if bf16 else t
+        vals = stored_values(target[b])
+        tokens[b, 0] = int(rng.integers(V))
+        for c in range(1, N):
+            if rng.random() < hit:
+                tokens[b, c] = int(np.argmax(vals[parents[c]]))
+            else:
+                tokens[b, c] = int(rng.integers(V))
+
+    _parallel(one, B, workers)
+    return TreeInputs(name, target, np.asarray(parents, np.int32), np.asarray(depth, np.int32),
+                      tokens, int(np.max(depth)))
+
+
+def make(name: str, workers=None):
+    """One of the five named workloads at full size (generator seed 1000 + k)."""
+    k = CONFIG_INDEX[name]
+    seed = 1000 + k
+    if name == "chain_f32_small":
+        return make_chain(name, 1, 4, 1000, bf16=False, seed=seed, target_sigma=2.0,
+                          draft_sigma=0.5, temperatures=(1.0,), workers=workers)
+    if name == "chain_bf16_peaked":
+        return make_chain(name, 64, 5, 32000, bf16=True, seed=seed, target_sigma=3.0, boost="peaks",
+                          n_boost=5, boost_value=8.0, draft_scale=0.8, draft_sigma=1.0,
+                          temperatures=(0.8,), workers=workers)
+    if name == "chain_bf16_llama":
+        return make_chain(name, 256, 8, 128256, bf16=True, seed=seed, target_sigma=3.0, boost="zipf",
+                          draft_sigma=(0.2, 2.0), temperatures=(0.0, 0.7, 1.0), workers=workers)
+    if name == "onehot_bf16_qwen":
+        return make_chain(name, 512, 6, 152064, bf16=True, seed=seed, target_sigma=3.0,
+                          temperatures=(1.0,), one_hot=True, onehot_hit=0.7, workers=workers)
+    if name == "tree_bf16_llama":
+        parents, depth = _c5_tree()
+        return make_tree(name, 32, 128256, parents, depth, bf16=True, seed=seed, workers=workers)
+    raise KeyError(name)
+
+
+def tree_c5_structure():
+    return _c5_tree()
