@@ -1,0 +1,201 @@
+"""Benchmark of the batched verify step on one MI355X.
+
+One step = one call of spec_verify_sample over one batch of the
+chain_bf16_llama workload (B=256 sequences, gamma=8 drafts, V=128256, bf16
+logits, temperatures drawn from {0, 0.7, 1.0}), inputs resident in HBM. Prints
+one JSON line: verified positions/s (B * gamma per step) as `value`, the
+logit-read bandwidth against the HBM roofline of the fused kernel measured with
+HIP events on its stream, and the CPU oracle timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified positions/s + logit-read GB/s (% of HBM peak), B=256 γ=8 V=128256"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "chain_bf16_llama"
+KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_chain.hip", "rejection_sampling_verify_amd/csrc/sv_tree.hip",
+                  "rejection_sampling_verify_amd/csrc/sv_device.h", "rejection_sampling_verify_amd/csrc/sv_internal.h",
+                  "rejection_sampling_verify_amd/csrc/sv_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def to_dev(a, torch, dev):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+def cpu_baseline(inp, is_tree: bool, positions_per_step: int):
+    """The oracle as it stands, on all host threads (capped at 16), over the
+    whole workload; repeated until about 10 s of CPU time or 3 runs."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 and (not times or time.perf_counter() - t_start < 10.0):
+        t0 = time.perf_counter()
+        if is_tree:
+            oracle.verify_tree(inp.target, inp.parents, inp.depth, inp.node_tokens, inp.max_depth, nthreads=threads)
+        else:
+            oracle.verify_sample(inp.target, inp.draft, inp.draft_ids, inp.temperature, seed=inp.seed,
+                                 offset=inp.offset, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": positions_per_step / t, "unit": "verified positions/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole workload (one step), %d run(s), median %.3f s, fp64 plain loops" % (len(times), t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rejection_sampling_verify_amd as rsv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    rsv.lib()
+    inp = workloads.make(args.workload)
+    is_tree = args.workload.startswith("tree")
+    print("[bench] workload %s generated" % args.workload, file=sys.stderr, flush=True)
+
+    # Two resident copies of the inputs, used alternately, so that no step
+    # finds its logits in the 256 MB Infinity Cache from the step before.
+    copies = []
+    for _ in range(2):
+        if is_tree:
+            copies.append(dict(t=to_dev(inp.target, torch, dev), par=torch.from_numpy(inp.parents).to(dev),
+                               dep=torch.from_numpy(inp.depth).to(dev), tok=torch.from_numpy(inp.node_tokens).to(dev)))
+        else:
+            copies.append(dict(t=to_dev(inp.target, torch, dev), d=to_dev(inp.draft, torch, dev),
+                               ids=torch.from_numpy(inp.draft_ids).to(dev),
+                               temp=torch.from_numpy(inp.temperature).to(dev)))
+    ws = rsv.Workspace(dev)
+    if is_tree:
+        B, N = inp.node_tokens.shape
+        wbuf = ws.get(B, N, inp.V)
+        out = (torch.empty((B, inp.max_depth + 1), dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+        positions = B * (N - 1)
+
+        def step(k):
+            c = copies[k % 2]
+            rsv.spec_verify_tree(c["t"], c["par"], c["dep"], c["tok"], inp.max_depth, out_path=out[0],
+                                 out_path_len=out[1], out_bonus=out[2], workspace=wbuf)
+    else:
+        B, G = inp.draft_ids.shape
+        wbuf = ws.get(B, G + 1, inp.V)
+        out = (torch.empty((B, G + 1), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+        positions = B * G
+
+        def step(k):
+            c = copies[k % 2]
+            rsv.spec_verify_sample(c["t"], c["d"], c["ids"], c["temp"], seed=inp.seed, offset=inp.offset,
+                                   out_tokens=out[0], out_num_accepted=out[1], workspace=wbuf)
+
+    stream = torch.cuda.current_stream()
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        step(k)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
+
+    ms_per_step = wall * 1e3 / args.steps
+    alg_bytes = inp.algorithmic_bytes()
+    t_launch = float(np.mean(launch_ms)) * 1e-3
+    achieved = alg_bytes / t_launch / 1e9
+    traffic = measured_traffic(args.workload)
+
+    if is_tree:
+        cfg = {"workload": args.workload, "B": int(B), "nodes": int(inp.node_tokens.shape[1]), "V": int(inp.V),
+               "input_dtype": str(inp.target.dtype).replace("uint16", "bf16"), "verify": "greedy tree"}
+        extra = {}
+    else:
+        n = out[1].cpu().numpy()
+        cfg = {"workload": args.workload, "B": int(B), "gamma": int(G), "V": int(inp.V),
+               "input_dtype": "bf16" if inp.is_bf16 else "f32",
+               "temperatures": sorted(set(float(x) for x in inp.temperature)),
+               "draft": "one-hot" if inp.draft is None else "dense"}
+        valid = n[n >= 0]
+        extra = {"mean_accepted": float(valid.mean()),
+                 "emitted_tokens_per_s": float((valid + 1).sum() / (ms_per_step * 1e-3)),
+                 "per_position_acceptance": [float(np.mean(n[n >= i] > i)) if np.any(n >= i) else None
+                                             for i in range(G)]}
+    rec = {
+        "metric": METRIC, "value": positions / (ms_per_step * 1e-3), "unit": "verified positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": cfg,
+        "logit_read_GBps": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_of_peak": alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": int(alg_bytes),
+        "launch_ms": {"mean": float(np.mean(launch_ms)), "p10": float(np.percentile(launch_ms, 10)),
+                      "p50": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        **extra,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(inp, is_tree, positions)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

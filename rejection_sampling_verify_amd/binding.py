@@ -1,0 +1,228 @@
+"""ctypes binding of librsv_hip.so (argument marshalling only).
+
+Tensors are torch tensors on the GPU; their ``data_ptr()`` is handed to the C
+ABI together with ``torch.cuda.current_stream().cuda_stream`` (the hipStream_t
+of ROCm builds of torch). Every step of the verify path runs in the library's
+kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librsv_hip.so")
+
+SV_DTYPE_F32 = 0
+SV_DTYPE_BF16 = 1
+SV_SEQ_BAD_TOKEN = -1
+SV_SEQ_BAD_TEMPERATURE = -2
+SV_SEQ_BAD_TREE = -3
+SV_SEQ_INTERNAL = -4
+
+EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
+           "spec_verify_greedy", "spec_verify_tree"]
+
+_lib = None
+
+
+class SVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, sv_status_string(status), status))
+
+
+class _Diag(ctypes.Structure):
+    _fields_ = [("accept_prob", ctypes.c_void_p), ("logz_target", ctypes.c_void_p),
+                ("logz_draft", ctypes.c_void_p), ("residual_mass", ctypes.c_void_p)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load librsv_hip.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("librsv_hip.so is not built; run rejection_sampling_verify_amd.build.build() "
+                               "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
+        L.sv_workspace_bytes.argtypes = [i32, i32, i32]
+        L.sv_workspace_bytes.restype = sz
+        L.sv_workspace_init.argtypes = [P, sz, P]
+        L.sv_workspace_init.restype = ctypes.c_int
+        L.sv_status_string.argtypes = [ctypes.c_int]
+        L.sv_status_string.restype = ctypes.c_char_p
+        L.spec_verify_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, i32, i32, i32, u64, u64, P, P,
+                                         ctypes.POINTER(_Diag), P, sz, P]
+        L.spec_verify_sample.restype = ctypes.c_int
+        L.spec_verify_greedy.argtypes = [P, i64, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P]
+        L.spec_verify_greedy.restype = ctypes.c_int
+        L.spec_verify_tree.argtypes = [P, i64, ctypes.c_int, P, P, P, i32, i32, i32, i32, P, P, P, P, sz, P]
+        L.spec_verify_tree.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def exported_symbols() -> list[str]:
+    L = lib()
+    return [name for name in EXPORTS if hasattr(L, name)]
+
+
+def sv_status_string(status: int) -> str:
+    return lib().sv_status_string(int(status)).decode()
+
+
+def sv_workspace_bytes(B: int, rows: int, V: int) -> int:
+    return int(lib().sv_workspace_bytes(B, rows, V))
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def sv_workspace_init(ws, stream=None) -> None:
+    st = lib().sv_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if st != 0:
+        raise SVError(st, "sv_workspace_init")
+
+
+class Workspace:
+    """Zeroed device workspace that grows to the largest call it has served."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, B: int, rows: int, V: int):
+        import torch
+        need = sv_workspace_bytes(B, rows, V)
+        if need == 0:
+            raise ValueError("shape out of range for the library")
+        if self.buf is None or self.buf.numel() < need:
+            # torch's caching allocator aligns blocks to at least 512 bytes.
+            self.buf = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SV_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SV_DTYPE_F32
+    raise TypeError("logits must be torch.bfloat16 or torch.float32, got %s" % t.dtype)
+
+
+def _row_stride(t, rows: int, V: int) -> int:
+    """Elements between consecutive rows of a [B, rows, >=V] view whose rows are
+    evenly spaced (contiguous innermost dimension)."""
+    if t.dim() != 3 or t.shape[1] != rows or t.stride(2) != 1:
+        raise ValueError("logits must be [B, %d, V] with a contiguous last dimension" % rows)
+    if t.shape[0] > 1 and t.stride(0) != rows * t.stride(1):
+        raise ValueError("rows of consecutive sequences must be evenly spaced")
+    return int(t.stride(1)) if rows > 1 or t.shape[0] == 1 else int(t.stride(0))
+
+
+def _check_i32(t, shape, name):
+    import torch
+    if t.dtype != torch.int32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError("%s must be a contiguous int32 CUDA tensor of shape %s" % (name, tuple(shape)))
+
+
+def spec_verify_sample(target_logits, draft_logits, draft_ids, temperature, seed: int = 0, offset: int = 0,
+                       out_tokens=None, out_num_accepted=None, diag: dict | None = None, workspace=None,
+                       V: int | None = None, stream=None):
+    """Sampled (temperature > 0) / greedy (temperature == 0) verification.
+
+    target_logits [B, gamma+1, V'] and draft_logits [B, gamma, V'] (or None for a
+    one-hot draft) of bf16 or fp32 with V' >= V; draft_ids [B, gamma] int32;
+    temperature [B] float32. Returns (out_tokens [B, gamma+1], out_num_accepted [B]).
+    diag: optional dict of preallocated float32 tensors with keys accept_prob,
+    logz_target, logz_draft ([B, gamma]) and residual_mass ([B]).
+    """
+    import torch
+    B, gamma = draft_ids.shape
+    V = int(target_logits.shape[2]) if V is None else int(V)
+    _check_i32(draft_ids, (B, gamma), "draft_ids")
+    if temperature.dtype != torch.float32 or tuple(temperature.shape) != (B,) or not temperature.is_contiguous():
+        raise ValueError("temperature must be a contiguous float32 tensor of shape [B]")
+    ts = _row_stride(target_logits, gamma + 1, V)
+    ds = 0
+    if draft_logits is not None:
+        if draft_logits.dtype != target_logits.dtype:
+            raise ValueError("draft and target logits must share a dtype")
+        ds = _row_stride(draft_logits, gamma, V)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=target_logits.device)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=target_logits.device)
+    d = None
+    if diag:
+        d = _Diag(*[diag[k].data_ptr() if diag.get(k) is not None else None
+                    for k in ("accept_prob", "logz_target", "logz_draft", "residual_mass")])
+    if workspace is None:
+        workspace = Workspace(target_logits.device).get(B, gamma + 1, V)
+    st = lib().spec_verify_sample(_ptr(target_logits), ts, _ptr(draft_logits), ds, _dtype_code(target_logits),
+                                  _ptr(draft_ids), _ptr(temperature), B, gamma, V, seed, offset,
+                                  _ptr(out_tokens), _ptr(out_num_accepted),
+                                  ctypes.byref(d) if d is not None else None,
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise SVError(st, "spec_verify_sample")
+    return out_tokens, out_num_accepted
+
+
+def spec_verify_greedy(target_logits, draft_ids, out_tokens=None, out_num_accepted=None, workspace=None,
+                       V: int | None = None, stream=None):
+    """Argmax-match verification; same outputs as spec_verify_sample."""
+    import torch
+    B, gamma = draft_ids.shape
+    V = int(target_logits.shape[2]) if V is None else int(V)
+    _check_i32(draft_ids, (B, gamma), "draft_ids")
+    ts = _row_stride(target_logits, gamma + 1, V)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=target_logits.device)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=target_logits.device)
+    if workspace is None:
+        workspace = Workspace(target_logits.device).get(B, gamma + 1, V)
+    st = lib().spec_verify_greedy(_ptr(target_logits), ts, _dtype_code(target_logits), _ptr(draft_ids), B, gamma,
+                                  V, _ptr(out_tokens), _ptr(out_num_accepted), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise SVError(st, "spec_verify_greedy")
+    return out_tokens, out_num_accepted
+
+
+def spec_verify_tree(target_logits, parents, depth, node_tokens, max_depth: int, out_path=None,
+                     out_path_len=None, out_bonus=None, workspace=None, V: int | None = None, stream=None):
+    """Greedy tree verification. Returns (out_path [B, max_depth+1], out_path_len [B], out_bonus [B])."""
+    import torch
+    B, N = node_tokens.shape
+    V = int(target_logits.shape[2]) if V is None else int(V)
+    _check_i32(node_tokens, (B, N), "node_tokens")
+    _check_i32(parents, (N,), "parents")
+    _check_i32(depth, (N,), "depth")
+    ts = _row_stride(target_logits, N, V)
+    dev = target_logits.device
+    if out_path is None:
+        out_path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    if out_path_len is None:
+        out_path_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_bonus is None:
+        out_bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = Workspace(dev).get(B, N, V)
+    st = lib().spec_verify_tree(_ptr(target_logits), ts, _dtype_code(target_logits), _ptr(parents), _ptr(depth),
+                                _ptr(node_tokens), B, N, V, max_depth, _ptr(out_path), _ptr(out_path_len),
+                                _ptr(out_bonus), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    if st != 0:
+        raise SVError(st, "spec_verify_tree")
+    return out_path, out_path_len, out_bonus

@@ -1,0 +1,286 @@
+// sv_api.hip — the C ABI of include/spec_verify.h: argument validation,
+// workspace layout, launch configuration. Host code only.
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/spec_verify.h"
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int32_t max_chunks(int32_t V) {
+  // Smallest chunk: one fp32 vector per thread.
+  const int32_t smallest = kThreads * 4;
+  return (V + smallest - 1) / smallest;
+}
+
+WsLayout ws_layout(int32_t B, int32_t rows, int32_t nchunks) {
+  WsLayout L;
+  size_t off = 0;
+  L.tickets = off;
+  off += (size_t)kMaxSets * kTicketStride * 4;
+  L.done = off;
+  off += 4096;
+  L.seq = off;
+  off = round_up(off + (size_t)B * sizeof(SeqState), 256);
+  L.p1 = off;
+  off = round_up(off + (size_t)B * rows * nchunks * sizeof(P1Partial), 256);
+  L.gath = off;
+  off = round_up(off + (size_t)B * rows * sizeof(Gathered), 256);
+  L.p2 = off;
+  off = round_up(off + (size_t)B * nchunks * sizeof(P2Partial), 256);
+  L.tree_arrive = off;
+  off = round_up(off + (size_t)B * 4, 256);
+  L.tree_part = off;
+  off = round_up(off + (size_t)B * rows * nchunks * sizeof(TreePartial), 256);
+  L.total = off;
+  return L;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+std::atomic<int> g_occ[kMaxDevices][4];
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+struct Tiling {
+  int kv, chunk, nchunks;
+};
+
+// Chunk length: as long as possible (8 vectors per thread) while the pass-1
+// item count stays at or above the target, so that small batches still spread
+// over the whole GPU.
+Tiling pick_tiling(long long rows, int32_t V, bool bf16) {
+  const int ev = bf16 ? 8 : 4;
+  const long long target = env_int("SV_TARGET_ITEMS", 4096);
+  int kv = kMaxVecsPerThread;
+  int forced = env_int("SV_KV", 0);
+  if (forced >= 1 && forced <= kMaxVecsPerThread && (forced & (forced - 1)) == 0) {
+    kv = forced;
+  } else {
+    while (kv > 1) {
+      const long long chunk = (long long)kThreads * ev * kv;
+      const long long items = rows * ((V + chunk - 1) / chunk);
+      if (items >= target) break;
+      kv >>= 1;
+    }
+  }
+  Tiling t;
+  t.kv = kv;
+  t.chunk = kThreads * ev * kv;
+  t.nchunks = (V + t.chunk - 1) / t.chunk;
+  return t;
+}
+
+bool device_info(int* dev, int* cus) {
+  if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= kMaxDevices) return false;
+  int n = g_cus[*dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, *dev) != hipSuccess || n <= 0)
+      return false;
+    g_cus[*dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
+  return true;
+}
+
+int occupancy(int dev, bool bf16, bool vec) {
+  const int k = (bf16 ? 2 : 0) + (vec ? 1 : 0);
+  int n = g_occ[dev][k].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    n = chain_occupancy(bf16, vec);
+    if (n <= 0) n = 1;
+    g_occ[dev][k].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+bool aligned16(const void* p, int64_t stride_bytes) {
+  return ((uintptr_t)p % 16 == 0) && (stride_bytes % 16 == 0);
+}
+
+sv_status_t check_workspace(void* ws, size_t bytes, size_t need) {
+  if (ws == nullptr || bytes < need) return SV_ERR_WORKSPACE;
+  if ((uintptr_t)ws % 256 != 0) return SV_ERR_BAD_ARG;
+  return SV_OK;
+}
+
+sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, int64_t d_stride,
+                      sv_dtype_t dtype, const int32_t* ids, const float* temperature, int32_t B,
+                      int32_t gamma, int32_t V, uint64_t seed, uint64_t offset, int32_t* out_tokens,
+                      int32_t* out_n, const sv_diag_t* diag, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!target || !ids || !out_tokens || !out_n) return SV_ERR_NULL_ARG;
+  if (B < 0 || B > SV_MAX_BATCH || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > (1 << 30))
+    return SV_ERR_BAD_SHAPE;
+  if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_BAD_DTYPE;
+  if (t_stride < V || (draft && d_stride < V)) return SV_ERR_BAD_ARG;
+  if (offset >= (1ull << 31)) return SV_ERR_BAD_ARG;
+  const size_t need = sv_workspace_bytes(B, gamma + 1, V);
+  const sv_status_t ws_ok = check_workspace(workspace, workspace_bytes, need);
+  if (ws_ok != SV_OK) return ws_ok;
+  if (B == 0) return SV_OK;
+
+  const bool bf16 = (dtype == SV_DTYPE_BF16);
+  const int es = bf16 ? 2 : 4;
+  const bool vec = aligned16(target, t_stride * es) && (!draft || aligned16(draft, d_stride * es));
+  const Tiling tl = pick_tiling((long long)B * gamma, V, bf16);
+  const WsLayout L = ws_layout(B, gamma + 1, max_chunks(V));
+  uint8_t* ws = (uint8_t*)workspace;
+
+  int dev = 0, cus = 0;
+  if (!device_info(&dev, &cus)) return SV_ERR_HIP;
+
+  ChainArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.target = (const uint8_t*)target;
+  a.t_stride = t_stride * es;
+  a.draft = (const uint8_t*)draft;
+  a.d_stride = d_stride * es;
+  a.ids = ids;
+  a.temperature = temperature;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.chunk = tl.chunk;
+  a.nchunks = tl.nchunks;
+  a.kv = tl.kv;
+  a.key0 = (uint32_t)seed;
+  a.key1 = (uint32_t)(seed >> 32);
+  a.ctr_accept = (uint32_t)(2u * (uint32_t)offset);
+  a.ctr_noise = (uint32_t)(2u * (uint32_t)offset + 1u);
+  a.out_tokens = out_tokens;
+  a.out_n = out_n;
+  if (diag) {
+    a.d_accept = diag->accept_prob;
+    a.d_logzt = diag->logz_target;
+    a.d_logzd = diag->logz_draft;
+    a.d_beta = diag->residual_mass;
+  }
+  a.tickets = (uint32_t*)(ws + L.tickets);
+  a.done = (uint32_t*)(ws + L.done);
+  a.seq = (SeqState*)(ws + L.seq);
+  a.p1 = (P1Partial*)(ws + L.p1);
+  a.gath = (Gathered*)(ws + L.gath);
+  a.p2 = (P2Partial*)(ws + L.p2);
+  a.nsets = kMaxSets;
+  a.fused = env_int("SV_FUSED", 1) ? 1 : 0;
+  a.spin_limit = 1u << 22;
+
+  int grid = env_int("SV_GRID", 0);
+  if (grid <= 0) grid = cus * occupancy(dev, bf16, vec);
+  const long long n1 = (long long)gamma * tl.nchunks;
+  const long long per_set_wgs = (grid + a.nsets - 1) / a.nsets;
+  a.lag = (int32_t)std::min<long long>((per_set_wgs + n1 - 1) / n1 + 1, 1 << 20);
+  const int forced_lag = env_int("SV_LAG", -1);
+  if (forced_lag >= 0) a.lag = forced_lag;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_chain(a, bf16, vec, grid, s) != hipSuccess) return SV_ERR_HIP;
+  if (!a.fused && launch_chain_p2(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+}  // namespace
+}  // namespace sv
+
+extern "C" {
+
+size_t sv_workspace_bytes(int32_t B, int32_t rows, int32_t V) {
+  if (B < 0 || B > SV_MAX_BATCH || rows < 1 || rows > SV_MAX_TREE_NODES || V < 1 || V > (1 << 30)) return 0;
+  return sv::ws_layout(B, rows, sv::max_chunks(V)).total;
+}
+
+sv_status_t sv_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return SV_ERR_NULL_ARG;
+  if ((uintptr_t)workspace % 256 != 0 || workspace_bytes % 4 != 0) return SV_ERR_BAD_ARG;
+  return sv::launch_fill_zero(workspace, workspace_bytes, (hipStream_t)stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+const char* sv_status_string(sv_status_t status) {
+  switch (status) {
+    case SV_OK: return "success";
+    case SV_ERR_NULL_ARG: return "a required pointer is NULL";
+    case SV_ERR_BAD_SHAPE: return "batch, draft length, node count, vocabulary or depth out of range";
+    case SV_ERR_BAD_DTYPE: return "unknown logits dtype";
+    case SV_ERR_BAD_ARG: return "bad stride, offset or alignment";
+    case SV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SV_ERR_HIP: return "HIP runtime or launch failure";
+  }
+  return "unknown status";
+}
+
+sv_status_t spec_verify_sample(const void* target_logits, int64_t target_row_stride, const void* draft_logits,
+                               int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* draft_ids,
+                               const float* temperature, int32_t B, int32_t gamma, int32_t V, uint64_t seed,
+                               uint64_t offset, int32_t* out_tokens, int32_t* out_num_accepted,
+                               const sv_diag_t* diag, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!temperature) return SV_ERR_NULL_ARG;
+  return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, dtype, draft_ids,
+                       temperature, B, gamma, V, seed, offset, out_tokens, out_num_accepted, diag, workspace,
+                       workspace_bytes, stream);
+}
+
+sv_status_t spec_verify_greedy(const void* target_logits, int64_t target_row_stride, sv_dtype_t dtype,
+                               const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
+                               int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
+  return sv::run_chain(target_logits, target_row_stride, nullptr, 0, dtype, draft_ids, nullptr, B, gamma, V, 0, 0,
+                       out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes, stream);
+}
+
+sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_stride, sv_dtype_t dtype,
+                             const int32_t* parents, const int32_t* depth, const int32_t* node_tokens, int32_t B,
+                             int32_t N, int32_t V, int32_t max_depth, int32_t* out_path, int32_t* out_path_len,
+                             int32_t* out_bonus, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!target_logits || !parents || !depth || !node_tokens || !out_path || !out_path_len || !out_bonus)
+    return SV_ERR_NULL_ARG;
+  if (B < 0 || B > SV_MAX_BATCH || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > (1 << 30) || max_depth < 0 ||
+      max_depth >= N)
+    return SV_ERR_BAD_SHAPE;
+  if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_BAD_DTYPE;
+  if (target_row_stride < V) return SV_ERR_BAD_ARG;
+  const size_t need = sv_workspace_bytes(B, N, V);
+  const sv_status_t ws_ok = sv::check_workspace(workspace, workspace_bytes, need);
+  if (ws_ok != SV_OK) return ws_ok;
+  if (B == 0) return SV_OK;
+  const bool bf16 = (dtype == SV_DTYPE_BF16);
+  const int es = bf16 ? 2 : 4;
+  const sv::Tiling tl = sv::pick_tiling((long long)B * N, V, bf16);
+  if ((long long)B * N * tl.nchunks >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
+  const sv::WsLayout L = sv::ws_layout(B, N, sv::max_chunks(V));
+  uint8_t* ws = (uint8_t*)workspace;
+  sv::TreeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.target = (const uint8_t*)target_logits;
+  a.t_stride = target_row_stride * es;
+  a.parents = parents;
+  a.depth = depth;
+  a.tokens = node_tokens;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.max_depth = max_depth;
+  a.chunk = tl.chunk;
+  a.nchunks = tl.nchunks;
+  a.kv = tl.kv;
+  a.out_path = out_path;
+  a.out_path_len = out_path_len;
+  a.out_bonus = out_bonus;
+  a.arrive = (uint32_t*)(ws + L.tree_arrive);
+  a.part = (sv::TreePartial*)(ws + L.tree_part);
+  const bool vec = sv::aligned16(target_logits, a.t_stride);
+  return sv::launch_tree(a, bf16, vec, (hipStream_t)stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+// sv_device.h — device building blocks of the verify kernels (gfx950, wave64).
+//
+// Counter-based random words (Philox4x32-10, Salmon et al. SC'11), the uniform
+// and Gumbel maps, logit loads (bf16 / fp32, 16-byte vectors), and wave /
+// workgroup reductions with fixed trees so that results do not depend on which
+// workgroup computes what.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kThreads = 256;  // threads per workgroup: 4 waves of 64
+constexpr int kWaves = kThreads / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// --------------------------------------------------------------------------
+// Philox4x32-10. c1..c3 and the key are the same for every lane of a row, so
+// the compiler keeps part of the first two rounds on the scalar unit.
+// --------------------------------------------------------------------------
+struct Words4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Words4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                           uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  Words4 o;
+  o.w[0] = c0;
+  o.w[1] = c1;
+  o.w[2] = c2;
+  o.w[3] = c3;
+  return o;
+}
+
+// u = (w >> 8) * 2^-24, exact in fp32, in [0, 1).
+__device__ __forceinline__ float uniform_accept(uint32_t w) {
+  return (float)(w >> 8) * 0x1p-24f;
+}
+
+// Gumbel noise G = -ln(-ln U), U = ((w >> 8) + 0.5) * 2^-24.
+// fp32 cannot hold U near 1, so E = -ln U is formed from whichever of U or
+// t = 1 - U is at most 1/2 (both are exact multiples of 2^-25 there):
+//   U <= 1/2          : E = -ln U;
+//   t < 2^-8          : E = -ln(1 - t) by its series t + t^2/2 + t^3/3 + t^4/4;
+//   otherwise         : E = -ln(1 - t) = -(ln u - e/u) where u = fl(1 - t) and
+//                       e = (u - 1) + t is the exact rounding error of u
+//                       (first-order correction; 1/u by its short series).
+__device__ __forceinline__ float gumbel(uint32_t w) {
+  const uint32_t j = w >> 8;
+  const bool low = j < (1u << 23);
+  const uint32_t k = low ? j : ((1u << 24) - 1u - j);
+  const float z = ((float)k + 0.5f) * 0x1p-24f;  // exact, in (0, 1/2]
+  const float u = 1.0f - z;                      // rounded when !low
+  const float arg = low ? z : u;
+  const float lnarg = __builtin_amdgcn_logf(arg) * kLn2;
+  const float e = (u - 1.0f) + z;                // exact rounding error of u
+  const float inv_u = 1.0f + z * (1.0f + z * (1.0f + z));
+  const float e_log = -(lnarg - e * inv_u);
+  const float e_ser = z * (1.0f + z * (0.5f + z * (0.33333334f + z * 0.25f)));
+  const float E = low ? -lnarg : (z < 0x1p-8f ? e_ser : e_log);
+  return -__builtin_amdgcn_logf(E) * kLn2;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ln(1 - e^x) for x < 0, accurate near x = 0 (Maechler's log1mexp split).
+__device__ __forceinline__ float log1mexp(float x) {
+  return (x > -kLn2) ? logf(-expm1f(x)) : log1pf(-expf(x));
+}
+
+// --------------------------------------------------------------------------
+// Logit access. Elements per 16-byte vector: 8 bf16 or 4 fp32.
+// --------------------------------------------------------------------------
+template <bool BF16>
+struct Elem;
+
+template <>
+struct Elem<true> {
+  static constexpr int kPerVec = 8;
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ float load(const uint8_t* row, int64_t v) {
+    const uint16_t h = *(const uint16_t*)(row + 2 * v);
+    return __uint_as_float((uint32_t)h << 16);
+  }
+  // Unpack one 16-byte vector to 8 floats.
+  __device__ static __forceinline__ void unpack(const u32x4& q, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = __uint_as_float(q[k] << 16);
+      f[2 * k + 1] = __uint_as_float(q[k] & 0xFFFF0000u);
+    }
+  }
+};
+
+template <>
+struct Elem<false> {
+  static constexpr int kPerVec = 4;
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ float load(const uint8_t* row, int64_t v) {
+    return *(const float*)(row + 4 * v);
+  }
+  __device__ static __forceinline__ void unpack(const u32x4& q, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(q[k]);
+  }
+};
+
+__device__ __forceinline__ u32x4 load_vec_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+// --------------------------------------------------------------------------
+// Reductions. Partial log-sum-exp states (M, s) mean sum exp2((l - M) * c)
+// over a set of raw logits l with max M, c = log2(e) / T.
+// --------------------------------------------------------------------------
+struct LseState {
+  float M;
+  float s;
+};
+
+__device__ __forceinline__ LseState lse_merge(LseState a, LseState b, float c) {
+  if (b.M == -INFINITY) return a;
+  if (a.M == -INFINITY) return b;
+  const float M = fmaxf(a.M, b.M);
+  // fp32 addition is commutative, so merge(a, b) and merge(b, a) agree
+  // bitwise: both lanes of a butterfly step hold the same result.
+  const float ta = a.s * fast_exp2((a.M - M) * c);
+  const float tb = b.s * fast_exp2((b.M - M) * c);
+  LseState r;
+  r.M = M;
+  r.s = ta + tb;
+  return r;
+}
+
+struct ArgMax {
+  float v;
+  int32_t i;
+};
+
+// Larger value wins; equal values go to the lower index. Logits are assumed
+// not to be NaN.
+__device__ __forceinline__ ArgMax argmax_merge(ArgMax a, ArgMax b) {
+  if (b.i < 0) return a;
+  if (a.i < 0) return b;
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+__device__ __forceinline__ int shfl_xor_i(int x, int m) { return __shfl_xor(x, m, 64); }
+
+__device__ __forceinline__ LseState wave_lse(LseState a, float c) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    LseState o;
+    o.M = shfl_xor_f(a.M, m);
+    o.s = shfl_xor_f(a.s, m);
+    a = lse_merge(a, o, c);
+  }
+  return a;
+}
+
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    ArgMax o;
+    o.v = shfl_xor_f(a.v, m);
+    o.i = shfl_xor_i(a.i, m);
+    a = argmax_merge(a, o);
+  }
+  return a;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += shfl_xor_f(x, m);
+  return x;
+}
+
+__device__ __forceinline__ int wave_or(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x |= shfl_xor_i(x, m);
+  return x;
+}
+
+// Workgroup id of the XCD (accelerator complex die) this workgroup runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11));  // HW_REG_XCC_ID[3:0]
+}
+
+}  // namespace sv

@@ -1,0 +1,247 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs. Ids, lengths and tree paths bit-exact (sequences the
+oracle marks as Gumbel near-ties or accept knife-edges excused and counted);
+accept probabilities, log-normalizers and residual mass within 1e-5."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import make_chain, make_tree
+
+from gpu_util import compare_chain, oracle_sample, run_sample, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rejection_sampling_verify_amd as rsv
+    rsv.lib()
+    return torch.device("cuda:0")
+
+
+def _report(label, s):
+    print("[parity] %s B=%d excused=%d %s" % (label, s["B"], len(s["excused"]),
+          {k: "%.2g" % v for k, v in s.items() if k.endswith("maxerr")}), flush=True)
+
+
+# -------------------------------------------------------------------------
+# Chains: small and scaled workloads (several chunks and a ragged tail)
+# -------------------------------------------------------------------------
+
+CHAIN_CASES = {
+    # name: kwargs of make_chain
+    "f32_small": dict(B=1, gamma=4, V=1000, bf16=False, seed=1000, target_sigma=2.0, draft_sigma=0.5),
+    "f32_ragged": dict(B=6, gamma=3, V=5003, bf16=False, seed=5, target_sigma=2.0, draft_sigma=0.8,
+                       temperatures=(0.0, 0.6, 1.3), row_stride=5004),
+    "bf16_peaked": dict(B=16, gamma=5, V=32000, bf16=True, seed=6, target_sigma=3.0, boost="peaks", n_boost=5,
+                        boost_value=8.0, draft_scale=0.8, draft_sigma=1.0, temperatures=(0.8,)),
+    "bf16_mixed_ragged": dict(B=24, gamma=8, V=40003, bf16=True, seed=7, target_sigma=3.0, boost="zipf",
+                              draft_sigma=(0.2, 2.0), temperatures=(0.0, 0.7, 1.0), row_stride=40008),
+    "bf16_onehot": dict(B=32, gamma=6, V=50000, bf16=True, seed=8, target_sigma=3.0, one_hot=True,
+                        temperatures=(1.0,)),
+    "bf16_onehot_mixed": dict(B=20, gamma=3, V=9001, bf16=True, seed=9, target_sigma=3.0, one_hot=True,
+                              temperatures=(0.0, 1.0, 0.5)),
+    "bf16_padded_rows": dict(B=8, gamma=4, V=20000, bf16=True, seed=10, target_sigma=3.0, draft_sigma=1.0,
+                             temperatures=(0.0, 1.0), row_stride=20040),
+    "bf16_misaligned_rows": dict(B=6, gamma=2, V=7001, bf16=True, seed=11, target_sigma=3.0, draft_sigma=1.0,
+                                 temperatures=(0.9,), row_stride=7001),
+    "bf16_gamma1": dict(B=40, gamma=1, V=3000, bf16=True, seed=12, target_sigma=1.0, draft_sigma=0.3,
+                        temperatures=(1.0,)),
+    "bf16_gamma16": dict(B=4, gamma=16, V=4096, bf16=True, seed=13, target_sigma=1.0, draft_sigma=0.2,
+                         temperatures=(1.0, 0.0)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CHAIN_CASES))
+def test_chain_parity(dev, name):
+    kw = dict(CHAIN_CASES[name])
+    inp = make_chain(name, kw.pop("B"), kw.pop("gamma"), kw.pop("V"), **kw)
+    got = run_sample(inp, torch, dev)
+    ref = oracle_sample(inp)
+    _report(name, compare_chain(got, ref, label=name))
+
+
+def test_chain_seeds_and_offsets(dev):
+    """Different seeds/offsets change the draws, and every one matches."""
+    inp = make_chain("offsets", 16, 4, 6000, bf16=True, seed=21, target_sigma=2.0, draft_sigma=1.5,
+                     temperatures=(1.0,))
+    outs = []
+    for seed, off in ((0, 0), (0, 1), (123456789012345, 7), (2**64 - 1, 2**31 - 1)):
+        got = run_sample(inp, torch, dev, seed=seed, offset=off)
+        ref = oracle_sample(inp, seed=seed, offset=off)
+        compare_chain(got, ref, label="seed %d off %d" % (seed, off))
+        outs.append(got["tokens"])
+    assert not all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_greedy_entry_point(dev):
+    import rejection_sampling_verify_amd as rsv
+    inp = make_chain("greedy", 64, 5, 30011, bf16=True, seed=22, target_sigma=1.0, draft_sigma=0.05,
+                     temperatures=(0.0,))
+    t = to_dev(inp.target, torch, dev)
+    ids = torch.from_numpy(inp.draft_ids).to(dev)
+    tok, n = rsv.spec_verify_greedy(t, ids)
+    torch.cuda.synchronize()
+    ref = oracle.verify_greedy(inp.target, inp.draft_ids)
+    assert np.array_equal(n.cpu().numpy(), ref["n"])
+    assert np.array_equal(tok.cpu().numpy(), ref["tokens"])
+    # the sampled entry point at temperature 0 gives the same answer
+    got = run_sample(inp, torch, dev)
+    assert np.array_equal(got["tokens"], ref["tokens"]) and np.array_equal(got["n"], ref["n"])
+
+
+def test_greedy_ties_lowest_index(dev):
+    import rejection_sampling_verify_amd as rsv
+    B, G, V = 4, 2, 20000
+    tgt = np.zeros((B, G + 1, V), np.float32)
+    for b in range(B):
+        tgt[b, :, [17 + b, 9000 + b, 19999 - b]] = 3.0  # three-way tie in every row
+    ids = np.array([[17 + b, 9000 + b] for b in range(B)], np.int32)
+    ids[1] = [17 + 1, 17 + 1]
+    t = torch.from_numpy(tgt).to(dev)
+    tok, n = rsv.spec_verify_greedy(t, torch.from_numpy(ids).to(dev))
+    ref = oracle.verify_greedy(tgt, ids)
+    assert np.array_equal(tok.cpu().numpy(), ref["tokens"]) and np.array_equal(n.cpu().numpy(), ref["n"])
+    assert ref["tokens"][0].tolist() == [17, 17, -1]
+
+
+def test_bad_inputs_per_sequence(dev):
+    inp = make_chain("bad", 6, 3, 2000, bf16=True, seed=23, target_sigma=1.0, draft_sigma=0.5,
+                     temperatures=(1.0,))
+    inp.draft_ids[1, 2] = 2000
+    inp.draft_ids[2, 0] = -5
+    inp.temperature[3] = -1.0
+    inp.temperature[4] = np.nan
+    got = run_sample(inp, torch, dev)
+    ref = oracle_sample(inp)
+    assert got["n"].tolist()[1:5] == [-1, -1, -2, -2]
+    assert np.all(got["tokens"][1:5] == -1)
+    compare_chain(got, ref, label="bad")
+
+
+def test_deterministic_and_grid_invariant(dev, monkeypatch):
+    """Bitwise identical outputs across runs, grid sizes, fusion and chunking."""
+    inp = make_chain("grid", 40, 6, 70001, bf16=True, seed=24, target_sigma=3.0, draft_sigma=(0.3, 1.5),
+                     temperatures=(0.0, 0.7, 1.0))
+    base = run_sample(inp, torch, dev)
+    ref = oracle_sample(inp)
+    compare_chain(base, ref, label="grid base")
+    variants = [{"SV_GRID": "1"}, {"SV_GRID": "7"}, {"SV_GRID": "256"}, {"SV_GRID": "2048"},
+                {"SV_FUSED": "0"}, {"SV_LAG": "0"}, {"SV_GRID": "5", "SV_LAG": "0"}, {}]
+    for env in variants:
+        for k in ("SV_GRID", "SV_FUSED", "SV_LAG"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        got = run_sample(inp, torch, dev)
+        for key in ("tokens", "n", "accept_prob", "logz_target", "logz_draft", "residual_mass"):
+            assert np.array_equal(got[key], base[key], equal_nan=True), (env, key)
+    for k in ("SV_GRID", "SV_FUSED", "SV_LAG"):
+        monkeypatch.delenv(k, raising=False)
+    # a different chunk length changes only rounding: still oracle-exact
+    for kv in ("1", "2", "8"):
+        monkeypatch.setenv("SV_KV", kv)
+        compare_chain(run_sample(inp, torch, dev), ref, label="kv " + kv)
+    monkeypatch.delenv("SV_KV", raising=False)
+
+
+def test_workspace_reuse_across_shapes(dev):
+    """One workspace serves calls of different shapes; each call leaves it zero."""
+    import rejection_sampling_verify_amd as rsv
+    ws = rsv.Workspace(dev).get(64, 17, 131072)
+    shapes = [(32, 8, 100000), (3, 2, 500), (64, 16, 131072), (1, 1, 7), (17, 5, 33333)]
+    for k, (B, G, V) in enumerate(shapes):
+        inp = make_chain("ws%d" % k, B, G, V, bf16=True, seed=30 + k, target_sigma=2.0, draft_sigma=1.0,
+                         temperatures=(0.0, 1.0))
+        got = run_sample(inp, torch, dev, workspace=ws)
+        compare_chain(got, oracle_sample(inp), label="ws %s" % (shapes[k],))
+    assert int(ws.count_nonzero().item()) == 0
+
+
+# -------------------------------------------------------------------------
+# Trees
+# -------------------------------------------------------------------------
+
+def _run_tree(inp, dev):
+    import rejection_sampling_verify_amd as rsv
+    t = to_dev(inp.target, torch, dev)
+    par = torch.from_numpy(inp.parents).to(dev)
+    dep = torch.from_numpy(inp.depth).to(dev)
+    tok = torch.from_numpy(inp.node_tokens).to(dev)
+    path, plen, bonus = rsv.spec_verify_tree(t, par, dep, tok, inp.max_depth)
+    torch.cuda.synchronize()
+    return path.cpu().numpy(), plen.cpu().numpy(), bonus.cpu().numpy()
+
+
+def _check_tree(inp, dev):
+    path, plen, bonus = _run_tree(inp, dev)
+    ref = oracle.verify_tree(inp.target, inp.parents, inp.depth, inp.node_tokens, inp.max_depth)
+    assert np.array_equal(plen, ref["path_len"])
+    assert np.array_equal(path, ref["path"])
+    assert np.array_equal(bonus, ref["bonus"])
+    return ref
+
+
+def test_tree_small(dev):
+    parents = np.array([-1, 0, 0, 0, 1, 1, 2, 3, 4, 4, 6], np.int32)
+    depth = np.array(oracle.tree_depths(parents), np.int32)
+    for V, hit in ((50, 0.9), (3001, 0.6), (20000, 0.5)):
+        inp = make_tree("t", 50, V, parents, depth, bf16=True, seed=40 + V, hit=hit)
+        _check_tree(inp, dev)
+
+
+def test_tree_chain_shaped_equals_greedy(dev):
+    import rejection_sampling_verify_amd as rsv
+    inp = make_chain("tchain", 30, 6, 12000, bf16=True, seed=41, target_sigma=1.0, draft_sigma=0.02,
+                     temperatures=(0.0,))
+    parents = np.array([-1] + list(range(6)), np.int32)
+    depth = np.arange(7, dtype=np.int32)
+    tok = np.concatenate([np.zeros((30, 1), np.int32), inp.draft_ids], axis=1)
+    t = to_dev(inp.target, torch, dev)
+    path, plen, bonus = rsv.spec_verify_tree(t, torch.from_numpy(parents).to(dev), torch.from_numpy(depth).to(dev),
+                                             torch.from_numpy(tok).to(dev), 6)
+    gtok, gn = rsv.spec_verify_greedy(t, torch.from_numpy(inp.draft_ids).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(plen.cpu().numpy() - 1, gn.cpu().numpy())
+    gtok = gtok.cpu().numpy()
+    for b in range(30):
+        n = int(gn[b])
+        assert bonus[b].item() == gtok[b, n]
+
+
+def test_tree_malformed(dev):
+    parents = np.array([-1, 0, 2, 1], np.int32)  # node 2 is its own parent
+    depth = np.array([0, 1, 2, 2], np.int32)
+    inp = make_tree("bad", 3, 100, parents, depth, bf16=True, seed=42)
+    path, plen, bonus = _run_tree(inp, dev)
+    assert np.all(plen == -3) and np.all(bonus == -1) and np.all(path == -1)
+
+
+# -------------------------------------------------------------------------
+# The five named workloads at full size
+# -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", workloads.CONFIGS)
+def test_named_workload_full_size(dev, name):
+    inp = workloads.make(name)
+    if name.startswith("tree"):
+        ref = _check_tree(inp, dev)
+        print("[parity] %s B=%d exact; first-match walk differs on %d sequences" %
+              (name, inp.B, int(np.sum(ref["first_match_node"] != ref["path"][np.arange(inp.B), ref["path_len"] - 1]))),
+              flush=True)
+        return
+    got = run_sample(inp, torch, dev)
+    ref = oracle_sample(inp)
+    s = compare_chain(got, ref, label=name)
+    _report(name, s)
+    n = got["n"]
+    print("[parity] %s mean accepted %.3f, emitted/step %.3f" % (name, n.mean(), n.mean() + 1), flush=True)
