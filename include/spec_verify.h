@@ -131,9 +131,10 @@ const char* sv_status_string(sv_status_t status);
  *   instead (same noise). With draft_logits == NULL the draft is one-hot at x_i
  *   ([SB] Exercise 4): a_i = p_i(x_i) and the residual is p_n without x_n.
  * For T == 0 the sequence is verified greedily ([SB] "Extending to a chain of
- * γ draft tokens", its temperature-0 paragraph): x_i is accepted iff it equals argmax_v of target row i (lowest index
- * on ties); the correction is that argmax, the bonus the argmax of row gamma;
- * draft logits and randomness are not used.
+ * γ draft tokens", its temperature-0 paragraph): x_i is accepted iff it
+ * equals argmax_v of target row i (lowest index on ties); the correction is
+ * that argmax, the bonus the argmax of row gamma; draft logits and randomness
+ * are not used.
  *
  * target_logits  [B, gamma+1, V] rows, stride target_row_stride elements.
  * draft_logits   [B, gamma, V] rows, stride draft_row_stride, or NULL.
@@ -197,6 +198,23 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
                              int32_t max_depth, int32_t* out_path, int32_t* out_path_len,
                              int32_t* out_bonus, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * Diagnostic entry points: the random primitives of the kernels, element by
+ * element, so that they can be checked against their definitions. All arrays
+ * are device arrays owned by the caller; work is enqueued on `stream`.
+ *
+ * sv_debug_philox — out[4i..4i+3] = Philox4x32-10(counter ctr[4i..4i+3],
+ *   key key[2i..2i+1]) for i < n (Salmon et al., SC'11).
+ * sv_debug_noise — for each 32-bit word w = words[i], i < n:
+ *   uniform_out[i] = (w >> 8) * 2^-24 (the accept uniform) and
+ *   gumbel_out[i] = -ln(-ln(((w >> 8) + 0.5) * 2^-24)) (the Gumbel noise),
+ *   each output optional (NULL).
+ * Both return SV_ERR_NULL_ARG / SV_ERR_BAD_SHAPE (n < 0) / SV_ERR_HIP.
+ */
+sv_status_t sv_debug_philox(const uint32_t* ctr, const uint32_t* key, uint32_t* out, int32_t n, void* stream);
+sv_status_t sv_debug_noise(const uint32_t* words, float* gumbel_out, float* uniform_out, int32_t n,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,8 @@ from .binding import (  # noqa: F401
     spec_verify_greedy,
     spec_verify_sample,
     spec_verify_tree,
+    sv_debug_noise,
+    sv_debug_philox,
     sv_status_string,
     sv_workspace_bytes,
     sv_workspace_init,

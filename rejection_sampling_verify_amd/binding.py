@@ -11,7 +11,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "librsv_hip.so")
+# SV_LIB_PATH selects another build of the same library (for A/B timing).
+LIB_PATH = os.environ.get("SV_LIB_PATH") or os.path.join(HERE, "librsv_hip.so")
 
 SV_DTYPE_F32 = 0
 SV_DTYPE_BF16 = 1
@@ -21,7 +22,7 @@ SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree"]
+           "spec_verify_greedy", "spec_verify_tree", "sv_debug_philox", "sv_debug_noise"]
 
 _lib = None
 
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_greedy.restype = ctypes.c_int
         L.spec_verify_tree.argtypes = [P, i64, ctypes.c_int, P, P, P, i32, i32, i32, i32, P, P, P, P, sz, P]
         L.spec_verify_tree.restype = ctypes.c_int
+        L.sv_debug_philox.argtypes = [P, P, P, i32, P]
+        L.sv_debug_philox.restype = ctypes.c_int
+        L.sv_debug_noise.argtypes = [P, P, P, i32, P]
+        L.sv_debug_noise.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -226,3 +231,28 @@ def spec_verify_tree(target_logits, parents, depth, node_tokens, max_depth: int,
     if st != 0:
         raise SVError(st, "spec_verify_tree")
     return out_path, out_path_len, out_bonus
+
+
+def sv_debug_philox(ctr, key, out=None, stream=None):
+    """Philox4x32-10 blocks on the device: ctr [n, 4] and key [n, 2] int32
+    tensors (bit patterns of uint32) -> out [n, 4]."""
+    import torch
+    n = ctr.shape[0]
+    if out is None:
+        out = torch.empty((n, 4), dtype=torch.int32, device=ctr.device)
+    st = lib().sv_debug_philox(_ptr(ctr), _ptr(key), _ptr(out), n, _stream(stream))
+    if st != 0:
+        raise SVError(st, "sv_debug_philox")
+    return out
+
+
+def sv_debug_noise(words, stream=None):
+    """Accept uniforms and Gumbel noise of 32-bit words (int32 tensor [n])."""
+    import torch
+    n = words.shape[0]
+    g = torch.empty(n, dtype=torch.float32, device=words.device)
+    u = torch.empty(n, dtype=torch.float32, device=words.device)
+    st = lib().sv_debug_noise(_ptr(words), _ptr(g), _ptr(u), n, _stream(stream))
+    if st != 0:
+        raise SVError(st, "sv_debug_noise")
+    return g, u

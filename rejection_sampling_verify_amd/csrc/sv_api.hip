@@ -22,18 +22,14 @@ int32_t max_chunks(int32_t V) {
 WsLayout ws_layout(int32_t B, int32_t rows, int32_t nchunks) {
   WsLayout L;
   size_t off = 0;
-  L.tickets = off;
-  off += (size_t)kMaxSets * kTicketStride * 4;
   L.done = off;
-  off += 4096;
+  off += 256;
   L.seq = off;
   off = round_up(off + (size_t)B * sizeof(SeqState), 256);
   L.p1 = off;
-  off = round_up(off + (size_t)B * rows * nchunks * sizeof(P1Partial), 256);
-  L.gath = off;
-  off = round_up(off + (size_t)B * rows * sizeof(Gathered), 256);
+  off = round_up(off + (size_t)B * rows * nchunks * sizeof(P1Slot), 256);
   L.p2 = off;
-  off = round_up(off + (size_t)B * nchunks * sizeof(P2Partial), 256);
+  off = round_up(off + (size_t)B * nchunks * sizeof(P2Slot), 256);
   L.tree_arrive = off;
   off = round_up(off + (size_t)B * 4, 256);
   L.tree_part = off;
@@ -156,6 +152,20 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   a.chunk = tl.chunk;
   a.nchunks = tl.nchunks;
   a.kv = tl.kv;
+  // Pass-2 chunks: about one resident workgroup per (sequence, chunk) over the
+  // whole GPU, each at least one pass-1 chunk long.
+  {
+    const long long resident = (long long)cus * occupancy(dev, bf16, vec);
+    long long c2 = (resident + B - 1) / B;
+    const int forced = env_int("SV_P2_CHUNKS", 0);
+    if (forced > 0) c2 = forced;
+    c2 = std::max<long long>(1, std::min<long long>(c2, tl.nchunks));
+    const int unit = kThreads * (bf16 ? 8 : 4);
+    long long len = (V + c2 - 1) / c2;
+    len = (len + unit - 1) / unit * unit;
+    a.p2_chunk = (int32_t)len;
+    a.p2_nchunks = (int32_t)((V + len - 1) / len);
+  }
   a.key0 = (uint32_t)seed;
   a.key1 = (uint32_t)(seed >> 32);
   a.ctr_accept = (uint32_t)(2u * (uint32_t)offset);
@@ -168,27 +178,28 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
     a.d_logzd = diag->logz_draft;
     a.d_beta = diag->residual_mass;
   }
-  a.tickets = (uint32_t*)(ws + L.tickets);
   a.done = (uint32_t*)(ws + L.done);
   a.seq = (SeqState*)(ws + L.seq);
-  a.p1 = (P1Partial*)(ws + L.p1);
-  a.gath = (Gathered*)(ws + L.gath);
-  a.p2 = (P2Partial*)(ws + L.p2);
-  a.nsets = kMaxSets;
+  a.p1 = (P1Slot*)(ws + L.p1);
+  a.p2 = (P2Slot*)(ws + L.p2);
   a.fused = env_int("SV_FUSED", 1) ? 1 : 0;
   a.spin_limit = 1u << 22;
-
-  int grid = env_int("SV_GRID", 0);
-  if (grid <= 0) grid = cus * occupancy(dev, bf16, vec);
+  // Lag: about one full GPU of resident workgroups between the pass-1 items
+  // of a sequence and its pass-2 items, so that they rarely wait.
   const long long n1 = (long long)gamma * tl.nchunks;
-  const long long per_set_wgs = (grid + a.nsets - 1) / a.nsets;
-  a.lag = (int32_t)std::min<long long>((per_set_wgs + n1 - 1) / n1 + 1, 1 << 20);
+  const long long resident = (long long)cus * occupancy(dev, bf16, vec);
+  a.lag = (int32_t)std::min<long long>((resident + n1 - 1) / n1 + 1, 1 << 20);
   const int forced_lag = env_int("SV_LAG", -1);
   if (forced_lag >= 0) a.lag = forced_lag;
 
   hipStream_t s = (hipStream_t)stream;
-  if (launch_chain(a, bf16, vec, grid, s) != hipSuccess) return SV_ERR_HIP;
-  if (!a.fused && launch_chain_p2(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
+  if (a.fused) {
+    if (launch_chain(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
+  } else {
+    // Two launches: pass 1 over every (sequence, position, chunk), then pass 2.
+    if (launch_chain_p1(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
+    if (launch_chain_p2(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
+  }
   return SV_OK;
 }
 

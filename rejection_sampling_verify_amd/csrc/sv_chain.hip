@@ -9,19 +9,22 @@
 //
 // Work decomposition. Every logit row is cut into chunks of `chunk` elements.
 //   pass-1 item (b, i, c): chunk c of target row i (and of draft row i): the
-//     partial log-sum-exp state of each row and, for greedy sequences, the
-//     partial argmax. The last pass-1 item of sequence b to finish takes the
-//     accept decisions of b (it sees every partial), writes the accepted
-//     drafts and publishes which row pass 2 must draw from.
-//   pass-2 item (b, c): chunk c of that row: a partial Gumbel-max (or argmax).
-//     The last one to finish merges the partials and writes the last token.
-// Items are handed out from per-XCD ticket queues by a persistent grid; the
-// pass-2 items of a sequence are queued `lag` sequences behind its pass-1
-// items so that pass 2 runs while other sequences stream pass 1. A pass-2
-// item whose sequence is not decided yet waits; every item it can wait for
-// holds an earlier ticket of the same queue, so it is already running and
-// never waits itself. Merges run in fixed chunk order, so results do not
-// depend on the grid, the queue order or which workgroup finishes last.
+//     partial log-sum-exp state of each row, or for greedy sequences the
+//     partial argmax, published as one 16-byte slot. Nothing waits on it.
+//   pass-2 item (b, c): waits for the gamma * nchunks pass-1 slots of b, takes
+//     the decision of b (every pass-2 item of b computes the same decision
+//     from the same slots; item 0 writes it out), then draws a partial
+//     Gumbel-max (or argmax) over chunk c of the row the decision names. The
+//     last pass-2 item of b to finish merges the partials and writes the last
+//     token.
+// One launch runs both: workgroup ids are laid out in blocks, block k holding
+// the pass-1 items of sequence k followed by the pass-2 items of sequence
+// k - lag, so pass 2 of earlier sequences runs while later ones stream pass 1.
+// The dispatcher starts workgroups in id order, so everything a pass-2 item
+// waits for has a smaller id and is already running; the wait is bounded
+// regardless. Merges run in fixed chunk order, so results do not depend on
+// the launch layout or on which item finishes last. Without fusion the two
+// passes are two launches and nothing waits.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -29,25 +32,31 @@ namespace sv {
 
 namespace {
 
-// ---------------------------------------------------------------------------
-// Shared-memory scratch of one workgroup.
-// ---------------------------------------------------------------------------
+enum SeqKind { KIND_BAD_T = 0, KIND_GREEDY = 1, KIND_SAMPLED = 2, KIND_BAD_ID = 3, KIND_STALLED = 4 };
+
+// The decision of one sequence, as every pass-2 item of it computes it.
+struct Decision {
+  int kind;
+  int n;          // accepted drafts, or the per-sequence error code
+  uint32_t mode;  // P2Mode
+  int row, x;
+  float T, c2, invT;
+  float zt2, zd2;  // log2-domain normalizers of target / draft row `row`
+  float a_row;     // accept probability at `row` (one-hot draft: p(x) there)
+};
+
 struct Smem {
   LseState lse[2][kWaves];
   ArgMax am[kWaves];
   float fsum[kWaves];
   int ior[kWaves];
-  uint32_t ticket;
   uint32_t flag_last;
-  // decision of one sequence
-  int32_t g[kMaxGamma + 1];
+  uint32_t stalled;
+  uint64_t slot[kThreads][2];  // one batch of polled pass-1 slots
+  LseState rt[kMaxGamma], rd[kMaxGamma];
+  ArgMax rg[kMaxGamma];
   int32_t acc[kMaxGamma];
-  float logz2_t[kMaxGamma];
-  float logz2_d[kMaxGamma];
-  // pass-2 parameters broadcast from thread 0
-  uint32_t mode, error;
-  int32_t row, x;
-  float z_t, z_d;
+  Decision dec;
 };
 
 __device__ __forceinline__ LseState block_lse(LseState st, float c, Smem& sm, int slot) {
@@ -98,10 +107,14 @@ __device__ __forceinline__ int block_or(int x, Smem& sm) {
   return r;
 }
 
-// Sequence classification from its temperature.
-enum SeqKind { KIND_BAD_T = 0, KIND_GREEDY = 1, KIND_SAMPLED = 2 };
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor_f(x, m));
+  return x;
+}
 
-__device__ __forceinline__ int seq_kind(const ChainArgs& a, int b, float* T_out) {
+// Sequence classification from its temperature alone.
+__device__ __forceinline__ int temp_kind(const ChainArgs& a, int b, float* T_out) {
   if (a.temperature == nullptr) {
     *T_out = 0.0f;
     return KIND_GREEDY;
@@ -118,6 +131,12 @@ __device__ __forceinline__ const uint8_t* target_row(const ChainArgs& a, int b, 
 __device__ __forceinline__ const uint8_t* draft_row(const ChainArgs& a, int b, int i) {
   return a.draft + ((int64_t)b * a.gamma + i) * a.d_stride;
 }
+
+__device__ __forceinline__ uint64_t pack(float hi, uint32_t lo) {
+  return ((uint64_t)__float_as_uint(hi) << 32) | lo;
+}
+__device__ __forceinline__ float hi_f(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
+__device__ __forceinline__ uint32_t lo_u(uint64_t w) { return (uint32_t)w; }
 
 // ---------------------------------------------------------------------------
 // Chunk loaders. A chunk [lo, hi) is read as 16-byte vectors: thread t holds
@@ -171,7 +190,6 @@ struct Chunk {
   }
 };
 
-// Partial log-sum-exp state of the thread's elements of a loaded chunk.
 template <bool BF16, bool VEC>
 __device__ __forceinline__ LseState chunk_lse(const Chunk<BF16, VEC>& ch, const uint8_t* row, int kv,
                                               float c) {
@@ -203,182 +221,24 @@ __device__ __forceinline__ ArgMax chunk_argmax(const Chunk<BF16, VEC>& ch, const
 }
 
 // ---------------------------------------------------------------------------
-// The decision of sequence b, taken by the last pass-1 item of b.
-// ---------------------------------------------------------------------------
-__device__ void decide(const ChainArgs& a, int b, Smem& sm) {
-  const int G = a.gamma;
-  const int C = a.nchunks;
-  const int tid = threadIdx.x;
-  float T;
-  const int kind = seq_kind(a, b, &T);
-  const int32_t* ids = a.ids + (int64_t)b * G;
-  int32_t* tok = a.out_tokens + (int64_t)b * (G + 1);
-  SeqState* st = a.seq + b;
-  bool bad_id = false;
-  for (int i = 0; i < G; ++i) bad_id |= (ids[i] < 0 || ids[i] >= a.V);
-  const float c2 = (kind == KIND_SAMPLED) ? kLog2e / T : 0.0f;
-
-  if (kind == KIND_GREEDY && !bad_id) {
-    if (tid < G) {
-      ArgMax m;
-      m.v = -INFINITY;
-      m.i = -1;
-      const P1Partial* pp = a.p1 + ((int64_t)b * G + tid) * C;
-      for (int c = 0; c < C; ++c) {
-        ArgMax o;
-        o.v = pp[c].a;
-        o.i = __float_as_int(pp[c].b);
-        m = argmax_merge(m, o);
-      }
-      sm.g[tid] = m.i;
-      if (a.d_accept) a.d_accept[(int64_t)b * G + tid] = (ids[tid] == m.i) ? 1.0f : 0.0f;
-      if (a.d_logzt) a.d_logzt[(int64_t)b * G + tid] = NAN;
-      if (a.d_logzd) a.d_logzd[(int64_t)b * G + tid] = NAN;
-    }
-  } else if (kind == KIND_SAMPLED && !bad_id) {
-    if (tid < G) {
-      LseState mt, md;
-      mt.M = -INFINITY;
-      mt.s = 0.0f;
-      md = mt;
-      const P1Partial* pp = a.p1 + ((int64_t)b * G + tid) * C;
-      for (int c = 0; c < C; ++c) {
-        LseState o;
-        o.M = pp[c].a;
-        o.s = pp[c].b;
-        mt = lse_merge(mt, o, c2);
-        o.M = pp[c].c;
-        o.s = pp[c].d;
-        md = lse_merge(md, o, c2);
-      }
-      const Gathered gx = a.gath[(int64_t)b * G + tid];
-      const float z2t = mt.M * c2 + fast_log2(mt.s);
-      const float lp2 = __builtin_fmaf(gx.lt, c2, -z2t);
-      float z2d = NAN, lq2 = 0.0f;
-      if (a.draft != nullptr) {
-        z2d = md.M * c2 + fast_log2(md.s);
-        lq2 = __builtin_fmaf(gx.ld, c2, -z2d);
-      }
-      const float acc_p = fast_exp2(fminf(0.0f, lp2 - lq2));
-      const Words4 w = philox10(0u, (uint32_t)tid, (uint32_t)b, a.ctr_accept, a.key0, a.key1);
-      const float u = uniform_accept(w.w[0]);
-      sm.acc[tid] = (u < acc_p) ? 1 : 0;
-      sm.logz2_t[tid] = z2t;
-      sm.logz2_d[tid] = z2d;
-      if (a.d_accept) a.d_accept[(int64_t)b * G + tid] = acc_p;
-      if (a.d_logzt) a.d_logzt[(int64_t)b * G + tid] = z2t * kLn2;
-      if (a.d_logzd) a.d_logzd[(int64_t)b * G + tid] = z2d * kLn2;
-    }
-  }
-  __syncthreads();
-
-  if (tid == 0) {
-    uint32_t mode = P2_NONE;
-    int row = 0, x = -1;
-    float zt = 0.0f, zd = 0.0f;
-    if (kind == KIND_BAD_T || bad_id) {
-      for (int i = 0; i <= G; ++i) tok[i] = -1;
-      a.out_n[b] = (kind == KIND_BAD_T) ? -2 : -1;
-      if (a.d_accept || a.d_logzt || a.d_logzd) {
-        for (int i = 0; i < G; ++i) {
-          if (a.d_accept) a.d_accept[(int64_t)b * G + i] = NAN;
-          if (a.d_logzt) a.d_logzt[(int64_t)b * G + i] = NAN;
-          if (a.d_logzd) a.d_logzd[(int64_t)b * G + i] = NAN;
-        }
-      }
-      if (a.d_beta) a.d_beta[b] = NAN;
-    } else if (kind == KIND_GREEDY) {
-      int n = G;
-      for (int i = 0; i < G; ++i)
-        if (ids[i] != sm.g[i]) {
-          n = i;
-          break;
-        }
-      for (int i = 0; i < n; ++i) tok[i] = ids[i];
-      for (int i = n + 1; i <= G; ++i) tok[i] = -1;
-      a.out_n[b] = n;
-      if (n < G) {
-        tok[n] = sm.g[n];
-      } else {
-        mode = P2_GREEDY_BONUS;
-        row = G;
-      }
-      if (a.d_beta) a.d_beta[b] = NAN;
-    } else {
-      int n = G;
-      for (int i = 0; i < G; ++i)
-        if (!sm.acc[i]) {
-          n = i;
-          break;
-        }
-      for (int i = 0; i < n; ++i) tok[i] = ids[i];
-      for (int i = n + 1; i <= G; ++i) tok[i] = -1;
-      a.out_n[b] = n;
-      if (n < G) {
-        mode = (a.draft != nullptr) ? P2_RESIDUAL : P2_RESIDUAL_ONEHOT;
-        row = n;
-        x = ids[n];
-        zt = sm.logz2_t[n];
-        zd = sm.logz2_d[n];
-      } else {
-        mode = P2_BONUS;
-        row = G;
-        if (a.d_beta) a.d_beta[b] = NAN;
-      }
-    }
-    st->mode = mode;
-    st->n = a.out_n[b];
-    st->row = row;
-    st->x = x;
-    st->logz2_t = zt;
-    st->logz2_d = zd;
-  }
-  // Pass-1 scratch of b is consumed: return it to zero.
-  for (int k = tid; k < G * C; k += kThreads) {
-    P1Partial z;
-    z.a = z.b = z.c = z.d = 0.0f;
-    a.p1[(int64_t)b * G * C + k] = z;
-  }
-  for (int k = tid; k < G; k += kThreads) {
-    Gathered z;
-    z.lt = z.ld = 0.0f;
-    a.gath[(int64_t)b * G + k] = z;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    st->p1_arrive = 0;
-    __threadfence();
-    __hip_atomic_store(&st->flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Pass 1: one chunk of one row pair.
+// Pass 1: one chunk of one row pair; publishes its slot and moves on.
 // ---------------------------------------------------------------------------
 template <bool BF16, bool VEC>
 __device__ void pass1_item(const ChainArgs& a, int b, int i, int c, Smem& sm) {
-  const int tid = threadIdx.x;
   float T;
-  const int kind = seq_kind(a, b, &T);
+  const int kind = temp_kind(a, b, &T);
+  if (kind == KIND_BAD_T) return;  // nobody reads the slots of such a sequence
   const int lo = c * a.chunk;
   const int hi = min(a.V, lo + a.chunk);
-  const int x = a.ids[(int64_t)b * a.gamma + i];
-  P1Partial out;
-  out.a = out.b = out.c = out.d = 0.0f;
-  Gathered gx;
-  gx.lt = gx.ld = 0.0f;
-  const bool owns_x = (x >= lo && x < hi);
-
+  const uint8_t* rt = target_row(a, b, i);
+  uint64_t w0, w1 = 1u;
   if (kind == KIND_GREEDY) {
-    const uint8_t* rt = target_row(a, b, i);
     Chunk<BF16, VEC> ct;
     ct.load(rt, lo, hi, a.kv);
     const ArgMax m = block_argmax(chunk_argmax(ct, rt, a.kv), sm);
-    out.a = m.v;
-    out.b = __int_as_float(m.i);
-  } else if (kind == KIND_SAMPLED) {
+    w0 = pack(m.v, (uint32_t)(m.i + 1));
+  } else {
     const float c2 = kLog2e / T;
-    const uint8_t* rt = target_row(a, b, i);
     Chunk<BF16, VEC> ct;
     ct.load(rt, lo, hi, a.kv);
     if (a.draft != nullptr) {
@@ -387,38 +247,205 @@ __device__ void pass1_item(const ChainArgs& a, int b, int i, int c, Smem& sm) {
       cd.load(rd, lo, hi, a.kv);
       const LseState lt = block_lse(chunk_lse(ct, rt, a.kv, c2), c2, sm, 0);
       const LseState ld = block_lse(chunk_lse(cd, rd, a.kv, c2), c2, sm, 1);
-      out.a = lt.M;
-      out.b = lt.s;
-      out.c = ld.M;
-      out.d = ld.s;
-      if (owns_x && tid == 0) {
-        gx.lt = Elem<BF16>::load(rt, x);
-        gx.ld = Elem<BF16>::load(rd, x);
-      }
+      w0 = pack(lt.M, __float_as_uint(lt.s));
+      w1 = pack(ld.M, __float_as_uint(ld.s));
     } else {
       const LseState lt = block_lse(chunk_lse(ct, rt, a.kv, c2), c2, sm, 0);
-      out.a = lt.M;
-      out.b = lt.s;
-      out.c = -INFINITY;
-      if (owns_x && tid == 0) gx.lt = Elem<BF16>::load(rt, x);
+      w0 = pack(lt.M, __float_as_uint(lt.s));
     }
   }
-  // A sequence with a bad temperature contributes nothing but its arrival.
+  if (threadIdx.x == 0) {
+    P1Slot* dst = a.p1 + ((int64_t)b * a.gamma + i) * a.nchunks + c;
+    xput64(&dst->w0, w0);
+    xput64(&dst->w1, w1);
+  }
+}
 
+// ---------------------------------------------------------------------------
+// The decision of sequence b from its pass-1 slots (all threads take part).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ void take_decision(const ChainArgs& a, int b, Smem& sm) {
+  const int G = a.gamma, C = a.nchunks, tid = threadIdx.x;
+  const int32_t* ids = a.ids + (int64_t)b * G;
+  float T;
+  int kind = temp_kind(a, b, &T);
+  const float c2 = (kind == KIND_SAMPLED) ? kLog2e / T : 0.0f;
+  // Inputs the decision needs besides the slots are requested first, so that
+  // they arrive while the slots are polled.
+  bool bad_id = false;
+  for (int i = 0; i < G; ++i) bad_id |= (ids[i] < 0 || ids[i] >= a.V);
+  float glt = 0.0f, gld = 0.0f;
+  if (tid < G && kind == KIND_SAMPLED && !bad_id) {
+    const int x = ids[tid];
+    glt = Elem<BF16>::load(target_row(a, b, tid), x);
+    if (a.draft != nullptr) gld = Elem<BF16>::load(draft_row(a, b, tid), x);
+  }
+  if (tid == 0) sm.stalled = 0u;
+  if (tid < G) {
+    sm.rt[tid].M = -INFINITY;
+    sm.rt[tid].s = 0.0f;
+    sm.rd[tid] = sm.rt[tid];
+    sm.rg[tid].v = -INFINITY;
+    sm.rg[tid].i = -1;
+  }
+  __syncthreads();
+  if (kind != KIND_BAD_T) {
+    // Wait for every slot (also when a drafted id turns out to be invalid, so
+    // that no slot can land after the sequence's scratch has been cleared),
+    // 256 at a time, and merge each row's chunks in order.
+    P1Slot* slots = a.p1 + (int64_t)b * G * C;
+    const int total = G * C;
+    for (int base = 0; base < total; base += kThreads) {
+      const int k = base + tid;
+      if (k < total) {
+        uint64_t w0 = xget64(&slots[k].w0), w1 = xget64(&slots[k].w1);
+        uint32_t spins = 0;
+        while (w0 == 0u || w1 == 0u) {
+          // A bounded wait: give up after spin_limit rounds, or soon after
+          // any other wait of this call gave up.
+          if (++spins > a.spin_limit || ((spins & 255u) == 0u && xget(&a.done[1]) != 0u)) {
+            atomicOr(&a.done[1], 1u);
+            sm.stalled = 1u;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+          w0 = xget64(&slots[k].w0);
+          w1 = xget64(&slots[k].w1);
+        }
+        sm.slot[tid][0] = w0;
+        sm.slot[tid][1] = w1;
+      }
+      __syncthreads();
+      if (tid < G) {
+        const int r0 = max(tid * C, base), r1 = min(tid * C + C, base + kThreads);
+        for (int r = r0; r < r1; ++r) {
+          const uint64_t w0 = sm.slot[r - base][0], w1 = sm.slot[r - base][1];
+          if (kind == KIND_GREEDY) {
+            ArgMax o;
+            o.v = hi_f(w0);
+            o.i = (int)lo_u(w0) - 1;
+            sm.rg[tid] = argmax_merge(sm.rg[tid], o);
+          } else {
+            LseState o;
+            o.M = hi_f(w0);
+            o.s = __uint_as_float(lo_u(w0));
+            sm.rt[tid] = lse_merge(sm.rt[tid], o, c2);
+            o.M = hi_f(w1);
+            o.s = __uint_as_float(lo_u(w1));
+            sm.rd[tid] = lse_merge(sm.rd[tid], o, c2);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (kind != KIND_BAD_T && bad_id) kind = KIND_BAD_ID;
+  if (sm.stalled) kind = KIND_STALLED;
+
+  // Accept tests, one thread per position.
+  if (tid < G && kind == KIND_SAMPLED) {
+    const float z2t = sm.rt[tid].M * c2 + fast_log2(sm.rt[tid].s);
+    const float lp2 = __builtin_fmaf(glt, c2, -z2t);
+    float z2d = NAN, lq2 = 0.0f;
+    if (a.draft != nullptr) {
+      z2d = sm.rd[tid].M * c2 + fast_log2(sm.rd[tid].s);
+      lq2 = __builtin_fmaf(gld, c2, -z2d);
+    }
+    const float acc_p = fast_exp2(fminf(0.0f, lp2 - lq2));
+    const Words4 w = philox10(0u, (uint32_t)tid, (uint32_t)b, a.ctr_accept, a.key0, a.key1);
+    sm.acc[tid] = (uniform_accept(w.w[0]) < acc_p) ? 1 : 0;
+    sm.rt[tid].M = z2t;  // from here on: the row normalizers and a_i
+    sm.rd[tid].M = z2d;
+    sm.rt[tid].s = acc_p;
+  }
+  __syncthreads();
   if (tid == 0) {
-    a.p1[((int64_t)b * a.gamma + i) * a.nchunks + c] = out;
-    if (owns_x && kind == KIND_SAMPLED) a.gath[(int64_t)b * a.gamma + i] = gx;
-    __threadfence();
-    const uint32_t old = atomicAdd(&a.seq[b].p1_arrive, 1u);
-    const bool last = (old == (uint32_t)(a.gamma * a.nchunks) - 1u);
-    sm.flag_last = last ? 1u : 0u;
+    Decision d;
+    d.kind = kind;
+    d.T = T;
+    d.c2 = c2;
+    d.invT = (kind == KIND_SAMPLED) ? 1.0f / T : 0.0f;
+    d.mode = P2_NONE;
+    d.row = 0;
+    d.x = -1;
+    d.zt2 = d.zd2 = 0.0f;
+    d.a_row = 0.0f;
+    if (kind == KIND_BAD_T) {
+      d.n = -2;
+    } else if (kind == KIND_BAD_ID) {
+      d.n = -1;
+    } else if (kind == KIND_STALLED) {
+      d.n = -4;
+    } else if (kind == KIND_GREEDY) {
+      d.n = G;
+      for (int i = 0; i < G; ++i)
+        if (ids[i] != sm.rg[i].i) {
+          d.n = i;
+          break;
+        }
+      if (d.n == G) {
+        d.mode = P2_GREEDY_BONUS;
+        d.row = G;
+      }
+    } else {
+      d.n = G;
+      for (int i = 0; i < G; ++i)
+        if (!sm.acc[i]) {
+          d.n = i;
+          break;
+        }
+      if (d.n < G) {
+        d.mode = (a.draft != nullptr) ? P2_RESIDUAL : P2_RESIDUAL_ONEHOT;
+        d.row = d.n;
+        d.x = ids[d.n];
+        d.zt2 = sm.rt[d.n].M;
+        d.zd2 = sm.rd[d.n].M;
+        d.a_row = sm.rt[d.n].s;
+      } else {
+        d.mode = P2_BONUS;
+        d.row = G;
+      }
+    }
+    sm.dec = d;
   }
   __syncthreads();
-  if (sm.flag_last) {
-    __threadfence();
-    decide(a, b, sm);
+}
+
+// Writes everything the decision fixes (pass-2 item 0 of b does this). The
+// token at position n is left to the last pass-2 item when a draw is pending.
+__device__ void write_decision(const ChainArgs& a, int b, Smem& sm) {
+  const int G = a.gamma, tid = threadIdx.x;
+  const Decision& d = sm.dec;
+  const int32_t* ids = a.ids + (int64_t)b * G;
+  int32_t* tok = a.out_tokens + (int64_t)b * (G + 1);
+  if (tid <= G) {
+    const bool pending = d.n >= 0 && tid == d.n && d.mode != P2_NONE;
+    if (!pending) {
+      int v = -1;
+      if (d.n >= 0) {
+        if (tid < d.n) v = ids[tid];
+        else if (tid == d.n) v = sm.rg[tid].i;  // greedy correction
+      }
+      tok[tid] = v;
+    }
   }
-  __syncthreads();
+  if (tid == 0) a.out_n[b] = d.n;
+  if (tid < G) {
+    const int64_t k = (int64_t)b * G + tid;
+    float ap = NAN, lzt = NAN, lzd = NAN;
+    if (d.kind == KIND_GREEDY) {
+      ap = (ids[tid] == sm.rg[tid].i) ? 1.0f : 0.0f;
+    } else if (d.kind == KIND_SAMPLED) {
+      ap = sm.rt[tid].s;
+      lzt = sm.rt[tid].M * kLn2;
+      lzd = sm.rd[tid].M * kLn2;
+    }
+    if (a.d_accept) a.d_accept[k] = ap;
+    if (a.d_logzt) a.d_logzt[k] = lzt;
+    if (a.d_logzd) a.d_logzd[k] = lzd;
+  }
+  if (tid == 0 && a.d_beta && d.mode != P2_RESIDUAL && d.mode != P2_RESIDUAL_ONEHOT) a.d_beta[b] = NAN;
 }
 
 // ---------------------------------------------------------------------------
@@ -436,87 +463,181 @@ __device__ __forceinline__ void best_push(Best& bst, float s, int idx) {
   }
 }
 
-// Gumbel-max (or argmax) partial over chunk [lo, hi) of the pass-2 row. This
-// pass is bound by arithmetic (a Philox block per 4 entries and two logs per
-// entry), so vectors are loaded one at a time inside a rolled loop to keep
-// registers low and let more waves share each SIMD.
-template <bool BF16, bool VEC>
-__device__ void pass2_chunk(const ChainArgs& a, int b, uint32_t mode, int row, int x, float zt, float zd,
-                            float T, int lo, int hi, Smem& sm, P2Partial* out) {
+// Exact pruning of the Gumbel-max draw. With E = -ln U, the noise is
+// G = -ln E and E >= 1 - U. An element of score s can beat a total L already
+// reached by some element of the row only if E < exp(s - L), hence only if
+// 1 - U < exp(s - L). With r = 2^24 - 1 - (w >> 8), 1 - U = (2r + 1) 2^-25,
+// which is at least 2^(floor(log2(2r + 1)) - 25). An element is therefore
+// skipped, without evaluating G, when floor(log2(2r + 1)) - 25 exceeds
+// log2(exp(s - L)) by more than a margin covering fp32 rounding; the draw is
+// unchanged. (The test loses at most a factor of two against the exact bound.)
+constexpr float kPruneMarginLog2 = 0x1p-12f;
+
+__device__ __forceinline__ bool may_win_log2(uint32_t w, float x2) {
+  const uint32_t odd = ((~w) >> 7) | 1u;        // 2r + 1
+  const int e = 31 - __builtin_clz(odd);        // floor(log2(2r + 1))
+  return !((float)(e - 25) > x2 + kPruneMarginLog2);
+}
+
+// Same test from a weight eps = exp(s - L) already computed in linear form.
+__device__ __forceinline__ bool may_win_lin(uint32_t w, float eps) {
+  const uint32_t odd = ((~w) >> 7) | 1u;
+  const float t = (float)odd * 0x1p-25f;        // 1 - U (exact below 2^24)
+  return !(t > eps * (1.0f + 0x1p-12f));
+}
+
+// One chunk of a Gumbel-max draw, specialised on what the score of an element
+// is (MODE = P2_RESIDUAL: ln(p - q) where p > q; P2_RESIDUAL_ONEHOT: l/T for
+// v != x; P2_BONUS: l/T). For each 16-byte vector the lane forms the Philox
+// words and the pruning test of its elements; the exact score and noise are
+// evaluated only when some element survives (rare once the bound has risen),
+// lowest index first. Vectors are prefetched three deep.
+template <bool BF16, bool VEC, int MODE>
+__device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm, P2Slot* out) {
   using E = Elem<BF16>;
   constexpr int EV = E::kPerVec;
-  const uint8_t* rt = target_row(a, b, row);
-
-  if (mode == P2_GREEDY_BONUS) {
-    Chunk<BF16, VEC> ct;
-    ct.load(rt, lo, hi, a.kv);
-    const ArgMax m = block_argmax(chunk_argmax(ct, rt, a.kv), sm);
-    out->score = m.v;
-    out->idx = m.i;
-    out->beta = 0.0f;
-    out->any = 1;
-    return;
-  }
-
-  const float c2 = kLog2e / T;
-  const float invT = 1.0f / T;
-  const uint32_t crow = (uint32_t)row, cseq = (uint32_t)b;
-  const bool residual = (mode == P2_RESIDUAL);
-  const bool onehot = (mode == P2_RESIDUAL_ONEHOT);
-  const uint8_t* rd = residual ? draft_row(a, b, row) : nullptr;
+  constexpr bool residual = (MODE == P2_RESIDUAL);
+  constexpr bool onehot = (MODE == P2_RESIDUAL_ONEHOT);
+  const uint8_t* rt = target_row(a, b, dec.row);
+  const uint8_t* rd = residual ? draft_row(a, b, dec.row) : nullptr;
+  const float c2 = dec.c2, invT = dec.invT, zt2 = dec.zt2, zd2 = dec.zd2;
+  const int xex = dec.x;
+  const uint32_t crow = (uint32_t)dec.row, cseq = (uint32_t)b;
+  const uint32_t ctr3 = a.ctr_noise, k0 = a.key0, k1 = a.key1;
   Best bst;
   bst.s = -INFINITY;
   bst.i = -1;
   float beta = 0.0f;
   int any = residual ? 0 : 1;
+  float L = -INFINITY;    // best total this wave has reached in the row
+  float nL2 = INFINITY;   // -L log2(e)
+  float scale = INFINITY; // exp(-L), for the residual's linear test
 
-  // One element: lt / ld raw logits, g its Gumbel noise.
-  auto visit = [&](float lt, float ld, float g, int idx) {
+  auto refresh = [&]() {
+    L = wave_max(L);
+    nL2 = -L * kLog2e;
+    if (residual) scale = fast_exp2(nL2);
+  };
+
+  // Residual mass and candidacy of one element (residual mode only).
+  auto accumulate = [&](float lt, float ld, float& r_out) -> bool {
+    const float lp2 = __builtin_fmaf(lt, c2, -zt2);
+    const float lq2 = __builtin_fmaf(ld, c2, -zd2);
+    const bool cand = lp2 > lq2;
+    const float p = fast_exp2(lp2), q = fast_exp2(lq2);
+    const float r = cand ? p - q : 0.0f;
+    beta += r;
+    any |= cand ? 1 : 0;
+    r_out = cand ? __builtin_fmaf(p, 0x1p-22f, r) : 0.0f;  // bound on p - q
+    return cand;
+  };
+  // Pruning test; r is the residual bound from accumulate().
+  auto test = [&](float lt, float r, uint32_t w, int idx) -> bool {
+    if (residual) return r > 0.0f && may_win_lin(w, r * scale);
+    if (onehot && idx == xex) return false;
+    return may_win_log2(w, __builtin_fmaf(lt, c2, nL2));  // log2 exp(l/T - L)
+  };
+  // Exact score and noise of a surviving element.
+  auto full = [&](float lt, float ld, uint32_t w, int idx) {
+    float s;
     if (residual) {
-      const float lp2 = __builtin_fmaf(lt, c2, -zt);
-      const float lq2 = __builtin_fmaf(ld, c2, -zd);
-      if (lp2 > lq2) {
-        const float r = lp2 * kLn2 + log1mexp((lq2 - lp2) * kLn2);  // ln (p - q)
-        beta += __expf(r);
-        any = 1;
-        best_push(bst, r + g, idx);
-      }
+      const float lp2 = __builtin_fmaf(lt, c2, -zt2);
+      const float lq2 = __builtin_fmaf(ld, c2, -zd2);
+      s = lp2 * kLn2 + log1mexp((lq2 - lp2) * kLn2);  // ln (p - q)
     } else {
-      if (onehot) {
-        if (idx == x) return;
-        beta += fast_exp2(__builtin_fmaf(lt, c2, -zt));
-      }
-      best_push(bst, lt * invT + g, idx);
+      s = lt * invT;
     }
+    const float tot = s + gumbel(w);
+    best_push(bst, tot, idx);
+    L = fmaxf(L, tot);
   };
 
   if (VEC) {
     const int nfull = (hi - lo) / EV;
-#pragma unroll 1
-    for (int vi = (int)threadIdx.x; vi < nfull; vi += kThreads) {
-      const int base = lo + vi * EV;
-      float vt[EV], vd[EV];
-      E::unpack(load_vec_stream(rt + (int64_t)base * E::kBytes), vt);
-      if (residual) E::unpack(load_vec_stream(rd + (int64_t)base * E::kBytes), vd);
-#pragma unroll
-      for (int g4 = 0; g4 < EV; g4 += 4) {
-        const Words4 w = philox10((uint32_t)(base + g4) >> 2, crow, cseq, a.ctr_noise, a.key0, a.key1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) visit(vt[g4 + e], residual ? vd[g4 + e] : 0.0f, gumbel(w.w[e]), base + g4 + e);
+    // Three vectors per lane in flight: vector r is processed while vectors
+    // r+1 and r+2 are still arriving (a rotating set of registers).
+    u32x4 qt0, qt1, qt2, qd0, qd1, qd2;
+    const int vi0 = (int)threadIdx.x;
+    auto fetch = [&](int vi, u32x4& qt, u32x4& qd) {
+      if (vi < nfull) {
+        qt = load_vec_stream(rt + (int64_t)(lo + vi * EV) * E::kBytes);
+        if (residual) qd = load_vec_stream(rd + (int64_t)(lo + vi * EV) * E::kBytes);
       }
+    };
+    fetch(vi0, qt0, qd0);
+    fetch(vi0 + kThreads, qt1, qd1);
+    const int rounds = (nfull + kThreads - 1) / kThreads;  // same for every lane
+#pragma unroll 1
+    for (int rnd = 0; rnd < rounds; ++rnd) {
+      const int vi = vi0 + rnd * kThreads;
+      fetch(vi + 2 * kThreads, qt2, qd2);
+      if (vi < nfull) {
+        const int base = lo + vi * EV;
+        float vt[EV], vd[EV], rr[EV];
+        uint32_t wd[EV];
+        E::unpack(qt0, vt);
+        if (residual) E::unpack(qd0, vd);
+        if (EV == 8) {  // two blocks per vector, computed side by side
+          Words4 wa, wb;
+          philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            wd[e] = wa.w[e];
+            wd[4 + e] = wb.w[e];
+          }
+        } else {
+          const Words4 w4 = philox10((uint32_t)base >> 2, crow, cseq, ctr3, k0, k1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wd[e] = w4.w[e];
+        }
+        bool surv = false;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          rr[e] = 0.0f;
+          if (residual) accumulate(vt[e], vd[e], rr[e]);
+          surv |= test(vt[e], rr[e], wd[e], base + e);
+        }
+        if (surv) {
+#pragma unroll
+          for (int e = 0; e < EV; ++e)
+            if (test(vt[e], rr[e], wd[e], base + e)) full(vt[e], residual ? vd[e] : 0.0f, wd[e], base + e);
+        }
+      }
+      qt0 = qt1;
+      qt1 = qt2;
+      if (residual) {
+        qd0 = qd1;
+        qd1 = qd2;
+      }
+      if ((rnd & 3) == 0 || rnd + 1 == rounds) refresh();
     }
     const int tail_lo = lo + nfull * EV;
     if (tail_lo < hi && (nfull % kThreads) == (int)threadIdx.x) {
       for (int idx = tail_lo; idx < hi; ++idx) {
-        const Words4 w = philox10((uint32_t)idx >> 2, crow, cseq, a.ctr_noise, a.key0, a.key1);
-        visit(E::load(rt, idx), residual ? E::load(rd, idx) : 0.0f, gumbel(w.w[idx & 3]), idx);
+        const Words4 w4 = philox10((uint32_t)idx >> 2, crow, cseq, ctr3, k0, k1);
+        const uint32_t w = word_at(w4, idx & 3);
+        const float lt = E::load(rt, idx), ld = residual ? E::load(rd, idx) : 0.0f;
+        float r = 0.0f;
+        if (residual) accumulate(lt, ld, r);
+        if (test(lt, r, w, idx)) full(lt, ld, w, idx);
       }
     }
   } else {
+    const int n = hi - lo;
+    int rnd = 0;
 #pragma unroll 1
-    for (int idx = lo + (int)threadIdx.x; idx < hi; idx += kThreads) {
-      const Words4 w = philox10((uint32_t)idx >> 2, crow, cseq, a.ctr_noise, a.key0, a.key1);
-      visit(E::load(rt, idx), residual ? E::load(rd, idx) : 0.0f, gumbel(w.w[idx & 3]), idx);
+    for (int k0i = 0; k0i < n; k0i += kThreads, ++rnd) {
+      const int k = k0i + (int)threadIdx.x;
+      if (k < n) {
+        const int idx = lo + k;
+        const Words4 w4 = philox10((uint32_t)idx >> 2, crow, cseq, ctr3, k0, k1);
+        const uint32_t w = word_at(w4, idx & 3);
+        const float lt = E::load(rt, idx), ld = residual ? E::load(rd, idx) : 0.0f;
+        float r = 0.0f;
+        if (residual) accumulate(lt, ld, r);
+        if (test(lt, r, w, idx)) full(lt, ld, w, idx);
+      }
+      if ((rnd & 3) == 0 || k0i + kThreads >= n) refresh();
     }
   }
   ArgMax m;
@@ -525,168 +646,152 @@ __device__ void pass2_chunk(const ChainArgs& a, int b, uint32_t mode, int row, i
   m = block_argmax(m, sm);
   const float bsum = block_sum(beta, sm);
   const int bany = block_or(any, sm);
-  out->score = m.v;
-  out->idx = m.i;
-  out->beta = bsum;
-  out->any = bany;
+  out->w0 = pack(m.v, (uint32_t)m.i);
+  out->w1 = pack(bsum, (uint32_t)bany);
 }
 
-// Last pass-2 item of b: merge the chunk partials and write the last token.
+template <bool BF16, bool VEC>
+__device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo, int hi, Smem& sm, P2Slot* out) {
+  if (d.mode == P2_GREEDY_BONUS) {
+    const uint8_t* rt = target_row(a, b, d.row);
+    ArgMax best;
+    best.v = -INFINITY;
+    best.i = -1;
+    for (int lo2 = lo; lo2 < hi; lo2 += a.chunk) {  // in pass-1 sized pieces
+      Chunk<BF16, VEC> ct;
+      ct.load(rt, lo2, min(hi, lo2 + a.chunk), a.kv);
+      best = argmax_merge(best, chunk_argmax(ct, rt, a.kv));
+    }
+    const ArgMax m = block_argmax(best, sm);
+    out->w0 = pack(m.v, (uint32_t)m.i);
+    out->w1 = pack(0.0f, 1u);
+  } else if (d.mode == P2_RESIDUAL) {
+    gumbel_chunk<BF16, VEC, P2_RESIDUAL>(a, b, d, lo, hi, sm, out);
+  } else if (d.mode == P2_RESIDUAL_ONEHOT) {
+    gumbel_chunk<BF16, VEC, P2_RESIDUAL_ONEHOT>(a, b, d, lo, hi, sm, out);
+  } else {
+    gumbel_chunk<BF16, VEC, P2_BONUS>(a, b, d, lo, hi, sm, out);
+  }
+}
+
+// Last pass-2 item of b: merge the chunk partials, write the last token and
+// return the sequence's scratch to zero.
 template <bool BF16, bool VEC>
 __device__ void finalize(const ChainArgs& a, int b, Smem& sm) {
-  const int C = a.nchunks;
-  const int G = a.gamma;
-  SeqState* st = a.seq + b;
-  const uint32_t mode = sm.mode;
-  if (sm.error) {
-    if (threadIdx.x == 0) {
-      for (int i = 0; i <= G; ++i) a.out_tokens[(int64_t)b * (G + 1) + i] = -1;
-      a.out_n[b] = -4;
-    }
-  } else if (mode != P2_NONE) {
-    const P2Partial* pp = a.p2 + (int64_t)b * C;
+  const int C2 = a.p2_nchunks, G = a.gamma, C = a.nchunks;
+  const Decision d = sm.dec;
+  P2Slot* ps = a.p2 + (int64_t)b * C2;
+  if (d.mode != P2_NONE) {
+    // Read every partial at once, then merge them in chunk order.
     ArgMax m;
     m.v = -INFINITY;
     m.i = -1;
     float beta = 0.0f;
     int any = 0;
-    for (int c = 0; c < C; ++c) {  // fixed order
-      ArgMax o;
-      o.v = pp[c].score;
-      o.i = pp[c].any ? pp[c].idx : -1;
-      m = argmax_merge(m, o);
-      beta += pp[c].beta;
-      any |= pp[c].any;
-    }
-    if (mode == P2_RESIDUAL && !any) {
-      // Empty residual (only through rounding): draw from p at the row instead.
-      float T;
-      seq_kind(a, b, &T);
-      m.v = -INFINITY;
-      m.i = -1;
-      for (int c = 0; c < C; ++c) {
-        P2Partial part;
-        const int lo = c * a.chunk;
-        pass2_chunk<BF16, VEC>(a, b, P2_BONUS, sm.row, -1, 0.0f, 0.0f, T, lo, min(a.V, lo + a.chunk), sm,
-                               &part);
-        ArgMax o;
-        o.v = part.score;
-        o.i = part.idx;
-        m = argmax_merge(m, o);
+    for (int base = 0; base < C2; base += kThreads) {
+      const int c = base + (int)threadIdx.x;
+      if (c < C2) {
+        sm.slot[threadIdx.x][0] = xget64(&ps[c].w0);
+        sm.slot[threadIdx.x][1] = xget64(&ps[c].w1);
       }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        for (int k = 0; k < min(kThreads, C2 - base); ++k) {
+          const uint64_t w0 = sm.slot[k][0], w1 = sm.slot[k][1];
+          const int an = (int)lo_u(w1);
+          ArgMax o;
+          o.v = hi_f(w0);
+          o.i = an ? (int)lo_u(w0) : -1;
+          m = argmax_merge(m, o);
+          beta += hi_f(w1);
+          any |= an;
+        }
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) sm.ior[0] = any;
+    __syncthreads();
+    any = sm.ior[0];
+    __syncthreads();
+    if (d.mode == P2_RESIDUAL && !any) {
+      // Empty residual (only through rounding): draw from p at the row instead.
+      Decision fb = d;
+      fb.mode = P2_BONUS;
+      ArgMax f;
+      f.v = -INFINITY;
+      f.i = -1;
+      for (int c = 0; c < C2; ++c) {
+        P2Slot part;
+        const int lo = c * a.p2_chunk;
+        pass2_chunk<BF16, VEC>(a, b, fb, lo, min(a.V, lo + a.p2_chunk), sm, &part);
+        ArgMax o;
+        o.v = hi_f(part.w0);
+        o.i = (int)lo_u(part.w0);
+        f = argmax_merge(f, o);
+      }
+      m = f;
       beta = 0.0f;
     }
     if (threadIdx.x == 0) {
-      int32_t* tok = a.out_tokens + (int64_t)b * (G + 1);
-      tok[st->n] = m.i;
-      if (a.d_beta && (mode == P2_RESIDUAL || mode == P2_RESIDUAL_ONEHOT)) a.d_beta[b] = beta;
+      a.out_tokens[(int64_t)b * (G + 1) + d.n] = m.i;
+      // One-hot draft: (p - delta_x)_+ has mass 1 - p(x) exactly.
+      if (a.d_beta && d.mode == P2_RESIDUAL) a.d_beta[b] = beta;
+      if (a.d_beta && d.mode == P2_RESIDUAL_ONEHOT) a.d_beta[b] = 1.0f - d.a_row;
     }
   }
-  // Return the sequence's scratch to zero.
-  for (int k = threadIdx.x; k < C; k += kThreads) {
-    P2Partial z;
-    z.score = 0.0f;
-    z.idx = 0;
-    z.beta = 0.0f;
-    z.any = 0;
-    a.p2[(int64_t)b * C + k] = z;
-  }
-  if (threadIdx.x == 0) {
-    st->mode = 0;
-    st->row = 0;
-    st->x = 0;
-    st->logz2_t = 0.0f;
-    st->logz2_d = 0.0f;
-    st->error = 0;
-    st->n = 0;
-    st->p2_arrive = 0;
-    st->flag = 0;
-    __threadfence();
-  }
-  __syncthreads();
+  uint64_t* w1 = (uint64_t*)(a.p1 + (int64_t)b * G * C);
+  for (int k = threadIdx.x; k < G * C * 2; k += kThreads) xput64(&w1[k], 0u);
+  uint64_t* w2 = (uint64_t*)ps;
+  for (int k = threadIdx.x; k < C2 * 2; k += kThreads) xput64(&w2[k], 0u);
+  if (threadIdx.x == 0) xput(&a.seq[b].p2_arrive, 0u);
 }
 
 template <bool BF16, bool VEC>
-__device__ void pass2_item(const ChainArgs& a, int b, int c, bool wait, Smem& sm) {
-  SeqState* st = a.seq + b;
-  if (threadIdx.x == 0) {
-    uint32_t err = 0;
-    if (wait) {
-      uint32_t spins = 0;
-      while (__hip_atomic_load(&st->flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-        __builtin_amdgcn_s_sleep(2);
-        // Give up after spin_limit rounds, or at once after any other wait
-        // of this call gave up, so that a broken invariant cannot hang the GPU.
-        if (++spins > a.spin_limit ||
-            ((spins & 255u) == 0u && __hip_atomic_load(&a.done[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-          err = 1;
-          atomicOr(&a.done[1], 1u);
-          break;
-        }
-      }
-    }
-    __threadfence();
-    sm.mode = st->mode;
-    sm.row = st->row;
-    sm.x = st->x;
-    sm.z_t = st->logz2_t;
-    sm.z_d = st->logz2_d;
-    sm.error = err;
-  }
-  __syncthreads();
-  const uint32_t mode = sm.mode;
-  P2Partial part;
-  part.score = -INFINITY;
-  part.idx = -1;
-  part.beta = 0.0f;
-  part.any = 0;
-  if (mode != P2_NONE && !sm.error) {
-    float T;
-    seq_kind(a, b, &T);
-    const int lo = c * a.chunk;
-    pass2_chunk<BF16, VEC>(a, b, mode, sm.row, sm.x, sm.z_t, sm.z_d, T, lo, min(a.V, lo + a.chunk), sm, &part);
+__device__ void pass2_item(const ChainArgs& a, int b, int c, Smem& sm) {
+  take_decision<BF16>(a, b, sm);
+  if (c == 0) write_decision(a, b, sm);
+  const Decision d = sm.dec;
+  P2Slot part;
+  part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
+  part.w1 = 0u;
+  if (d.mode != P2_NONE) {
+    const int lo = c * a.p2_chunk;
+    pass2_chunk<BF16, VEC>(a, b, d, lo, min(a.V, lo + a.p2_chunk), sm, &part);
   }
   if (threadIdx.x == 0) {
-    if (sm.error) atomicOr(&st->error, 1u);
-    a.p2[(int64_t)b * a.nchunks + c] = part;
-    __threadfence();
-    const uint32_t old = atomicAdd(&st->p2_arrive, 1u);
-    sm.flag_last = (old == (uint32_t)a.nchunks - 1u) ? 1u : 0u;
+    P2Slot* dst = a.p2 + (int64_t)b * a.p2_nchunks + c;
+    xput64(&dst->w0, part.w0);
+    xput64(&dst->w1, part.w1);
+    wait_vmem();  // the slot (and item 0's outputs) have landed first
+    const uint32_t old = atomicAdd(&a.seq[b].p2_arrive, 1u);
+    sm.flag_last = (old == (uint32_t)a.p2_nchunks - 1u) ? 1u : 0u;
   }
   __syncthreads();
-  if (sm.flag_last) {
-    __threadfence();
-    if (threadIdx.x == 0) sm.error = __hip_atomic_load(&st->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    finalize<BF16, VEC>(a, b, sm);
-  }
+  if (sm.flag_last) finalize<BF16, VEC>(a, b, sm);
   __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// Ticket queues. Queue X serves sequences b = X, X + nsets, ...; its item list
-// is laid out in blocks: block k holds the pass-1 items of local sequence k
-// (when k < m) followed by the pass-2 items of local sequence k - lag (when
-// that exists). Without fusion only pass-1 items are queued.
+// Fused launch layout. Block k holds the pass-1 items of sequence k (when
+// k < B) followed by the pass-2 items of sequence k - lag (when that exists).
 // ---------------------------------------------------------------------------
-struct QueueShape {
-  int m;       // sequences in the queue
+struct Layout {
+  int m;       // sequences
   int n1, n2;  // items per sequence of each pass
   int L;       // effective lag
-  __device__ __forceinline__ uint32_t total() const { return (uint32_t)m * (uint32_t)(n1 + n2); }
 };
 
-__device__ __forceinline__ QueueShape queue_shape(const ChainArgs& a, int X) {
-  QueueShape q;
-  q.m = (X < a.B) ? (a.B - X + a.nsets - 1) / a.nsets : 0;
+__device__ __forceinline__ Layout fused_layout(const ChainArgs& a) {
+  Layout q;
+  q.m = a.B;
   q.n1 = a.gamma * a.nchunks;
-  q.n2 = a.fused ? a.nchunks : 0;
+  q.n2 = a.p2_nchunks;
   q.L = min(a.lag, q.m);
   return q;
 }
 
-// Decode ticket t of queue X: returns pass (1 or 2), local sequence and item.
-__device__ __forceinline__ int decode_ticket(const QueueShape& q, uint32_t t, int* k, int* r) {
+// Workgroup id t -> pass (1 or 2), sequence and item.
+__device__ __forceinline__ int decode_item(const Layout& q, uint32_t t, int* k, int* r) {
   const uint32_t seg_a = (uint32_t)q.L * q.n1;
   if (t < seg_a) {
     *k = (int)(t / q.n1);
@@ -717,60 +822,33 @@ __device__ __forceinline__ int decode_ticket(const QueueShape& q, uint32_t t, in
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   __shared__ Smem sm;
-  const int tid = threadIdx.x;
-  const int home = (int)(xcc_id() % (uint32_t)a.nsets);
-  int X = home, tries = 0;
-  if (tid == 0) sm.ticket = atomicAdd(&a.tickets[X * kTicketStride], 1u);
-  __syncthreads();
-  uint32_t t = sm.ticket;
-  __syncthreads();
-  while (true) {
-    QueueShape q = queue_shape(a, X);
-    if (t >= q.total()) {
-      if (++tries == a.nsets) break;
-      X = (home + tries) % a.nsets;
-      if (tid == 0) sm.ticket = atomicAdd(&a.tickets[X * kTicketStride], 1u);
-      __syncthreads();
-      t = sm.ticket;
-      __syncthreads();
-      continue;
-    }
-    // Ask for the next ticket now; the answer is only needed after this item.
-    uint32_t next = 0;
-    if (tid == 0) next = atomicAdd(&a.tickets[X * kTicketStride], 1u);
-    int k, r;
-    const int pass = decode_ticket(q, t, &k, &r);
-    const int b = k * a.nsets + X;
-    if (pass == 1)
-      pass1_item<BF16, VEC>(a, b, r / a.nchunks, r % a.nchunks, sm);
-    else
-      pass2_item<BF16, VEC>(a, b, r, true, sm);
-    if (tid == 0) sm.ticket = next;
-    __syncthreads();
-    t = sm.ticket;
-    __syncthreads();
-  }
-  // The last workgroup to leave returns the queue counters to zero.
-  if (tid == 0) {
-    __threadfence();
-    const uint32_t old = atomicAdd(&a.done[0], 1u);
-    if (old == gridDim.x - 1u) {
-      __threadfence();
-      for (int s = 0; s < kMaxSets; ++s) a.tickets[s * kTicketStride] = 0u;
-      a.done[0] = 0u;
-      a.done[1] = 0u;
-      __threadfence();
-    }
-  }
+  const Layout q = fused_layout(a);
+  int k, r;
+  const int pass = decode_item(q, blockIdx.x, &k, &r);
+  if (pass == 1)
+    pass1_item<BF16, VEC>(a, k, r / a.nchunks, r % a.nchunks, sm);
+  else
+    pass2_item<BF16, VEC>(a, k, r, sm);
 }
 
-// Pass 2 as its own launch (no waiting): one workgroup per (b, chunk).
+// Pass 1 as its own launch: one workgroup per (b, position, chunk), handed
+// out by the hardware dispatcher in sequence order.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void chain_p1_kernel(ChainArgs a) {
+  __shared__ Smem sm;
+  const int per_seq = a.gamma * a.nchunks;
+  const int b = blockIdx.x / per_seq;
+  const int r = blockIdx.x % per_seq;
+  pass1_item<BF16, VEC>(a, b, r / a.nchunks, r % a.nchunks, sm);
+}
+
+// Pass 2 as its own launch (no waiting needed): one workgroup per (b, chunk).
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
   __shared__ Smem sm;
-  const int b = blockIdx.x / a.nchunks;
-  const int c = blockIdx.x % a.nchunks;
-  pass2_item<BF16, VEC>(a, b, c, false, sm);
+  const int b = blockIdx.x / a.p2_nchunks;
+  const int c = blockIdx.x % a.p2_nchunks;
+  pass2_item<BF16, VEC>(a, b, c, sm);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t nwords) {
@@ -779,14 +857,21 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t nwords) {
 }
 
 template <bool BF16, bool VEC>
-hipError_t launch_chain_t(const ChainArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((chain_kernel<BF16, VEC>), dim3(grid), dim3(kThreads), 0, stream, a);
+hipError_t launch_chain_t(const ChainArgs& a, hipStream_t stream) {
+  const long long grid = (long long)a.B * ((long long)a.gamma * a.nchunks + a.p2_nchunks);
+  hipLaunchKernelGGL((chain_kernel<BF16, VEC>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool VEC>
+hipError_t launch_chain_p1_t(const ChainArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((chain_p1_kernel<BF16, VEC>), dim3(a.B * a.gamma * a.nchunks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool BF16, bool VEC>
 hipError_t launch_chain_p2_t(const ChainArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((chain_p2_kernel<BF16, VEC>), dim3(a.B * a.nchunks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((chain_p2_kernel<BF16, VEC>), dim3(a.B * a.p2_nchunks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -799,9 +884,14 @@ int occupancy_t() {
 
 }  // namespace
 
-hipError_t launch_chain(const ChainArgs& a, bool bf16, bool vec, int grid, hipStream_t stream) {
-  if (bf16) return vec ? launch_chain_t<true, true>(a, grid, stream) : launch_chain_t<true, false>(a, grid, stream);
-  return vec ? launch_chain_t<false, true>(a, grid, stream) : launch_chain_t<false, false>(a, grid, stream);
+hipError_t launch_chain(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream) {
+  if (bf16) return vec ? launch_chain_t<true, true>(a, stream) : launch_chain_t<true, false>(a, stream);
+  return vec ? launch_chain_t<false, true>(a, stream) : launch_chain_t<false, false>(a, stream);
+}
+
+hipError_t launch_chain_p1(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream) {
+  if (bf16) return vec ? launch_chain_p1_t<true, true>(a, stream) : launch_chain_p1_t<true, false>(a, stream);
+  return vec ? launch_chain_p1_t<false, true>(a, stream) : launch_chain_p1_t<false, false>(a, stream);
 }
 
 hipError_t launch_chain_p2(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream) {

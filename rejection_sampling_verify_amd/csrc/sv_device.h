@@ -50,6 +50,50 @@ __device__ __forceinline__ Words4 philox10(uint32_t c0, uint32_t c1, uint32_t c2
   return o;
 }
 
+// Two independent Philox4x32-10 blocks (counters differing only in word 0),
+// with their rounds interleaved so that one block's multiplies issue while
+// the other's are in flight.
+__device__ __forceinline__ void philox10x2(uint32_t a0, uint32_t b0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                           uint32_t k0, uint32_t k1, Words4& wa, Words4& wb) {
+  uint32_t a1 = c1, a2 = c2, a3 = c3, b1 = c1, b2 = c2, b3 = c3;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t pa0 = (uint64_t)0xD2511F53u * a0;
+    const uint64_t pb0 = (uint64_t)0xD2511F53u * b0;
+    const uint64_t pa1 = (uint64_t)0xCD9E8D57u * a2;
+    const uint64_t pb1 = (uint64_t)0xCD9E8D57u * b2;
+    const uint32_t na0 = (uint32_t)(pa1 >> 32) ^ a1 ^ k0;
+    const uint32_t nb0 = (uint32_t)(pb1 >> 32) ^ b1 ^ k0;
+    const uint32_t na2 = (uint32_t)(pa0 >> 32) ^ a3 ^ k1;
+    const uint32_t nb2 = (uint32_t)(pb0 >> 32) ^ b3 ^ k1;
+    a1 = (uint32_t)pa1;
+    b1 = (uint32_t)pb1;
+    a3 = (uint32_t)pa0;
+    b3 = (uint32_t)pb0;
+    a0 = na0;
+    b0 = nb0;
+    a2 = na2;
+    b2 = nb2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  wa.w[0] = a0;
+  wa.w[1] = a1;
+  wa.w[2] = a2;
+  wa.w[3] = a3;
+  wb.w[0] = b0;
+  wb.w[1] = b1;
+  wb.w[2] = b2;
+  wb.w[3] = b3;
+}
+
+// Word k (0..3) of a block, by selects rather than an indexed array.
+__device__ __forceinline__ uint32_t word_at(const Words4& w, int k) {
+  const uint32_t lo = (k & 1) ? w.w[1] : w.w[0];
+  const uint32_t hi = (k & 1) ? w.w[3] : w.w[2];
+  return (k & 2) ? hi : lo;
+}
+
 // u = (w >> 8) * 2^-24, exact in fp32, in [0, 1).
 __device__ __forceinline__ float uniform_accept(uint32_t w) {
   return (float)(w >> 8) * 0x1p-24f;
@@ -202,7 +246,32 @@ __device__ __forceinline__ int wave_or(int x) {
   return x;
 }
 
-// Workgroup id of the XCD (accelerator complex die) this workgroup runs on.
+// --------------------------------------------------------------------------
+// Cross-workgroup exchange. Workgroups on different XCDs do not share an L2,
+// and agent-scope fences make coherent by writing back and invalidating the
+// whole L2 of the XCD, which costs far more than the data exchanged here.
+// Instead every word one workgroup hands to another is written and read with
+// atomic read-modify-write operations, which the device performs at its
+// coherence point for all XCDs; a wave that must publish data before a
+// signal waits for its outstanding memory operations to complete first.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ void xput(uint32_t* p, uint32_t v) { atomicExch(p, v); }
+__device__ __forceinline__ void xput(int32_t* p, int32_t v) { atomicExch(p, v); }
+__device__ __forceinline__ void xput(float* p, float v) { atomicExch((uint32_t*)p, __float_as_uint(v)); }
+__device__ __forceinline__ uint32_t xget(uint32_t* p) { return atomicOr(p, 0u); }
+__device__ __forceinline__ int32_t xget(int32_t* p) { return atomicOr(p, 0); }
+__device__ __forceinline__ float xget(float* p) { return __uint_as_float(atomicOr((uint32_t*)p, 0u)); }
+// 64-bit words: device-scope atomic loads and stores (single-copy atomic).
+__device__ __forceinline__ void xput64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t xget64(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// All vector memory operations of this wave (loads, stores, atomics) done.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Index of the XCD (accelerator complex die) this workgroup runs on.
 __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11));  // HW_REG_XCC_ID[3:0]
 }

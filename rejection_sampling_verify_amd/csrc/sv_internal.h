@@ -8,8 +8,6 @@
 
 namespace sv {
 
-constexpr int kMaxSets = 8;           // ticket queues (one per XCD of an MI355X)
-constexpr int kTicketStride = 1024;   // words between ticket counters (4 KiB)
 constexpr int kMaxVecsPerThread = 8;  // 16-byte vectors per thread per row chunk
 constexpr int kMaxGamma = 16;
 constexpr int kMaxTreeNodes = 1024;
@@ -23,35 +21,27 @@ enum P2Mode : uint32_t {
   P2_GREEDY_BONUS = 4     // argmax of row gamma
 };
 
-// Per-sequence record in the workspace (64 bytes). All fields are zero
-// between calls.
+// Per-sequence record in the workspace (64 bytes). Zero between calls.
 struct SeqState {
-  uint32_t p1_arrive;  // pass-1 items finished
   uint32_t p2_arrive;  // pass-2 items finished
-  uint32_t flag;       // 1 once the decision and the fields below are published
-  uint32_t mode;       // P2Mode
-  int32_t row;         // row position of the pass-2 draw
-  int32_t x;           // drafted id at `row` (excluded by the one-hot residual)
-  float logz2_t;       // log2-domain normalizer of target row `row`
-  float logz2_d;       // same for the draft row
-  uint32_t error;      // nonzero: a bounded wait gave up
-  int32_t n;           // accepted drafts
-  uint32_t pad[6];
+  uint32_t pad[15];
 };
 
-struct P1Partial {  // sampled rows: (Mt, st, Md, sd); greedy rows: (value, index bits, 0, 0)
-  float a, b, c, d;
+// Pass-1 result of one chunk of one row pair, published as two 64-bit words
+// that are never zero once written (so a reader can wait for them):
+//   sampled:  w0 = (M_target bits << 32) | s_target bits,
+//             w1 = (M_draft bits << 32) | s_draft bits  (dense draft) or 1;
+//   greedy:   w0 = (max value bits << 32) | (argmax + 1), w1 = 1.
+// M is the chunk's largest raw logit and s = sum exp2((l - M) * log2(e) / T)
+// (>= 1, so the word is nonzero even when M = +0.0).
+struct P1Slot {
+  uint64_t w0, w1;
 };
 
-struct Gathered {  // raw logits of the drafted id in its target / draft row
-  float lt, ld;
-};
-
-struct P2Partial {
-  float score;
-  int32_t idx;
-  float beta;
-  int32_t any;  // the chunk held at least one candidate
+// Pass-2 result of one chunk: w0 = (score bits << 32) | index (0xffffffff:
+// no candidate), w1 = (residual mass bits << 32) | candidate flag.
+struct P2Slot {
+  uint64_t w0, w1;
 };
 
 struct TreePartial {
@@ -67,9 +57,11 @@ struct ChainArgs {
   const int32_t* ids;          // [B, gamma]
   const float* temperature;    // [B] or NULL: every sequence greedy
   int32_t B, gamma, V;
-  int32_t chunk;    // elements per chunk
-  int32_t nchunks;  // chunks per row
-  int32_t kv;       // 16-byte vectors per thread per chunk (<= kMaxVecsPerThread)
+  int32_t chunk;    // elements per pass-1 chunk
+  int32_t nchunks;  // pass-1 chunks per row
+  int32_t kv;       // 16-byte vectors per thread per pass-1 chunk (<= kMaxVecsPerThread)
+  int32_t p2_chunk;    // elements per pass-2 chunk
+  int32_t p2_nchunks;  // pass-2 chunks per row
   uint32_t key0, key1;
   uint32_t ctr_accept, ctr_noise;  // counter word 3 of the two Philox streams
   int32_t* out_tokens;
@@ -78,15 +70,12 @@ struct ChainArgs {
   float* d_logzt;
   float* d_logzd;
   float* d_beta;
-  uint32_t* tickets;  // [kMaxSets * kTicketStride]
-  uint32_t* done;     // [0]: workgroups finished; [1]: a bounded wait gave up
+  uint32_t* done;     // [1]: nonzero once a bounded wait of a call gave up (sticky)
   SeqState* seq;      // [B]
-  P1Partial* p1;      // [B, gamma, nchunks]
-  Gathered* gath;     // [B, gamma]
-  P2Partial* p2;      // [B, nchunks]
-  int32_t nsets;
-  int32_t lag;        // pass-2 items of local sequence k follow pass-1 items of k + lag
-  int32_t fused;      // pass-2 items share the ticket queues with pass 1
+  P1Slot* p1;         // [B, gamma, nchunks]
+  P2Slot* p2;         // [B, p2_nchunks]
+  int32_t lag;        // pass-2 items of sequence k follow the pass-1 items of k + lag
+  int32_t fused;      // one launch for both passes
   uint32_t spin_limit;
 };
 
@@ -107,14 +96,15 @@ struct TreeArgs {
 
 // Workspace carve-up; every offset is a multiple of 256 bytes.
 struct WsLayout {
-  size_t tickets, done, seq, p1, gath, p2, tree_arrive, tree_part, total;
+  size_t done, seq, p1, p2, tree_arrive, tree_part, total;
 };
 
 WsLayout ws_layout(int32_t B, int32_t rows, int32_t nchunks);
 int32_t max_chunks(int32_t V);
 
 // Launchers (host). Return hipSuccess or the first HIP error.
-hipError_t launch_chain(const ChainArgs& a, bool bf16, bool vec, int grid, hipStream_t stream);
+hipError_t launch_chain(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream);
+hipError_t launch_chain_p1(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_chain_p2(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);

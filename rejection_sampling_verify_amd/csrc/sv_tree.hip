@@ -10,7 +10,7 @@
 //
 // One workgroup per (sequence, node, chunk) computes a partial argmax; the
 // last one of a sequence merges them in fixed order and walks the tree. No
-// workgroup waits on another.
+// workgroup waits on another; partials travel through exchange operations.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -82,11 +82,12 @@ __device__ void tree_decide(const TreeArgs& a, int b, TreeSmem& sm) {
     ArgMax m;
     m.v = -INFINITY;
     m.i = -1;
-    const TreePartial* pp = a.part + ((int64_t)b * N + node) * C;
+    TreePartial* pp = a.part + ((int64_t)b * N + node) * C;
+#pragma unroll 4
     for (int c = 0; c < C; ++c) {
       ArgMax o;
-      o.v = pp[c].v;
-      o.i = pp[c].i;
+      o.v = xget(&pp[c].v);
+      o.i = xget(&pp[c].i);
       m = argmax_merge(m, o);
     }
     sm.g[node] = m.i;
@@ -134,13 +135,9 @@ __device__ void tree_decide(const TreeArgs& a, int b, TreeSmem& sm) {
     }
   }
   // Return the scratch of b to zero.
-  for (int k = tid; k < N * C; k += kThreads) {
-    TreePartial z;
-    z.v = 0.0f;
-    z.i = 0;
-    a.part[(int64_t)b * N * C + k] = z;
-  }
-  if (tid == 0) a.arrive[b] = 0u;
+  uint32_t* words = (uint32_t*)(a.part + (int64_t)b * N * C);
+  for (int k = tid; k < N * C * 2; k += kThreads) xput(&words[k], 0u);
+  if (tid == 0) xput(&a.arrive[b], 0u);
 }
 
 template <bool BF16, bool VEC>
@@ -161,19 +158,15 @@ __global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
   if (threadIdx.x == 0) {
     ArgMax t = sm.am[0];
     for (int k = 1; k < kWaves; ++k) t = argmax_merge(t, sm.am[k]);
-    TreePartial p;
-    p.v = t.v;
-    p.i = t.i;
-    a.part[((int64_t)b * a.N + node) * a.nchunks + c] = p;
-    __threadfence();
+    TreePartial* p = a.part + ((int64_t)b * a.N + node) * a.nchunks + c;
+    xput(&p->v, t.v);
+    xput(&p->i, t.i);
+    wait_vmem();
     const uint32_t old = atomicAdd(&a.arrive[b], 1u);
     sm.last = (old == (uint32_t)per_seq - 1u) ? 1u : 0u;
   }
   __syncthreads();
-  if (sm.last) {
-    __threadfence();
-    tree_decide(a, b, sm);
-  }
+  if (sm.last) tree_decide(a, b, sm);
 }
 
 template <bool BF16, bool VEC>

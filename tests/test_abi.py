@@ -1,0 +1,108 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every entry point
+include/spec_verify.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+rsv = pytest.importorskip("rejection_sampling_verify_amd")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:sv_status_t|size_t|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rsv.LIB_PATH):
+        pytest.skip("library not built")
+    return rsv.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert set(names) >= {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree", "sv_workspace_bytes",
+                          "sv_workspace_init", "sv_status_string", "sv_debug_philox", "sv_debug_noise"}
+    out = subprocess.run(["nm", "-D", "--defined-only", rsv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(rsv.binding.EXPORTS) == names
+
+
+def test_status_strings(L):
+    for code in range(7):
+        assert rsv.sv_status_string(code)
+    assert rsv.sv_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes(L):
+    a = rsv.sv_workspace_bytes(256, 9, 128256)
+    assert a > 0 and a % 256 == 0
+    assert rsv.sv_workspace_bytes(512, 9, 128256) > a
+    assert rsv.sv_workspace_bytes(0, 9, 1000) > 0
+    for bad in ((-1, 9, 1000), (1, 0, 1000), (1, 9, 0), (1, 2000, 10)):
+        assert rsv.sv_workspace_bytes(*bad) == 0
+
+
+class _Fake:
+    """Host memory standing in for device pointers: validation never reads them."""
+
+    def __init__(self, nbytes=1 << 16):
+        self.buf = ctypes.create_string_buffer(nbytes + 256)
+        addr = ctypes.addressof(self.buf)
+        self.ptr = ctypes.c_void_p((addr + 255) // 256 * 256)
+        self.nbytes = nbytes
+
+
+def _sample(L, **kw):
+    f = _Fake(1 << 20)
+    args = dict(target=f.ptr, ts=1000, draft=f.ptr, ds=1000, dtype=1, ids=f.ptr, temp=f.ptr, B=4, gamma=3,
+                V=1000, seed=0, offset=0, tok=f.ptr, n=f.ptr, diag=None, ws=f.ptr, wsb=f.nbytes, stream=None)
+    args.update(kw)
+    return L.spec_verify_sample(args["target"], args["ts"], args["draft"], args["ds"], args["dtype"], args["ids"],
+                                args["temp"], args["B"], args["gamma"], args["V"], args["seed"], args["offset"],
+                                args["tok"], args["n"], args["diag"], args["ws"], args["wsb"], args["stream"])
+
+
+def test_sample_argument_validation(L):
+    assert _sample(L, target=None) == 1
+    assert _sample(L, ids=None) == 1
+    assert _sample(L, temp=None) == 1
+    assert _sample(L, gamma=0) == 2 and _sample(L, gamma=17) == 2
+    assert _sample(L, V=0) == 2 and _sample(L, B=-1) == 2
+    assert _sample(L, dtype=7) == 3
+    assert _sample(L, ts=999) == 4 and _sample(L, ds=10) == 4
+    assert _sample(L, offset=1 << 31) == 4
+    assert _sample(L, ws=None) == 5 and _sample(L, wsb=100) == 5
+    f = _Fake(1 << 20)
+    assert _sample(L, ws=ctypes.c_void_p(f.ptr.value + 16)) == 4  # misaligned workspace
+    assert _sample(L, B=0) == 0  # nothing to do, nothing launched
+
+
+def test_greedy_and_tree_argument_validation(L):
+    f = _Fake(1 << 20)
+    P = f.ptr
+    assert L.spec_verify_greedy(None, 100, 1, P, 2, 2, 100, P, P, P, f.nbytes, None) == 1
+    assert L.spec_verify_greedy(P, 100, 1, P, 2, 0, 100, P, P, P, f.nbytes, None) == 2
+    assert L.spec_verify_greedy(P, 50, 1, P, 2, 2, 100, P, P, P, f.nbytes, None) == 4
+    assert L.spec_verify_greedy(P, 100, 1, P, 0, 2, 100, P, P, P, f.nbytes, None) == 0
+    tree = lambda **k: L.spec_verify_tree(k.get("t", P), k.get("ts", 100), k.get("dt", 1), k.get("par", P), P, P,
+                                          k.get("B", 2), k.get("N", 5), k.get("V", 100), k.get("md", 3), P, P, P,
+                                          k.get("ws", P), k.get("wsb", f.nbytes), None)
+    assert tree(par=None) == 1
+    assert tree(N=0) == 2 and tree(N=1025) == 2 and tree(md=5) == 2 and tree(md=-1) == 2
+    assert tree(dt=2) == 3
+    assert tree(ts=99) == 4
+    assert tree(wsb=10) == 5
+    assert tree(B=0) == 0
+    assert L.sv_debug_philox(None, P, P, 1, None) == 1
+    assert L.sv_debug_noise(P, None, None, -1, None) == 2
+    assert L.sv_workspace_init(None, 1024, None) == 1

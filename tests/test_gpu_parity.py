@@ -129,14 +129,15 @@ def test_bad_inputs_per_sequence(dev):
 
 
 def test_deterministic_and_grid_invariant(dev, monkeypatch):
-    """Bitwise identical outputs across runs, grid sizes, fusion and chunking."""
+    """Bitwise identical outputs across runs, launch layouts (one fused launch
+    with any lag, or two launches) and chunking."""
     inp = make_chain("grid", 40, 6, 70001, bf16=True, seed=24, target_sigma=3.0, draft_sigma=(0.3, 1.5),
                      temperatures=(0.0, 0.7, 1.0))
     base = run_sample(inp, torch, dev)
     ref = oracle_sample(inp)
     compare_chain(base, ref, label="grid base")
-    variants = [{"SV_GRID": "1"}, {"SV_GRID": "7"}, {"SV_GRID": "256"}, {"SV_GRID": "2048"},
-                {"SV_FUSED": "0"}, {"SV_LAG": "0"}, {"SV_GRID": "5", "SV_LAG": "0"}, {}]
+    variants = [{"SV_FUSED": "0"}, {"SV_LAG": "0"}, {"SV_LAG": "1"}, {"SV_LAG": "3"}, {"SV_LAG": "100000"},
+                {"SV_FUSED": "0", "SV_LAG": "0"}, {}]
     for env in variants:
         for k in ("SV_GRID", "SV_FUSED", "SV_LAG"):
             monkeypatch.delenv(k, raising=False)
