@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified positions/s + logit-read GB/s (% of HBM peak), B=256 γ=8 V=128256"
 HBM_PEAK_GBPS = 8000.0
+COPY_BYTES = 1 << 30
 DEFAULT_WORKLOAD = "chain_bf16_llama"
 KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_chain.hip", "rejection_sampling_verify_amd/csrc/sv_tree.hip",
                   "rejection_sampling_verify_amd/csrc/sv_device.h", "rejection_sampling_verify_amd/csrc/sv_internal.h",
@@ -80,6 +81,17 @@ def cpu_baseline(inp, is_tree: bool, positions_per_step: int):
             "sample": "the whole workload (one step), %d run(s), median %.3f s, fp64 plain loops" % (len(times), t)}
 
 
+def copy_calibration(torch, dev, steps: int):
+    """Copies of a 1 GiB buffer into another: each launch reads and writes
+    exactly COPY_BYTES, the yardstick for the HBM byte counters."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +99,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run device-to-device copies of a known size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -98,6 +112,9 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev, args.steps)
+        return
     rsv.lib()
     inp = workloads.make(args.workload)
     is_tree = args.workload.startswith("tree")

@@ -28,6 +28,10 @@
  *    counter (c0, position, sequence, 2*offset + stream);
  *  - an empty residual (only reachable through rounding) falls back to p;
  *  - a tree accepts its deepest valid node, smallest index among equals.
+ * Parity unpinned by the pages: the Philox counter layout, the word-to-float
+ * maps, the Gumbel transform, the tie rule and the empty-residual fallback are
+ * this library's written convention. The tests pin the distribution they
+ * produce (exact enumeration, chi-square, closed forms), not single samples.
  */
 #include <math.h>
 #include <stdint.h>
