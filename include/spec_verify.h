@@ -79,7 +79,10 @@ typedef enum {
 #define SV_SEQ_BAD_TOKEN (-1)       /* a drafted / node token outside [0, V)      */
 #define SV_SEQ_BAD_TEMPERATURE (-2) /* temperature < 0, NaN or infinite           */
 #define SV_SEQ_BAD_TREE (-3)        /* parents/depth do not describe a tree       */
-#define SV_SEQ_INTERNAL (-4)        /* a bounded device-side wait gave up         */
+#define SV_SEQ_INTERNAL (-4)        /* a bounded device-side wait gave up; the
+                                     * workspace is then left dirty and must be
+                                     * re-initialized (sv_workspace_init) before
+                                     * its next use                               */
 
 /* Optional diagnostics of spec_verify_sample; the struct and each field may
  * be NULL. All are device arrays of fp32. */

@@ -30,10 +30,8 @@ WsLayout ws_layout(int32_t B, int32_t rows, int32_t nchunks) {
   off = round_up(off + (size_t)B * rows * nchunks * sizeof(P1Slot), 256);
   L.p2 = off;
   off = round_up(off + (size_t)B * nchunks * sizeof(P2Slot), 256);
-  L.tree_arrive = off;
-  off = round_up(off + (size_t)B * 4, 256);
-  L.tree_part = off;
-  off = round_up(off + (size_t)B * rows * nchunks * sizeof(TreePartial), 256);
+  L.tree_slot = off;
+  off = round_up(off + (size_t)B * rows * nchunks * sizeof(TreeSlot), 256);
   L.total = off;
   return L;
 }
@@ -43,6 +41,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kMaxDevices][4];
+std::atomic<int> g_tree_occ[kMaxDevices][4];
 
 int env_int(const char* name, int dflt) {
   const char* s = std::getenv(name);
@@ -91,6 +90,8 @@ bool device_info(int* dev, int* cus) {
   return true;
 }
 
+// Resident workgroups per CU of the chain / tree kernels, queried once per
+// device and configuration.
 int occupancy(int dev, bool bf16, bool vec) {
   const int k = (bf16 ? 2 : 0) + (vec ? 1 : 0);
   int n = g_occ[dev][k].load(std::memory_order_relaxed);
@@ -98,6 +99,17 @@ int occupancy(int dev, bool bf16, bool vec) {
     n = chain_occupancy(bf16, vec);
     if (n <= 0) n = 1;
     g_occ[dev][k].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+int tree_occupancy_cached(int dev, bool bf16, bool vec) {
+  const int k = (bf16 ? 2 : 0) + (vec ? 1 : 0);
+  int n = g_tree_occ[dev][k].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    n = tree_occupancy(bf16, vec);
+    if (n <= 0) n = 1;
+    g_tree_occ[dev][k].store(n, std::memory_order_relaxed);
   }
   return n;
 }
@@ -131,7 +143,7 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   const bool bf16 = (dtype == SV_DTYPE_BF16);
   const int es = bf16 ? 2 : 4;
   const bool vec = aligned16(target, t_stride * es) && (!draft || aligned16(draft, d_stride * es));
-  const Tiling tl = pick_tiling((long long)B * gamma, V, bf16);
+  const Tiling tl = pick_tiling((long long)B * gamma * (draft ? 2 : 1), V, bf16);
   const WsLayout L = ws_layout(B, gamma + 1, max_chunks(V));
   uint8_t* ws = (uint8_t*)workspace;
 
@@ -156,11 +168,11 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   // whole GPU, each at least one pass-1 chunk long.
   {
     const long long resident = (long long)cus * occupancy(dev, bf16, vec);
-    long long c2 = (resident + B - 1) / B;
+    const int unit = kThreads * (bf16 ? 8 : 4);
+    long long c2 = (2 * resident + B - 1) / B;
     const int forced = env_int("SV_P2_CHUNKS", 0);
     if (forced > 0) c2 = forced;
-    c2 = std::max<long long>(1, std::min<long long>(c2, tl.nchunks));
-    const int unit = kThreads * (bf16 ? 8 : 4);
+    c2 = std::max<long long>(1, std::min<long long>(c2, (V + 2 * unit - 1) / (2 * unit)));
     long long len = (V + c2 - 1) / c2;
     len = (len + unit - 1) / unit * unit;
     a.p2_chunk = (int32_t)len;
@@ -184,13 +196,22 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   a.p2 = (P2Slot*)(ws + L.p2);
   a.fused = env_int("SV_FUSED", 1) ? 1 : 0;
   a.spin_limit = 1u << 22;
-  // Lag: about one full GPU of resident workgroups between the pass-1 items
-  // of a sequence and its pass-2 items, so that they rarely wait.
-  const long long n1 = (long long)gamma * tl.nchunks;
+  // Lags of the fused launch: about one resident GPU of workgroups between
+  // the pass-1 items of a sequence and its decision, so that the decision
+  // rarely waits, and half as many again before its pass-2 items, which
+  // wait for the decision.
+  const long long n1 = (long long)gamma * tl.nchunks * (draft ? 2 : 1);
+  const long long per = n1 + 1 + a.p2_nchunks;
   const long long resident = (long long)cus * occupancy(dev, bf16, vec);
-  a.lag = (int32_t)std::min<long long>((resident + n1 - 1) / n1 + 1, 1 << 20);
-  const int forced_lag = env_int("SV_LAG", -1);
-  if (forced_lag >= 0) a.lag = forced_lag;
+  const long long lag = (resident + per - 1) / per + 1;
+  a.lag = (int32_t)std::min<long long>(lag, 1 << 20);
+  a.lag2 = (int32_t)std::min<long long>(lag + (lag + 1) / 2, 1 << 20);
+  const int forced_lag = env_int("SV_LAG", -1), forced_lag2 = env_int("SV_LAG2", -1);
+  if (forced_lag >= 0) a.lag = std::min(forced_lag, 1 << 20);
+  if (forced_lag2 >= 0) a.lag2 = a.lag + std::min(forced_lag2, 1 << 20);
+  if (a.lag2 < a.lag) a.lag2 = a.lag;
+  if ((long long)(B + a.lag2) * per >= (1ll << 31) || (long long)B * (n1 + 1) >= (1ll << 31))
+    return SV_ERR_BAD_SHAPE;
 
   hipStream_t s = (hipStream_t)stream;
   if (a.fused) {
@@ -268,7 +289,7 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
   const bool bf16 = (dtype == SV_DTYPE_BF16);
   const int es = bf16 ? 2 : 4;
   const sv::Tiling tl = sv::pick_tiling((long long)B * N, V, bf16);
-  if ((long long)B * N * tl.nchunks >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
+  if ((long long)B * N * tl.nchunks + B >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
   const sv::WsLayout L = sv::ws_layout(B, N, sv::max_chunks(V));
   uint8_t* ws = (uint8_t*)workspace;
   sv::TreeArgs a;
@@ -288,9 +309,20 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
   a.out_path = out_path;
   a.out_path_len = out_path_len;
   a.out_bonus = out_bonus;
-  a.arrive = (uint32_t*)(ws + L.tree_arrive);
-  a.part = (sv::TreePartial*)(ws + L.tree_part);
+  a.done = (uint32_t*)(ws + L.done);
+  a.slot = (sv::TreeSlot*)(ws + L.tree_slot);
   const bool vec = sv::aligned16(target_logits, a.t_stride);
+  a.fused = sv::env_int("SV_FUSED", 1) ? 1 : 0;
+  a.spin_limit = 1u << 22;
+  int dev = 0, cus = 0;
+  if (!sv::device_info(&dev, &cus)) return SV_ERR_HIP;
+  // Lag: about one resident GPU's worth of items between a sequence's items
+  // and its decision.
+  const long long n1 = (long long)N * tl.nchunks;
+  const long long resident = (long long)cus * sv::tree_occupancy_cached(dev, bf16, vec);
+  a.lag = (int32_t)std::min<long long>((resident + n1 - 1) / n1 + 1, 1 << 20);
+  const int forced_lag = sv::env_int("SV_LAG", -1);
+  if (forced_lag >= 0) a.lag = forced_lag;
   return sv::launch_tree(a, bf16, vec, (hipStream_t)stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

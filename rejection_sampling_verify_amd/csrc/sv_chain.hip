@@ -8,23 +8,27 @@
 // to argmax matching.
 //
 // Work decomposition. Every logit row is cut into chunks of `chunk` elements.
-//   pass-1 item (b, i, c): chunk c of target row i (and of draft row i): the
+//   pass-1 item (b, i, c): chunk c of target row i (or of draft row i): the
 //     partial log-sum-exp state of each row, or for greedy sequences the
-//     partial argmax, published as one 16-byte slot. Nothing waits on it.
-//   pass-2 item (b, c): waits for the gamma * nchunks pass-1 slots of b, takes
-//     the decision of b (every pass-2 item of b computes the same decision
-//     from the same slots; item 0 writes it out), then draws a partial
+//     partial argmax, published in a 16-byte slot (a dense draft's rows are
+//     items of their own, filling the slot's second word). Nothing waits on it.
+//   decision item (b): waits for the gamma * nchunks slots of b, takes the
+//     decision (accept tests, first rejection), writes everything it fixes and
+//     publishes a small decision record.
+//   pass-2 item (b, c): reads the decision record of b and draws a partial
 //     Gumbel-max (or argmax) over chunk c of the row the decision names. The
 //     last pass-2 item of b to finish merges the partials and writes the last
 //     token.
-// One launch runs both: workgroup ids are laid out in blocks, block k holding
-// the pass-1 items of sequence k followed by the pass-2 items of sequence
-// k - lag, so pass 2 of earlier sequences runs while later ones stream pass 1.
-// The dispatcher starts workgroups in id order, so everything a pass-2 item
-// waits for has a smaller id and is already running; the wait is bounded
-// regardless. Merges run in fixed chunk order, so results do not depend on
-// the launch layout or on which item finishes last. Without fusion the two
-// passes are two launches and nothing waits.
+// One launch runs all three: workgroup ids are laid out in groups, group g
+// holding the pass-1 items of sequence g, the decision item of sequence g - Ld
+// and the pass-2 items of sequence g - L2 (L2 >= Ld; ids naming no sequence
+// exit at once), so the decisions and pass 2 of earlier sequences run while
+// later ones stream pass 1. The dispatcher starts workgroups in id order, so
+// whatever an item waits for has a smaller id and is already running; every
+// wait is bounded regardless. Merges run in fixed chunk order, so results do
+// not depend on the launch layout or on which item finishes last. Without
+// fusion there are two launches: pass 1 followed by the decision items, then
+// pass 2, which finds every decision taken.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -43,6 +47,7 @@ struct Decision {
   float T, c2, invT;
   float zt2, zd2;  // log2-domain normalizers of target / draft row `row`
   float a_row;     // accept probability at `row` (one-hot draft: p(x) there)
+  int tok;         // token at position n when the decision already fixes it
 };
 
 struct Smem {
@@ -52,17 +57,30 @@ struct Smem {
   int ior[kWaves];
   uint32_t flag_last;
   uint32_t stalled;
-  uint64_t slot[kThreads][2];  // one batch of polled pass-1 slots
+  union {
+    uint64_t slot[kThreads][2];    // decision: one batch of polled pass-1 slots
+  } u;
   LseState rt[kMaxGamma], rd[kMaxGamma];
   ArgMax rg[kMaxGamma];
   int32_t acc[kMaxGamma];
   Decision dec;
 };
 
+// Block-wide log-sum-exp merge: within a wave the maximum first, then every
+// lane rescales its sum to it and the sums are added (one exponential per
+// lane); the four wave states are merged through LDS.
 __device__ __forceinline__ LseState block_lse(LseState st, float c, Smem& sm, int slot) {
-  st = wave_lse(st, c);
+  float M = st.M;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
+  float sum = (st.M == -INFINITY) ? 0.0f : st.s * fast_exp2((st.M - M) * c);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) sum += shfl_xor_f(sum, m);
   const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) sm.lse[slot][w] = st;
+  if ((threadIdx.x & 63) == 0) {
+    sm.lse[slot][w].M = M;
+    sm.lse[slot][w].s = sum;
+  }
   __syncthreads();
   LseState r = sm.lse[slot][0];
 #pragma unroll
@@ -111,6 +129,31 @@ __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor_f(x, m));
   return x;
+}
+
+__device__ __forceinline__ float block_max(float x, Smem& sm) {
+  x = wave_max(x);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sm.fsum[w] = x;
+  __syncthreads();
+  float r = sm.fsum[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) r = fmaxf(r, sm.fsum[k]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int block_min_int(int x, Smem& sm) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = min(x, shfl_xor_i(x, m));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sm.ior[w] = x;
+  __syncthreads();
+  int r = sm.ior[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) r = min(r, sm.ior[k]);
+  __syncthreads();
+  return r;
 }
 
 // Sequence classification from its temperature alone.
@@ -221,58 +264,190 @@ __device__ __forceinline__ ArgMax chunk_argmax(const Chunk<BF16, VEC>& ch, const
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1: one chunk of one row pair; publishes its slot and moves on.
+// Whole-chunk fast paths for bf16 rows: every thread holds kMaxVecsPerThread
+// full vectors, so there is no per-element predication, and the maximum is
+// taken on the packed words before anything is unpacked.
 // ---------------------------------------------------------------------------
-template <bool BF16, bool VEC>
-__device__ void pass1_item(const ChainArgs& a, int b, int i, int c, Smem& sm) {
-  float T;
-  const int kind = temp_kind(a, b, &T);
-  if (kind == KIND_BAD_T) return;  // nobody reads the slots of such a sequence
-  const int lo = c * a.chunk;
-  const int hi = min(a.V, lo + a.chunk);
-  const uint8_t* rt = target_row(a, b, i);
-  uint64_t w0, w1 = 1u;
-  if (kind == KIND_GREEDY) {
-    Chunk<BF16, VEC> ct;
-    ct.load(rt, lo, hi, a.kv);
-    const ArgMax m = block_argmax(chunk_argmax(ct, rt, a.kv), sm);
-    w0 = pack(m.v, (uint32_t)(m.i + 1));
-  } else {
-    const float c2 = kLog2e / T;
-    Chunk<BF16, VEC> ct;
-    ct.load(rt, lo, hi, a.kv);
-    if (a.draft != nullptr) {
-      const uint8_t* rd = draft_row(a, b, i);
-      Chunk<BF16, VEC> cd;
-      cd.load(rd, lo, hi, a.kv);
-      const LseState lt = block_lse(chunk_lse(ct, rt, a.kv, c2), c2, sm, 0);
-      const LseState ld = block_lse(chunk_lse(cd, rd, a.kv, c2), c2, sm, 1);
-      w0 = pack(lt.M, __float_as_uint(lt.s));
-      w1 = pack(ld.M, __float_as_uint(ld.s));
-    } else {
-      const LseState lt = block_lse(chunk_lse(ct, rt, a.kv, c2), c2, sm, 0);
-      w0 = pack(lt.M, __float_as_uint(lt.s));
+
+// Largest element held by this thread, exactly, as a bf16 value in fp32. The
+// two bf16 halves of every word are compared as f16 numbers (one packed max
+// per two elements): both formats are sign-magnitude, so the f16 order of bf16
+// bit patterns is the bf16 order for every logit of magnitude below 2^120;
+// -inf halves read as f16 NaNs and are ignored by the max. (Logits are finite
+// with magnitude below 2^120, or -inf.) The accumulators start at the most
+// negative finite f16 pattern, below every such logit.
+__device__ __forceinline__ uint32_t pk_max_f16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+__device__ __forceinline__ float packed_max_bf16(const u32x4 (&q)[kMaxVecsPerThread]) {
+  uint32_t m0 = 0xFBFFFBFFu, m1 = 0xFBFFFBFFu;
+#pragma unroll
+  for (int k = 0; k < kMaxVecsPerThread; ++k) {
+    m0 = pk_max_f16(m0, q[k][0]);
+    m1 = pk_max_f16(m1, q[k][1]);
+    m0 = pk_max_f16(m0, q[k][2]);
+    m1 = pk_max_f16(m1, q[k][3]);
+  }
+  const uint32_t m = pk_max_f16(m0, m1);
+  const float hi = __uint_as_float(m & 0xFFFF0000u), lo = __uint_as_float(m << 16);
+  // Every element -inf: report -inf.
+  const float r = fmaxf(hi, lo);
+  return (m == 0xFBFFFBFFu) ? -INFINITY : r;
+}
+
+// Keeps the compiler from holding the unpacked elements of a max pass in
+// registers until a later pass (unpacking again is cheaper than 32 registers).
+__device__ __forceinline__ void opaque(u32x4 (&q)[kMaxVecsPerThread]) {
+#pragma unroll
+  for (int k = 0; k < kMaxVecsPerThread; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = q[k][j];
+      asm volatile("" : "+v"(w));
+      q[k][j] = w;
+    }
+}
+
+__device__ __forceinline__ LseState lse_packed_bf16(u32x4 (&q)[kMaxVecsPerThread], float c) {
+  LseState st;
+  st.M = packed_max_bf16(q);
+  st.s = 0.0f;
+  if (st.M != -INFINITY) {
+    const float Mc = st.M * c;
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxVecsPerThread; ++k) {
+      s0 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][0] << 16), c, -Mc));
+      s1 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][0] & 0xFFFF0000u), c, -Mc));
+      s2 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][1] << 16), c, -Mc));
+      s3 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][1] & 0xFFFF0000u), c, -Mc));
+      s0 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][2] << 16), c, -Mc));
+      s1 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][2] & 0xFFFF0000u), c, -Mc));
+      s2 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][3] << 16), c, -Mc));
+      s3 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][3] & 0xFFFF0000u), c, -Mc));
+    }
+    st.s = (s0 + s1) + (s2 + s3);
+  }
+  return st;
+}
+
+// Argmax of the chunk [lo, lo + chunk) (lowest index among equal values): the
+// block maximum first, then the lowest index holding it, searched only by the
+// threads that hold it.
+__device__ __forceinline__ ArgMax argmax_packed_bf16(u32x4 (&q)[kMaxVecsPerThread], int lo, Smem& sm) {
+  const float m = packed_max_bf16(q);
+  opaque(q);
+  const float bm = block_max(m, sm);
+  int idx = 0x7FFFFFFF;
+  if (m == bm) {
+#pragma unroll
+    for (int k = kMaxVecsPerThread - 1; k >= 0; --k) {
+      const int base = lo + (k * kThreads + (int)threadIdx.x) * 8;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (__uint_as_float(q[k][j] & 0xFFFF0000u) == bm) idx = base + 2 * j + 1;
+        if (__uint_as_float(q[k][j] << 16) == bm) idx = base + 2 * j;
+      }
     }
   }
-  if (threadIdx.x == 0) {
-    P1Slot* dst = a.p1 + ((int64_t)b * a.gamma + i) * a.nchunks + c;
-    xput64(&dst->w0, w0);
-    xput64(&dst->w1, w1);
-  }
+  ArgMax r;
+  r.v = bm;
+  r.i = block_min_int(idx, sm);
+  return r;
 }
 
 // ---------------------------------------------------------------------------
-// The decision of sequence b from its pass-1 slots (all threads take part).
+// Gumbel-max pieces shared by both passes.
 // ---------------------------------------------------------------------------
+struct Best {
+  float s;
+  int32_t i;
+};
+
+// Larger total wins; equal totals go to the lower index (elements may be
+// visited out of index order).
+__device__ __forceinline__ void best_push(Best& bst, float s, int idx) {
+  if (bst.i < 0 || s > bst.s || (s == bst.s && idx < bst.i)) {
+    bst.s = s;
+    bst.i = idx;
+  }
+}
+
+// Exact pruning of the Gumbel-max draw. With E = -ln U, the noise is
+// G = -ln E and E >= 1 - U. An element of score s can beat a total L already
+// reached by some element of the row only if E < exp(s - L), hence only if
+// 1 - U < exp(s - L). With r = 2^24 - 1 - (w >> 8), 1 - U = (2r + 1) 2^-25,
+// which is at least 2^(floor(log2(2r + 1)) - 25). An element is therefore
+// skipped, without evaluating G, when floor(log2(2r + 1)) - 25 exceeds
+// log2(exp(s - L)) by more than a margin covering fp32 rounding; the draw is
+// unchanged. (The test loses at most a factor of two against the exact bound.)
+constexpr float kPruneMarginLog2 = 0x1p-12f;
+
+__device__ __forceinline__ bool may_win_log2(uint32_t w, float x2) {
+  const uint32_t odd = ((~w) >> 7) | 1u;        // 2r + 1
+  const int e = 31 - __builtin_clz(odd);        // floor(log2(2r + 1))
+  return !((float)(e - 25) > x2 + kPruneMarginLog2);
+}
+
+// Same test from a weight eps = exp(s - L) already computed in linear form.
+__device__ __forceinline__ bool may_win_lin(uint32_t w, float eps) {
+  const uint32_t odd = ((~w) >> 7) | 1u;
+  const float t = (float)odd * 0x1p-25f;        // 1 - U (exact below 2^24)
+  return !(t > eps * (1.0f + 0x1p-12f));
+}
+
+// ---------------------------------------------------------------------------
+// The decision of sequence b, taken by its decision item (all threads).
+// ---------------------------------------------------------------------------
+
+// Writes everything the decision fixes. The token at position n is left to
+// the last pass-2 item when a draw is still pending.
+__device__ void write_decision(const ChainArgs& a, int b, Smem& sm) {
+  const int G = a.gamma, tid = threadIdx.x;
+  const Decision& d = sm.dec;
+  const int32_t* ids = a.ids + (int64_t)b * G;
+  int32_t* tok = a.out_tokens + (int64_t)b * (G + 1);
+  if (tid <= G) {
+    const bool pending = d.n >= 0 && tid == d.n && d.mode != P2_NONE;
+    if (!pending) {
+      int v = -1;
+      if (d.n >= 0) {
+        if (tid < d.n) v = ids[tid];
+        else if (tid == d.n) v = d.tok;
+      }
+      tok[tid] = v;
+    }
+  }
+  if (tid == 0) a.out_n[b] = d.n;
+  if (tid < G) {
+    const int64_t k = (int64_t)b * G + tid;
+    float ap = NAN, lzt = NAN, lzd = NAN;
+    if (d.kind == KIND_GREEDY) {
+      ap = (ids[tid] == sm.rg[tid].i) ? 1.0f : 0.0f;
+    } else if (d.kind == KIND_SAMPLED) {
+      ap = sm.rt[tid].s;
+      lzt = sm.rt[tid].M * kLn2;
+      lzd = sm.rd[tid].M * kLn2;
+    }
+    if (a.d_accept) a.d_accept[k] = ap;
+    if (a.d_logzt) a.d_logzt[k] = lzt;
+    if (a.d_logzd) a.d_logzd[k] = lzd;
+  }
+  // A pending residual draw writes its mass itself.
+  if (tid == 0 && a.d_beta && d.mode != P2_RESIDUAL && d.mode != P2_RESIDUAL_ONEHOT) a.d_beta[b] = NAN;
+}
+
 template <bool BF16>
-__device__ void take_decision(const ChainArgs& a, int b, Smem& sm) {
+__device__ void decide(const ChainArgs& a, int b, Smem& sm) {
   const int G = a.gamma, C = a.nchunks, tid = threadIdx.x;
   const int32_t* ids = a.ids + (int64_t)b * G;
   float T;
   int kind = temp_kind(a, b, &T);
   const float c2 = (kind == KIND_SAMPLED) ? kLog2e / T : 0.0f;
-  // Inputs the decision needs besides the slots are requested first, so that
-  // they arrive while the slots are polled.
+  // The inputs besides the slots are requested first.
   bool bad_id = false;
   for (int i = 0; i < G; ++i) bad_id |= (ids[i] < 0 || ids[i] >= a.V);
   float glt = 0.0f, gld = 0.0f;
@@ -281,7 +456,6 @@ __device__ void take_decision(const ChainArgs& a, int b, Smem& sm) {
     glt = Elem<BF16>::load(target_row(a, b, tid), x);
     if (a.draft != nullptr) gld = Elem<BF16>::load(draft_row(a, b, tid), x);
   }
-  if (tid == 0) sm.stalled = 0u;
   if (tid < G) {
     sm.rt[tid].M = -INFINITY;
     sm.rt[tid].s = 0.0f;
@@ -289,11 +463,12 @@ __device__ void take_decision(const ChainArgs& a, int b, Smem& sm) {
     sm.rg[tid].v = -INFINITY;
     sm.rg[tid].i = -1;
   }
+  if (tid == 0) sm.stalled = 0u;
   __syncthreads();
   if (kind != KIND_BAD_T) {
     // Wait for every slot (also when a drafted id turns out to be invalid, so
-    // that no slot can land after the sequence's scratch has been cleared),
-    // 256 at a time, and merge each row's chunks in order.
+    // that no slot can land after they have been cleared), 256 at a time;
+    // return them to zero and merge each row's chunks in order.
     P1Slot* slots = a.p1 + (int64_t)b * G * C;
     const int total = G * C;
     for (int base = 0; base < total; base += kThreads) {
@@ -313,14 +488,18 @@ __device__ void take_decision(const ChainArgs& a, int b, Smem& sm) {
           w0 = xget64(&slots[k].w0);
           w1 = xget64(&slots[k].w1);
         }
-        sm.slot[tid][0] = w0;
-        sm.slot[tid][1] = w1;
+        sm.u.slot[tid][0] = w0;
+        sm.u.slot[tid][1] = w1;
       }
       __syncthreads();
+      if (k < total) {
+        xput64(&slots[k].w0, 0u);
+        xput64(&slots[k].w1, 0u);
+      }
       if (tid < G) {
         const int r0 = max(tid * C, base), r1 = min(tid * C + C, base + kThreads);
         for (int r = r0; r < r1; ++r) {
-          const uint64_t w0 = sm.slot[r - base][0], w1 = sm.slot[r - base][1];
+          const uint64_t w0 = sm.u.slot[r - base][0], w1 = sm.u.slot[r - base][1];
           if (kind == KIND_GREEDY) {
             ArgMax o;
             o.v = hi_f(w0);
@@ -331,9 +510,11 @@ __device__ void take_decision(const ChainArgs& a, int b, Smem& sm) {
             o.M = hi_f(w0);
             o.s = __uint_as_float(lo_u(w0));
             sm.rt[tid] = lse_merge(sm.rt[tid], o, c2);
-            o.M = hi_f(w1);
-            o.s = __uint_as_float(lo_u(w1));
-            sm.rd[tid] = lse_merge(sm.rd[tid], o, c2);
+            if (a.draft != nullptr) {
+              o.M = hi_f(w1);
+              o.s = __uint_as_float(lo_u(w1));
+              sm.rd[tid] = lse_merge(sm.rd[tid], o, c2);
+            }
           }
         }
       }
@@ -371,6 +552,7 @@ __device__ void take_decision(const ChainArgs& a, int b, Smem& sm) {
     d.x = -1;
     d.zt2 = d.zd2 = 0.0f;
     d.a_row = 0.0f;
+    d.tok = -1;
     if (kind == KIND_BAD_T) {
       d.n = -2;
     } else if (kind == KIND_BAD_ID) {
@@ -387,6 +569,8 @@ __device__ void take_decision(const ChainArgs& a, int b, Smem& sm) {
       if (d.n == G) {
         d.mode = P2_GREEDY_BONUS;
         d.row = G;
+      } else {
+        d.tok = sm.rg[d.n].i;  // the correction is the argmax itself
       }
     } else {
       d.n = G;
@@ -410,82 +594,77 @@ __device__ void take_decision(const ChainArgs& a, int b, Smem& sm) {
     sm.dec = d;
   }
   __syncthreads();
+  write_decision(a, b, sm);
+  if (tid == 0) {
+    // Publish the record for the pass-2 items: the payload, then (once it has
+    // landed) the word they wait on.
+    const Decision& d = sm.dec;
+    SeqState* st = a.seq + b;
+    xput64(&st->dec[1], pack(d.zt2, __float_as_uint(d.zd2)));
+    xput64(&st->dec[2], pack(d.c2, __float_as_uint(d.invT)));
+    xput64(&st->dec[3], pack(d.a_row, (uint32_t)d.x));
+    wait_vmem();
+    xput64(&st->dec[0], (1ull << 63) | ((uint64_t)(uint32_t)d.row << 32) | ((uint32_t)(d.n + 64) << 8) | d.mode);
+  }
 }
 
-// Writes everything the decision fixes (pass-2 item 0 of b does this). The
-// token at position n is left to the last pass-2 item when a draw is pending.
-__device__ void write_decision(const ChainArgs& a, int b, Smem& sm) {
-  const int G = a.gamma, tid = threadIdx.x;
-  const Decision& d = sm.dec;
-  const int32_t* ids = a.ids + (int64_t)b * G;
-  int32_t* tok = a.out_tokens + (int64_t)b * (G + 1);
-  if (tid <= G) {
-    const bool pending = d.n >= 0 && tid == d.n && d.mode != P2_NONE;
-    if (!pending) {
-      int v = -1;
-      if (d.n >= 0) {
-        if (tid < d.n) v = ids[tid];
-        else if (tid == d.n) v = sm.rg[tid].i;  // greedy correction
-      }
-      tok[tid] = v;
+// ---------------------------------------------------------------------------
+// Pass 1: one chunk of one row pair; publishes its slot and moves on.
+// ---------------------------------------------------------------------------
+// Items of pass 1 per sequence: one per (row, chunk) of the target, and with
+// a dense draft one more per (row, chunk) of the draft.
+__device__ __forceinline__ int p1_items_per_seq(const ChainArgs& a) {
+  return a.gamma * a.nchunks * (a.draft != nullptr ? 2 : 1);
+}
+
+template <bool BF16, bool VEC>
+__device__ void pass1_item(const ChainArgs& a, int b, int r, Smem& sm) {
+  const int GC = a.gamma * a.nchunks;
+  const bool draft_item = r >= GC;  // item of a dense draft row
+  if (draft_item) r -= GC;
+  const int i = r / a.nchunks, c = r % a.nchunks;
+  float T;
+  const int kind = temp_kind(a, b, &T);
+  // Nothing to compute for a bad temperature; greedy sequences read no draft.
+  if (kind == KIND_BAD_T || (draft_item && kind != KIND_SAMPLED)) return;
+  const int lo = c * a.chunk;
+  const int hi = min(a.V, lo + a.chunk);
+  const uint8_t* row = draft_item ? draft_row(a, b, i) : target_row(a, b, i);
+  // Whole 16-byte-aligned bf16 chunk at the full tile width: fast path.
+  const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && hi - lo == a.chunk;
+  Chunk<BF16, VEC> ch;
+  ch.load(row, lo, hi, a.kv);
+  // w0 belongs to the target item, w1 to the draft item of a dense draft and
+  // to the target item otherwise.
+  uint64_t w0 = 0u, w1 = 1u;
+  if (kind == KIND_GREEDY) {
+    ArgMax m;
+    if (fast) m = argmax_packed_bf16(ch.q, lo, sm);
+    // (The packed search can miss only for subnormal maxima flushed by the
+    // f16 comparison; then the plain scan decides.)
+    if (!fast || m.i == 0x7FFFFFFF) m = block_argmax(chunk_argmax(ch, row, a.kv), sm);
+    w0 = pack(m.v, (uint32_t)(m.i + 1));
+  } else {
+    const float c2 = kLog2e / T;
+    const LseState st = block_lse(fast ? lse_packed_bf16(ch.q, c2) : chunk_lse(ch, row, a.kv, c2), c2, sm, 0);
+    const uint64_t w = pack(st.M, __float_as_uint(st.s));
+    if (draft_item) w1 = w;
+    else w0 = w;
+  }
+  if (threadIdx.x == 0) {
+    P1Slot* dst = a.p1 + ((int64_t)b * a.gamma + i) * a.nchunks + c;
+    if (draft_item) {
+      xput64(&dst->w1, w1);
+    } else {
+      xput64(&dst->w0, w0);
+      if (a.draft == nullptr || kind == KIND_GREEDY) xput64(&dst->w1, w1);
     }
   }
-  if (tid == 0) a.out_n[b] = d.n;
-  if (tid < G) {
-    const int64_t k = (int64_t)b * G + tid;
-    float ap = NAN, lzt = NAN, lzd = NAN;
-    if (d.kind == KIND_GREEDY) {
-      ap = (ids[tid] == sm.rg[tid].i) ? 1.0f : 0.0f;
-    } else if (d.kind == KIND_SAMPLED) {
-      ap = sm.rt[tid].s;
-      lzt = sm.rt[tid].M * kLn2;
-      lzd = sm.rd[tid].M * kLn2;
-    }
-    if (a.d_accept) a.d_accept[k] = ap;
-    if (a.d_logzt) a.d_logzt[k] = lzt;
-    if (a.d_logzd) a.d_logzd[k] = lzd;
-  }
-  if (tid == 0 && a.d_beta && d.mode != P2_RESIDUAL && d.mode != P2_RESIDUAL_ONEHOT) a.d_beta[b] = NAN;
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2: one chunk of the row a decided sequence draws its last token from.
 // ---------------------------------------------------------------------------
-struct Best {
-  float s;
-  int32_t i;
-};
-
-__device__ __forceinline__ void best_push(Best& bst, float s, int idx) {
-  if (bst.i < 0 || s > bst.s) {
-    bst.s = s;
-    bst.i = idx;
-  }
-}
-
-// Exact pruning of the Gumbel-max draw. With E = -ln U, the noise is
-// G = -ln E and E >= 1 - U. An element of score s can beat a total L already
-// reached by some element of the row only if E < exp(s - L), hence only if
-// 1 - U < exp(s - L). With r = 2^24 - 1 - (w >> 8), 1 - U = (2r + 1) 2^-25,
-// which is at least 2^(floor(log2(2r + 1)) - 25). An element is therefore
-// skipped, without evaluating G, when floor(log2(2r + 1)) - 25 exceeds
-// log2(exp(s - L)) by more than a margin covering fp32 rounding; the draw is
-// unchanged. (The test loses at most a factor of two against the exact bound.)
-constexpr float kPruneMarginLog2 = 0x1p-12f;
-
-__device__ __forceinline__ bool may_win_log2(uint32_t w, float x2) {
-  const uint32_t odd = ((~w) >> 7) | 1u;        // 2r + 1
-  const int e = 31 - __builtin_clz(odd);        // floor(log2(2r + 1))
-  return !((float)(e - 25) > x2 + kPruneMarginLog2);
-}
-
-// Same test from a weight eps = exp(s - L) already computed in linear form.
-__device__ __forceinline__ bool may_win_lin(uint32_t w, float eps) {
-  const uint32_t odd = ((~w) >> 7) | 1u;
-  const float t = (float)odd * 0x1p-25f;        // 1 - U (exact below 2^24)
-  return !(t > eps * (1.0f + 0x1p-12f));
-}
-
 // One chunk of a Gumbel-max draw, specialised on what the score of an element
 // is (MODE = P2_RESIDUAL: ln(p - q) where p > q; P2_RESIDUAL_ONEHOT: l/T for
 // v != x; P2_BONUS: l/T). For each 16-byte vector the lane forms the Philox
@@ -650,6 +829,180 @@ __device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int 
   out->w1 = pack(bsum, (uint32_t)bany);
 }
 
+// One chunk of a Gumbel-max draw over 16-byte-aligned bf16 rows. Each lane
+// takes one 8-element vector per round (prefetched two rounds ahead), forms
+// the scores' cheap bound quantities, the Philox words of its two 4-element
+// blocks and the exact pruning test; only the survivors (rare once the running
+// best total L has risen) get their exact score and noise. The first round
+// seeds L with the exact total of the wave's highest-scoring element, so that
+// even the first round prunes. L is shared by the wave and raised after every
+// round.
+template <int MODE>
+__device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm,
+                                  P2Slot* out) {
+  using E = Elem<true>;
+  constexpr bool residual = (MODE == P2_RESIDUAL);
+  constexpr bool onehot = (MODE == P2_RESIDUAL_ONEHOT);
+  const uint8_t* rt = target_row(a, b, dec.row);
+  const uint8_t* rd = residual ? draft_row(a, b, dec.row) : nullptr;
+  const float c2 = dec.c2, invT = dec.invT, zt2 = dec.zt2, zd2 = dec.zd2;
+  const int xex = dec.x;
+  const uint32_t crow = (uint32_t)dec.row, cseq = (uint32_t)b;
+  const uint32_t ctr3 = a.ctr_noise, k0 = a.key0, k1 = a.key1;
+  const int lane = (int)(threadIdx.x & 63);
+  Best bst;
+  bst.s = -INFINITY;
+  bst.i = -1;
+  float beta = 0.0f;
+  int any = residual ? 0 : 1;
+  float mine = -INFINITY;  // best total this lane has reached
+  float L = -INFINITY, nL2 = INFINITY, scale = INFINITY;  // wave-uniform
+  auto set_L = [&](float l) {
+    L = l;
+    nL2 = -L * kLog2e;
+    if (residual) scale = fast_exp2(nL2);
+  };
+  auto total = [&](float lt, float ld, uint32_t w) -> float {
+    float sc;
+    if (residual) {
+      const float lp2 = __builtin_fmaf(lt, c2, -zt2);
+      const float lq2 = __builtin_fmaf(ld, c2, -zd2);
+      sc = lp2 * kLn2 + log1mexp((lq2 - lp2) * kLn2);  // ln (p - q)
+    } else {
+      sc = lt * invT;
+    }
+    return sc + gumbel(w);
+  };
+
+  const int nfull = (hi - lo) / 8;
+  u32x4 qt0, qt1, qt2, qd0, qd1, qd2;
+  const int vi0 = (int)threadIdx.x;
+  auto fetch = [&](int vi, u32x4& qt, u32x4& qd) {
+    if (vi < nfull) {
+      qt = load_vec_stream(rt + (int64_t)(lo + vi * 8) * 2);
+      if (residual) qd = load_vec_stream(rd + (int64_t)(lo + vi * 8) * 2);
+    }
+  };
+  fetch(vi0, qt0, qd0);
+  fetch(vi0 + kThreads, qt1, qd1);
+  const int rounds = (nfull + kThreads - 1) / kThreads;  // same for every lane
+#pragma unroll 1
+  for (int rnd = 0; rnd < rounds; ++rnd) {
+    const int vi = vi0 + rnd * kThreads;
+    fetch(vi + 2 * kThreads, qt2, qd2);
+    const bool have = vi < nfull;
+    const int base = lo + vi * 8;
+    float lt[8], ld[8], wg[8];  // wg: residual weight bound (>= p - q), 0 if p <= q
+    if (have) {
+      E::unpack(qt0, lt);
+      if (residual) {
+        E::unpack(qd0, ld);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lp2 = __builtin_fmaf(lt[e], c2, -zt2), lq2 = __builtin_fmaf(ld[e], c2, -zd2);
+          const float p = fast_exp2(lp2), r = p - fast_exp2(lq2);
+          const bool cand = lp2 > lq2;
+          beta += cand ? r : 0.0f;
+          any |= cand ? 1 : 0;
+          wg[e] = cand ? __builtin_fmaf(p, 0x1p-22f, r) : 0.0f;
+        }
+      }
+    }
+    if (rnd == 0) {
+      // Seed L: the exact total of the wave's highest-scoring element.
+      float key = -INFINITY, klt = 0.0f, kld = 0.0f;
+      int kidx = -1;
+      if (have) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float k = residual ? (wg[e] > 0.0f ? wg[e] : -INFINITY)
+                                   : ((onehot && base + e == xex) ? -INFINITY : lt[e]);
+          if (k > key) {
+            key = k;
+            klt = lt[e];
+            kld = residual ? ld[e] : 0.0f;
+            kidx = base + e;
+          }
+        }
+      }
+      const float wm = wave_max(key);
+      if (wm != -INFINITY) {
+        const uint64_t bal = __ballot(kidx >= 0 && key == wm);
+        const int src = (int)__builtin_ctzll(bal);
+        float t0 = -INFINITY;
+        if (lane == src) {
+          t0 = total(klt, kld, word_at(philox10((uint32_t)kidx >> 2, crow, cseq, ctr3, k0, k1), kidx & 3));
+          best_push(bst, t0, kidx);
+          mine = t0;
+        }
+        set_L(__shfl(t0, src, 64));
+      }
+    }
+    if (have) {
+      Words4 wa, wb;
+      philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
+      uint32_t wd[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wd[e] = wa.w[e];
+        wd[4 + e] = wb.w[e];
+      }
+      bool keep[8];
+      bool surv = false;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (residual) keep[e] = wg[e] > 0.0f && may_win_lin(wd[e], wg[e] * scale);
+        else keep[e] = !(onehot && base + e == xex) && may_win_log2(wd[e], __builtin_fmaf(lt[e], c2, nL2));
+        surv |= keep[e];
+      }
+      if (surv) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (keep[e]) {
+            const float tot = total(lt[e], residual ? ld[e] : 0.0f, wd[e]);
+            best_push(bst, tot, base + e);
+            mine = fmaxf(mine, tot);
+          }
+      }
+    }
+    set_L(fmaxf(L, wave_max(mine)));
+    qt0 = qt1;
+    qt1 = qt2;
+    if (residual) {
+      qd0 = qd1;
+      qd1 = qd2;
+    }
+  }
+  // Elements past the last whole vector, one by one.
+  const int tail_lo = lo + nfull * 8;
+  if (tail_lo < hi && (nfull % kThreads) == (int)threadIdx.x) {
+    for (int idx = tail_lo; idx < hi; ++idx) {
+      const uint32_t w = word_at(philox10((uint32_t)idx >> 2, crow, cseq, ctr3, k0, k1), idx & 3);
+      const float lt = E::load(rt, idx), ld = residual ? E::load(rd, idx) : 0.0f;
+      bool keep;
+      if (residual) {
+        const float lp2 = __builtin_fmaf(lt, c2, -zt2), lq2 = __builtin_fmaf(ld, c2, -zd2);
+        keep = lp2 > lq2;
+        if (keep) {
+          beta += fast_exp2(lp2) - fast_exp2(lq2);
+          any = 1;
+        }
+      } else {
+        keep = !(onehot && idx == xex);
+      }
+      if (keep) best_push(bst, total(lt, ld, w), idx);
+    }
+  }
+  ArgMax m;
+  m.v = bst.s;
+  m.i = bst.i;
+  m = block_argmax(m, sm);
+  const float bsum = block_sum(beta, sm);
+  const int bany = block_or(any, sm);
+  out->w0 = pack(m.v, (uint32_t)m.i);
+  out->w1 = pack(bsum, (uint32_t)bany);
+}
+
 template <bool BF16, bool VEC>
 __device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo, int hi, Smem& sm, P2Slot* out) {
   if (d.mode == P2_GREEDY_BONUS) {
@@ -665,6 +1018,10 @@ __device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo,
     const ArgMax m = block_argmax(best, sm);
     out->w0 = pack(m.v, (uint32_t)m.i);
     out->w1 = pack(0.0f, 1u);
+  } else if (BF16 && VEC) {
+    if (d.mode == P2_RESIDUAL) gumbel_chunk_bf16<P2_RESIDUAL>(a, b, d, lo, hi, sm, out);
+    else if (d.mode == P2_RESIDUAL_ONEHOT) gumbel_chunk_bf16<P2_RESIDUAL_ONEHOT>(a, b, d, lo, hi, sm, out);
+    else gumbel_chunk_bf16<P2_BONUS>(a, b, d, lo, hi, sm, out);
   } else if (d.mode == P2_RESIDUAL) {
     gumbel_chunk<BF16, VEC, P2_RESIDUAL>(a, b, d, lo, hi, sm, out);
   } else if (d.mode == P2_RESIDUAL_ONEHOT) {
@@ -678,7 +1035,7 @@ __device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo,
 // return the sequence's scratch to zero.
 template <bool BF16, bool VEC>
 __device__ void finalize(const ChainArgs& a, int b, Smem& sm) {
-  const int C2 = a.p2_nchunks, G = a.gamma, C = a.nchunks;
+  const int C2 = a.p2_nchunks, G = a.gamma;
   const Decision d = sm.dec;
   P2Slot* ps = a.p2 + (int64_t)b * C2;
   if (d.mode != P2_NONE) {
@@ -691,13 +1048,13 @@ __device__ void finalize(const ChainArgs& a, int b, Smem& sm) {
     for (int base = 0; base < C2; base += kThreads) {
       const int c = base + (int)threadIdx.x;
       if (c < C2) {
-        sm.slot[threadIdx.x][0] = xget64(&ps[c].w0);
-        sm.slot[threadIdx.x][1] = xget64(&ps[c].w1);
+        sm.u.slot[threadIdx.x][0] = xget64(&ps[c].w0);
+        sm.u.slot[threadIdx.x][1] = xget64(&ps[c].w1);
       }
       __syncthreads();
       if (threadIdx.x == 0) {
         for (int k = 0; k < min(kThreads, C2 - base); ++k) {
-          const uint64_t w0 = sm.slot[k][0], w1 = sm.slot[k][1];
+          const uint64_t w0 = sm.u.slot[k][0], w1 = sm.u.slot[k][1];
           const int an = (int)lo_u(w1);
           ArgMax o;
           o.v = hi_f(w0);
@@ -739,17 +1096,62 @@ __device__ void finalize(const ChainArgs& a, int b, Smem& sm) {
       if (a.d_beta && d.mode == P2_RESIDUAL_ONEHOT) a.d_beta[b] = 1.0f - d.a_row;
     }
   }
-  uint64_t* w1 = (uint64_t*)(a.p1 + (int64_t)b * G * C);
-  for (int k = threadIdx.x; k < G * C * 2; k += kThreads) xput64(&w1[k], 0u);
-  uint64_t* w2 = (uint64_t*)ps;
-  for (int k = threadIdx.x; k < C2 * 2; k += kThreads) xput64(&w2[k], 0u);
+  if (d.mode != P2_NONE) {
+    uint64_t* w2 = (uint64_t*)ps;
+    for (int k = threadIdx.x; k < C2 * 2; k += kThreads) xput64(&w2[k], 0u);
+  }
+  if (threadIdx.x < 4) xput64(&a.seq[b].dec[threadIdx.x], 0u);
   if (threadIdx.x == 0) xput(&a.seq[b].p2_arrive, 0u);
+}
+
+// Reads the decision record of b (thread 0; bounded wait in the fused
+// launch). Returns false if the wait gave up.
+__device__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
+  uint64_t* rec = a.seq[b].dec;
+  uint64_t d0 = xget64(&rec[0]);
+  uint32_t spins = 0;
+  while (d0 == 0u) {
+    // Give up after spin_limit rounds, or soon after any other wait of this
+    // call gave up.
+    if (++spins > a.spin_limit || ((spins & 255u) == 0u && xget(&a.done[1]) != 0u)) {
+      atomicOr(&a.done[1], 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    d0 = xget64(&rec[0]);
+  }
+  const uint64_t d1 = xget64(&rec[1]), d2 = xget64(&rec[2]), d3 = xget64(&rec[3]);
+  Decision d;
+  d.kind = KIND_SAMPLED;  // not used by pass 2
+  d.T = 0.0f;
+  d.mode = (uint32_t)(d0 & 0xFFu);
+  d.n = (int)((d0 >> 8) & 0xFFu) - 64;
+  d.row = (int)((d0 >> 32) & 0x7FFFFFFFu);
+  d.zt2 = hi_f(d1);
+  d.zd2 = __uint_as_float(lo_u(d1));
+  d.c2 = hi_f(d2);
+  d.invT = __uint_as_float(lo_u(d2));
+  d.a_row = hi_f(d3);
+  d.x = (int)lo_u(d3);
+  d.tok = -1;
+  *out = d;
+  return true;
 }
 
 template <bool BF16, bool VEC>
 __device__ void pass2_item(const ChainArgs& a, int b, int c, Smem& sm) {
-  take_decision<BF16>(a, b, sm);
-  if (c == 0) write_decision(a, b, sm);
+  if (threadIdx.x == 0) {
+    Decision d;
+    const bool ok = read_decision(a, b, &d);
+    if (!ok) {
+      d.mode = P2_NONE;
+      d.n = -4;
+      a.out_n[b] = -4;
+    }
+    sm.dec = d;
+    sm.stalled = ok ? 0u : 1u;
+  }
+  __syncthreads();
   const Decision d = sm.dec;
   P2Slot part;
   part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
@@ -759,90 +1161,62 @@ __device__ void pass2_item(const ChainArgs& a, int b, int c, Smem& sm) {
     pass2_chunk<BF16, VEC>(a, b, d, lo, min(a.V, lo + a.p2_chunk), sm, &part);
   }
   if (threadIdx.x == 0) {
-    P2Slot* dst = a.p2 + (int64_t)b * a.p2_nchunks + c;
-    xput64(&dst->w0, part.w0);
-    xput64(&dst->w1, part.w1);
-    wait_vmem();  // the slot (and item 0's outputs) have landed first
-    const uint32_t old = atomicAdd(&a.seq[b].p2_arrive, 1u);
-    sm.flag_last = (old == (uint32_t)a.p2_nchunks - 1u) ? 1u : 0u;
+    sm.flag_last = 0u;
+    if (!sm.stalled) {
+      if (d.mode != P2_NONE) {
+        P2Slot* dst = a.p2 + (int64_t)b * a.p2_nchunks + c;
+        xput64(&dst->w0, part.w0);
+        xput64(&dst->w1, part.w1);
+        wait_vmem();  // the slot has landed before the arrival
+      }
+      const uint32_t old = atomicAdd(&a.seq[b].p2_arrive, 1u);
+      sm.flag_last = (old == (uint32_t)a.p2_nchunks - 1u) ? 1u : 0u;
+    }
   }
   __syncthreads();
   if (sm.flag_last) finalize<BF16, VEC>(a, b, sm);
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// Fused launch layout. Block k holds the pass-1 items of sequence k (when
-// k < B) followed by the pass-2 items of sequence k - lag (when that exists).
+// Launch layouts.
 // ---------------------------------------------------------------------------
-struct Layout {
-  int m;       // sequences
-  int n1, n2;  // items per sequence of each pass
-  int L;       // effective lag
-};
-
-__device__ __forceinline__ Layout fused_layout(const ChainArgs& a) {
-  Layout q;
-  q.m = a.B;
-  q.n1 = a.gamma * a.nchunks;
-  q.n2 = a.p2_nchunks;
-  q.L = min(a.lag, q.m);
-  return q;
-}
-
-// Workgroup id t -> pass (1 or 2), sequence and item.
-__device__ __forceinline__ int decode_item(const Layout& q, uint32_t t, int* k, int* r) {
-  const uint32_t seg_a = (uint32_t)q.L * q.n1;
-  if (t < seg_a) {
-    *k = (int)(t / q.n1);
-    *r = (int)(t % q.n1);
-    return 1;
-  }
-  t -= seg_a;
-  const uint32_t per = (uint32_t)(q.n1 + q.n2);
-  const uint32_t seg_b = (uint32_t)(q.m - q.L) * per;
-  if (t < seg_b) {
-    const int blk = (int)(t / per);
-    const int rr = (int)(t % per);
-    if (rr < q.n1) {
-      *k = q.L + blk;
-      *r = rr;
-      return 1;
-    }
-    *k = blk;
-    *r = rr - q.n1;
-    return 2;
-  }
-  t -= seg_b;
-  *k = (q.m - q.L) + (int)(t / q.n2);
-  *r = (int)(t % q.n2);
-  return 2;
-}
-
+// Fused: group g = [pass-1 items of g][decision of g - lag_d][pass-2 items of
+// g - lag_2], for g in [0, B + lag_2).
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   __shared__ Smem sm;
-  const Layout q = fused_layout(a);
-  int k, r;
-  const int pass = decode_item(q, blockIdx.x, &k, &r);
-  if (pass == 1)
-    pass1_item<BF16, VEC>(a, k, r / a.nchunks, r % a.nchunks, sm);
-  else
-    pass2_item<BF16, VEC>(a, k, r, sm);
+  const int n1 = p1_items_per_seq(a), per = n1 + 1 + a.p2_nchunks;
+  const int g = (int)(blockIdx.x / (uint32_t)per);
+  const int r = (int)(blockIdx.x % (uint32_t)per);
+  if (r < n1) {
+    if (g < a.B) pass1_item<BF16, VEC>(a, g, r, sm);
+  } else if (r == n1) {
+    const int b = g - a.lag;
+    if (b >= 0 && b < a.B) decide<BF16>(a, b, sm);
+  } else {
+    const int b = g - a.lag2;
+    if (b >= 0 && b < a.B) pass2_item<BF16, VEC>(a, b, r - n1 - 1, sm);
+  }
 }
 
-// Pass 1 as its own launch: one workgroup per (b, position, chunk), handed
-// out by the hardware dispatcher in sequence order.
+// Split, first launch: every pass-1 item, then one decision item per
+// sequence (all pass-1 items have been dispatched before any decision).
+// Eight waves per SIMD: pass 1 is bound by how many row chunks are in flight.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void chain_p1_kernel(ChainArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void chain_p1_kernel(ChainArgs a) {
   __shared__ Smem sm;
-  const int per_seq = a.gamma * a.nchunks;
-  const int b = blockIdx.x / per_seq;
-  const int r = blockIdx.x % per_seq;
-  pass1_item<BF16, VEC>(a, b, r / a.nchunks, r % a.nchunks, sm);
+  const int per_seq = p1_items_per_seq(a);
+  const uint32_t items = (uint32_t)a.B * per_seq;
+  if (blockIdx.x < items) {
+    const int b = blockIdx.x / per_seq;
+    const int r = blockIdx.x % per_seq;
+    pass1_item<BF16, VEC>(a, b, r, sm);
+  } else {
+    decide<BF16>(a, (int)(blockIdx.x - items), sm);
+  }
 }
 
-// Pass 2 as its own launch (no waiting needed): one workgroup per (b, chunk).
+// Split, second launch: every decision is taken; one workgroup per (b, chunk).
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
   __shared__ Smem sm;
@@ -858,14 +1232,16 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t nwords) {
 
 template <bool BF16, bool VEC>
 hipError_t launch_chain_t(const ChainArgs& a, hipStream_t stream) {
-  const long long grid = (long long)a.B * ((long long)a.gamma * a.nchunks + a.p2_nchunks);
+  const long long n1 = (long long)a.gamma * a.nchunks * (a.draft != nullptr ? 2 : 1);
+  const long long grid = (long long)(a.B + a.lag2) * (n1 + 1 + a.p2_nchunks);
   hipLaunchKernelGGL((chain_kernel<BF16, VEC>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool BF16, bool VEC>
 hipError_t launch_chain_p1_t(const ChainArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((chain_p1_kernel<BF16, VEC>), dim3(a.B * a.gamma * a.nchunks), dim3(kThreads), 0, stream, a);
+  const long long n1 = (long long)a.gamma * a.nchunks * (a.draft != nullptr ? 2 : 1);
+  hipLaunchKernelGGL((chain_p1_kernel<BF16, VEC>), dim3((unsigned)(a.B * (n1 + 1))), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -27,14 +27,19 @@ struct Words4 {
   uint32_t w[4];
 };
 
+// a ^ b ^ c in one gfx950 three-input bit operation (truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ Words4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                            uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -62,10 +67,10 @@ __device__ __forceinline__ void philox10x2(uint32_t a0, uint32_t b0, uint32_t c1
     const uint64_t pb0 = (uint64_t)0xD2511F53u * b0;
     const uint64_t pa1 = (uint64_t)0xCD9E8D57u * a2;
     const uint64_t pb1 = (uint64_t)0xCD9E8D57u * b2;
-    const uint32_t na0 = (uint32_t)(pa1 >> 32) ^ a1 ^ k0;
-    const uint32_t nb0 = (uint32_t)(pb1 >> 32) ^ b1 ^ k0;
-    const uint32_t na2 = (uint32_t)(pa0 >> 32) ^ a3 ^ k1;
-    const uint32_t nb2 = (uint32_t)(pb0 >> 32) ^ b3 ^ k1;
+    const uint32_t na0 = xor3((uint32_t)(pa1 >> 32), a1, k0);
+    const uint32_t nb0 = xor3((uint32_t)(pb1 >> 32), b1, k0);
+    const uint32_t na2 = xor3((uint32_t)(pa0 >> 32), a3, k1);
+    const uint32_t nb2 = xor3((uint32_t)(pb0 >> 32), b3, k1);
     a1 = (uint32_t)pa1;
     b1 = (uint32_t)pb1;
     a3 = (uint32_t)pa0;
@@ -120,7 +125,9 @@ __device__ __forceinline__ float gumbel(uint32_t w) {
   const float e_log = -(lnarg - e * inv_u);
   const float e_ser = z * (1.0f + z * (0.5f + z * (0.33333334f + z * 0.25f)));
   const float E = low ? -lnarg : (z < 0x1p-8f ? e_ser : e_log);
-  return -__builtin_amdgcn_logf(E) * kLn2;
+  // The outer logarithm by the library's logf (about 1 ulp; the hardware
+  // log2 is a few ulp off here): G decides comparisons of totals.
+  return -logf(E);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

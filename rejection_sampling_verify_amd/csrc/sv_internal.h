@@ -21,16 +21,26 @@ enum P2Mode : uint32_t {
   P2_GREEDY_BONUS = 4     // argmax of row gamma
 };
 
-// Per-sequence record in the workspace (64 bytes). Zero between calls.
+// Per-sequence record in the workspace: one 128-byte line per sequence, so
+// that the arrival counters of different sequences never share a line. Zero
+// between calls.
 struct SeqState {
   uint32_t p2_arrive;  // pass-2 items finished
-  uint32_t pad[15];
+  uint32_t pad0[3];
+  // The decision record:
+  //   dec[1] = (zt2 bits << 32) | zd2 bits     (log2-domain normalizers)
+  //   dec[2] = (c2 bits << 32) | invT bits
+  //   dec[3] = (a_row bits << 32) | x
+  //   dec[0] = 2^63 | row << 32 | (n + 64) << 8 | mode, stored last.
+  // Written by the decision item of the sequence, read by its pass-2 items.
+  uint64_t dec[4];
+  uint32_t pad1[20];
 };
+static_assert(sizeof(SeqState) == 128, "one line per sequence");
 
-// Pass-1 result of one chunk of one row pair, published as two 64-bit words
-// that are never zero once written (so a reader can wait for them):
+// Pass-1 result of one chunk of one row pair, published as two 64-bit words:
 //   sampled:  w0 = (M_target bits << 32) | s_target bits,
-//             w1 = (M_draft bits << 32) | s_draft bits  (dense draft) or 1;
+//             w1 = (M_draft bits << 32) | s_draft bits  (dense draft), else 1;
 //   greedy:   w0 = (max value bits << 32) | (argmax + 1), w1 = 1.
 // M is the chunk's largest raw logit and s = sum exp2((l - M) * log2(e) / T)
 // (>= 1, so the word is nonzero even when M = +0.0).
@@ -44,10 +54,9 @@ struct P2Slot {
   uint64_t w0, w1;
 };
 
-struct TreePartial {
-  float v;
-  int32_t i;
-};
+// Tree: argmax of one chunk of one node row, (value bits << 32) | (index + 1),
+// never zero once written.
+typedef uint64_t TreeSlot;
 
 struct ChainArgs {
   const uint8_t* target;
@@ -70,11 +79,14 @@ struct ChainArgs {
   float* d_logzt;
   float* d_logzd;
   float* d_beta;
-  uint32_t* done;     // [1]: nonzero once a bounded wait of a call gave up (sticky)
+  uint32_t* done;     // [1]: nonzero once a bounded wait gave up (the workspace
+                      // must then be re-initialized before its next use)
   SeqState* seq;      // [B]
   P1Slot* p1;         // [B, gamma, nchunks]
   P2Slot* p2;         // [B, p2_nchunks]
-  int32_t lag;        // pass-2 items of sequence k follow the pass-1 items of k + lag
+  int32_t lag;        // fused launch: the decision of sequence k follows the
+                      // pass-1 items of k + lag,
+  int32_t lag2;       // and its pass-2 items those of k + lag2 (lag2 >= lag)
   int32_t fused;      // one launch for both passes
   uint32_t spin_limit;
 };
@@ -90,13 +102,56 @@ struct TreeArgs {
   int32_t* out_path;
   int32_t* out_path_len;
   int32_t* out_bonus;
-  uint32_t* arrive;       // [B]
-  TreePartial* part;      // [B, N, nchunks]
+  uint32_t* done;         // as in ChainArgs
+  TreeSlot* slot;         // [B, N, nchunks]
+  int32_t lag;            // the decision of sequence k follows the items of k + lag
+  int32_t fused;          // items and decisions in one launch
+  uint32_t spin_limit;
 };
+
+// Block order of a launch that holds both the streaming items (n1 per
+// sequence) and the dependent items (n2 per sequence) of m sequences: the
+// dependent items of sequence k are placed after the streaming items of
+// sequence k + L, so that in the hardware's in-order dispatch they find their
+// inputs (nearly always) complete.
+struct Layout {
+  int m;       // sequences
+  int n1, n2;  // items per sequence of each kind
+  int L;       // lag
+};
+
+// Workgroup id t -> kind (1 streaming, 2 dependent), sequence k, item r.
+__device__ __forceinline__ int decode_item(const Layout& q, uint32_t t, int* k, int* r) {
+  const uint32_t seg_a = (uint32_t)q.L * q.n1;
+  if (t < seg_a) {
+    *k = (int)(t / q.n1);
+    *r = (int)(t % q.n1);
+    return 1;
+  }
+  t -= seg_a;
+  const uint32_t per = (uint32_t)(q.n1 + q.n2);
+  const uint32_t seg_b = (uint32_t)(q.m - q.L) * per;
+  if (t < seg_b) {
+    const int blk = (int)(t / per);
+    const int rr = (int)(t % per);
+    if (rr < q.n1) {
+      *k = q.L + blk;
+      *r = rr;
+      return 1;
+    }
+    *k = blk;
+    *r = rr - q.n1;
+    return 2;
+  }
+  t -= seg_b;
+  *k = (q.m - q.L) + (int)(t / q.n2);
+  *r = (int)(t % q.n2);
+  return 2;
+}
 
 // Workspace carve-up; every offset is a multiple of 256 bytes.
 struct WsLayout {
-  size_t done, seq, p1, p2, tree_arrive, tree_part, total;
+  size_t done, seq, p1, p2, tree_slot, total;
 };
 
 WsLayout ws_layout(int32_t B, int32_t rows, int32_t nchunks);
@@ -107,6 +162,7 @@ hipError_t launch_chain(const ChainArgs& a, bool bf16, bool vec, hipStream_t str
 hipError_t launch_chain_p1(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_chain_p2(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, bool bf16, bool vec, hipStream_t stream);
+int tree_occupancy(bool bf16, bool vec);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 int chain_occupancy(bool bf16, bool vec);
 

@@ -8,9 +8,11 @@
 // index among equally deep ones) and the argmax at its last node is the bonus
 // token.
 //
-// One workgroup per (sequence, node, chunk) computes a partial argmax; the
-// last one of a sequence merges them in fixed order and walks the tree. No
-// workgroup waits on another; partials travel through exchange operations.
+// One workgroup per (sequence, node, chunk) computes a partial argmax and
+// publishes it in a 64-bit slot, without waiting and without atomics (an
+// arrival counter per sequence would serialize hundreds of read-modify-writes
+// on one cache line). One decision workgroup per sequence, placed later in
+// dispatch order, collects the slots in fixed order and walks the tree.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -60,94 +62,29 @@ __device__ __forceinline__ ArgMax tree_chunk_argmax(const uint8_t* row, int lo, 
 
 struct TreeSmem {
   ArgMax am[kWaves];
-  uint32_t last;
-  int32_t bad_tree, bad_tok;
+  int32_t red[kWaves];
+  int32_t bad_tree, bad_tok, stalled, maxdep;
   int32_t g[kMaxTreeNodes];
-  int32_t par[kMaxTreeNodes];
-  int32_t dep[kMaxTreeNodes];
   int32_t tok[kMaxTreeNodes];
+  int16_t par[kMaxTreeNodes];
+  int16_t dep[kMaxTreeNodes];
   uint8_t alive[kMaxTreeNodes];
 };
 
-__device__ void tree_decide(const TreeArgs& a, int b, TreeSmem& sm) {
-  const int N = a.N, C = a.nchunks, tid = threadIdx.x;
-  const int32_t* tok = a.tokens + (int64_t)b * N;
-  if (tid == 0) {
-    sm.bad_tree = 0;
-    sm.bad_tok = 0;
-  }
+__device__ __forceinline__ int block_max_int(int v, TreeSmem& sm) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) sm.red[threadIdx.x >> 6] = v;
   __syncthreads();
-  // Stage the tree and merge each node's argmax over its chunks, in order.
-  for (int node = tid; node < N; node += kThreads) {
-    ArgMax m;
-    m.v = -INFINITY;
-    m.i = -1;
-    TreePartial* pp = a.part + ((int64_t)b * N + node) * C;
-#pragma unroll 4
-    for (int c = 0; c < C; ++c) {
-      ArgMax o;
-      o.v = xget(&pp[c].v);
-      o.i = xget(&pp[c].i);
-      m = argmax_merge(m, o);
-    }
-    sm.g[node] = m.i;
-    sm.par[node] = a.parents[node];
-    sm.dep[node] = a.depth[node];
-    sm.tok[node] = tok[node];
-  }
-  __syncthreads();
-  // The tree must be in parent-before-child order with consistent depths.
-  for (int i = tid; i < N; i += kThreads) {
-    bool ok;
-    if (i == 0) {
-      ok = (sm.par[0] == -1) && (sm.dep[0] == 0);
-    } else {
-      const int p = sm.par[i];
-      ok = (p >= 0) && (p < i) && (sm.dep[i] == sm.dep[p] + 1) && (sm.dep[i] <= a.max_depth);
-      if (sm.tok[i] < 0 || sm.tok[i] >= a.V) atomicOr(&sm.bad_tok, 1);
-    }
-    if (!ok) atomicOr(&sm.bad_tree, 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int32_t* path = a.out_path + (int64_t)b * (a.max_depth + 1);
-    for (int k = 0; k <= a.max_depth; ++k) path[k] = -1;
-    if (sm.bad_tree) {
-      a.out_path_len[b] = -3;
-      a.out_bonus[b] = -1;
-    } else if (sm.bad_tok) {
-      a.out_path_len[b] = -1;
-      a.out_bonus[b] = -1;
-    } else {
-      // Survival in index order: a parent precedes its children.
-      sm.alive[0] = 1;
-      int best = 0;
-      for (int c = 1; c < N; ++c) {
-        const int p = sm.par[c];
-        const uint8_t alive = (sm.alive[p] && sm.tok[c] == sm.g[p]) ? 1 : 0;
-        sm.alive[c] = alive;
-        if (alive && sm.dep[c] > sm.dep[best]) best = c;
-      }
-      const int len = sm.dep[best] + 1;
-      for (int c = best, k = len - 1; c != -1; c = sm.par[c], --k) path[k] = c;
-      a.out_path_len[b] = len;
-      a.out_bonus[b] = sm.g[best];
-    }
-  }
-  // Return the scratch of b to zero.
-  uint32_t* words = (uint32_t*)(a.part + (int64_t)b * N * C);
-  for (int k = tid; k < N * C * 2; k += kThreads) xput(&words[k], 0u);
-  if (tid == 0) xput(&a.arrive[b], 0u);
+  int r = sm.red[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) r = max(r, sm.red[k]);
+  return r;
 }
 
+// Argmax of one chunk of one node row, published to its slot.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
-  __shared__ TreeSmem sm;
-  const int per_seq = a.N * a.nchunks;
-  const int b = blockIdx.x / per_seq;
-  const int r = blockIdx.x % per_seq;
-  const int node = r / a.nchunks;
-  const int c = r % a.nchunks;
+__device__ void tree_item(const TreeArgs& a, int b, int node, int c, TreeSmem& sm) {
   const int lo = c * a.chunk;
   const int hi = min(a.V, lo + a.chunk);
   const uint8_t* row = a.target + ((int64_t)b * a.N + node) * a.t_stride;
@@ -158,22 +95,185 @@ __global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
   if (threadIdx.x == 0) {
     ArgMax t = sm.am[0];
     for (int k = 1; k < kWaves; ++k) t = argmax_merge(t, sm.am[k]);
-    TreePartial* p = a.part + ((int64_t)b * a.N + node) * a.nchunks + c;
-    xput(&p->v, t.v);
-    xput(&p->i, t.i);
-    wait_vmem();
-    const uint32_t old = atomicAdd(&a.arrive[b], 1u);
-    sm.last = (old == (uint32_t)per_seq - 1u) ? 1u : 0u;
+    // A non-empty chunk always has an index >= 0, so the word is non-zero.
+    const uint64_t word = ((uint64_t)__float_as_uint(t.v) << 32) | (uint32_t)(t.i + 1);
+    xput64(&a.slot[((int64_t)b * a.N + node) * a.nchunks + c], word);
+  }
+}
+
+// Waits (bounded) for one slot; returns 0 if the wait gave up.
+__device__ __forceinline__ uint64_t tree_wait_slot(const TreeArgs& a, TreeSlot* p, uint64_t w) {
+  uint32_t spins = 0;
+  while (w == 0u) {
+    if (++spins > a.spin_limit || ((spins & 255u) == 0u && xget(&a.done[1]) != 0u)) {
+      atomicOr(&a.done[1], 1u);
+      return 0u;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    w = xget64(p);
+  }
+  return w;
+}
+
+// Decision of sequence b: collect every node's argmax (chunks merged in
+// order), validate the tree, find the surviving nodes level by level, pick the
+// deepest (smallest index among equals), write the outputs and return the
+// slots of b to zero.
+__device__ void tree_decide(const TreeArgs& a, int b, TreeSmem& sm) {
+  const int N = a.N, C = a.nchunks, tid = threadIdx.x;
+  const int32_t* tok = a.tokens + (int64_t)b * N;
+  if (tid == 0) {
+    sm.bad_tree = 0;
+    sm.bad_tok = 0;
+    sm.stalled = 0;
+    sm.maxdep = 0;
+  }
+  // The tree description first: its loads overlap the slot polling below.
+  for (int node = tid; node < N; node += kThreads) {
+    sm.par[node] = (int16_t)max(-1, min(a.parents[node], kMaxTreeNodes));
+    sm.dep[node] = (int16_t)max(-1, min(a.depth[node], kMaxTreeNodes));
+    sm.tok[node] = tok[node];
+  }
+  // One thread per node; its chunks are read eight at a time so that the
+  // loads overlap.
+  for (int node = tid; node < N; node += kThreads) {
+    ArgMax m;
+    m.v = -INFINITY;
+    m.i = -1;
+    TreeSlot* ps = a.slot + ((int64_t)b * N + node) * C;
+    bool stalled = false;
+    for (int c0 = 0; c0 < C; c0 += 8) {
+      uint64_t w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = (c0 + j < C) ? xget64(&ps[c0 + j]) : 1u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (c0 + j < C) {
+          const uint64_t v = tree_wait_slot(a, &ps[c0 + j], w[j]);
+          if (v == 0u) {
+            stalled = true;
+          } else {
+            ArgMax o;
+            o.v = __uint_as_float((uint32_t)(v >> 32));
+            o.i = (int)(uint32_t)v - 1;
+            m = argmax_merge(m, o);
+            xput64(&ps[c0 + j], 0u);
+          }
+        }
+      }
+    }
+    if (stalled) atomicOr(&sm.stalled, 1);
+    sm.g[node] = m.i;
   }
   __syncthreads();
-  if (sm.last) tree_decide(a, b, sm);
+  // Parent-before-child order with consistent depths, tokens in range.
+  for (int node = tid; node < N; node += kThreads) {
+    const int p = sm.par[node], d = sm.dep[node];
+    bool ok;
+    if (node == 0) {
+      ok = (p == -1) && (d == 0);
+    } else {
+      ok = (p >= 0) && (p < node) && (d <= a.max_depth) && (d == sm.dep[p] + 1);
+      if (sm.tok[node] < 0 || sm.tok[node] >= a.V) atomicOr(&sm.bad_tok, 1);
+    }
+    if (!ok) atomicOr(&sm.bad_tree, 1);
+    sm.alive[node] = (node == 0) ? 1 : 0;
+    if (ok) atomicMax(&sm.maxdep, d);
+  }
+  __syncthreads();
+  const bool good = !(sm.stalled | sm.bad_tree | sm.bad_tok);
+  if (good) {
+    // Survival, one depth level at a time (a node's parent is one level up).
+    const int D = sm.maxdep;
+    for (int d = 1; d <= D; ++d) {
+      for (int c = tid; c < N; c += kThreads) {
+        if (sm.dep[c] == d) {
+          const int p = sm.par[c];
+          sm.alive[c] = (sm.alive[p] && sm.tok[c] == sm.g[p]) ? 1 : 0;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // Deepest surviving node, smallest index among equals: maximize
+  // depth * 2^16 + (65535 - index).
+  int key = -1;
+  if (good)
+    for (int c = tid; c < N; c += kThreads)
+      if (sm.alive[c]) key = max(key, (int)sm.dep[c] * 65536 + (65535 - c));
+  key = block_max_int(key, sm);
+  if (tid == 0) {
+    int32_t* path = a.out_path + (int64_t)b * (a.max_depth + 1);
+    for (int k = 0; k <= a.max_depth; ++k) path[k] = -1;
+    if (sm.stalled) {
+      a.out_path_len[b] = -4;
+      a.out_bonus[b] = -1;
+    } else if (sm.bad_tree) {
+      a.out_path_len[b] = -3;
+      a.out_bonus[b] = -1;
+    } else if (sm.bad_tok) {
+      a.out_path_len[b] = -1;
+      a.out_bonus[b] = -1;
+    } else {
+      const int best = 65535 - (key & 0xFFFF);
+      const int len = sm.dep[best] + 1;
+      for (int c = best, k = len - 1; c != -1; c = sm.par[c], --k) path[k] = c;
+      a.out_path_len[b] = len;
+      a.out_bonus[b] = sm.g[best];
+    }
+  }
+}
+
+// Items and decisions in one grid (decision of k after the items of k + lag).
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
+  __shared__ TreeSmem sm;
+  Layout q;
+  q.m = a.B;
+  q.n1 = a.N * a.nchunks;
+  q.n2 = 1;
+  q.L = min(a.lag, q.m);
+  int k, r;
+  if (decode_item(q, blockIdx.x, &k, &r) == 1)
+    tree_item<BF16, VEC>(a, k, r / a.nchunks, r % a.nchunks, sm);
+  else
+    tree_decide(a, k, sm);
+}
+
+// The two kinds as separate launches.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void tree_items_kernel(TreeArgs a) {
+  __shared__ TreeSmem sm;
+  const int per_seq = a.N * a.nchunks;
+  const int b = blockIdx.x / per_seq;
+  const int r = blockIdx.x % per_seq;
+  tree_item<BF16, VEC>(a, b, r / a.nchunks, r % a.nchunks, sm);
+}
+
+__global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeArgs a) {
+  __shared__ TreeSmem sm;
+  tree_decide(a, blockIdx.x, sm);
 }
 
 template <bool BF16, bool VEC>
 hipError_t launch_tree_t(const TreeArgs& a, hipStream_t stream) {
-  const long long grid = (long long)a.B * a.N * a.nchunks;
-  hipLaunchKernelGGL((tree_kernel<BF16, VEC>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  const long long items = (long long)a.B * a.N * a.nchunks;
+  if (a.fused) {
+    hipLaunchKernelGGL((tree_kernel<BF16, VEC>), dim3((unsigned)(items + a.B)), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((tree_items_kernel<BF16, VEC>), dim3((unsigned)items), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tree_decide_kernel, dim3((unsigned)a.B), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <bool BF16, bool VEC>
+int tree_occupancy_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tree_kernel<BF16, VEC>, kThreads, 0) != hipSuccess) n = 0;
+  return n;
 }
 
 }  // namespace
@@ -181,6 +281,11 @@ hipError_t launch_tree_t(const TreeArgs& a, hipStream_t stream) {
 hipError_t launch_tree(const TreeArgs& a, bool bf16, bool vec, hipStream_t stream) {
   if (bf16) return vec ? launch_tree_t<true, true>(a, stream) : launch_tree_t<true, false>(a, stream);
   return vec ? launch_tree_t<false, true>(a, stream) : launch_tree_t<false, false>(a, stream);
+}
+
+int tree_occupancy(bool bf16, bool vec) {
+  if (bf16) return vec ? tree_occupancy_t<true, true>() : tree_occupancy_t<true, false>();
+  return vec ? tree_occupancy_t<false, true>() : tree_occupancy_t<false, false>();
 }
 
 }  // namespace sv

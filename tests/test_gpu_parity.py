@@ -137,16 +137,19 @@ def test_deterministic_and_grid_invariant(dev, monkeypatch):
     ref = oracle_sample(inp)
     compare_chain(base, ref, label="grid base")
     variants = [{"SV_FUSED": "0"}, {"SV_LAG": "0"}, {"SV_LAG": "1"}, {"SV_LAG": "3"}, {"SV_LAG": "100000"},
-                {"SV_FUSED": "0", "SV_LAG": "0"}, {}]
+                {"SV_FUSED": "0", "SV_LAG": "0"}, {"SV_LAG": "0", "SV_LAG2": "0"}, {"SV_LAG": "1", "SV_LAG2": "9"},
+                {"SV_P2_CHUNKS": "1"}, {"SV_P2_CHUNKS": "3"}, {"SV_P2_CHUNKS": "1000"}, {}]
     for env in variants:
-        for k in ("SV_GRID", "SV_FUSED", "SV_LAG"):
+        for k in ("SV_GRID", "SV_FUSED", "SV_LAG", "SV_LAG2", "SV_P2_CHUNKS"):
             monkeypatch.delenv(k, raising=False)
         for k, v in env.items():
             monkeypatch.setenv(k, v)
         got = run_sample(inp, torch, dev)
-        for key in ("tokens", "n", "accept_prob", "logz_target", "logz_draft", "residual_mass"):
+        for key in ("tokens", "n", "accept_prob", "logz_target", "logz_draft"):
             assert np.array_equal(got[key], base[key], equal_nan=True), (env, key)
-    for k in ("SV_GRID", "SV_FUSED", "SV_LAG"):
+        # the residual mass is summed over pass-2 chunks: their count changes rounding only
+        np.testing.assert_allclose(got["residual_mass"], base["residual_mass"], rtol=0, atol=1e-6)
+    for k in ("SV_GRID", "SV_FUSED", "SV_LAG", "SV_LAG2", "SV_P2_CHUNKS"):
         monkeypatch.delenv(k, raising=False)
     # a different chunk length changes only rounding: still oracle-exact
     for kv in ("1", "2", "8"):
@@ -155,14 +158,42 @@ def test_deterministic_and_grid_invariant(dev, monkeypatch):
     monkeypatch.delenv("SV_KV", raising=False)
 
 
+def test_onehot_launch_layouts(dev, monkeypatch):
+    """One-hot drafts at mixed accept lengths: one fused launch with any lags
+    and two launches give identical, oracle-exact outputs and leave the
+    workspace zero."""
+    import rejection_sampling_verify_amd as rsv
+    inp = make_chain("onehot_layouts", 48, 5, 30011, bf16=True, seed=25, target_sigma=6.0,
+                     temperatures=(0.6, 1.0), one_hot=True, onehot_hit=0.85)
+    ref = oracle_sample(inp)
+    ws = rsv.Workspace(dev).get(48, 6, 30011)
+    base = None
+    for env in ({"SV_FUSED": "1"}, {"SV_FUSED": "0"}, {"SV_LAG": "0", "SV_LAG2": "0"}, {"SV_LAG": "2", "SV_LAG2": "7"},
+                {"SV_LAG": "100000"}):
+        for k in ("SV_FUSED", "SV_LAG", "SV_LAG2"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        got = run_sample(inp, torch, dev, workspace=ws)
+        compare_chain(got, ref, label="onehot %s" % env)
+        if base is None:
+            base = got
+        for key in ("tokens", "n", "accept_prob", "logz_target", "residual_mass"):
+            assert np.array_equal(got[key], base[key], equal_nan=True), (env, key)
+        assert int(ws.count_nonzero().item()) == 0
+    for k in ("SV_FUSED", "SV_LAG", "SV_LAG2"):
+        monkeypatch.delenv(k, raising=False)
+    assert set(np.unique(base["n"])) >= {0, 1, 2, 5}
+
+
 def test_workspace_reuse_across_shapes(dev):
     """One workspace serves calls of different shapes; each call leaves it zero."""
     import rejection_sampling_verify_amd as rsv
     ws = rsv.Workspace(dev).get(64, 17, 131072)
-    shapes = [(32, 8, 100000), (3, 2, 500), (64, 16, 131072), (1, 1, 7), (17, 5, 33333)]
+    shapes = [(32, 8, 100000), (3, 2, 500), (64, 16, 131072), (1, 1, 7), (17, 5, 33333), (40, 7, 60000)]
     for k, (B, G, V) in enumerate(shapes):
         inp = make_chain("ws%d" % k, B, G, V, bf16=True, seed=30 + k, target_sigma=2.0, draft_sigma=1.0,
-                         temperatures=(0.0, 1.0))
+                         temperatures=(0.0, 1.0), one_hot=(k % 2 == 1))
         got = run_sample(inp, torch, dev, workspace=ws)
         compare_chain(got, oracle_sample(inp), label="ws %s" % (shapes[k],))
     assert int(ws.count_nonzero().item()) == 0
@@ -217,6 +248,32 @@ def test_tree_chain_shaped_equals_greedy(dev):
     for b in range(30):
         n = int(gn[b])
         assert bonus[b].item() == gtok[b, n]
+
+
+def test_tree_fp32_and_launch_layouts(dev, monkeypatch):
+    """fp32 trees, and identical results for one fused launch with any lag or
+    two launches; every call returns its workspace to zero."""
+    import rejection_sampling_verify_amd as rsv
+    parents, depth = workloads.tree_c5_structure()
+    inp = make_tree("tl", 24, 20011, parents, depth, bf16=False, seed=43, hit=0.6)
+    base = _check_tree(inp, dev)
+    ws = rsv.Workspace(dev).get(24, len(parents), 20011)
+    t = to_dev(inp.target, torch, dev)
+    args = (t, torch.from_numpy(inp.parents).to(dev), torch.from_numpy(inp.depth).to(dev),
+            torch.from_numpy(inp.node_tokens).to(dev), inp.max_depth)
+    for env in ({"SV_FUSED": "0"}, {"SV_LAG": "0"}, {"SV_LAG": "1"}, {"SV_LAG": "100000"}, {}):
+        for k in ("SV_FUSED", "SV_LAG"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        path, plen, bonus = rsv.spec_verify_tree(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(plen.cpu().numpy(), base["path_len"]), env
+        assert np.array_equal(path.cpu().numpy(), base["path"]), env
+        assert np.array_equal(bonus.cpu().numpy(), base["bonus"]), env
+        assert int(ws.count_nonzero().item()) == 0, env
+    for k in ("SV_FUSED", "SV_LAG"):
+        monkeypatch.delenv(k, raising=False)
 
 
 def test_tree_malformed(dev):
