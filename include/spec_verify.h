@@ -213,11 +213,16 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
  *   uniform_out[i] = (w >> 8) * 2^-24 (the accept uniform) and
  *   gumbel_out[i] = -ln(-ln(((w >> 8) + 0.5) * 2^-24)) (the Gumbel noise),
  *   each output optional (NULL).
- * Both return SV_ERR_NULL_ARG / SV_ERR_BAD_SHAPE (n < 0) / SV_ERR_HIP.
+ * They return SV_ERR_NULL_ARG / SV_ERR_BAD_SHAPE (n < 0) / SV_ERR_HIP.
  */
 sv_status_t sv_debug_philox(const uint32_t* ctr, const uint32_t* key, uint32_t* out, int32_t n, void* stream);
 sv_status_t sv_debug_noise(const uint32_t* words, float* gumbel_out, float* uniform_out, int32_t n,
                            void* stream);
+/* sv_debug_wave_max — for each group w < nwaves of 64 consecutive inputs, one
+ * wavefront reduces in[64w .. 64w+63] with the kernels' wave-wide maximum and
+ * every lane writes its result: out[64w + j] = max of the group, for all j.
+ * in, out: device fp32 arrays of 64 * nwaves elements. */
+sv_status_t sv_debug_wave_max(const float* in, float* out, int32_t nwaves, void* stream);
 
 #ifdef __cplusplus
 }

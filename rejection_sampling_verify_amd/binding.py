@@ -22,7 +22,7 @@ SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree", "sv_debug_philox", "sv_debug_noise"]
+           "spec_verify_greedy", "spec_verify_tree", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max"]
 
 _lib = None
 
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.sv_debug_philox.restype = ctypes.c_int
         L.sv_debug_noise.argtypes = [P, P, P, i32, P]
         L.sv_debug_noise.restype = ctypes.c_int
+        L.sv_debug_wave_max.argtypes = [P, P, i32, P]
+        L.sv_debug_wave_max.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -256,3 +258,16 @@ def sv_debug_noise(words, stream=None):
     if st != 0:
         raise SVError(st, "sv_debug_noise")
     return g, u
+
+
+def sv_debug_wave_max(x, stream=None):
+    """Wave-wide maximum of each group of 64 consecutive fp32 values (device
+    tensor [64 * n]); returns [64 * n], every lane's result."""
+    import torch
+    if x.numel() % 64:
+        raise ValueError("need a multiple of 64 values")
+    out = torch.empty_like(x)
+    st = lib().sv_debug_wave_max(_ptr(x), _ptr(out), x.numel() // 64, _stream(stream))
+    if st != 0:
+        raise SVError(st, "sv_debug_wave_max")
+    return out

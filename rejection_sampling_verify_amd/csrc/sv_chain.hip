@@ -19,16 +19,19 @@
 //     Gumbel-max (or argmax) over chunk c of the row the decision names. The
 //     last pass-2 item of b to finish merges the partials and writes the last
 //     token.
-// One launch runs all three: workgroup ids are laid out in groups, group g
+// By default two launches run them: every pass-1 item followed by the
+// decision items (which wait, boundedly, for slots of items dispatched before
+// them), then pass 2, which finds every decision taken; pass 1 then runs at
+// eight waves per SIMD and keeps the most row chunks in flight. One fused
+// launch is also available: workgroup ids are laid out in groups, group g
 // holding the pass-1 items of sequence g, the decision item of sequence g - Ld
 // and the pass-2 items of sequence g - L2 (L2 >= Ld; ids naming no sequence
-// exit at once), so the decisions and pass 2 of earlier sequences run while
-// later ones stream pass 1. The dispatcher starts workgroups in id order, so
-// whatever an item waits for has a smaller id and is already running; every
-// wait is bounded regardless. Merges run in fixed chunk order, so results do
-// not depend on the launch layout or on which item finishes last. Without
-// fusion there are two launches: pass 1 followed by the decision items, then
-// pass 2, which finds every decision taken.
+// exit at once), so that the decisions and pass 2 of earlier sequences run
+// while later ones stream pass 1. The dispatcher starts workgroups in id
+// order, so whatever an item waits for has a smaller id and is already
+// running; every wait is bounded regardless. Merges run in fixed chunk order,
+// so results do not depend on the launch layout or on which item finishes
+// last.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -123,12 +126,6 @@ __device__ __forceinline__ int block_or(int x, Smem& sm) {
   for (int k = 0; k < kWaves; ++k) r |= sm.ior[k];
   __syncthreads();
   return r;
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor_f(x, m));
-  return x;
 }
 
 __device__ __forceinline__ float block_max(float x, Smem& sm) {
@@ -399,6 +396,22 @@ __device__ __forceinline__ bool may_win_lin(uint32_t w, float eps) {
   return !(t > eps * (1.0f + 0x1p-12f));
 }
 
+// Cheaper forms of the same tests for the bulk of a row, one bit looser. With
+// n = ~w, 1 - U >= n 2^-32 / 2 (the bits of w below U's 24 only lower n), so
+// an element can be skipped when n > 2^33 exp(s - L) (1 + 2^-12).
+// Linear form: eps2 = exp(s - L) 2^33 (1 + 2^-12) given by the caller.
+__device__ __forceinline__ bool may_win_lin_fast(uint32_t w, float eps2) {
+  return !((float)(~w) > eps2);
+}
+// Log form: the fp32 bit pattern of n, read as an integer and divided by
+// 2^23, is at most log2(n) + 127 (the exponent plus a mantissa that bounds
+// log2(1 + m) from below), so skipping when that pattern exceeds
+// (log2(exp(s - L)) + 33 + 127 + 2^-12) 2^23 skips only elements the exact
+// test skips. The caller passes that bound as the integer t.
+__device__ __forceinline__ bool may_win_log2_fast(uint32_t w, int t) {
+  return !((int)__float_as_uint((float)(~w)) > t);
+}
+
 // ---------------------------------------------------------------------------
 // The decision of sequence b, taken by its decision item (all threads).
 // ---------------------------------------------------------------------------
@@ -595,9 +608,9 @@ __device__ void decide(const ChainArgs& a, int b, Smem& sm) {
   }
   __syncthreads();
   write_decision(a, b, sm);
+  // Publish the record for the pass-2 items: the payload, then (once it has
+  // landed) the word they wait on.
   if (tid == 0) {
-    // Publish the record for the pass-2 items: the payload, then (once it has
-    // landed) the word they wait on.
     const Decision& d = sm.dec;
     SeqState* st = a.seq + b;
     xput64(&st->dec[1], pack(d.zt2, __float_as_uint(d.zd2)));
@@ -830,13 +843,12 @@ __device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int 
 }
 
 // One chunk of a Gumbel-max draw over 16-byte-aligned bf16 rows. Each lane
-// takes one 8-element vector per round (prefetched two rounds ahead), forms
-// the scores' cheap bound quantities, the Philox words of its two 4-element
-// blocks and the exact pruning test; only the survivors (rare once the running
-// best total L has risen) get their exact score and noise. The first round
-// seeds L with the exact total of the wave's highest-scoring element, so that
-// even the first round prunes. L is shared by the wave and raised after every
-// round.
+// takes one 8-element vector per round (prefetched a round ahead), forms the
+// Philox words of its two 4-element blocks and a cheap, conservative pruning
+// test; only the survivors (about one per 512 elements once the running best
+// total L has risen) get their exact score and noise. The first round seeds L
+// with the exact total of the wave's highest-scoring element; L is shared by
+// the wave and rises after every round.
 template <int MODE>
 __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm,
                                   P2Slot* out) {
@@ -874,8 +886,21 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
     return sc + gumbel(w);
   };
 
+  // Element e (0..7) of a packed 8-element vector.
+  auto el = [](const u32x4& q, int e) -> float {
+    return __uint_as_float((e & 1) ? (q[e >> 1] & 0xFFFF0000u) : (q[e >> 1] << 16));
+  };
+  // Bounds of the fast tests for the current L: the residual compares n with
+  // wg * lin_scale; the others compare bits(n) with l * c2s + log_bias.
+  float lin_scale = INFINITY, c2s = 0.0f, log_bias = INFINITY;
+  auto set_bounds = [&]() {
+    if (residual) lin_scale = scale * (0x1p33f * (1.0f + 0x1p-12f));
+    c2s = c2 * 0x1p23f;
+    log_bias = (nL2 + (33.0f + 127.0f + 0x1p-12f)) * 0x1p23f;
+  };
+  set_bounds();
   const int nfull = (hi - lo) / 8;
-  u32x4 qt0, qt1, qt2, qd0, qd1, qd2;
+  u32x4 qt0, qt1, qd0, qd1;
   const int vi0 = (int)threadIdx.x;
   auto fetch = [&](int vi, u32x4& qt, u32x4& qd) {
     if (vi < nfull) {
@@ -884,94 +909,93 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
     }
   };
   fetch(vi0, qt0, qd0);
-  fetch(vi0 + kThreads, qt1, qd1);
   const int rounds = (nfull + kThreads - 1) / kThreads;  // same for every lane
 #pragma unroll 1
   for (int rnd = 0; rnd < rounds; ++rnd) {
     const int vi = vi0 + rnd * kThreads;
-    fetch(vi + 2 * kThreads, qt2, qd2);
+    fetch(vi + kThreads, qt1, qd1);  // the next round's vector, one round ahead
     const bool have = vi < nfull;
     const int base = lo + vi * 8;
-    float lt[8], ld[8], wg[8];  // wg: residual weight bound (>= p - q), 0 if p <= q
-    if (have) {
-      E::unpack(qt0, lt);
-      if (residual) {
-        E::unpack(qd0, ld);
+    float wg[8];  // residual weight bound (>= p - q), 0 if p <= q
+    if (residual && have) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float lp2 = __builtin_fmaf(lt[e], c2, -zt2), lq2 = __builtin_fmaf(ld[e], c2, -zd2);
-          const float p = fast_exp2(lp2), r = p - fast_exp2(lq2);
-          const bool cand = lp2 > lq2;
-          beta += cand ? r : 0.0f;
-          any |= cand ? 1 : 0;
-          wg[e] = cand ? __builtin_fmaf(p, 0x1p-22f, r) : 0.0f;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
+        const float p = fast_exp2(lp2), r = p - fast_exp2(lq2);
+        const bool cand = lp2 > lq2;
+        beta += cand ? r : 0.0f;
+        any |= cand ? 1 : 0;
+        wg[e] = cand ? __builtin_fmaf(p, 0x1p-22f, r) : 0.0f;
       }
     }
     if (rnd == 0) {
       // Seed L: the exact total of the wave's highest-scoring element.
-      float key = -INFINITY, klt = 0.0f, kld = 0.0f;
-      int kidx = -1;
+      float key = -INFINITY;
+      int ke = -1;
       if (have) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float k = residual ? (wg[e] > 0.0f ? wg[e] : -INFINITY)
-                                   : ((onehot && base + e == xex) ? -INFINITY : lt[e]);
+                                   : ((onehot && base + e == xex) ? -INFINITY : el(qt0, e));
           if (k > key) {
             key = k;
-            klt = lt[e];
-            kld = residual ? ld[e] : 0.0f;
-            kidx = base + e;
+            ke = e;
           }
         }
       }
       const float wm = wave_max(key);
       if (wm != -INFINITY) {
-        const uint64_t bal = __ballot(kidx >= 0 && key == wm);
+        const uint64_t bal = __ballot(ke >= 0 && key == wm);
         const int src = (int)__builtin_ctzll(bal);
         float t0 = -INFINITY;
         if (lane == src) {
+          float klt = 0.0f, kld = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e == ke) {
+              klt = el(qt0, e);
+              if (residual) kld = el(qd0, e);
+            }
+          const int kidx = base + ke;
           t0 = total(klt, kld, word_at(philox10((uint32_t)kidx >> 2, crow, cseq, ctr3, k0, k1), kidx & 3));
           best_push(bst, t0, kidx);
           mine = t0;
         }
         set_L(__shfl(t0, src, 64));
+        set_bounds();
       }
     }
     if (have) {
       Words4 wa, wb;
       philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
-      uint32_t wd[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wd[e] = wa.w[e];
-        wd[4 + e] = wb.w[e];
-      }
       bool keep[8];
       bool surv = false;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (residual) keep[e] = wg[e] > 0.0f && may_win_lin(wd[e], wg[e] * scale);
-        else keep[e] = !(onehot && base + e == xex) && may_win_log2(wd[e], __builtin_fmaf(lt[e], c2, nL2));
+        const uint32_t w = (e < 4) ? wa.w[e & 3] : wb.w[e & 3];
+        if (residual) {
+          keep[e] = wg[e] > 0.0f && may_win_lin_fast(w, wg[e] * lin_scale);
+        } else {
+          const int t = (int)__builtin_fminf(__builtin_fmaxf(__builtin_fmaf(el(qt0, e), c2s, log_bias), -1.0f), 2147483520.0f);
+          keep[e] = !(onehot && base + e == xex) && may_win_log2_fast(w, t);
+        }
         surv |= keep[e];
       }
       if (surv) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (keep[e]) {
-            const float tot = total(lt[e], residual ? ld[e] : 0.0f, wd[e]);
+            const uint32_t w = (e < 4) ? wa.w[e & 3] : wb.w[e & 3];
+            const float tot = total(el(qt0, e), residual ? el(qd0, e) : 0.0f, w);
             best_push(bst, tot, base + e);
             mine = fmaxf(mine, tot);
           }
       }
     }
     set_L(fmaxf(L, wave_max(mine)));
+    set_bounds();
     qt0 = qt1;
-    qt1 = qt2;
-    if (residual) {
-      qd0 = qd1;
-      qd1 = qd2;
-    }
+    if (residual) qd0 = qd1;
   }
   // Elements past the last whole vector, one by one.
   const int tail_lo = lo + nfull * 8;
@@ -1034,8 +1058,8 @@ __device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo,
 // Last pass-2 item of b: merge the chunk partials, write the last token and
 // return the sequence's scratch to zero.
 template <bool BF16, bool VEC>
-__device__ void finalize(const ChainArgs& a, int b, Smem& sm) {
-  const int C2 = a.p2_nchunks, G = a.gamma;
+__device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks, Smem& sm) {
+  const int C2 = p2_nchunks, G = a.gamma;
   const Decision d = sm.dec;
   P2Slot* ps = a.p2 + (int64_t)b * C2;
   if (d.mode != P2_NONE) {
@@ -1079,8 +1103,8 @@ __device__ void finalize(const ChainArgs& a, int b, Smem& sm) {
       f.i = -1;
       for (int c = 0; c < C2; ++c) {
         P2Slot part;
-        const int lo = c * a.p2_chunk;
-        pass2_chunk<BF16, VEC>(a, b, fb, lo, min(a.V, lo + a.p2_chunk), sm, &part);
+        const int lo = c * p2_chunk;
+        pass2_chunk<BF16, VEC>(a, b, fb, lo, min(a.V, lo + p2_chunk), sm, &part);
         ArgMax o;
         o.v = hi_f(part.w0);
         o.i = (int)lo_u(part.w0);
@@ -1139,7 +1163,7 @@ __device__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
 }
 
 template <bool BF16, bool VEC>
-__device__ void pass2_item(const ChainArgs& a, int b, int c, Smem& sm) {
+__device__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p2_nchunks, Smem& sm) {
   if (threadIdx.x == 0) {
     Decision d;
     const bool ok = read_decision(a, b, &d);
@@ -1157,24 +1181,25 @@ __device__ void pass2_item(const ChainArgs& a, int b, int c, Smem& sm) {
   part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
   part.w1 = 0u;
   if (d.mode != P2_NONE) {
-    const int lo = c * a.p2_chunk;
-    pass2_chunk<BF16, VEC>(a, b, d, lo, min(a.V, lo + a.p2_chunk), sm, &part);
+    const int lo = c * p2_chunk;
+    pass2_chunk<BF16, VEC>(a, b, d, lo, min(a.V, lo + p2_chunk), sm, &part);
   }
   if (threadIdx.x == 0) {
     sm.flag_last = 0u;
     if (!sm.stalled) {
       if (d.mode != P2_NONE) {
-        P2Slot* dst = a.p2 + (int64_t)b * a.p2_nchunks + c;
+        P2Slot* dst = a.p2 + (int64_t)b * p2_nchunks + c;
         xput64(&dst->w0, part.w0);
         xput64(&dst->w1, part.w1);
         wait_vmem();  // the slot has landed before the arrival
       }
       const uint32_t old = atomicAdd(&a.seq[b].p2_arrive, 1u);
-      sm.flag_last = (old == (uint32_t)a.p2_nchunks - 1u) ? 1u : 0u;
+      sm.flag_last = (old == (uint32_t)p2_nchunks - 1u) ? 1u : 0u;
     }
   }
   __syncthreads();
-  if (sm.flag_last) finalize<BF16, VEC>(a, b, sm);
+  if (sm.flag_last) finalize<BF16, VEC>(a, b, p2_chunk, p2_nchunks, sm);
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -1195,7 +1220,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     if (b >= 0 && b < a.B) decide<BF16>(a, b, sm);
   } else {
     const int b = g - a.lag2;
-    if (b >= 0 && b < a.B) pass2_item<BF16, VEC>(a, b, r - n1 - 1, sm);
+    if (b >= 0 && b < a.B) pass2_item<BF16, VEC>(a, b, r - n1 - 1, a.p2_chunk, a.p2_nchunks, sm);
   }
 }
 
@@ -1222,7 +1247,7 @@ __global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
   __shared__ Smem sm;
   const int b = blockIdx.x / a.p2_nchunks;
   const int c = blockIdx.x % a.p2_nchunks;
-  pass2_item<BF16, VEC>(a, b, c, sm);
+  pass2_item<BF16, VEC>(a, b, c, a.p2_chunk, a.p2_nchunks, sm);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t nwords) {

@@ -1,6 +1,6 @@
-// sv_debug.hip — element-wise access to the device random primitives, so that
-// tests can hold the kernels' Philox blocks, accept uniforms and Gumbel noise
-// against their definitions directly.
+// sv_debug.hip — element-wise access to the device primitives, so that tests
+// can hold the kernels' Philox blocks, accept uniforms, Gumbel noise and
+// wave-wide reductions against their definitions directly.
 #include "../../include/spec_verify.h"
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -22,6 +22,14 @@ __global__ void noise_kernel(const uint32_t* words, float* gumbel_out, float* un
   if (uniform_out) uniform_out[i] = uniform_accept(words[i]);
 }
 
+// One wave per 64 inputs; every lane writes the wave-wide maximum it holds.
+__global__ void wave_max_kernel(const float* in, float* out, int32_t nwaves) {
+  const int w = blockIdx.x * (blockDim.x / 64) + (int)(threadIdx.x >> 6);
+  if (w >= nwaves) return;  // whole waves exit together
+  const int i = w * 64 + (int)(threadIdx.x & 63);
+  out[i] = wave_max(in[i]);
+}
+
 }  // namespace
 }  // namespace sv
 
@@ -32,6 +40,14 @@ sv_status_t sv_debug_philox(const uint32_t* ctr, const uint32_t* key, uint32_t* 
   if (n < 0) return SV_ERR_BAD_SHAPE;
   if (n == 0) return SV_OK;
   hipLaunchKernelGGL(sv::philox_kernel, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, ctr, key, out, n);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status_t sv_debug_wave_max(const float* in, float* out, int32_t nwaves, void* stream) {
+  if (!in || !out) return SV_ERR_NULL_ARG;
+  if (nwaves < 0) return SV_ERR_BAD_SHAPE;
+  if (nwaves == 0) return SV_OK;
+  hipLaunchKernelGGL(sv::wave_max_kernel, dim3((nwaves + 3) / 4), dim3(256), 0, (hipStream_t)stream, in, out, nwaves);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

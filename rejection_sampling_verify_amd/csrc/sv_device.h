@@ -241,6 +241,40 @@ __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
   return a;
 }
 
+// Lane exchanges without LDS: DPP within 16-lane rows, then the gfx950 row
+// swaps (16 lanes, then 32). After lane_swaps(v), each lane holds v of the
+// lane its row swap pairs it with in one of the two results (the other holds
+// its own v), so a reduction over v and both results is a reduction with that
+// partner row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Wave-wide maximum, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+  float a, b;
+  swap16(x, a, b);
+  x = fmaxf(x, fmaxf(a, b));
+  swap32(x, a, b);
+  return fmaxf(x, fmaxf(a, b));
+}
+
+// Wave-wide sum, in every lane (fixed order).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x += shfl_xor_f(x, m);

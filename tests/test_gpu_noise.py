@@ -114,3 +114,28 @@ def test_noise_maps_extreme_words(dev):
           % (err.max(), int(j[worst]), gref[worst]))
     assert np.all(err <= _gumbel_tol(gref))
     assert np.all(np.diff(g[np.argsort(j, kind="stable")]) >= 0)  # monotone in U
+
+
+def test_wave_max(dev):
+    """The wave-wide maximum the kernels use (row-local DPP steps, then the
+    16- and 32-lane row swaps): every lane of every wave holds the group max,
+    for maxima in every lane position and with -inf and ties."""
+    import rejection_sampling_verify_amd as rsv
+    rng = np.random.default_rng(8)
+    groups = []
+    for pos in range(64):  # the maximum in each lane position
+        g = rng.standard_normal(64).astype(np.float32)
+        g[pos] = 10.0 + pos
+        groups.append(g)
+    groups.append(np.full(64, -np.inf, np.float32))
+    g = np.full(64, -np.inf, np.float32)
+    g[37] = -5.0
+    groups.append(g)
+    groups.append(np.full(64, 3.25, np.float32))
+    for _ in range(64):
+        groups.append(rng.standard_normal(64).astype(np.float32) * 100)
+    x = np.concatenate(groups)
+    out = rsv.sv_debug_wave_max(torch.from_numpy(x).to(dev)).cpu().numpy()
+    torch.cuda.synchronize()
+    want = np.repeat(x.reshape(-1, 64).max(axis=1), 64)
+    assert np.array_equal(out, want)

@@ -129,16 +129,18 @@ def test_bad_inputs_per_sequence(dev):
 
 
 def test_deterministic_and_grid_invariant(dev, monkeypatch):
-    """Bitwise identical outputs across runs, launch layouts (one fused launch
-    with any lag, or two launches) and chunking."""
+    """Bitwise identical outputs across runs and launch layouts (two launches,
+    or one fused launch with any lags), and oracle-exact at any chunking."""
     inp = make_chain("grid", 40, 6, 70001, bf16=True, seed=24, target_sigma=3.0, draft_sigma=(0.3, 1.5),
                      temperatures=(0.0, 0.7, 1.0))
     base = run_sample(inp, torch, dev)
     ref = oracle_sample(inp)
     compare_chain(base, ref, label="grid base")
-    variants = [{"SV_FUSED": "0"}, {"SV_LAG": "0"}, {"SV_LAG": "1"}, {"SV_LAG": "3"}, {"SV_LAG": "100000"},
-                {"SV_FUSED": "0", "SV_LAG": "0"}, {"SV_LAG": "0", "SV_LAG2": "0"}, {"SV_LAG": "1", "SV_LAG2": "9"},
-                {"SV_P2_CHUNKS": "1"}, {"SV_P2_CHUNKS": "3"}, {"SV_P2_CHUNKS": "1000"}, {}]
+    F = {"SV_FUSED": "1"}
+    variants = [F, {**F, "SV_LAG": "0"}, {**F, "SV_LAG": "1"}, {**F, "SV_LAG": "3"}, {**F, "SV_LAG": "100000"},
+                {"SV_FUSED": "0", "SV_LAG": "0"}, {**F, "SV_LAG": "0", "SV_LAG2": "0"},
+                {**F, "SV_LAG": "1", "SV_LAG2": "9"}, {"SV_P2_CHUNKS": "1"}, {"SV_P2_CHUNKS": "3"},
+                {**F, "SV_P2_CHUNKS": "7"}, {"SV_P2_CHUNKS": "1000"}, {}]
     for env in variants:
         for k in ("SV_GRID", "SV_FUSED", "SV_LAG", "SV_LAG2", "SV_P2_CHUNKS"):
             monkeypatch.delenv(k, raising=False)
@@ -168,8 +170,8 @@ def test_onehot_launch_layouts(dev, monkeypatch):
     ref = oracle_sample(inp)
     ws = rsv.Workspace(dev).get(48, 6, 30011)
     base = None
-    for env in ({"SV_FUSED": "1"}, {"SV_FUSED": "0"}, {"SV_LAG": "0", "SV_LAG2": "0"}, {"SV_LAG": "2", "SV_LAG2": "7"},
-                {"SV_LAG": "100000"}):
+    for env in ({"SV_FUSED": "1"}, {"SV_FUSED": "0"}, {"SV_FUSED": "1", "SV_LAG": "0", "SV_LAG2": "0"},
+                {"SV_FUSED": "1", "SV_LAG": "2", "SV_LAG2": "7"}, {"SV_FUSED": "1", "SV_LAG": "100000"}):
         for k in ("SV_FUSED", "SV_LAG", "SV_LAG2"):
             monkeypatch.delenv(k, raising=False)
         for k, v in env.items():
