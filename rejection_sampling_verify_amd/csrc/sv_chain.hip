@@ -617,7 +617,7 @@ __device__ void decide(const ChainArgs& a, int b, Smem& sm) {
     xput64(&st->dec[2], pack(d.c2, __float_as_uint(d.invT)));
     xput64(&st->dec[3], pack(d.a_row, (uint32_t)d.x));
     wait_vmem();
-    xput64(&st->dec[0], (1ull << 63) | ((uint64_t)(uint32_t)d.row << 32) | ((uint32_t)(d.n + 64) << 8) | d.mode);
+    xput64(&st->dec[0], kRecPublished | ((uint64_t)(uint32_t)d.row << 32) | ((uint32_t)(d.n + 64) << 8) | d.mode);
   }
 }
 
@@ -1132,9 +1132,21 @@ __device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks
 // launch). Returns false if the wait gave up.
 __device__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
   uint64_t* rec = a.seq[b].dec;
-  uint64_t d0 = xget64(&rec[0]);
+  uint64_t d0, d1 = 0u, d2 = 0u, d3 = 0u;
+  if (!a.fused) {
+    // Two launches: the first has completed, so the record is complete; its
+    // four words in one round trip.
+    d0 = xget64(&rec[0]);
+    d1 = xget64(&rec[1]);
+    d2 = xget64(&rec[2]);
+    d3 = xget64(&rec[3]);
+    if (!(d0 & kRecPublished)) return false;
+  } else {
+    // Fused: wait for the word stored last, then read the others.
+    d0 = xget64(&rec[0]);
+  }
   uint32_t spins = 0;
-  while (d0 == 0u) {
+  while (!(d0 & kRecPublished)) {
     // Give up after spin_limit rounds, or soon after any other wait of this
     // call gave up.
     if (++spins > a.spin_limit || ((spins & 255u) == 0u && xget(&a.done[1]) != 0u)) {
@@ -1144,7 +1156,11 @@ __device__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
     __builtin_amdgcn_s_sleep(2);
     d0 = xget64(&rec[0]);
   }
-  const uint64_t d1 = xget64(&rec[1]), d2 = xget64(&rec[2]), d3 = xget64(&rec[3]);
+  if (a.fused) {
+    d1 = xget64(&rec[1]);
+    d2 = xget64(&rec[2]);
+    d3 = xget64(&rec[3]);
+  }
   Decision d;
   d.kind = KIND_SAMPLED;  // not used by pass 2
   d.T = 0.0f;

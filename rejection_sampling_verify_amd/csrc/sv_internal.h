@@ -37,6 +37,7 @@ struct SeqState {
   uint32_t pad1[20];
 };
 static_assert(sizeof(SeqState) == 128, "one line per sequence");
+constexpr uint64_t kRecPublished = 1ull << 63;
 
 // Pass-1 result of one chunk of one row pair, published as two 64-bit words:
 //   sampled:  w0 = (M_target bits << 32) | s_target bits,
