@@ -4,8 +4,9 @@ One step = one call of spec_verify_sample over one batch of the
 chain_bf16_llama workload (B=256 sequences, gamma=8 drafts, V=128256, bf16
 logits, temperatures drawn from {0, 0.7, 1.0}), inputs resident in HBM. Prints
 one JSON line: verified positions/s (B * gamma per step) as `value`, the
-logit-read bandwidth against the HBM roofline of the fused kernel measured with
-HIP events on its stream, and the CPU oracle timed on the host as a baseline.
+logit-read bandwidth against the HBM roofline of one verify call (the kernels
+it launches back to back on one stream, timed with HIP events on that stream),
+and the CPU oracle timed on the host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
