@@ -32,6 +32,8 @@ WsLayout ws_layout(int32_t B, int32_t rows, int32_t nchunks) {
   off = round_up(off + (size_t)B * nchunks * sizeof(P2Slot), 256);
   L.tree_slot = off;
   off = round_up(off + (size_t)B * rows * nchunks * sizeof(TreeSlot), 256);
+  L.work = off;
+  off = round_up(off + (size_t)B * sizeof(uint32_t), 256);
   L.total = off;
   return L;
 }
@@ -40,7 +42,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
-std::atomic<int> g_occ[kMaxDevices][4];
+std::atomic<int> g_occ[kMaxDevices][8];
 std::atomic<int> g_tree_occ[kMaxDevices][4];
 
 int env_int(const char* name, int dflt) {
@@ -97,6 +99,18 @@ int occupancy(int dev, bool bf16, bool vec) {
   int n = g_occ[dev][k].load(std::memory_order_relaxed);
   if (n <= 0) {
     n = chain_occupancy(bf16, vec);
+    if (n <= 0) n = 1;
+    g_occ[dev][k].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Resident workgroups per CU of the second of the two chain launches.
+int p2_occupancy(int dev, bool bf16, bool vec) {
+  const int k = 4 + (bf16 ? 2 : 0) + (vec ? 1 : 0);
+  int n = g_occ[dev][k].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    n = chain_p2_occupancy(bf16, vec);
     if (n <= 0) n = 1;
     g_occ[dev][k].store(n, std::memory_order_relaxed);
   }
@@ -164,19 +178,31 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   a.chunk = tl.chunk;
   a.nchunks = tl.nchunks;
   a.kv = tl.kv;
-  // Pass-2 chunks: about one resident workgroup per (sequence, chunk) over the
-  // whole GPU, each at least one pass-1 chunk long.
+  // Pass-2 chunks. The fused launch sizes them for about two resident
+  // workgroups per (sequence, chunk) over the whole GPU. The second of two
+  // launches sizes them on the device, once the number of sequences with a
+  // pending draw is known: as many chunks per row as fill one resident
+  // wave of its workgroups. Either way a chunk is at least four streaming
+  // units long (one unit: one vector per thread).
   {
-    const long long resident = (long long)cus * occupancy(dev, bf16, vec);
     const int unit = kThreads * (bf16 ? 8 : 4);
-    long long c2 = (2 * resident + B - 1) / B;
+    const long long cap = std::max<long long>(1, (V + 4 * unit - 1) / (4 * unit));
     const int forced = env_int("SV_P2_CHUNKS", 0);
-    if (forced > 0) c2 = forced;
-    c2 = std::max<long long>(1, std::min<long long>(c2, (V + 2 * unit - 1) / (2 * unit)));
+    const long long resident = (long long)cus * occupancy(dev, bf16, vec);
+    long long c2 = forced > 0 ? forced : (2 * resident + B - 1) / B;
+    c2 = std::max<long long>(1, std::min<long long>(c2, cap));
     long long len = (V + c2 - 1) / c2;
     len = (len + unit - 1) / unit * unit;
     a.p2_chunk = (int32_t)len;
     a.p2_nchunks = (int32_t)((V + len - 1) / len);
+    a.p2_stride = max_chunks(V);
+    a.p2_unit = unit;
+    a.p2_cap = (int32_t)cap;
+    a.p2_force = forced > 0 ? (int32_t)std::min<long long>(forced, cap) : 0;
+    const long long resident2 = (long long)cus * p2_occupancy(dev, bf16, vec);
+    const long long grid2 = a.p2_force > 0 ? (long long)B * a.p2_force : std::max<long long>(resident2, B);
+    if (grid2 >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
+    a.p2_grid = (int32_t)grid2;
   }
   a.key0 = (uint32_t)seed;
   a.key1 = (uint32_t)(seed >> 32);
@@ -194,6 +220,7 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   a.seq = (SeqState*)(ws + L.seq);
   a.p1 = (P1Slot*)(ws + L.p1);
   a.p2 = (P2Slot*)(ws + L.p2);
+  a.work = (uint32_t*)(ws + L.work);
   // Two launches by default (measured faster on MI355X: pass 1 keeps eight
   // waves per SIMD streaming); one fused launch on request.
   a.fused = env_int("SV_FUSED", 0) ? 1 : 0;

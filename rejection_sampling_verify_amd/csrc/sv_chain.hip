@@ -60,6 +60,10 @@ struct Smem {
   int ior[kWaves];
   uint32_t flag_last;
   uint32_t stalled;
+  uint32_t lkey;   // pass 2: order key of the best total the workgroup has reached
+  uint32_t nwork;  // second launch: sequences on the pass-2 work list
+  int32_t unit[5]; // second launch: this workgroup's sequence, chunk, chunk length, chunks per
+                   // row, and the sequence's place on the work list
   union {
     uint64_t slot[kThreads][2];    // decision: one batch of polled pass-1 slots
   } u;
@@ -396,20 +400,42 @@ __device__ __forceinline__ bool may_win_lin(uint32_t w, float eps) {
   return !(t > eps * (1.0f + 0x1p-12f));
 }
 
-// Cheaper forms of the same tests for the bulk of a row, one bit looser. With
+// Cheaper form of the same test for the bulk of a row, one bit looser. With
 // n = ~w, 1 - U >= n 2^-32 / 2 (the bits of w below U's 24 only lower n), so
-// an element can be skipped when n > 2^33 exp(s - L) (1 + 2^-12).
-// Linear form: eps2 = exp(s - L) 2^33 (1 + 2^-12) given by the caller.
-__device__ __forceinline__ bool may_win_lin_fast(uint32_t w, float eps2) {
-  return !((float)(~w) > eps2);
+// an element can be skipped when log2(n) > log2(exp(s - L)) + 33 + 2^-12.
+// The fp32 bit pattern of a positive x, read as an integer and divided by
+// 2^23, is at most log2(x) + 127 (the exponent, plus a mantissa m that bounds
+// log2(1 + m) from below), so the test compares that pattern of n, converted
+// to fp32, with t = (log2(exp(s - L)) + 160 + 2^-12) 2^23 given by the caller;
+// the conversions err by at most 2^7 against the margin's 2^11.
+__device__ __forceinline__ bool may_win_bits(uint32_t w, float t) {
+  return !((float)(int)__float_as_uint((float)(~w)) > t);
 }
-// Log form: the fp32 bit pattern of n, read as an integer and divided by
-// 2^23, is at most log2(n) + 127 (the exponent plus a mantissa that bounds
-// log2(1 + m) from below), so skipping when that pattern exceeds
-// (log2(exp(s - L)) + 33 + 127 + 2^-12) 2^23 skips only elements the exact
-// test skips. The caller passes that bound as the integer t.
-__device__ __forceinline__ bool may_win_log2_fast(uint32_t w, int t) {
-  return !((int)__float_as_uint((float)(~w)) > t);
+
+// Upper bound, in log2 units, on log2 (p - q) for log2 p = lp2 > lq2 = log2 q:
+// p - q = p (1 - 2^-d) with d = lp2 - lq2, and 1 - e^-x <= min(1, x), so
+// log2 (p - q) <= lp2 + min(0, log2 d + log2 ln 2). log2 d is bounded from
+// above by its fp32 bit pattern read as above plus 0.0860714 (the largest gap
+// between log2(1 + m) and m); 127 - 0.0860714 - log2 ln 2 = 127.442695, taken
+// a little smaller. d is raised to 2^-100 first, which only loosens the bound
+// and keeps it off subnormals.
+__device__ __forceinline__ float residual_log2_bound(float lp2, float lq2) {
+  const float d = __builtin_fmaxf(lp2 - lq2, 0x1p-100f);
+  const float lg = (float)(int)__float_as_uint(d) * 0x1p-23f - 127.44268798828125f;
+  return lp2 + __builtin_fminf(lg, 0.0f);
+}
+
+// Totals shared between the waves of a workgroup (LDS) and the workgroups of a
+// sequence (its record) as unsigned order keys: larger key, larger total; 0
+// stands for none yet. Any total that some element of the row reaches is a
+// valid pruning threshold for every other part of the row, so these are read
+// without ordering and may be stale.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_total(uint32_t k) {
+  return k == 0u ? -INFINITY : __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 // ---------------------------------------------------------------------------
@@ -609,15 +635,23 @@ __device__ void decide(const ChainArgs& a, int b, Smem& sm) {
   __syncthreads();
   write_decision(a, b, sm);
   // Publish the record for the pass-2 items: the payload, then (once it has
-  // landed) the word they wait on.
+  // landed) the word they wait on. With two launches only a sequence with a
+  // pending draw has pass-2 items; it is appended to the work list.
   if (tid == 0) {
     const Decision& d = sm.dec;
-    SeqState* st = a.seq + b;
-    xput64(&st->dec[1], pack(d.zt2, __float_as_uint(d.zd2)));
-    xput64(&st->dec[2], pack(d.c2, __float_as_uint(d.invT)));
-    xput64(&st->dec[3], pack(d.a_row, (uint32_t)d.x));
-    wait_vmem();
-    xput64(&st->dec[0], kRecPublished | ((uint64_t)(uint32_t)d.row << 32) | ((uint32_t)(d.n + 64) << 8) | d.mode);
+    if (a.fused || d.mode != P2_NONE) {
+      SeqState* st = a.seq + b;
+      xput64(&st->dec[1], pack(d.zt2, __float_as_uint(d.zd2)));
+      xput64(&st->dec[2], pack(d.c2, __float_as_uint(d.invT)));
+      xput64(&st->dec[3], pack(d.a_row, (uint32_t)d.x));
+      wait_vmem();
+      xput64(&st->dec[0], kRecPublished | ((uint64_t)(uint32_t)d.row << 32) | ((uint32_t)(d.n + 64) << 8) | d.mode);
+    }
+    if (!a.fused && d.mode != P2_NONE) {
+      const uint32_t idx = atomicAdd(&a.done[kDoneNWork], 1u);
+      if (idx < (uint32_t)a.B) xput(&a.work[idx], (uint32_t)b);
+      else atomicOr(&a.done[1], 1u);  // a list left over from an aborted call
+    }
   }
 }
 
@@ -845,11 +879,13 @@ __device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int 
 // One chunk of a Gumbel-max draw over 16-byte-aligned bf16 rows. Each lane
 // takes one 8-element vector per round (prefetched a round ahead), forms the
 // Philox words of its two 4-element blocks and a cheap, conservative pruning
-// test; only the survivors (about one per 512 elements once the running best
-// total L has risen) get their exact score and noise. The first round seeds L
-// with the exact total of the wave's highest-scoring element; L is shared by
-// the wave and rises after every round.
-template <int MODE>
+// test; only the survivors get their exact score and noise. The first round
+// seeds the wave's threshold L with the exact total of its highest-scoring
+// element. L is wave-uniform and rises whenever a survivor beats it, or
+// another wave of the workgroup (through LDS) or another workgroup of the
+// same row (through the sequence record, read one round late) reports a
+// higher total.
+template <int MODE, bool BETA>
 __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm,
                                   P2Slot* out) {
   using E = Elem<true>;
@@ -868,11 +904,15 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
   float beta = 0.0f;
   int any = residual ? 0 : 1;
   float mine = -INFINITY;  // best total this lane has reached
-  float L = -INFINITY, nL2 = INFINITY, scale = INFINITY;  // wave-uniform
+  float L = -INFINITY, nL2 = INFINITY;  // wave-uniform
+  // The residual mass is summed only for the caller's diagnostics (BETA).
+  constexpr bool want_beta = residual && BETA;
+  float Lpost = -INFINITY;  // the largest total this wave has reported
+  uint32_t* const gkey = &a.seq[b].lbest;
+  uint32_t gnext = 0u;      // the sequence's key, loaded a round ahead
   auto set_L = [&](float l) {
     L = l;
     nL2 = -L * kLog2e;
-    if (residual) scale = fast_exp2(nL2);
   };
   auto total = [&](float lt, float ld, uint32_t w) -> float {
     float sc;
@@ -890,13 +930,14 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
   auto el = [](const u32x4& q, int e) -> float {
     return __uint_as_float((e & 1) ? (q[e >> 1] & 0xFFFF0000u) : (q[e >> 1] << 16));
   };
-  // Bounds of the fast tests for the current L: the residual compares n with
-  // wg * lin_scale; the others compare bits(n) with l * c2s + log_bias.
-  float lin_scale = INFINITY, c2s = 0.0f, log_bias = INFINITY;
+  // Bounds of the fast test for the current L: the pattern of n is compared
+  // with b 2^23 + log_bias, b an upper bound on the score in log2 units (l c2
+  // for the bonus draws). log_bias stays finite (no threshold yet: everything
+  // passes), so that b = -inf (p <= q) always fails.
+  float c2s = 0.0f, log_bias = 0x1p120f;
   auto set_bounds = [&]() {
-    if (residual) lin_scale = scale * (0x1p33f * (1.0f + 0x1p-12f));
     c2s = c2 * 0x1p23f;
-    log_bias = (nL2 + (33.0f + 127.0f + 0x1p-12f)) * 0x1p23f;
+    log_bias = __builtin_fminf((nL2 + (33.0f + 127.0f + 0x1p-12f)) * 0x1p23f, 0x1p120f);
   };
   set_bounds();
   const int nfull = (hi - lo) / 8;
@@ -909,6 +950,58 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
     }
   };
   fetch(vi0, qt0, qd0);
+  // The first vectors have landed before the loop (vmcnt(0)): inside it the
+  // compiler then waits only for the vectors of the round it works on, not for
+  // the prefetch of the next.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  {
+    // Seed L: every lane's highest-scoring element of its first vector gets
+    // its exact total, and L starts at the largest of them over the
+    // workgroup. (The first round tests these elements again: they are
+    // pushed twice, to no effect.)
+    const int base = lo + vi0 * 8;
+    float key = -INFINITY;
+    int ke = -1;
+    if (vi0 < nfull) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float k;
+        if (residual) {
+          const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
+          k = lp2 > lq2 ? residual_log2_bound(lp2, lq2) : -INFINITY;
+        } else {
+          k = (onehot && base + e == xex) ? -INFINITY : el(qt0, e);
+        }
+        if (k > key) {
+          key = k;
+          ke = e;
+        }
+      }
+    }
+    float t0 = -INFINITY;
+    if (ke >= 0) {
+      float klt = 0.0f, kld = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e == ke) {
+          klt = el(qt0, e);
+          if (residual) kld = el(qd0, e);
+        }
+      const int kidx = base + ke;
+      t0 = total(klt, kld, word_at(philox10((uint32_t)kidx >> 2, crow, cseq, ctr3, k0, k1), kidx & 3));
+      best_push(bst, t0, kidx);
+      mine = t0;
+    }
+    const float wm = wave_max(t0);
+    if (lane == 0 && wm != -INFINITY) atomicMax(&sm.lkey, order_key(wm));
+    __syncthreads();
+    const float ls = key_total(__builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(&sm.lkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
+    if (ls != -INFINITY) {
+      set_L(ls);
+      set_bounds();
+    }
+  }
   const int rounds = (nfull + kThreads - 1) / kThreads;  // same for every lane
 #pragma unroll 1
   for (int rnd = 0; rnd < rounds; ++rnd) {
@@ -916,71 +1009,42 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
     fetch(vi + kThreads, qt1, qd1);  // the next round's vector, one round ahead
     const bool have = vi < nfull;
     const int base = lo + vi * 8;
-    float wg[8];  // residual weight bound (>= p - q), 0 if p <= q
+    float bnd[8];  // residual: upper bound on log2 (p - q), -inf if p <= q
     if (residual && have) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
-        const float p = fast_exp2(lp2), r = p - fast_exp2(lq2);
         const bool cand = lp2 > lq2;
-        beta += cand ? r : 0.0f;
         any |= cand ? 1 : 0;
-        wg[e] = cand ? __builtin_fmaf(p, 0x1p-22f, r) : 0.0f;
+        bnd[e] = cand ? residual_log2_bound(lp2, lq2) : -INFINITY;
       }
-    }
-    if (rnd == 0) {
-      // Seed L: the exact total of the wave's highest-scoring element.
-      float key = -INFINITY;
-      int ke = -1;
-      if (have) {
+      if (want_beta) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float k = residual ? (wg[e] > 0.0f ? wg[e] : -INFINITY)
-                                   : ((onehot && base + e == xex) ? -INFINITY : el(qt0, e));
-          if (k > key) {
-            key = k;
-            ke = e;
-          }
+          const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
+          beta += lp2 > lq2 ? fast_exp2(lp2) - fast_exp2(lq2) : 0.0f;
         }
-      }
-      const float wm = wave_max(key);
-      if (wm != -INFINITY) {
-        const uint64_t bal = __ballot(ke >= 0 && key == wm);
-        const int src = (int)__builtin_ctzll(bal);
-        float t0 = -INFINITY;
-        if (lane == src) {
-          float klt = 0.0f, kld = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e == ke) {
-              klt = el(qt0, e);
-              if (residual) kld = el(qd0, e);
-            }
-          const int kidx = base + ke;
-          t0 = total(klt, kld, word_at(philox10((uint32_t)kidx >> 2, crow, cseq, ctr3, k0, k1), kidx & 3));
-          best_push(bst, t0, kidx);
-          mine = t0;
-        }
-        set_L(__shfl(t0, src, 64));
-        set_bounds();
       }
     }
+    Words4 wa, wb;
+    if (have) philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
+    bool surv = false;
     if (have) {
-      Words4 wa, wb;
-      philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
+      // One-hot: the draft token is excluded (xrel: its place in this vector,
+      // if it is there).
+      const int xrel = onehot ? xex - base : -1;
       bool keep[8];
-      bool surv = false;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t w = (e < 4) ? wa.w[e & 3] : wb.w[e & 3];
         if (residual) {
-          keep[e] = wg[e] > 0.0f && may_win_lin_fast(w, wg[e] * lin_scale);
+          keep[e] = may_win_bits(w, __builtin_fmaf(bnd[e], 0x1p23f, log_bias));
         } else {
-          const int t = (int)__builtin_fminf(__builtin_fmaxf(__builtin_fmaf(el(qt0, e), c2s, log_bias), -1.0f), 2147483520.0f);
-          keep[e] = !(onehot && base + e == xex) && may_win_log2_fast(w, t);
+          keep[e] = (e != xrel) & may_win_bits(w, __builtin_fmaf(el(qt0, e), c2s, log_bias));
         }
-        surv |= keep[e];
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) surv |= keep[e];
       if (surv) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -992,8 +1056,23 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
           }
       }
     }
-    set_L(fmaxf(L, wave_max(mine)));
-    set_bounds();
+    // Share and collect totals: only a wave with survivors can have a new one.
+    float Ln = L;
+    if (__ballot(surv) != 0ull) Ln = fmaxf(Ln, wave_max(mine));
+    if (Ln > Lpost) {
+      if (lane == 0) {
+        atomicMax(&sm.lkey, order_key(Ln));
+        atomicMax(gkey, order_key(Ln));
+      }
+      Lpost = Ln;
+    }
+    const uint32_t lk = __builtin_amdgcn_readfirstlane(__hip_atomic_load(&sm.lkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    Ln = fmaxf(Ln, fmaxf(key_total(lk), key_total(__builtin_amdgcn_readfirstlane(gnext))));
+    gnext = xload(gkey);
+    if (Ln > L) {
+      set_L(Ln);
+      set_bounds();
+    }
     qt0 = qt1;
     if (residual) qd0 = qd1;
   }
@@ -1027,7 +1106,7 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
   out->w1 = pack(bsum, (uint32_t)bany);
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool BETA>
 __device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo, int hi, Smem& sm, P2Slot* out) {
   if (d.mode == P2_GREEDY_BONUS) {
     const uint8_t* rt = target_row(a, b, d.row);
@@ -1043,9 +1122,13 @@ __device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo,
     out->w0 = pack(m.v, (uint32_t)m.i);
     out->w1 = pack(0.0f, 1u);
   } else if (BF16 && VEC) {
-    if (d.mode == P2_RESIDUAL) gumbel_chunk_bf16<P2_RESIDUAL>(a, b, d, lo, hi, sm, out);
-    else if (d.mode == P2_RESIDUAL_ONEHOT) gumbel_chunk_bf16<P2_RESIDUAL_ONEHOT>(a, b, d, lo, hi, sm, out);
-    else gumbel_chunk_bf16<P2_BONUS>(a, b, d, lo, hi, sm, out);
+    if (d.mode == P2_RESIDUAL) {
+      gumbel_chunk_bf16<P2_RESIDUAL, BETA>(a, b, d, lo, hi, sm, out);
+    } else if (d.mode == P2_RESIDUAL_ONEHOT) {
+      gumbel_chunk_bf16<P2_RESIDUAL_ONEHOT, false>(a, b, d, lo, hi, sm, out);
+    } else {
+      gumbel_chunk_bf16<P2_BONUS, false>(a, b, d, lo, hi, sm, out);
+    }
   } else if (d.mode == P2_RESIDUAL) {
     gumbel_chunk<BF16, VEC, P2_RESIDUAL>(a, b, d, lo, hi, sm, out);
   } else if (d.mode == P2_RESIDUAL_ONEHOT) {
@@ -1057,11 +1140,11 @@ __device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo,
 
 // Last pass-2 item of b: merge the chunk partials, write the last token and
 // return the sequence's scratch to zero.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool BETA>
 __device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks, Smem& sm) {
   const int C2 = p2_nchunks, G = a.gamma;
   const Decision d = sm.dec;
-  P2Slot* ps = a.p2 + (int64_t)b * C2;
+  P2Slot* ps = a.p2 + (int64_t)b * a.p2_stride;
   if (d.mode != P2_NONE) {
     // Read every partial at once, then merge them in chunk order.
     ArgMax m;
@@ -1096,6 +1179,9 @@ __device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks
     __syncthreads();
     if (d.mode == P2_RESIDUAL && !any) {
       // Empty residual (only through rounding): draw from p at the row instead.
+      // No residual total was ever reported (there was no candidate).
+      if (threadIdx.x == 0) sm.lkey = 0u;
+      __syncthreads();
       Decision fb = d;
       fb.mode = P2_BONUS;
       ArgMax f;
@@ -1104,7 +1190,7 @@ __device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks
       for (int c = 0; c < C2; ++c) {
         P2Slot part;
         const int lo = c * p2_chunk;
-        pass2_chunk<BF16, VEC>(a, b, fb, lo, min(a.V, lo + p2_chunk), sm, &part);
+        pass2_chunk<BF16, VEC, BETA>(a, b, fb, lo, min(a.V, lo + p2_chunk), sm, &part);
         ArgMax o;
         o.v = hi_f(part.w0);
         o.i = (int)lo_u(part.w0);
@@ -1125,7 +1211,20 @@ __device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks
     for (int k = threadIdx.x; k < C2 * 2; k += kThreads) xput64(&w2[k], 0u);
   }
   if (threadIdx.x < 4) xput64(&a.seq[b].dec[threadIdx.x], 0u);
-  if (threadIdx.x == 0) xput(&a.seq[b].p2_arrive, 0u);
+  if (threadIdx.x == 0) {
+    xput(&a.seq[b].p2_arrive, 0u);
+    xput(&a.seq[b].lbest, 0u);
+    if (!a.fused) {
+      // Every item on the work list has read it once all draws are done: the
+      // last sequence to finish returns the list to empty.
+      xput(&a.work[sm.unit[4]], 0u);
+      const uint32_t fin = atomicAdd(&a.done[kDoneNFinal], 1u) + 1u;
+      if (fin == sm.nwork) {
+        xput(&a.done[kDoneNWork], 0u);
+        xput(&a.done[kDoneNFinal], 0u);
+      }
+    }
+  }
 }
 
 // Reads the decision record of b (thread 0; bounded wait in the fused
@@ -1178,7 +1277,7 @@ __device__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
   return true;
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool BETA>
 __device__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p2_nchunks, Smem& sm) {
   if (threadIdx.x == 0) {
     Decision d;
@@ -1190,6 +1289,7 @@ __device__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p
     }
     sm.dec = d;
     sm.stalled = ok ? 0u : 1u;
+    sm.lkey = 0u;
   }
   __syncthreads();
   const Decision d = sm.dec;
@@ -1198,13 +1298,13 @@ __device__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p
   part.w1 = 0u;
   if (d.mode != P2_NONE) {
     const int lo = c * p2_chunk;
-    pass2_chunk<BF16, VEC>(a, b, d, lo, min(a.V, lo + p2_chunk), sm, &part);
+    pass2_chunk<BF16, VEC, BETA>(a, b, d, lo, min(a.V, lo + p2_chunk), sm, &part);
   }
   if (threadIdx.x == 0) {
     sm.flag_last = 0u;
     if (!sm.stalled) {
       if (d.mode != P2_NONE) {
-        P2Slot* dst = a.p2 + (int64_t)b * p2_nchunks + c;
+        P2Slot* dst = a.p2 + (int64_t)b * a.p2_stride + c;
         xput64(&dst->w0, part.w0);
         xput64(&dst->w1, part.w1);
         wait_vmem();  // the slot has landed before the arrival
@@ -1214,7 +1314,7 @@ __device__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p
     }
   }
   __syncthreads();
-  if (sm.flag_last) finalize<BF16, VEC>(a, b, p2_chunk, p2_nchunks, sm);
+  if (sm.flag_last) finalize<BF16, VEC, BETA>(a, b, p2_chunk, p2_nchunks, sm);
   __syncthreads();
 }
 
@@ -1223,7 +1323,7 @@ __device__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p
 // ---------------------------------------------------------------------------
 // Fused: group g = [pass-1 items of g][decision of g - lag_d][pass-2 items of
 // g - lag_2], for g in [0, B + lag_2).
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool BETA>
 __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   __shared__ Smem sm;
   const int n1 = p1_items_per_seq(a), per = n1 + 1 + a.p2_nchunks;
@@ -1236,7 +1336,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     if (b >= 0 && b < a.B) decide<BF16>(a, b, sm);
   } else {
     const int b = g - a.lag2;
-    if (b >= 0 && b < a.B) pass2_item<BF16, VEC>(a, b, r - n1 - 1, a.p2_chunk, a.p2_nchunks, sm);
+    if (b >= 0 && b < a.B) pass2_item<BF16, VEC, BETA>(a, b, r - n1 - 1, a.p2_chunk, a.p2_nchunks, sm);
   }
 }
 
@@ -1257,13 +1357,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   }
 }
 
-// Split, second launch: every decision is taken; one workgroup per (b, chunk).
-template <bool BF16, bool VEC>
+// Split, second launch: every decision is taken and the sequences with a
+// pending draw are on the work list. Their rows are cut into as many chunks
+// as fill the launch's workgroups (one resident wave of them), and workgroup
+// u takes chunk u mod n of list entry u / n; the others have nothing to do.
+template <bool BF16, bool VEC, bool BETA>
 __global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
   __shared__ Smem sm;
-  const int b = blockIdx.x / a.p2_nchunks;
-  const int c = blockIdx.x % a.p2_nchunks;
-  pass2_item<BF16, VEC>(a, b, c, a.p2_chunk, a.p2_nchunks, sm);
+  if (threadIdx.x == 0) {
+    const uint32_t nw = min(xload(&a.done[kDoneNWork]), (uint32_t)a.B);
+    int b = -1, c = 0, len = 0, nc = 0, li = 0;
+    if (nw > 0) {
+      int c2 = a.p2_force > 0 ? a.p2_force : a.p2_grid / (int)nw;
+      c2 = max(1, min(c2, a.p2_cap));
+      len = (a.V + c2 - 1) / c2;
+      len = (len + a.p2_unit - 1) / a.p2_unit * a.p2_unit;
+      nc = (a.V + len - 1) / len;
+      const uint32_t u = blockIdx.x;
+      if (u < nw * (uint32_t)nc) {
+        li = (int)(u / (uint32_t)nc);
+        b = (int)xload(&a.work[li]);
+        c = (int)(u % (uint32_t)nc);
+        if (b >= a.B) b = -1;
+      }
+    }
+    sm.nwork = nw;
+    sm.unit[0] = b;
+    sm.unit[1] = c;
+    sm.unit[2] = len;
+    sm.unit[3] = nc;
+    sm.unit[4] = li;
+  }
+  __syncthreads();
+  const int b = sm.unit[0];
+  if (b < 0) return;
+  pass2_item<BF16, VEC, BETA>(a, b, sm.unit[1], sm.unit[2], sm.unit[3], sm);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t nwords) {
@@ -1275,7 +1403,10 @@ template <bool BF16, bool VEC>
 hipError_t launch_chain_t(const ChainArgs& a, hipStream_t stream) {
   const long long n1 = (long long)a.gamma * a.nchunks * (a.draft != nullptr ? 2 : 1);
   const long long grid = (long long)(a.B + a.lag2) * (n1 + 1 + a.p2_nchunks);
-  hipLaunchKernelGGL((chain_kernel<BF16, VEC>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  if (a.d_beta)
+    hipLaunchKernelGGL((chain_kernel<BF16, VEC, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((chain_kernel<BF16, VEC, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1288,14 +1419,18 @@ hipError_t launch_chain_p1_t(const ChainArgs& a, hipStream_t stream) {
 
 template <bool BF16, bool VEC>
 hipError_t launch_chain_p2_t(const ChainArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((chain_p2_kernel<BF16, VEC>), dim3(a.B * a.p2_nchunks), dim3(kThreads), 0, stream, a);
+  // The variant that also sums the residual mass runs only for diagnostics.
+  if (a.d_beta)
+    hipLaunchKernelGGL((chain_p2_kernel<BF16, VEC, true>), dim3((unsigned)a.p2_grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((chain_p2_kernel<BF16, VEC, false>), dim3((unsigned)a.p2_grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool BF16, bool VEC>
 int occupancy_t() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chain_kernel<BF16, VEC>, kThreads, 0) != hipSuccess) n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chain_kernel<BF16, VEC, false>, kThreads, 0) != hipSuccess) n = 0;
   return n;
 }
 
@@ -1314,6 +1449,18 @@ hipError_t launch_chain_p1(const ChainArgs& a, bool bf16, bool vec, hipStream_t 
 hipError_t launch_chain_p2(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream) {
   if (bf16) return vec ? launch_chain_p2_t<true, true>(a, stream) : launch_chain_p2_t<true, false>(a, stream);
   return vec ? launch_chain_p2_t<false, true>(a, stream) : launch_chain_p2_t<false, false>(a, stream);
+}
+
+template <bool BF16, bool VEC>
+int p2_occupancy_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chain_p2_kernel<BF16, VEC, false>, kThreads, 0) != hipSuccess) n = 0;
+  return n;
+}
+
+int chain_p2_occupancy(bool bf16, bool vec) {
+  if (bf16) return vec ? p2_occupancy_t<true, true>() : p2_occupancy_t<true, false>();
+  return vec ? p2_occupancy_t<false, true>() : p2_occupancy_t<false, false>();
 }
 
 int chain_occupancy(bool bf16, bool vec) {

@@ -302,6 +302,11 @@ __device__ __forceinline__ void xput(float* p, float v) { atomicExch((uint32_t*)
 __device__ __forceinline__ uint32_t xget(uint32_t* p) { return atomicOr(p, 0u); }
 __device__ __forceinline__ int32_t xget(int32_t* p) { return atomicOr(p, 0); }
 __device__ __forceinline__ float xget(float* p) { return __uint_as_float(atomicOr((uint32_t*)p, 0u)); }
+// Plain device-scope atomic load of a 32-bit word (no read-modify-write: many
+// readers of one word do not serialize).
+__device__ __forceinline__ uint32_t xload(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // 64-bit words: device-scope atomic loads and stores (single-copy atomic).
 __device__ __forceinline__ void xput64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

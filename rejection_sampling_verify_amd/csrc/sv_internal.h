@@ -26,7 +26,9 @@ enum P2Mode : uint32_t {
 // between calls.
 struct SeqState {
   uint32_t p2_arrive;  // pass-2 items finished
-  uint32_t pad0[3];
+  uint32_t lbest;      // pass 2: the largest Gumbel total any item of the
+                       // sequence has reached so far, as an order key (0: none)
+  uint32_t pad0[2];
   // The decision record:
   //   dec[1] = (zt2 bits << 32) | zd2 bits     (log2-domain normalizers)
   //   dec[2] = (c2 bits << 32) | invT bits
@@ -38,6 +40,13 @@ struct SeqState {
 };
 static_assert(sizeof(SeqState) == 128, "one line per sequence");
 constexpr uint64_t kRecPublished = 1ull << 63;
+
+// Words of the workspace's control line (ChainArgs::done), on their own
+// 128-byte line: sequences appended to the pass-2 work list by the first of two
+// launches, and sequences whose pass-2 draw the second launch has finished.
+// The last of those returns both to zero.
+constexpr int kDoneNWork = 32;
+constexpr int kDoneNFinal = 33;
 
 // Pass-1 result of one chunk of one row pair, published as two 64-bit words:
 //   sampled:  w0 = (M_target bits << 32) | s_target bits,
@@ -70,8 +79,13 @@ struct ChainArgs {
   int32_t chunk;    // elements per pass-1 chunk
   int32_t nchunks;  // pass-1 chunks per row
   int32_t kv;       // 16-byte vectors per thread per pass-1 chunk (<= kMaxVecsPerThread)
-  int32_t p2_chunk;    // elements per pass-2 chunk
-  int32_t p2_nchunks;  // pass-2 chunks per row
+  int32_t p2_chunk;    // fused launch: elements per pass-2 chunk
+  int32_t p2_nchunks;  // fused launch: pass-2 chunks per row
+  int32_t p2_stride;   // pass-2 slots per sequence (>= any chunk count)
+  int32_t p2_grid;     // two launches: workgroups of the second launch
+  int32_t p2_cap;      // two launches: most pass-2 chunks per row
+  int32_t p2_force;    // two launches: chunks per row when > 0 (else sized to fill p2_grid)
+  int32_t p2_unit;     // pass-2 chunk lengths are multiples of this
   uint32_t key0, key1;
   uint32_t ctr_accept, ctr_noise;  // counter word 3 of the two Philox streams
   int32_t* out_tokens;
@@ -80,11 +94,14 @@ struct ChainArgs {
   float* d_logzt;
   float* d_logzd;
   float* d_beta;
-  uint32_t* done;     // [1]: nonzero once a bounded wait gave up (the workspace
-                      // must then be re-initialized before its next use)
+  uint32_t* done;     // [64]: [1] nonzero once a bounded wait gave up (the
+                      // workspace must then be re-initialized before its next
+                      // use); [kDoneNWork], [kDoneNFinal]: the pass-2 work list
   SeqState* seq;      // [B]
   P1Slot* p1;         // [B, gamma, nchunks]
-  P2Slot* p2;         // [B, p2_nchunks]
+  P2Slot* p2;         // [B, p2_stride]
+  uint32_t* work;     // [B] two launches: sequences with pass-2 work, in the
+                      // order their decisions were taken
   int32_t lag;        // fused launch: the decision of sequence k follows the
                       // pass-1 items of k + lag,
   int32_t lag2;       // and its pass-2 items those of k + lag2 (lag2 >= lag)
@@ -152,7 +169,7 @@ __device__ __forceinline__ int decode_item(const Layout& q, uint32_t t, int* k, 
 
 // Workspace carve-up; every offset is a multiple of 256 bytes.
 struct WsLayout {
-  size_t done, seq, p1, p2, tree_slot, total;
+  size_t done, seq, p1, p2, tree_slot, work, total;
 };
 
 WsLayout ws_layout(int32_t B, int32_t rows, int32_t nchunks);
@@ -166,5 +183,6 @@ hipError_t launch_tree(const TreeArgs& a, bool bf16, bool vec, hipStream_t strea
 int tree_occupancy(bool bf16, bool vec);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 int chain_occupancy(bool bf16, bool vec);
+int chain_p2_occupancy(bool bf16, bool vec);
 
 }  // namespace sv

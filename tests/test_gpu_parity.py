@@ -201,6 +201,20 @@ def test_workspace_reuse_across_shapes(dev):
     assert int(ws.count_nonzero().item()) == 0
 
 
+def test_more_sequences_than_resident_workgroups(dev):
+    """More sequences with a pending draw than pass-2 workgroups fit on the
+    GPU at once: one chunk per row, every sequence still drawn, oracle-exact,
+    workspace left zero."""
+    import rejection_sampling_verify_amd as rsv
+    B, G, V = 2600, 3, 900
+    inp = make_chain("many", B, G, V, bf16=True, seed=41, target_sigma=2.0, draft_sigma=1.0,
+                     temperatures=(0.0, 0.8, 1.0))
+    ws = rsv.Workspace(dev).get(B, G + 1, V)
+    got = run_sample(inp, torch, dev, workspace=ws)
+    compare_chain(got, oracle_sample(inp), label="many sequences")
+    assert int(ws.count_nonzero().item()) == 0
+
+
 # -------------------------------------------------------------------------
 # Trees
 # -------------------------------------------------------------------------
