@@ -876,6 +876,16 @@ __device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int 
   out->w1 = pack(bsum, (uint32_t)bany);
 }
 
+// How many rounds ahead (0 or 1) the bf16 Gumbel loop loads its vectors. With
+// few waves per SIMD, as at the end of the pass or for small batches, a
+// round's load latency is otherwise exposed; the lead costs 4 registers per
+// row read.
+#ifndef SV_P2_DEPTH
+#define SV_P2_DEPTH 1
+#endif
+constexpr int kP2Depth = SV_P2_DEPTH;
+static_assert(kP2Depth == 0 || kP2Depth == 1, "lead of 0 or 1 round");
+
 // One chunk of a Gumbel-max draw over 16-byte-aligned bf16 rows. Each lane
 // takes one 8-element vector per round (prefetched a round ahead), forms the
 // Philox words of its two 4-element blocks and a cheap, conservative pruning
@@ -941,7 +951,8 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
   };
   set_bounds();
   const int nfull = (hi - lo) / 8;
-  u32x4 qt0, qt1, qd0, qd1;
+  constexpr int D = kP2Depth;
+  u32x4 qt[D + 1], qd[D + 1];  // qt[0], qd[0]: this round's vectors
   const int vi0 = (int)threadIdx.x;
   auto fetch = [&](int vi, u32x4& qt, u32x4& qd) {
     if (vi < nfull) {
@@ -949,11 +960,14 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
       if (residual) qd = load_vec_stream(rd + (int64_t)(lo + vi * 8) * 2);
     }
   };
-  fetch(vi0, qt0, qd0);
+#pragma unroll
+  for (int j = 0; j < (D > 0 ? D : 1); ++j) fetch(vi0 + j * kThreads, qt[j], qd[j]);
   // The first vectors have landed before the loop (vmcnt(0)): inside it the
   // compiler then waits only for the vectors of the round it works on, not for
-  // the prefetch of the next.
+  // the prefetches of the next.
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  const u32x4& qt0 = qt[0];  // the seed's vectors
+  const u32x4& qd0 = qd[0];
   {
     // Seed L: every lane's highest-scoring element of its first vector gets
     // its exact total, and L starts at the largest of them over the
@@ -1003,31 +1017,27 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
     }
   }
   const int rounds = (nfull + kThreads - 1) / kThreads;  // same for every lane
-#pragma unroll 1
-  for (int rnd = 0; rnd < rounds; ++rnd) {
+  // One round over vectors qt0/qd0, starting the load of round rnd + D into
+  // qn/dn. (A deeper lead would need the loop unrolled, to rotate buffers
+  // without moves that wait for the loads, and costs more registers than the
+  // waves it would save.)
+  auto round = [&](int rnd, const u32x4& qt0, const u32x4& qd0, u32x4& qn, u32x4& dn) {
     const int vi = vi0 + rnd * kThreads;
-    fetch(vi + kThreads, qt1, qd1);  // the next round's vector, one round ahead
+    // The sequence's best total, read now and used at the end of the round.
+    const uint32_t gk = xload(gkey);
+    if (D > 0) fetch(vi + D * kThreads, qn, dn);
     const bool have = vi < nfull;
     const int base = lo + vi * 8;
-    float bnd[8];  // residual: upper bound on log2 (p - q), -inf if p <= q
-    if (residual && have) {
+    // The Philox words first: they do not wait for the vectors.
+    Words4 wa, wb;
+    if (have) philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
+    if (want_beta && have) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
-        const bool cand = lp2 > lq2;
-        any |= cand ? 1 : 0;
-        bnd[e] = cand ? residual_log2_bound(lp2, lq2) : -INFINITY;
-      }
-      if (want_beta) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
-          beta += lp2 > lq2 ? fast_exp2(lp2) - fast_exp2(lq2) : 0.0f;
-        }
+        beta += lp2 > lq2 ? fast_exp2(lp2) - fast_exp2(lq2) : 0.0f;
       }
     }
-    Words4 wa, wb;
-    if (have) philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
     bool surv = false;
     if (have) {
       // One-hot: the draft token is excluded (xrel: its place in this vector,
@@ -1038,7 +1048,12 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
       for (int e = 0; e < 8; ++e) {
         const uint32_t w = (e < 4) ? wa.w[e & 3] : wb.w[e & 3];
         if (residual) {
-          keep[e] = may_win_bits(w, __builtin_fmaf(bnd[e], 0x1p23f, log_bias));
+          // Upper bound on log2 (p - q), -inf if p <= q.
+          const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
+          const bool cand = lp2 > lq2;
+          any |= cand ? 1 : 0;
+          const float bnd = cand ? residual_log2_bound(lp2, lq2) : -INFINITY;
+          keep[e] = may_win_bits(w, __builtin_fmaf(bnd, 0x1p23f, log_bias));
         } else {
           keep[e] = (e != xrel) & may_win_bits(w, __builtin_fmaf(el(qt0, e), c2s, log_bias));
         }
@@ -1067,14 +1082,25 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
       Lpost = Ln;
     }
     const uint32_t lk = __builtin_amdgcn_readfirstlane(__hip_atomic_load(&sm.lkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-    Ln = fmaxf(Ln, fmaxf(key_total(lk), key_total(__builtin_amdgcn_readfirstlane(gnext))));
-    gnext = xload(gkey);
+    Ln = fmaxf(Ln, fmaxf(key_total(lk), key_total(__builtin_amdgcn_readfirstlane(gk))));
     if (Ln > L) {
       set_L(Ln);
       set_bounds();
     }
-    qt0 = qt1;
-    if (residual) qd0 = qd1;
+  };
+  if (D == 0) {
+#pragma unroll 1
+    for (int rnd = 0; rnd < rounds; ++rnd) {
+      if (rnd > 0) fetch(vi0 + rnd * kThreads, qt[0], qd[0]);
+      round(rnd, qt[0], qd[0], qt[0], qd[0]);
+    }
+  } else {
+#pragma unroll 1
+    for (int rnd = 0; rnd < rounds; ++rnd) {
+      round(rnd, qt[0], qd[0], qt[1], qd[1]);
+      qt[0] = qt[1];
+      if (residual) qd[0] = qd[1];
+    }
   }
   // Elements past the last whole vector, one by one.
   const int tail_lo = lo + nfull * 8;
