@@ -201,6 +201,26 @@ def test_workspace_reuse_across_shapes(dev):
     assert int(ws.count_nonzero().item()) == 0
 
 
+@pytest.mark.parametrize("name", ["chain_bf16_peaked", "chain_bf16_llama", "onehot_bf16_qwen"])
+def test_without_diagnostics(dev, monkeypatch, name):
+    """The call without diagnostic outputs (the kernels that skip the residual
+    mass, as the benchmark runs them) gives the same ids and lengths as the
+    call with them, at the default and at forced pass-2 chunk counts, and
+    matches the oracle."""
+    inp = workloads.make(name)
+    ref = oracle_sample(inp)
+    with_diag = run_sample(inp, torch, dev)
+    for chunks in (None, "1", "5"):
+        monkeypatch.delenv("SV_P2_CHUNKS", raising=False)
+        if chunks:
+            monkeypatch.setenv("SV_P2_CHUNKS", chunks)
+        got = run_sample(inp, torch, dev, diag=False)
+        assert np.array_equal(got["n"], with_diag["n"]), (name, chunks)
+        assert np.array_equal(got["tokens"], with_diag["tokens"]), (name, chunks)
+        compare_chain(got, ref, check_diag=False, label="%s no diagnostics" % name)
+    monkeypatch.delenv("SV_P2_CHUNKS", raising=False)
+
+
 def test_more_sequences_than_resident_workgroups(dev):
     """More sequences with a pending draw than pass-2 workgroups fit on the
     GPU at once: one chunk per row, every sequence still drawn, oracle-exact,
