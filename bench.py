@@ -6,7 +6,11 @@ logits, temperatures drawn from {0, 0.7, 1.0}), inputs resident in HBM. Prints
 one JSON line: verified positions/s (B * gamma per step) as `value`, the
 logit-read bandwidth against the HBM roofline of one verify call (the kernels
 it launches back to back on one stream, timed with HIP events on that stream),
-and the CPU oracle timed on the host as a baseline.
+and the CPU oracle timed on the host as a baseline (all host threads, and one).
+Beside the roofline it reports the GPU's streaming-read rate measured in the
+same run (the library's read yardstick over a 2 GiB buffer) and the call's
+fraction of it, and a warm-cache launch time (the same input copy every step,
+labelled as such; the timed steps alternate two copies).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -62,14 +66,15 @@ def to_dev(a, torch, dev):
     return torch.from_numpy(a).to(dev)
 
 
-def cpu_baseline(inp, is_tree: bool, positions_per_step: int):
-    """The oracle as it stands, on all host threads (capped at 16), over the
-    whole workload; repeated until about 10 s of CPU time or 3 runs."""
+def cpu_baseline(inp, is_tree: bool, positions_per_step: int, threads: int | None = None, max_runs: int = 3):
+    """The oracle as it stands, on all host threads (capped at 16) unless
+    told otherwise, over the whole workload; repeated until about 10 s of CPU
+    time or max_runs runs."""
     import oracle
-    threads = min(16, os.cpu_count() or 1)
+    threads = threads or min(16, os.cpu_count() or 1)
     times = []
     t_start = time.perf_counter()
-    while len(times) < 3 and (not times or time.perf_counter() - t_start < 10.0):
+    while len(times) < max_runs and (not times or time.perf_counter() - t_start < 10.0):
         t0 = time.perf_counter()
         if is_tree:
             oracle.verify_tree(inp.target, inp.parents, inp.depth, inp.node_tokens, inp.max_depth, nthreads=threads)
@@ -80,6 +85,25 @@ def cpu_baseline(inp, is_tree: bool, positions_per_step: int):
     t = float(np.median(times))
     return {"value": positions_per_step / t, "unit": "verified positions/s", "cores": threads, "kind": "oracle",
             "sample": "the whole workload (one step), %d run(s), median %.3f s, fp64 plain loops" % (len(times), t)}
+
+
+def read_ceiling(torch, dev, rsv, nbytes: int = 2 << 30, launches: int = 10):
+    """Streaming-read rate of this GPU: one plain read of a 2 GiB buffer per
+    launch (the library's read yardstick), HIP events around each launch."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    nblocks = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(4 * nblocks, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        rsv.sv_debug_read_stream(buf, nblocks, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in ev:
+        a.record()
+        rsv.sv_debug_read_stream(buf, nblocks, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def copy_calibration(torch, dev, steps: int):
@@ -174,6 +198,20 @@ def main():
     launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
 
+    # Warm cache, labelled as such: the same input copy every step, so that
+    # part of it is still in the 256 MB MALL from the step before.
+    warm = []
+    for k in range(max(5, args.steps // 5)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(0)
+        b.record(stream)
+        warm.append((a, b))
+    torch.cuda.synchronize()
+    warm_ms = np.array([a.elapsed_time(b) for a, b in warm])
+    ceiling = read_ceiling(torch, dev, rsv)
+    print("[bench] warm-cache steps and read ceiling done", file=sys.stderr, flush=True)
+
     ms_per_step = wall * 1e3 / args.steps
     alg_bytes = inp.algorithmic_bytes()
     t_launch = float(np.mean(launch_ms)) * 1e-3
@@ -207,11 +245,15 @@ def main():
                       "p50": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "hbm_read_ceiling_GBps": ceiling,
+        "frac_of_read_ceiling": achieved / ceiling,
+        "warm_cache_launch_ms": {"p50": float(np.median(warm_ms)), "note": "same input copy every step"},
         **extra,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, is_tree, positions)
+        rec["cpu_baseline_1thread"] = cpu_baseline(inp, is_tree, positions, threads=1, max_runs=1)
     print(json.dumps(rec), flush=True)
 
 

@@ -223,6 +223,16 @@ sv_status_t sv_debug_noise(const uint32_t* words, float* gumbel_out, float* unif
  * every lane writes its result: out[64w + j] = max of the group, for all j.
  * in, out: device fp32 arrays of 64 * nwaves elements. */
 sv_status_t sv_debug_wave_max(const float* in, float* out, int32_t nwaves, void* stream);
+/* sv_debug_read_stream — the read-bandwidth yardstick for the verify kernels
+ * (no operation of the pages): reads the `bytes` bytes at src (device,
+ * 16-byte aligned, bytes a multiple of 16) once with 16-byte nontemporal
+ * loads over a grid of nblocks workgroups of 256 threads (each a contiguous
+ * share of the buffer), and writes the XOR
+ * of the 32-bit words each wavefront read to out[4 * block + wave] (out:
+ * device, 4 * nblocks words). Returns SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE
+ * (nblocks < 1 or bytes not a multiple of 16), SV_ERR_BAD_ARG (src not 16-byte
+ * aligned) or SV_ERR_HIP. */
+sv_status_t sv_debug_read_stream(const void* src, size_t bytes, uint32_t* out, int32_t nblocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,8 @@ SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max"]
+           "spec_verify_greedy", "spec_verify_tree", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
+           "sv_debug_read_stream"]
 
 _lib = None
 
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.sv_debug_noise.restype = ctypes.c_int
         L.sv_debug_wave_max.argtypes = [P, P, i32, P]
         L.sv_debug_wave_max.restype = ctypes.c_int
+        L.sv_debug_read_stream.argtypes = [P, sz, P, i32, P]
+        L.sv_debug_read_stream.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -258,6 +261,19 @@ def sv_debug_noise(words, stream=None):
     if st != 0:
         raise SVError(st, "sv_debug_noise")
     return g, u
+
+
+def sv_debug_read_stream(buf, nblocks: int, out=None, stream=None):
+    """One plain streaming read of a device buffer (the read-bandwidth
+    yardstick); returns the [4 * nblocks] int32 tensor of per-wave XOR folds."""
+    import torch
+    if out is None:
+        out = torch.empty(4 * nblocks, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().sv_debug_read_stream(_ptr(buf), nbytes, _ptr(out), nblocks, _stream(stream))
+    if st != 0:
+        raise SVError(st, "sv_debug_read_stream")
+    return out
 
 
 def sv_debug_wave_max(x, stream=None):

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert set(names) >= {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree", "sv_workspace_bytes",
                           "sv_workspace_init", "sv_status_string", "sv_debug_philox", "sv_debug_noise",
-                          "sv_debug_wave_max"}
+                          "sv_debug_wave_max", "sv_debug_read_stream"}
     out = subprocess.run(["nm", "-D", "--defined-only", rsv.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     missing = [n for n in names if n not in exported]
@@ -107,4 +107,9 @@ def test_greedy_and_tree_argument_validation(L):
     assert L.sv_debug_philox(None, P, P, 1, None) == 1
     assert L.sv_debug_noise(P, None, None, -1, None) == 2
     assert L.sv_debug_wave_max(None, P, 1, None) == 1 and L.sv_debug_wave_max(P, P, -1, None) == 2
+    # the read yardstick: validation happens before any launch
+    A16, A17 = ctypes.c_void_p(4096), ctypes.c_void_p(4097)
+    assert L.sv_debug_read_stream(None, 16, P, 1, None) == 1 and L.sv_debug_read_stream(A16, 16, None, 1, None) == 1
+    assert L.sv_debug_read_stream(A16, 16, P, 0, None) == 2 and L.sv_debug_read_stream(A16, 15, P, 1, None) == 2
+    assert L.sv_debug_read_stream(A17, 16, P, 1, None) == 4
     assert L.sv_workspace_init(None, 1024, None) == 1

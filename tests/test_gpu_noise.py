@@ -139,3 +139,18 @@ def test_wave_max(dev):
     torch.cuda.synchronize()
     want = np.repeat(x.reshape(-1, 64).max(axis=1), 64)
     assert np.array_equal(out, want)
+
+
+def test_read_stream_reads_every_word_once(dev):
+    """The read-bandwidth yardstick reads each 16-byte word exactly once: the
+    XOR of its per-wave folds equals the XOR of all words, for a ragged size
+    and an odd grid."""
+    import rejection_sampling_verify_amd as rsv
+    rng = np.random.default_rng(9)
+    for nwords, nblocks in ((4 * (1 << 20) + 12, 37), (4 * 1000, 2048), (4, 1)):
+        h = rng.integers(0, 1 << 32, size=nwords, dtype=np.uint64).astype(np.uint32)
+        buf = torch.from_numpy(h.view(np.int32)).to(dev)
+        out = rsv.sv_debug_read_stream(buf, nblocks)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(h), (nwords, nblocks)
