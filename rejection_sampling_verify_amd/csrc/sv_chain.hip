@@ -412,6 +412,16 @@ __device__ __forceinline__ bool may_win_bits(uint32_t w, float t) {
   return !((float)(int)__float_as_uint((float)(~w)) > t);
 }
 
+// may_win_bits over a wave: the mask of active lanes whose element may win,
+// straight from the compare (a ballot of the verdict costs two more vector
+// operations per element). Same test, also true for an unordered compare.
+__device__ __forceinline__ uint64_t lanes_may_win(uint32_t w, float t) {
+  const float n = (float)(int)__float_as_uint((float)(~w));
+  uint64_t m;
+  asm("v_cmp_ngt_f32 %0, %1, %2" : "=s"(m) : "v"(n), "v"(t));
+  return m;
+}
+
 // Upper bound, in log2 units, on log2 (p - q) for log2 p = lp2 > lq2 = log2 q:
 // p - q = p (1 - 2^-d) with d = lp2 - lq2, and 1 - e^-x <= min(1, x), so
 // log2 (p - q) <= lp2 + min(0, log2 d + log2 ln 2). log2 d is bounded from
@@ -895,6 +905,21 @@ static_assert(kP2Depth == 0 || kP2Depth == 1, "lead of 0 or 1 round");
 // another wave of the workgroup (through LDS) or another workgroup of the
 // same row (through the sequence record, read one round late) reports a
 // higher total.
+// Wave priority from progress through a chunk: 3 in its first quarter of
+// rounds, down to 0 in its last. The pass-2 workgroups of a launch start
+// together with equal work, and a SIMD otherwise issues its oldest wave
+// first, so those dispatched last would finish last by far; a wave that is
+// ahead now yields to those behind it. (Wave priority only, set with
+// s_setprio; the queues and streams keep their default priority.)
+__device__ __forceinline__ void set_phase_priority(int rnd, int rounds) {
+  const int ph = (4 * rnd) / rounds;
+  if (rnd > 0 && ph == (4 * (rnd - 1)) / rounds) return;
+  if (ph == 0) __builtin_amdgcn_s_setprio(3);
+  else if (ph == 1) __builtin_amdgcn_s_setprio(2);
+  else if (ph == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 template <int MODE, bool BETA>
 __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm,
                                   P2Slot* out) {
@@ -1030,7 +1055,9 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
     const int base = lo + vi * 8;
     // The Philox words first: they do not wait for the vectors.
     Words4 wa, wb;
-    if (have) philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
+    // (Every lane forms them: a lane past the chunk's end costs the wave
+    // nothing more, and its words are masked out below.)
+    philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
     if (want_beta && have) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -1038,42 +1065,51 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
         beta += lp2 > lq2 ? fast_exp2(lp2) - fast_exp2(lq2) : 0.0f;
       }
     }
-    bool surv = false;
-    if (have) {
+    // The fast test of element e: its threshold t for the bit-pattern test
+    // of its noise word. For the residual it uses the bound on log2 (p - q)
+    // without first asking whether p > q (for p <= q the bound is at most
+    // log2 p - 100, which the survivor path then discards), and for one-hot
+    // draws it does not exclude the draft token (the survivor path does).
+    auto fast_t = [&](int e) -> float {
+      if (residual) {
+        const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
+        return __builtin_fmaf(residual_log2_bound(lp2, lq2), 0x1p23f, log_bias);
+      }
+      return __builtin_fmaf(el(qt0, e), c2s, log_bias);
+    };
+    // Only whether some lane of the wave has a survivor is kept: the
+    // verdicts are lane masks OR-ed on the scalar unit.
+    uint64_t surv = 0ull;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) surv |= lanes_may_win((e < 4) ? wa.w[e & 3] : wb.w[e & 3], fast_t(e));
+    surv &= __builtin_amdgcn_ballot_w64(have);
+    if (surv != 0ull && have) {
       // One-hot: the draft token is excluded (xrel: its place in this vector,
       // if it is there).
       const int xrel = onehot ? xex - base : -1;
-      bool keep[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w = (e < 4) ? wa.w[e & 3] : wb.w[e & 3];
+        uint32_t w = (e < 4) ? wa.w[e & 3] : wb.w[e & 3];
+        // Tested again on a word the compiler cannot match with the first
+        // test, so that it does not keep the eight verdicts in registers.
+        asm volatile("" : "+v"(w));
+        bool k;
         if (residual) {
-          // Upper bound on log2 (p - q), -inf if p <= q.
           const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
-          const bool cand = lp2 > lq2;
-          any |= cand ? 1 : 0;
-          const float bnd = cand ? residual_log2_bound(lp2, lq2) : -INFINITY;
-          keep[e] = may_win_bits(w, __builtin_fmaf(bnd, 0x1p23f, log_bias));
+          k = lp2 > lq2 && may_win_bits(w, __builtin_fmaf(residual_log2_bound(lp2, lq2), 0x1p23f, log_bias));
         } else {
-          keep[e] = (e != xrel) & may_win_bits(w, __builtin_fmaf(el(qt0, e), c2s, log_bias));
+          k = (e != xrel) && may_win_bits(w, __builtin_fmaf(el(qt0, e), c2s, log_bias));
         }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) surv |= keep[e];
-      if (surv) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (keep[e]) {
-            const uint32_t w = (e < 4) ? wa.w[e & 3] : wb.w[e & 3];
-            const float tot = total(el(qt0, e), residual ? el(qd0, e) : 0.0f, w);
-            best_push(bst, tot, base + e);
-            mine = fmaxf(mine, tot);
-          }
+        if (k) {
+          const float tot = total(el(qt0, e), residual ? el(qd0, e) : 0.0f, w);
+          best_push(bst, tot, base + e);
+          mine = fmaxf(mine, tot);
+        }
       }
     }
     // Share and collect totals: only a wave with survivors can have a new one.
     float Ln = L;
-    if (__ballot(surv) != 0ull) Ln = fmaxf(Ln, wave_max(mine));
+    if (surv != 0ull) Ln = fmaxf(Ln, wave_max(mine));
     if (Ln > Lpost) {
       if (lane == 0) {
         atomicMax(&sm.lkey, order_key(Ln));
@@ -1091,12 +1127,14 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
   if (D == 0) {
 #pragma unroll 1
     for (int rnd = 0; rnd < rounds; ++rnd) {
+      set_phase_priority(rnd, rounds);
       if (rnd > 0) fetch(vi0 + rnd * kThreads, qt[0], qd[0]);
       round(rnd, qt[0], qd[0], qt[0], qd[0]);
     }
   } else {
 #pragma unroll 1
     for (int rnd = 0; rnd < rounds; ++rnd) {
+      set_phase_priority(rnd, rounds);
       round(rnd, qt[0], qd[0], qt[1], qd[1]);
       qt[0] = qt[1];
       if (residual) qd[0] = qd[1];
@@ -1122,6 +1160,12 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
       if (keep) best_push(bst, total(lt, ld, w), idx);
     }
   }
+  // A residual chunk with a candidate (p > q) has a finite best total: the
+  // pruning skips an element only below a total some element of the row has
+  // reached, and with no such total yet every candidate is evaluated. So the
+  // row has a candidate iff some chunk reports a finite best; the main loop
+  // does not track candidates separately.
+  if (residual && bst.i >= 0) any = 1;
   ArgMax m;
   m.v = bst.s;
   m.i = bst.i;
@@ -1132,21 +1176,28 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
   out->w1 = pack(bsum, (uint32_t)bany);
 }
 
+// Greedy bonus draw over [lo, hi): the target row's argmax (lowest index on
+// ties).
+template <bool BF16, bool VEC>
+__device__ void greedy_chunk(const ChainArgs& a, int b, const Decision d, int lo, int hi, Smem& sm, P2Slot* out) {
+  const uint8_t* rt = target_row(a, b, d.row);
+  ArgMax best;
+  best.v = -INFINITY;
+  best.i = -1;
+  for (int lo2 = lo; lo2 < hi; lo2 += a.chunk) {  // in pass-1 sized pieces
+    Chunk<BF16, VEC> ct;
+    ct.load(rt, lo2, min(hi, lo2 + a.chunk), a.kv);
+    best = argmax_merge(best, chunk_argmax(ct, rt, a.kv));
+  }
+  const ArgMax m = block_argmax(best, sm);
+  out->w0 = pack(m.v, (uint32_t)m.i);
+  out->w1 = pack(0.0f, 1u);
+}
+
 template <bool BF16, bool VEC, bool BETA>
 __device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo, int hi, Smem& sm, P2Slot* out) {
   if (d.mode == P2_GREEDY_BONUS) {
-    const uint8_t* rt = target_row(a, b, d.row);
-    ArgMax best;
-    best.v = -INFINITY;
-    best.i = -1;
-    for (int lo2 = lo; lo2 < hi; lo2 += a.chunk) {  // in pass-1 sized pieces
-      Chunk<BF16, VEC> ct;
-      ct.load(rt, lo2, min(hi, lo2 + a.chunk), a.kv);
-      best = argmax_merge(best, chunk_argmax(ct, rt, a.kv));
-    }
-    const ArgMax m = block_argmax(best, sm);
-    out->w0 = pack(m.v, (uint32_t)m.i);
-    out->w1 = pack(0.0f, 1u);
+    greedy_chunk<BF16, VEC>(a, b, d, lo, hi, sm, out);
   } else if (BF16 && VEC) {
     if (d.mode == P2_RESIDUAL) {
       gumbel_chunk_bf16<P2_RESIDUAL, BETA>(a, b, d, lo, hi, sm, out);
@@ -1216,7 +1267,10 @@ __device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks
       for (int c = 0; c < C2; ++c) {
         P2Slot part;
         const int lo = c * p2_chunk;
-        pass2_chunk<BF16, VEC, BETA>(a, b, fb, lo, min(a.V, lo + p2_chunk), sm, &part);
+        if constexpr (BF16 && VEC)
+          gumbel_chunk_bf16<P2_BONUS, false>(a, b, fb, lo, min(a.V, lo + p2_chunk), sm, &part);
+        else
+          pass2_chunk<BF16, VEC, BETA>(a, b, fb, lo, min(a.V, lo + p2_chunk), sm, &part);
         ArgMax o;
         o.v = hi_f(part.w0);
         o.i = (int)lo_u(part.w0);
