@@ -27,7 +27,13 @@
  *  - random words come from Philox4x32-10 with key (seed_lo, seed_hi) and
  *    counter (c0, position, sequence, 2*offset + stream);
  *  - an empty residual (only reachable through rounding) falls back to p;
- *  - a tree accepts its deepest valid node, smallest index among equals.
+ *  - a tree accepts its deepest valid node, smallest index among equals;
+ *  - sampled trees ([SB] "Tree Attention", multi-round rejection sampling):
+ *    the children of a node are i.i.d. draws from the draft distribution at
+ *    that node (draft row = the node), tested in index order; the accept
+ *    uniform of the j-th tested sibling under node v uses counter word 0 = j
+ *    and position v, and a draw at node v uses position v, so a tree shaped
+ *    like a chain verifies exactly as the chain.
  * Parity unpinned by the pages: the Philox counter layout, the word-to-float
  * maps, the Gumbel transform, the tie rule and the empty-residual fallback are
  * this library's written convention. The tests pin the distribution they
@@ -472,6 +478,162 @@ int or_verify_tree(const void* target, int64_t tstride, int dtype, const int32_t
     free(row);
     free(g);
     free(valid);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sampled trees ([SB] "Tree Attention": multi-round rejection sampling)     */
+/* ------------------------------------------------------------------------ */
+
+/* Accept uniform of the round-th sibling tested under node `node`: stream 0,
+ * word 0, counter word 0 = round. Round 0 is the chain's accept uniform of
+ * position `node`, so that a tree shaped like a chain verifies as the chain. */
+static double or_tree_accept_uniform(uint64_t seed, uint64_t offset, int32_t b, int32_t node,
+                                     int32_t round) {
+  uint32_t w[4];
+  or_words(seed, (uint32_t)round, (uint32_t)node, (uint32_t)b, (uint32_t)(2u * (uint32_t)offset), w);
+  return (double)(w[0] >> 8) * (1.0 / 16777216.0);
+}
+
+/* p = softmax(row / T) in fp64, from the decoded row. */
+static void or_softmax(const void* base, int dtype, int64_t stride, int64_t r, int32_t V, double T,
+                       double* y, double* prob) {
+  or_load_row(base, dtype, stride, r, V, y);
+  for (int32_t v = 0; v < V; ++v) y[v] /= T;
+  const double lz = or_logsumexp(y, V);
+  for (int32_t v = 0; v < V; ++v) prob[v] = exp(y[v] - lz);
+}
+
+/* One sequence. From the root, at each node v with children c_1 < ... < c_k
+ * (drawn i.i.d. from q_v, the draft distribution at v): the target
+ * distribution starts as p_v; child c_j is accepted with probability
+ * min(1, p(x_j) / q_v(x_j)); on a rejection p is replaced by the normalized
+ * residual (p - q_v)_+ / ||(p - q_v)_+||_1 and the next sibling is tested
+ * against it. The first accepted child becomes the new node. A node without
+ * children ends the walk with a bonus token drawn from p at that node; a node
+ * whose children are all rejected ends it with a token drawn from the final
+ * residual. (A residual of zero mass, reachable only through rounding, leaves
+ * p as it was, as the chain's fallback draws from p.) */
+static void or_tree_sample_one(const void* target, int64_t tstride, const void* draft,
+                               int64_t dstride, int dtype, const int32_t* parents,
+                               const int32_t* tok, double T, int32_t b, int32_t N, int32_t V,
+                               int32_t max_depth, uint64_t seed, uint64_t offset, double* y,
+                               double* P, double* Q, int32_t* path, int32_t* out_len,
+                               int32_t* out_token, double* top_gap, int32_t* flags,
+                               int32_t* rejections) {
+  int32_t node = 0, len = 1, nrej = 0, fl = 0;
+  path[0] = 0;
+  or_top2_t top;
+  or_top2_init(&top);
+  for (;;) {
+    int32_t first = -1;
+    for (int32_t c = node + 1; c < N; ++c)
+      if (parents[c] == node) {
+        first = c;
+        break;
+      }
+    if (first < 0) {
+      /* Leaf: the bonus token, from p at this node. */
+      or_load_row(target, dtype, tstride, (int64_t)b * N + node, V, y);
+      for (int32_t v = 0; v < V; ++v) or_top2_push(&top, y[v] / T + or_gumbel(seed, offset, b, node, v), v);
+      break;
+    }
+    or_softmax(target, dtype, tstride, (int64_t)b * N + node, V, T, y, P);
+    or_softmax(draft, dtype, dstride, (int64_t)b * N + node, V, T, y, Q);
+    int32_t next = -1, round = 0, updated = 0;
+    for (int32_t c = first; c < N; ++c) {
+      if (parents[c] != node) continue;
+      const int32_t x = tok[c];
+      /* a = min(1, p(x)/q(x)); q(x) = 0 gives a = 1. */
+      const double a = (Q[x] > 0.0) ? fmin(1.0, P[x] / Q[x]) : 1.0;
+      const double u = or_tree_accept_uniform(seed, offset, b, node, round);
+      if (fabs(u - a) < OR_KNIFE_EDGE) fl |= OR_FLAG_KNIFE_EDGE;
+      ++round;
+      if (u < a) {
+        next = c;
+        break;
+      }
+      ++nrej;
+      double Z = 0.0;
+      for (int32_t v = 0; v < V; ++v) Z += fmax(P[v] - Q[v], 0.0);
+      if (Z > 0.0) {
+        for (int32_t v = 0; v < V; ++v) P[v] = fmax(P[v] - Q[v], 0.0) / Z;
+        updated = 1;
+      } else {
+        fl |= OR_FLAG_FALLBACK;
+      }
+    }
+    if (next < 0) {
+      /* Every child rejected: the replacement token from the final residual
+       * (p itself if no residual had mass). */
+      (void)updated;
+      for (int32_t v = 0; v < V; ++v)
+        if (P[v] > 0.0) or_top2_push(&top, log(P[v]) + or_gumbel(seed, offset, b, node, v), v);
+      break;
+    }
+    node = next;
+    path[len++] = node;
+    if (len > max_depth + 1) break; /* cannot happen in a valid tree */
+  }
+  *out_len = len;
+  *out_token = top.v1;
+  if (top_gap) *top_gap = or_top2_gap(&top);
+  if (flags) *flags = fl;
+  if (rejections) *rejections = nrej;
+}
+
+int or_verify_tree_sample(const void* target, int64_t tstride, const void* draft, int64_t dstride,
+                          int dtype, const int32_t* parents, const int32_t* depth,
+                          const int32_t* node_tokens, const float* temperature, int32_t B,
+                          int32_t N, int32_t V, int32_t max_depth, uint64_t seed, uint64_t offset,
+                          int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
+                          double* top_gap, int32_t* flags, int32_t* rejections, int nthreads) {
+  if (!target || !draft || !parents || !depth || !node_tokens || !temperature || !out_path ||
+      !out_path_len || !out_token)
+    return 1;
+  if (B < 0 || N < 1 || N > OR_MAX_TREE_NODES || V < 1 || max_depth < 0) return 2;
+  if (dtype != OR_DTYPE_F32 && dtype != OR_DTYPE_BF16) return 3;
+  if (tstride < V || dstride < V) return 4;
+  const int tree_ok = or_tree_is_valid(parents, depth, N, max_depth);
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+  {
+    double* y = (double*)malloc(sizeof(double) * (size_t)V);
+    double* P = (double*)malloc(sizeof(double) * (size_t)V);
+    double* Q = (double*)malloc(sizeof(double) * (size_t)V);
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t b = 0; b < B; ++b) {
+      const int32_t* tok = node_tokens + (int64_t)b * N;
+      int32_t* path = out_path + (int64_t)b * (max_depth + 1);
+      for (int32_t k = 0; k <= max_depth; ++k) path[k] = -1;
+      out_token[b] = -1;
+      if (top_gap) top_gap[b] = INFINITY;
+      if (flags) flags[b] = 0;
+      if (rejections) rejections[b] = 0;
+      const double T = (double)temperature[b];
+      if (!tree_ok) {
+        out_path_len[b] = OR_SEQ_BAD_TREE;
+        continue;
+      }
+      if (!(T > 0.0) || isinf(T)) {
+        out_path_len[b] = OR_SEQ_BAD_TEMPERATURE;
+        continue;
+      }
+      int bad = 0;
+      for (int32_t c = 1; c < N; ++c)
+        if (tok[c] < 0 || tok[c] >= V) bad = 1;
+      if (bad) {
+        out_path_len[b] = OR_SEQ_BAD_TOKEN;
+        continue;
+      }
+      or_tree_sample_one(target, tstride, draft, dstride, dtype, parents, tok, T, b, N, V,
+                         max_depth, seed, offset, y, P, Q, path, &out_path_len[b], &out_token[b],
+                         top_gap ? &top_gap[b] : NULL, flags ? &flags[b] : NULL,
+                         rejections ? &rejections[b] : NULL);
+    }
+    free(y);
+    free(P);
+    free(Q);
   }
   return 0;
 }
