@@ -202,6 +202,42 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
                              int32_t* out_bonus, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* spec_verify_tree_sample — sampled verification of a draft tree by
+ * multi-round rejection sampling ([SB] "Tree Attention": the children of a
+ * node are tested one by one; after each rejection the target distribution
+ * becomes the normalized residual (p - q)_+ / ||(p - q)_+||_1 and the next
+ * sibling is tested against it; if every child is rejected the replacement
+ * token is drawn from the final residual; a leaf ends the path with a bonus
+ * token drawn from p there).
+ *   target_logits: device [B, N, V] (row stride target_row_stride elements):
+ *     row v of sequence b scores the token after node v.
+ *   draft_logits: device [B, N, V] (row stride draft_row_stride): row v is
+ *     the draft distribution q at node v, from which v's children were drawn
+ *     (i.i.d.); rows of leaves are not read.
+ *   parents, depth: device [N], a tree in parent-before-child order rooted at
+ *     node 0 (as for spec_verify_tree); node_tokens: device [B, N], token of
+ *     each node (node 0's is not read); temperature: device [B], each > 0.
+ *   seed, offset: Philox key and per-step counter word, as for
+ *     spec_verify_sample. The accept uniform of the j-th sibling tested under
+ *     node v is word 0 of counter (j, v, b, 2 offset); the noise of a draw at
+ *     node v is that of position v. A tree shaped like a chain therefore
+ *     verifies exactly as spec_verify_sample verifies the chain.
+ *   Outputs (device): out_path [B, max_depth + 1] (accepted nodes from the
+ *     root, -1 padded), out_path_len [B] (nodes on the path; -1 a node token
+ *     out of range, -2 a temperature not > 0, -3 an invalid tree, -4 a bounded
+ *     wait gave up), out_token [B] (the bonus or replacement token).
+ *   workspace: sv_workspace_bytes(B, N, V) bytes, as for spec_verify_tree.
+ * Returns SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE (B, N, V or max_depth out of
+ * range, or a vocabulary too long for one launch), SV_ERR_BAD_DTYPE,
+ * SV_ERR_BAD_ARG (a stride < V, offset >= 2^31), SV_ERR_WORKSPACE or
+ * SV_ERR_HIP; nothing is launched on an error. */
+sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_row_stride, const void* draft_logits,
+                                    int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* parents,
+                                    const int32_t* depth, const int32_t* node_tokens, const float* temperature,
+                                    int32_t B, int32_t N, int32_t V, int32_t max_depth, uint64_t seed,
+                                    uint64_t offset, int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Diagnostic entry points: the random primitives of the kernels, element by
  * element, so that they can be checked against their definitions. All arrays

@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_int]
         L.or_verify_tree.restype = ctypes.c_int
         L.or_verify_tree_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, P, P, i32, i32, i32, i32,
-                                            u64, u64, P, P, P, P, P, P, ctypes.c_int]
+                                            u64, u64, P, P, P, P, P, P, P, ctypes.c_int]
         L.or_verify_tree_sample.restype = ctypes.c_int
         L.or_tree_depths.argtypes = [P, i32, P]
         L.or_tree_depths.restype = ctypes.c_int
@@ -203,7 +203,8 @@ def verify_tree_sample(target, draft, parents, depth, node_tokens, temperature, 
     Attention"). target and draft are [B, N, Vs] (draft row v: q at node v,
     from which v's children were drawn). Returns path [B, max_depth + 1],
     path_len [B] (nodes on the path, or a negative code), token [B] (the bonus
-    or replacement token after the path), top_gap, flags and rejections [B]."""
+    or replacement token after the path), top_gap, flags, rejections and
+    margin (the smallest |u - a| over the siblings tested) [B]."""
     tok = np.ascontiguousarray(node_tokens, dtype=np.int32)
     B, N = tok.shape
     V, tstride = _rows(target, N, V)
@@ -216,12 +217,14 @@ def verify_tree_sample(target, draft, parents, depth, node_tokens, temperature, 
     assert par.shape == (N,) and dep.shape == (N,) and temp.shape == (B,)
     out = {"path": np.zeros((B, max_depth + 1), np.int32), "path_len": np.zeros(B, np.int32),
            "token": np.zeros(B, np.int32), "top_gap": np.zeros(B, np.float64),
-           "flags": np.zeros(B, np.int32), "rejections": np.zeros(B, np.int32)}
+           "flags": np.zeros(B, np.int32), "rejections": np.zeros(B, np.int32),
+           "margin": np.zeros(B, np.float64)}
     nt = nthreads or os.cpu_count() or 1
     rc = lib().or_verify_tree_sample(_ptr(target), tstride, _ptr(draft), dstride, _logits_dtype(target),
                                      _ptr(par), _ptr(dep), _ptr(tok), _ptr(temp), B, N, V, max_depth,
                                      seed, offset, _ptr(out["path"]), _ptr(out["path_len"]), _ptr(out["token"]),
-                                     _ptr(out["top_gap"]), _ptr(out["flags"]), _ptr(out["rejections"]), nt)
+                                     _ptr(out["top_gap"]), _ptr(out["flags"]), _ptr(out["rejections"]),
+                                     _ptr(out["margin"]), nt)
     if rc != 0:
         raise ValueError("or_verify_tree_sample rejected its arguments (code %d)" % rc)
     return out

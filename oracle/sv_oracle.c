@@ -521,8 +521,9 @@ static void or_tree_sample_one(const void* target, int64_t tstride, const void* 
                                int32_t max_depth, uint64_t seed, uint64_t offset, double* y,
                                double* P, double* Q, int32_t* path, int32_t* out_len,
                                int32_t* out_token, double* top_gap, int32_t* flags,
-                               int32_t* rejections) {
+                               int32_t* rejections, double* margin) {
   int32_t node = 0, len = 1, nrej = 0, fl = 0;
+  double mg = INFINITY;
   path[0] = 0;
   or_top2_t top;
   or_top2_init(&top);
@@ -549,6 +550,7 @@ static void or_tree_sample_one(const void* target, int64_t tstride, const void* 
       const double a = (Q[x] > 0.0) ? fmin(1.0, P[x] / Q[x]) : 1.0;
       const double u = or_tree_accept_uniform(seed, offset, b, node, round);
       if (fabs(u - a) < OR_KNIFE_EDGE) fl |= OR_FLAG_KNIFE_EDGE;
+      if (fabs(u - a) < mg) mg = fabs(u - a);
       ++round;
       if (u < a) {
         next = c;
@@ -581,6 +583,7 @@ static void or_tree_sample_one(const void* target, int64_t tstride, const void* 
   if (top_gap) *top_gap = or_top2_gap(&top);
   if (flags) *flags = fl;
   if (rejections) *rejections = nrej;
+  if (margin) *margin = mg;
 }
 
 int or_verify_tree_sample(const void* target, int64_t tstride, const void* draft, int64_t dstride,
@@ -588,7 +591,8 @@ int or_verify_tree_sample(const void* target, int64_t tstride, const void* draft
                           const int32_t* node_tokens, const float* temperature, int32_t B,
                           int32_t N, int32_t V, int32_t max_depth, uint64_t seed, uint64_t offset,
                           int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
-                          double* top_gap, int32_t* flags, int32_t* rejections, int nthreads) {
+                          double* top_gap, int32_t* flags, int32_t* rejections, double* margin,
+                          int nthreads) {
   if (!target || !draft || !parents || !depth || !node_tokens || !temperature || !out_path ||
       !out_path_len || !out_token)
     return 1;
@@ -610,6 +614,7 @@ int or_verify_tree_sample(const void* target, int64_t tstride, const void* draft
       if (top_gap) top_gap[b] = INFINITY;
       if (flags) flags[b] = 0;
       if (rejections) rejections[b] = 0;
+      if (margin) margin[b] = INFINITY;
       const double T = (double)temperature[b];
       if (!tree_ok) {
         out_path_len[b] = OR_SEQ_BAD_TREE;
@@ -629,7 +634,7 @@ int or_verify_tree_sample(const void* target, int64_t tstride, const void* draft
       or_tree_sample_one(target, tstride, draft, dstride, dtype, parents, tok, T, b, N, V,
                          max_depth, seed, offset, y, P, Q, path, &out_path_len[b], &out_token[b],
                          top_gap ? &top_gap[b] : NULL, flags ? &flags[b] : NULL,
-                         rejections ? &rejections[b] : NULL);
+                         rejections ? &rejections[b] : NULL, margin ? &margin[b] : NULL);
     }
     free(y);
     free(P);

@@ -68,13 +68,15 @@ int or_verify_tree(const void* target, int64_t tstride, int dtype, const int32_t
  * sequence: out_path [max_depth + 1] (root first, -1 padded), out_path_len
  * (nodes on the path, or an OR_SEQ_* code), out_token (the bonus or
  * replacement token after the path); optional top_gap, flags and the number
- * of rejected siblings. */
+ * of rejected siblings, and margin: the smallest |u - a| over the siblings
+ * tested. */
 int or_verify_tree_sample(const void* target, int64_t tstride, const void* draft, int64_t dstride,
                           int dtype, const int32_t* parents, const int32_t* depth,
                           const int32_t* node_tokens, const float* temperature, int32_t B,
                           int32_t N, int32_t V, int32_t max_depth, uint64_t seed, uint64_t offset,
                           int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
-                          double* top_gap, int32_t* flags, int32_t* rejections, int nthreads);
+                          double* top_gap, int32_t* flags, int32_t* rejections, double* margin,
+                          int nthreads);
 
 int or_tree_depths(const int32_t* parents, int32_t N, int32_t* depth_out);
 

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     spec_verify_greedy,
     spec_verify_sample,
     spec_verify_tree,
+    spec_verify_tree_sample,
     sv_debug_noise,
     sv_debug_read_stream,
     sv_debug_wave_max,

@@ -22,7 +22,7 @@ SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
+           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
            "sv_debug_read_stream"]
 
 _lib = None
@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_greedy.restype = ctypes.c_int
         L.spec_verify_tree.argtypes = [P, i64, ctypes.c_int, P, P, P, i32, i32, i32, i32, P, P, P, P, sz, P]
         L.spec_verify_tree.restype = ctypes.c_int
+        L.spec_verify_tree_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, u64, u64,
+                                              P, P, P, P, sz, P]
+        L.spec_verify_tree_sample.restype = ctypes.c_int
         L.sv_debug_philox.argtypes = [P, P, P, i32, P]
         L.sv_debug_philox.restype = ctypes.c_int
         L.sv_debug_noise.argtypes = [P, P, P, i32, P]
@@ -236,6 +239,42 @@ def spec_verify_tree(target_logits, parents, depth, node_tokens, max_depth: int,
     if st != 0:
         raise SVError(st, "spec_verify_tree")
     return out_path, out_path_len, out_bonus
+
+
+def spec_verify_tree_sample(target_logits, draft_logits, parents, depth, node_tokens, temperature, max_depth: int,
+                            seed: int = 0, offset: int = 0, out_path=None, out_path_len=None, out_token=None,
+                            workspace=None, V: int | None = None, stream=None):
+    """Sampled tree verification (multi-round rejection sampling). target and
+    draft logits [B, N, V] (draft row v: q at node v), temperature [B] > 0.
+    Returns (out_path [B, max_depth+1], out_path_len [B], out_token [B])."""
+    import torch
+    B, N = node_tokens.shape
+    V = int(target_logits.shape[2]) if V is None else int(V)
+    _check_i32(node_tokens, (B, N), "node_tokens")
+    _check_i32(parents, (N,), "parents")
+    _check_i32(depth, (N,), "depth")
+    if temperature.dtype != torch.float32 or tuple(temperature.shape) != (B,) or not temperature.is_contiguous():
+        raise ValueError("temperature must be a contiguous float32 tensor of shape [B]")
+    if draft_logits.dtype != target_logits.dtype:
+        raise ValueError("target and draft logits must have the same dtype")
+    ts = _row_stride(target_logits, N, V)
+    ds = _row_stride(draft_logits, N, V)
+    dev = target_logits.device
+    if out_path is None:
+        out_path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    if out_path_len is None:
+        out_path_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_token is None:
+        out_token = torch.empty((B,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = Workspace(dev).get(B, N, V)
+    st = lib().spec_verify_tree_sample(_ptr(target_logits), ts, _ptr(draft_logits), ds, _dtype_code(target_logits),
+                                       _ptr(parents), _ptr(depth), _ptr(node_tokens), _ptr(temperature), B, N, V,
+                                       max_depth, seed, offset, _ptr(out_path), _ptr(out_path_len), _ptr(out_token),
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise SVError(st, "spec_verify_tree_sample")
+    return out_path, out_path_len, out_token
 
 
 def sv_debug_philox(ctr, key, out=None, stream=None):

@@ -42,7 +42,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
-std::atomic<int> g_occ[kMaxDevices][8];
+std::atomic<int> g_occ[kMaxDevices][12];
 std::atomic<int> g_tree_occ[kMaxDevices][4];
 
 int env_int(const char* name, int dflt) {
@@ -117,6 +117,18 @@ int p2_occupancy(int dev, bool bf16, bool vec) {
   return n;
 }
 
+// Resident workgroups per CU of the sampled-tree walk launch.
+int tree_walk_occupancy_cached(int dev, bool bf16, bool vec) {
+  const int k = 8 + (bf16 ? 2 : 0) + (vec ? 1 : 0);
+  int n = g_occ[dev][k].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    n = tree_sample_walk_occupancy(bf16, vec);
+    if (n <= 0) n = 1;
+    g_occ[dev][k].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 int tree_occupancy_cached(int dev, bool bf16, bool vec) {
   const int k = (bf16 ? 2 : 0) + (vec ? 1 : 0);
   int n = g_tree_occ[dev][k].load(std::memory_order_relaxed);
@@ -170,6 +182,7 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   a.t_stride = t_stride * es;
   a.draft = (const uint8_t*)draft;
   a.d_stride = d_stride * es;
+  a.d_rows = gamma;
   a.ids = ids;
   a.temperature = temperature;
   a.B = B;
@@ -353,6 +366,88 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
   const int forced_lag = sv::env_int("SV_LAG", -1);
   if (forced_lag >= 0) a.lag = forced_lag;
   return sv::launch_tree(a, bf16, vec, (hipStream_t)stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_row_stride, const void* draft_logits,
+                                    int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* parents,
+                                    const int32_t* depth, const int32_t* node_tokens, const float* temperature,
+                                    int32_t B, int32_t N, int32_t V, int32_t max_depth, uint64_t seed,
+                                    uint64_t offset, int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!target_logits || !draft_logits || !parents || !depth || !node_tokens || !temperature || !out_path ||
+      !out_path_len || !out_token)
+    return SV_ERR_NULL_ARG;
+  if (B < 0 || B > SV_MAX_BATCH || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > (1 << 30) || max_depth < 0 ||
+      max_depth >= N)
+    return SV_ERR_BAD_SHAPE;
+  if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_BAD_DTYPE;
+  if (target_row_stride < V || draft_row_stride < V) return SV_ERR_BAD_ARG;
+  if (offset >= (1ull << 31)) return SV_ERR_BAD_ARG;
+  const size_t need = sv_workspace_bytes(B, N, V);
+  const sv_status_t ws_ok = sv::check_workspace(workspace, workspace_bytes, need);
+  if (ws_ok != SV_OK) return ws_ok;
+  if (B == 0) return SV_OK;
+  const bool bf16 = (dtype == SV_DTYPE_BF16);
+  const int es = bf16 ? 2 : 4;
+  const sv::Tiling tl = sv::pick_tiling((long long)B * N * 2, V, bf16);
+  if ((long long)B * N * 2 * tl.nchunks >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
+  const sv::WsLayout L = sv::ws_layout(B, N, sv::max_chunks(V));
+  uint8_t* ws = (uint8_t*)workspace;
+  int dev = 0, cus = 0;
+  if (!sv::device_info(&dev, &cus)) return SV_ERR_HIP;
+
+  sv::TreeSampleArgs a;
+  std::memset(&a, 0, sizeof(a));
+  sv::ChainArgs& c = a.c;
+  c.target = (const uint8_t*)target_logits;
+  c.t_stride = target_row_stride * es;
+  c.draft = (const uint8_t*)draft_logits;
+  c.d_stride = draft_row_stride * es;
+  c.d_rows = N;
+  c.temperature = temperature;
+  c.B = B;
+  c.gamma = N - 1;  // target row (b, v) is row b * N + v
+  c.V = V;
+  c.chunk = tl.chunk;
+  c.nchunks = tl.nchunks;
+  c.kv = tl.kv;
+  c.p2_stride = sv::max_chunks(V);
+  c.key0 = (uint32_t)seed;
+  c.key1 = (uint32_t)(seed >> 32);
+  c.ctr_accept = (uint32_t)(2u * (uint32_t)offset);
+  c.ctr_noise = (uint32_t)(2u * (uint32_t)offset + 1u);
+  c.done = (uint32_t*)(ws + L.done);
+  c.seq = (sv::SeqState*)(ws + L.seq);
+  c.p1 = (sv::P1Slot*)(ws + L.p1);
+  c.p2 = (sv::P2Slot*)(ws + L.p2);
+  c.spin_limit = 1u << 22;
+  a.parents = parents;
+  a.depth = depth;
+  a.tokens = node_tokens;
+  a.N = N;
+  a.max_depth = max_depth;
+  a.out_path = out_path;
+  a.out_len = out_path_len;
+  a.out_token = out_token;
+  const bool vec = sv::aligned16(target_logits, c.t_stride) && sv::aligned16(draft_logits, c.d_stride);
+  // Walk: about 16K elements of a row per workgroup (whole streaming rounds),
+  // and as many sequences per launch as keep every workgroup resident.
+  const int unit = sv::kThreads * (bf16 ? 8 : 4);
+  const int w0 = std::max(1, (V + 16383) / 16384);
+  a.wlen = ((V + w0 - 1) / w0 + unit - 1) / unit * unit;
+  a.W = (V + a.wlen - 1) / a.wlen;
+  if (a.W > c.p2_stride) return SV_ERR_BAD_SHAPE;
+  const long long resident = (long long)cus * sv::tree_walk_occupancy_cached(dev, bf16, vec);
+  if (a.W > resident) return SV_ERR_BAD_SHAPE;
+  const long long per_launch = std::max<long long>(1, resident / a.W);
+  hipStream_t st = (hipStream_t)stream;
+  if (sv::launch_tree_sample_stats(a, bf16, vec, st) != hipSuccess) return SV_ERR_HIP;
+  for (long long b0 = 0; b0 < B; b0 += per_launch) {
+    a.b_base = (int32_t)b0;
+    a.b_count = (int32_t)std::min<long long>(per_launch, B - b0);
+    if (sv::launch_tree_sample_walk(a, bf16, vec, st) != hipSuccess) return SV_ERR_HIP;
+  }
+  return SV_OK;
 }
 
 }  // extern "C"

@@ -71,6 +71,7 @@ struct Smem {
   ArgMax rg[kMaxGamma];
   int32_t acc[kMaxGamma];
   Decision dec;
+  uint64_t trec[4];  // sampled trees: the sequence's current action record
 };
 
 // Block-wide log-sum-exp merge: within a wave the maximum first, then every
@@ -173,7 +174,7 @@ __device__ __forceinline__ const uint8_t* target_row(const ChainArgs& a, int b, 
   return a.target + ((int64_t)b * (a.gamma + 1) + i) * a.t_stride;
 }
 __device__ __forceinline__ const uint8_t* draft_row(const ChainArgs& a, int b, int i) {
-  return a.draft + ((int64_t)b * a.gamma + i) * a.d_stride;
+  return a.draft + ((int64_t)b * a.d_rows + i) * a.d_stride;
 }
 
 __device__ __forceinline__ uint64_t pack(float hi, uint32_t lo) {
@@ -1474,6 +1475,390 @@ __global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
   pass2_item<BF16, VEC, BETA>(a, b, sm.unit[1], sm.unit[2], sm.unit[3], sm);
 }
 
+// ===========================================================================
+// Sampled trees: multi-round rejection sampling (the pages' "Tree Attention"
+// section). Two launches:
+//   stats: one item per (sequence, node with children, row kind, chunk): the
+//          chunk's (max, sum exp2) of the node's target row, or of its draft
+//          row (q at the node: the distribution its children were drawn from);
+//   walk:  W workgroups per sequence, each owning wlen elements of a row. The
+//          last of them to arrive after an action (the leader) takes the
+//          sequence's next decisions serially and publishes the next action;
+//          all W then carry it out on their part of the row: a residual-mass
+//          pass, or the final Gumbel-max draw.
+// After some rejections at a node the target distribution is
+// p' = (p - A q)_+ / B. It starts at A = 0, B = 1, and a rejection moves it to
+// A' = A + B, B' = sum_v (p - A' q)_+ (one pass over the row pair). This is the
+// pages' repeated residual (p' - q)_+ / ||.||_1 in closed form: the accept
+// test reads p'(x) from two gathered logits, and the final draw is the
+// residual draw of the chains with q scaled by A (log2 A folded into the draft
+// normalizer).
+// ===========================================================================
+enum TreeAction : uint32_t { TA_NONE = 0, TA_PASS = 1, TA_DRAW_RESIDUAL = 2, TA_DRAW_BONUS = 3, TA_DONE = 4 };
+
+// The action record, in the sequence's SeqState (dec[0] stored last):
+//   dec[0] = epoch << 40 | action << 32 | node
+//   dec[1] = A bits << 32 | B bits
+//   dec[2] = zt2 bits << 32 | zd2 bits   (the node's log2-domain normalizers)
+//   dec[3] = round << 32 | path length   (round: the sibling last tested)
+struct TreeState {
+  int node, round, len;
+  float A, Bv, zt2, zd2;
+};
+
+__device__ __forceinline__ TreeState tree_state_of(const uint64_t rec[4]) {
+  TreeState t;
+  t.node = (int)(uint32_t)rec[0];
+  t.A = hi_f(rec[1]);
+  t.Bv = __uint_as_float(lo_u(rec[1]));
+  t.zt2 = hi_f(rec[2]);
+  t.zd2 = __uint_as_float(lo_u(rec[2]));
+  t.round = (int)(rec[3] >> 32);
+  t.len = (int)(uint32_t)rec[3];
+  return t;
+}
+
+// Thread 0: publishes the next action (payload first, then the word the
+// other workgroups wait on).
+__device__ void tree_publish(const TreeSampleArgs& ta, int b, uint32_t epoch, uint32_t action, const TreeState& t) {
+  SeqState* st = ta.c.seq + b;
+  xput64(&st->dec[1], pack(t.A, __float_as_uint(t.Bv)));
+  xput64(&st->dec[2], pack(t.zt2, __float_as_uint(t.zd2)));
+  xput64(&st->dec[3], ((uint64_t)(uint32_t)t.round << 32) | (uint32_t)t.len);
+  wait_vmem();
+  xput64(&st->dec[0], ((uint64_t)(epoch + 1u) << 40) | ((uint64_t)action << 32) | (uint32_t)t.node);
+}
+
+// The j-th child (index order) of node v, or -1. Children follow their parent.
+__device__ int tree_child(const TreeSampleArgs& ta, int v, int j) {
+  for (int c = v + 1; c < ta.N; ++c)
+    if (ta.parents[c] == v) {
+      if (j == 0) return c;
+      --j;
+    }
+  return -1;
+}
+
+// Row normalizers of node v (log2 domain): its stats slots merged in chunk order.
+__device__ void tree_node_stats(const TreeSampleArgs& ta, int b, int v, float c2, float* zt2, float* zd2) {
+  LseState t, d;
+  t.M = d.M = -INFINITY;
+  t.s = d.s = 0.0f;
+  P1Slot* sl = ta.c.p1 + ((int64_t)b * ta.N + v) * ta.c.nchunks;
+  for (int k = 0; k < ta.c.nchunks; ++k) {
+    const uint64_t w0 = xget64(&sl[k].w0), w1 = xget64(&sl[k].w1);
+    LseState o;
+    o.M = hi_f(w0);
+    o.s = __uint_as_float(lo_u(w0));
+    t = lse_merge(t, o, c2);
+    o.M = hi_f(w1);
+    o.s = __uint_as_float(lo_u(w1));
+    d = lse_merge(d, o, c2);
+  }
+  *zt2 = t.M * c2 + fast_log2(t.s);
+  *zd2 = d.M * c2 + fast_log2(d.s);
+}
+
+// Thread 0 of the leader: the sequence's decisions up to its next action.
+// After a pass (prev = TA_PASS) the workgroups' partial masses are summed in
+// workgroup order and the target distribution is updated; then siblings are
+// tested (an accepted child becomes the node, and its children are tested in
+// turn) until a rejection needs the next pass, or the walk ends in a draw.
+template <bool BF16>
+__device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32_t epoch, const uint64_t rec[4]) {
+  using E = Elem<BF16>;
+  const ChainArgs& a = ta.c;
+  const float T = a.temperature[b];
+  TreeState s;
+  float c2 = 0.0f;
+  if (prev == TA_NONE) {
+    int code = 0;
+    bool tree_ok = ta.parents[0] == -1 && ta.depth[0] == 0;
+    for (int c = 1; c < ta.N && tree_ok; ++c) {
+      const int pc = ta.parents[c];
+      tree_ok = pc >= 0 && pc < c && ta.depth[c] == ta.depth[pc] + 1 && ta.depth[c] <= ta.max_depth;
+    }
+    const int32_t* tok = ta.tokens + (int64_t)b * ta.N;
+    bool tok_ok = true;
+    for (int c = 1; c < ta.N; ++c) tok_ok = tok_ok && tok[c] >= 0 && tok[c] < a.V;
+    if (!tree_ok) code = -3;
+    else if (!(T > 0.0f) || T == INFINITY) code = -2;
+    else if (!tok_ok) code = -1;
+    // Outputs are written with device-coherent stores: later leaders of this
+    // sequence may run on other XCDs, and plain stores to one line from two
+    // L2s would be written back in either order.
+    int32_t* path = ta.out_path + (int64_t)b * (ta.max_depth + 1);
+    for (int k = 0; k <= ta.max_depth; ++k) xput(&path[k], -1);
+    xput(&ta.out_token[b], -1);
+    s.node = 0;
+    s.round = 0;
+    s.len = 1;
+    s.A = 0.0f;
+    s.Bv = 1.0f;
+    s.zt2 = s.zd2 = 0.0f;
+    if (code != 0) {
+      xput(&ta.out_len[b], code);
+      tree_publish(ta, b, epoch, TA_DONE, s);
+      return;
+    }
+    xput(&path[0], 0);
+    c2 = kLog2e / T;
+    if (tree_child(ta, 0, 0) >= 0) tree_node_stats(ta, b, 0, c2, &s.zt2, &s.zd2);
+  } else {
+    s = tree_state_of(rec);
+    c2 = kLog2e / T;
+    const P2Slot* sl = a.p2 + (int64_t)b * a.p2_stride;
+    float S = 0.0f;
+    for (int w = 0; w < ta.W; ++w) S += __uint_as_float((uint32_t)xget64((uint64_t*)&sl[w].w0));
+    if (S > 0.0f) {  // (a residual of zero mass leaves p as it was)
+      s.A = s.A + s.Bv;
+      s.Bv = S;
+    }
+    s.round += 1;
+  }
+  const int32_t* tok = ta.tokens + (int64_t)b * ta.N;
+  for (int guard = 0; guard <= ta.N; ++guard) {
+    const int c = tree_child(ta, s.node, s.round);
+    if (c < 0) {
+      // A leaf (no child tested) draws the bonus from p; a node whose
+      // children were all rejected draws from its final residual (or from p
+      // if no residual had mass).
+      tree_publish(ta, b, epoch, (s.round > 0 && s.A > 0.0f) ? TA_DRAW_RESIDUAL : TA_DRAW_BONUS, s);
+      return;
+    }
+    const int x = tok[c];
+    const float lt = E::load(target_row(a, b, s.node), x), ld = E::load(draft_row(a, b, s.node), x);
+    const float lp2 = __builtin_fmaf(lt, c2, -s.zt2), lq2 = __builtin_fmaf(ld, c2, -s.zd2);
+    float acc;
+    if (s.A == 0.0f && s.Bv == 1.0f) {
+      acc = fast_exp2(fminf(0.0f, lp2 - lq2));  // min(1, p/q), as the chains compute it
+    } else {
+      const float p = fast_exp2(lp2), q = fast_exp2(lq2);
+      acc = q > 0.0f ? fminf(1.0f, fmaxf(0.0f, p - s.A * q) / (s.Bv * q)) : 1.0f;
+    }
+    const Words4 wu = philox10((uint32_t)s.round, (uint32_t)s.node, (uint32_t)b, a.ctr_accept, a.key0, a.key1);
+    if (uniform_accept(wu.w[0]) < acc) {
+      if (s.len <= ta.max_depth) xput(&ta.out_path[(int64_t)b * (ta.max_depth + 1) + s.len], c);
+      s.len += 1;
+      s.node = c;
+      s.round = 0;
+      s.A = 0.0f;
+      s.Bv = 1.0f;
+      if (tree_child(ta, c, 0) >= 0) tree_node_stats(ta, b, c, c2, &s.zt2, &s.zd2);
+      continue;
+    }
+    tree_publish(ta, b, epoch, TA_PASS, s);  // the mass of (p - (A + B) q)_+ at this node
+    return;
+  }
+}
+
+// This workgroup's part of sum_v (p(v) - A q(v))_+ over [lo, hi), with the
+// factor A folded into the draft normalizer (zd2s = zd2 - log2 A).
+template <bool BF16, bool VEC>
+__device__ float residual_mass_part(const uint8_t* rt, const uint8_t* rd, int lo, int hi, float c2, float zt2,
+                                    float zd2s) {
+  using E = Elem<BF16>;
+  constexpr int EV = E::kPerVec;
+  float s = 0.0f;
+  auto add = [&](float lt, float ld) {
+    const float lp2 = __builtin_fmaf(lt, c2, -zt2), lq2 = __builtin_fmaf(ld, c2, -zd2s);
+    if (lp2 > lq2) s += fast_exp2(lp2) - fast_exp2(lq2);
+  };
+  int idx0 = lo;
+  if (VEC) {
+    const int nfull = (hi - lo) / EV;
+    for (int base = 0; base < nfull; base += 4 * kThreads) {
+      u32x4 qt[4], qd[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int vi = base + k * kThreads + (int)threadIdx.x;
+        if (vi < nfull) {
+          qt[k] = load_vec_stream(rt + (int64_t)(lo + vi * EV) * E::kBytes);
+          qd[k] = load_vec_stream(rd + (int64_t)(lo + vi * EV) * E::kBytes);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int vi = base + k * kThreads + (int)threadIdx.x;
+        if (vi < nfull) {
+          float vt[EV], vd[EV];
+          E::unpack(qt[k], vt);
+          E::unpack(qd[k], vd);
+#pragma unroll
+          for (int e = 0; e < EV; ++e) add(vt[e], vd[e]);
+        }
+      }
+    }
+    idx0 = lo + nfull * EV;
+  }
+  for (int idx = idx0 + (int)threadIdx.x; idx < hi; idx += kThreads) add(E::load(rt, idx), E::load(rd, idx));
+  return s;
+}
+
+// The last workgroup after the final action: the drawn token (workgroup
+// parts merged in workgroup order, lowest index on ties), the outputs, and the
+// sequence's workspace returned to zero.
+template <bool BF16, bool VEC>
+__device__ void tree_finish(const TreeSampleArgs& ta, int b, uint32_t action, Smem& sm) {
+  const ChainArgs& a = ta.c;
+  P2Slot* sl = a.p2 + (int64_t)b * a.p2_stride;
+  if (threadIdx.x == 0 && action != TA_DONE) {
+    ArgMax m;
+    m.v = -INFINITY;
+    m.i = -1;
+    for (int w = 0; w < ta.W; ++w) {
+      const uint64_t w0 = xget64(&sl[w].w0);
+      ArgMax o;
+      o.v = hi_f(w0);
+      o.i = (int)lo_u(w0);
+      m = argmax_merge(m, o);
+    }
+    xput(&ta.out_token[b], m.i);
+    xput(&ta.out_len[b], (int)(uint32_t)sm.trec[3]);
+  }
+  __syncthreads();
+  const int nslots = ta.N * a.nchunks;
+  uint64_t* p1 = (uint64_t*)(a.p1 + (int64_t)b * nslots);
+  for (int k = threadIdx.x; k < 2 * nslots; k += kThreads) xput64(&p1[k], 0u);
+  for (int k = threadIdx.x; k < 2 * ta.W; k += kThreads) xput64(&((uint64_t*)sl)[k], 0u);
+  SeqState* st = a.seq + b;
+  if (threadIdx.x < 4) xput64(&st->dec[threadIdx.x], 0u);
+  if (threadIdx.x == 0) {
+    xput(&st->lbest, 0u);
+    xput(&st->p2_arrive, 0u);
+  }
+}
+
+// Stats launch: item (b, v, kind, c) in that order, c fastest.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void tree_stats_kernel(TreeSampleArgs ta) {
+  __shared__ Smem sm;
+  const ChainArgs& a = ta.c;
+  const int C = a.nchunks;
+  int64_t r = blockIdx.x;
+  const int c = (int)(r % C);
+  r /= C;
+  const int kind = (int)(r % 2);
+  r /= 2;
+  const int v = (int)(r % ta.N);
+  const int b = (int)(r / ta.N);
+  const float T = a.temperature[b];
+  if (!(T > 0.0f) || T == INFINITY) return;
+  bool leaf = true;  // leaf rows are not needed: a leaf's bonus draw reads raw logits
+  for (int k = v + 1; k < ta.N; ++k)
+    if (ta.parents[k] == v) {
+      leaf = false;
+      break;
+    }
+  if (leaf) return;
+  const uint8_t* row = kind ? draft_row(a, b, v) : target_row(a, b, v);
+  const int lo = c * a.chunk, hi = min(a.V, lo + a.chunk);
+  const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && hi - lo == a.chunk;
+  Chunk<BF16, VEC> ch;
+  ch.load(row, lo, hi, a.kv);
+  const float c2 = kLog2e / T;
+  const LseState st = block_lse(fast ? lse_packed_bf16(ch.q, c2) : chunk_lse(ch, row, a.kv, c2), c2, sm, 0);
+  if (threadIdx.x == 0) {
+    P1Slot* dst = a.p1 + ((int64_t)b * ta.N + v) * C + c;
+    xput64(kind ? &dst->w1 : &dst->w0, pack(st.M, __float_as_uint(st.s)));
+  }
+}
+
+// Walk launch: W workgroups per sequence, sequences [b_base, b_base + b_count).
+// Every workgroup of the launch must be resident at once (the host sizes the
+// launch for that); each wait is bounded all the same.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) {
+  __shared__ Smem sm;
+  const ChainArgs& a = ta.c;
+  const int b = ta.b_base + (int)(blockIdx.x / (uint32_t)ta.W);
+  const int w = (int)(blockIdx.x % (uint32_t)ta.W);
+  if (b >= ta.b_base + ta.b_count) return;  // whole sequences only
+  SeqState* st = a.seq + b;
+  const int lo = w * ta.wlen, hi = min(a.V, lo + ta.wlen);
+  uint32_t epoch = 0, action = TA_NONE;
+  float partial = 0.0f;
+  P2Slot part;
+  part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
+  part.w1 = 0u;
+  for (int iter = 0; iter <= ta.N + 2; ++iter) {
+    // Arrive with this workgroup's part of the action just carried out.
+    if (threadIdx.x == 0) {
+      P2Slot* slot = a.p2 + (int64_t)b * a.p2_stride + w;
+      if (action == TA_PASS) xput64(&slot->w0, (uint64_t)__float_as_uint(partial));
+      if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) xput64(&slot->w0, part.w0);
+      wait_vmem();
+      const uint32_t old = atomicAdd(&st->p2_arrive, 1u);
+      sm.flag_last = (old + 1u == (uint32_t)ta.W) ? 1u : 0u;
+      if (sm.flag_last) xput(&st->p2_arrive, 0u);
+    }
+    __syncthreads();
+    const bool last = sm.flag_last != 0u;
+    if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS || action == TA_DONE) {
+      if (last) tree_finish<BF16, VEC>(ta, b, action, sm);
+      return;
+    }
+    if (last && threadIdx.x == 0) tree_lead<BF16>(ta, b, action, epoch, sm.trec);
+    __syncthreads();
+    // Wait for the next action (bounded).
+    if (threadIdx.x == 0) {
+      uint64_t r0 = xget64(&st->dec[0]);
+      uint32_t spins = 0;
+      sm.stalled = 0u;
+      while ((uint32_t)(r0 >> 40) == epoch) {
+        if (++spins > a.spin_limit || ((spins & 255u) == 0u && xget(&a.done[1]) != 0u)) {
+          atomicOr(&a.done[1], 1u);
+          xput(&ta.out_len[b], -4);
+          sm.stalled = 1u;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        r0 = xget64(&st->dec[0]);
+      }
+      sm.trec[0] = r0;
+      if (!sm.stalled) {
+        sm.trec[1] = xget64(&st->dec[1]);
+        sm.trec[2] = xget64(&st->dec[2]);
+        sm.trec[3] = xget64(&st->dec[3]);
+      }
+      sm.lkey = 0u;
+    }
+    __syncthreads();
+    if (sm.stalled) return;
+    epoch += 1u;
+    action = (uint32_t)(sm.trec[0] >> 32) & 0xFFu;
+    const TreeState t = tree_state_of(sm.trec);
+    const float c2 = kLog2e / a.temperature[b];
+    if (action == TA_PASS) {
+      const float zd2s = t.zd2 - fast_log2(t.A + t.Bv);
+      partial = block_sum(residual_mass_part<BF16, VEC>(target_row(a, b, t.node), draft_row(a, b, t.node), lo, hi, c2,
+                                                        t.zt2, zd2s),
+                          sm);
+    } else if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) {
+      Decision d;
+      d.kind = KIND_SAMPLED;
+      d.n = 0;
+      d.row = t.node;
+      d.x = -1;
+      d.T = a.temperature[b];
+      d.c2 = c2;
+      d.invT = 1.0f / d.T;
+      d.zt2 = t.zt2;
+      d.zd2 = action == TA_DRAW_RESIDUAL ? t.zd2 - fast_log2(t.A) : t.zd2;
+      d.a_row = 0.0f;
+      d.tok = -1;
+      d.mode = action == TA_DRAW_RESIDUAL ? P2_RESIDUAL : P2_BONUS;
+      if (BF16 && VEC) {
+        if (action == TA_DRAW_RESIDUAL) gumbel_chunk_bf16<P2_RESIDUAL, false>(a, b, d, lo, hi, sm, &part);
+        else gumbel_chunk_bf16<P2_BONUS, false>(a, b, d, lo, hi, sm, &part);
+      } else {
+        if (action == TA_DRAW_RESIDUAL) gumbel_chunk<BF16, VEC, P2_RESIDUAL>(a, b, d, lo, hi, sm, &part);
+        else gumbel_chunk<BF16, VEC, P2_BONUS>(a, b, d, lo, hi, sm, &part);
+      }
+    }
+  }
+}
+
 __global__ void fill_zero_kernel(uint32_t* p, size_t nwords) {
   for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < nwords; k += (size_t)gridDim.x * blockDim.x)
     p[k] = 0u;
@@ -1546,6 +1931,42 @@ int chain_p2_occupancy(bool bf16, bool vec) {
 int chain_occupancy(bool bf16, bool vec) {
   if (bf16) return vec ? occupancy_t<true, true>() : occupancy_t<true, false>();
   return vec ? occupancy_t<false, true>() : occupancy_t<false, false>();
+}
+
+template <bool BF16, bool VEC>
+hipError_t launch_tree_sample_stats_t(const TreeSampleArgs& a, hipStream_t stream) {
+  const long long grid = (long long)a.c.B * a.N * 2 * a.c.nchunks;
+  hipLaunchKernelGGL((tree_stats_kernel<BF16, VEC>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool VEC>
+hipError_t launch_tree_sample_walk_t(const TreeSampleArgs& a, hipStream_t stream) {
+  const long long grid = (long long)a.b_count * a.W;
+  hipLaunchKernelGGL((tree_walk_kernel<BF16, VEC>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_sample_stats(const TreeSampleArgs& a, bool bf16, bool vec, hipStream_t stream) {
+  if (bf16) return vec ? launch_tree_sample_stats_t<true, true>(a, stream) : launch_tree_sample_stats_t<true, false>(a, stream);
+  return vec ? launch_tree_sample_stats_t<false, true>(a, stream) : launch_tree_sample_stats_t<false, false>(a, stream);
+}
+
+hipError_t launch_tree_sample_walk(const TreeSampleArgs& a, bool bf16, bool vec, hipStream_t stream) {
+  if (bf16) return vec ? launch_tree_sample_walk_t<true, true>(a, stream) : launch_tree_sample_walk_t<true, false>(a, stream);
+  return vec ? launch_tree_sample_walk_t<false, true>(a, stream) : launch_tree_sample_walk_t<false, false>(a, stream);
+}
+
+template <bool BF16, bool VEC>
+int tree_walk_occupancy_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tree_walk_kernel<BF16, VEC>, kThreads, 0) != hipSuccess) n = 0;
+  return n;
+}
+
+int tree_sample_walk_occupancy(bool bf16, bool vec) {
+  if (bf16) return vec ? tree_walk_occupancy_t<true, true>() : tree_walk_occupancy_t<true, false>();
+  return vec ? tree_walk_occupancy_t<false, true>() : tree_walk_occupancy_t<false, false>();
 }
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {

@@ -73,6 +73,7 @@ struct ChainArgs {
   int64_t t_stride;  // bytes between rows
   const uint8_t* draft;  // NULL: one-hot draft
   int64_t d_stride;
+  int32_t d_rows;              // draft rows per sequence: gamma (chains) or N (sampled trees)
   const int32_t* ids;          // [B, gamma]
   const float* temperature;    // [B] or NULL: every sequence greedy
   int32_t B, gamma, V;
@@ -107,6 +108,23 @@ struct ChainArgs {
   int32_t lag2;       // and its pass-2 items those of k + lag2 (lag2 >= lag)
   int32_t fused;      // one launch for both passes
   uint32_t spin_limit;
+};
+
+// Sampled trees (multi-round rejection sampling): the chain arguments with
+// gamma = N - 1 (so that target row (b, v) is row b * N + v) and d_rows = N,
+// plus the tree. The walk launch gives each sequence W workgroups, each owning
+// wlen elements of a row, for the residual-mass passes and the final draw.
+struct TreeSampleArgs {
+  ChainArgs c;
+  const int32_t* parents;  // [N]
+  const int32_t* depth;    // [N]
+  const int32_t* tokens;   // [B, N]
+  int32_t N, max_depth;
+  int32_t W, wlen;         // walk: workgroups per sequence, elements per workgroup
+  int32_t b_base, b_count; // walk: the sequences of this launch
+  int32_t* out_path;       // [B, max_depth + 1]
+  int32_t* out_len;        // [B]
+  int32_t* out_token;      // [B]
 };
 
 struct TreeArgs {
@@ -184,5 +202,8 @@ int tree_occupancy(bool bf16, bool vec);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 int chain_occupancy(bool bf16, bool vec);
 int chain_p2_occupancy(bool bf16, bool vec);
+hipError_t launch_tree_sample_stats(const TreeSampleArgs& a, bool bf16, bool vec, hipStream_t stream);
+hipError_t launch_tree_sample_walk(const TreeSampleArgs& a, bool bf16, bool vec, hipStream_t stream);
+int tree_sample_walk_occupancy(bool bf16, bool vec);
 
 }  // namespace sv

@@ -28,7 +28,8 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
-    assert set(names) >= {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree", "sv_workspace_bytes",
+    assert set(names) >= {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample",
+                          "sv_workspace_bytes",
                           "sv_workspace_init", "sv_status_string", "sv_debug_philox", "sv_debug_noise",
                           "sv_debug_wave_max", "sv_debug_read_stream"}
     out = subprocess.run(["nm", "-D", "--defined-only", rsv.LIB_PATH], capture_output=True, text=True).stdout
@@ -113,3 +114,19 @@ def test_greedy_and_tree_argument_validation(L):
     assert L.sv_debug_read_stream(A16, 16, P, 0, None) == 2 and L.sv_debug_read_stream(A16, 15, P, 1, None) == 2
     assert L.sv_debug_read_stream(A17, 16, P, 1, None) == 4
     assert L.sv_workspace_init(None, 1024, None) == 1
+
+
+def test_tree_sample_argument_validation(L):
+    f = _Fake(1 << 20)
+    P = f.ptr
+    ts = lambda **k: L.spec_verify_tree_sample(k.get("t", P), k.get("ts", 100), k.get("d", P), k.get("ds", 100),
+                                               k.get("dt", 1), k.get("par", P), P, P, k.get("temp", P),
+                                               k.get("B", 2), k.get("N", 5), k.get("V", 100), k.get("md", 3),
+                                               0, k.get("off", 0), P, P, P, k.get("ws", P), k.get("wsb", f.nbytes),
+                                               None)
+    assert ts(d=None) == 1 and ts(temp=None) == 1 and ts(par=None) == 1
+    assert ts(N=0) == 2 and ts(N=1025) == 2 and ts(md=5) == 2 and ts(md=-1) == 2 and ts(B=-1) == 2
+    assert ts(dt=2) == 3
+    assert ts(ts=99) == 4 and ts(ds=99) == 4 and ts(off=1 << 31) == 4
+    assert ts(wsb=10) == 5
+    assert ts(B=0) == 0

@@ -1,0 +1,183 @@
+"""GPU parity of sampled tree verification (multi-round rejection sampling)
+against the CPU oracle, through the C ABI.
+
+Paths, path lengths and tokens are bit-exact, except sequences the oracle
+marks as a Gumbel near-tie of its final draw (relative top-two gap < 1e-6) or
+as an accept knife-edge. For trees the knife-edge margin is 1e-4 rather than
+the chains' 1e-5: after k rejections the kernels read the target distribution
+as (p - A q)_+ / B in fp32, and the error of an accept probability computed that
+way grows like (A + B) / B times the rounding of p and q (B, the residual mass
+left, can be small). Excused sequences are counted and printed."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import make_tree_sample
+
+from gpu_util import NEAR_TIE, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TREE_KNIFE = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rejection_sampling_verify_amd as rsv
+    rsv.lib()
+    return torch.device("cuda:0")
+
+
+def _run(inp, dev, seed=0, offset=0, workspace=None, temperature=None, parents=None, tokens=None):
+    import rejection_sampling_verify_amd as rsv
+    t = to_dev(inp.target, torch, dev)
+    d = to_dev(inp.draft, torch, dev)
+    par = torch.from_numpy(inp.parents if parents is None else parents).to(dev)
+    dep = torch.from_numpy(inp.depth).to(dev)
+    tok = torch.from_numpy(inp.node_tokens if tokens is None else tokens).to(dev)
+    temp = torch.from_numpy(inp.temperature if temperature is None else temperature).to(dev)
+    path, plen, token = rsv.spec_verify_tree_sample(t, d, par, dep, tok, temp, inp.max_depth, seed=seed,
+                                                    offset=offset, workspace=workspace)
+    torch.cuda.synchronize()
+    return {"path": path.cpu().numpy(), "path_len": plen.cpu().numpy(), "token": token.cpu().numpy()}
+
+
+def _compare(got, ref, label):
+    B = ref["path_len"].shape[0]
+    excused = []
+    for b in range(B):
+        if (got["path_len"][b] == ref["path_len"][b] and np.array_equal(got["path"][b], ref["path"][b])
+                and got["token"][b] == ref["token"][b]):
+            continue
+        ok = ref["top_gap"][b] < NEAR_TIE or ref["margin"][b] < TREE_KNIFE
+        assert ok, ("%s sequence %d differs: gpu len %d path %s token %d, oracle len %d path %s token %d "
+                    "(gap %.3g, margin %.3g)" % (label, b, got["path_len"][b], got["path"][b].tolist(),
+                                                 got["token"][b], ref["path_len"][b], ref["path"][b].tolist(),
+                                                 ref["token"][b], ref["top_gap"][b], ref["margin"][b]))
+        excused.append(b)
+    print("[tree-sample parity] %s B=%d excused=%d rejections=%s" % (label, B, len(excused),
+          np.bincount(np.maximum(ref["rejections"], 0)).tolist()), flush=True)
+    return excused
+
+
+def _oracle(inp, seed=0, offset=0, temperature=None, parents=None, tokens=None):
+    return oracle.verify_tree_sample(inp.target, inp.draft, inp.parents if parents is None else parents, inp.depth,
+                                     inp.node_tokens if tokens is None else tokens,
+                                     inp.temperature if temperature is None else temperature, inp.max_depth,
+                                     seed=seed, offset=offset)
+
+
+def _random_tree(rng, N, branching=(1, 4)):
+    parents = [-1]
+    frontier = [0]
+    while len(parents) < N:
+        nxt = []
+        for p in frontier:
+            for _ in range(int(rng.integers(branching[0], branching[1] + 1))):
+                if len(parents) < N:
+                    parents.append(p)
+                    nxt.append(len(parents) - 1)
+        frontier = nxt or [len(parents) - 1]
+    par = np.array(parents, np.int32)
+    return par, oracle.tree_depths(par)
+
+
+CASES = {
+    # name: (B, N, V, bf16, temperatures, seed)
+    "f32_small": (24, 9, 1000, False, (0.6, 1.0, 1.8), 1),
+    "f32_ragged": (16, 17, 5003, False, (1.0,), 2),
+    "bf16_deep": (12, 13, 20000, True, (0.7, 1.0), 3),
+    "bf16_wide": (16, 21, 40003, True, (1.0, 0.5), 4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_tree_sample_parity(dev, name):
+    B, N, V, bf16, temps, seed = CASES[name]
+    rng = np.random.default_rng(seed)
+    parents, depth = _random_tree(rng, N)
+    inp = make_tree_sample(name, B, V, parents, depth, bf16=bf16, seed=seed, temperatures=temps,
+                           target_sigma=2.0, zipf=0.0 if not bf16 else 1.1, draft_sigma=(0.3, 1.5))
+    for s, off in ((0, 0), (7, 3)):
+        got = _run(inp, dev, seed=s, offset=off)
+        _compare(got, _oracle(inp, seed=s, offset=off), "%s seed %d" % (name, s))
+
+
+def test_chain_shaped_tree_matches_the_chain_oracle(dev):
+    """A tree in which every node has one child verifies as the chain
+    (the same keying of the random words)."""
+    B, G, V = 32, 6, 3000
+    inp = make_tree_sample("chain", B, V, np.arange(-1, G, dtype=np.int32), np.arange(0, G + 1, dtype=np.int32),
+                           bf16=True, seed=21, temperatures=(0.7, 1.0, 1.5), draft_sigma=(0.5, 2.0))
+    got = _run(inp, dev, seed=5, offset=1)
+    ch = oracle.verify_sample(inp.target, np.ascontiguousarray(inp.draft[:, :G]), inp.node_tokens[:, 1:],
+                              inp.temperature, seed=5, offset=1)
+    ref = _oracle(inp, seed=5, offset=1)
+    assert np.array_equal(ref["path_len"] - 1, ch["n"])
+    _compare(got, ref, "chain-shaped")
+    assert len(set((got["path_len"] - 1).tolist())) > 2
+
+
+def test_draft_equal_to_target_follows_first_children(dev):
+    B, V = 8, 4096
+    parents = np.array([-1, 0, 0, 1, 1, 2, 3], np.int32)
+    depth = oracle.tree_depths(parents)
+    inp = make_tree_sample("q_eq_p", B, V, parents, depth, bf16=True, seed=22, temperatures=(1.0,))
+    inp.draft[:] = inp.target
+    got = _run(inp, dev, seed=2)
+    assert np.all(got["path"] == np.array([0, 1, 3, 6], np.int32))
+    _compare(got, _oracle(inp, seed=2), "q = p")
+
+
+def test_bad_inputs_and_workspace(dev):
+    """Per-sequence codes (bad temperature -2, bad token -1, invalid tree -3)
+    match the oracle, and every call returns its workspace to zero."""
+    import rejection_sampling_verify_amd as rsv
+    B, V = 6, 2000
+    parents = np.array([-1, 0, 0, 1, 2], np.int32)
+    depth = oracle.tree_depths(parents)
+    inp = make_tree_sample("bad", B, V, parents, depth, bf16=False, seed=23, temperatures=(1.0,))
+    ws = rsv.Workspace(dev).get(B, len(parents), V)
+    temp = inp.temperature.copy()
+    temp[1] = 0.0
+    temp[2] = -1.0
+    tok = inp.node_tokens.copy()
+    tok[3, 2] = V
+    got = _run(inp, dev, temperature=temp, tokens=tok, workspace=ws)
+    ref = _oracle(inp, temperature=temp, tokens=tok)
+    assert list(got["path_len"][1:4]) == [-2, -2, -1]
+    _compare(got, ref, "bad inputs")
+    assert int(ws.count_nonzero().item()) == 0
+    bad_parents = parents.copy()
+    bad_parents[3] = 4  # a child before its parent
+    got = _run(inp, dev, parents=bad_parents, workspace=ws)
+    assert np.all(got["path_len"] == -3) and np.all(got["token"] == -1)
+    assert int(ws.count_nonzero().item()) == 0
+
+
+def test_more_sequences_than_one_walk_launch(dev):
+    """Enough sequences that the walk runs in several launches (every
+    workgroup of a launch must be resident at once)."""
+    import rejection_sampling_verify_amd as rsv
+    B, V = 3000, 1000
+    parents = np.array([-1, 0, 0, 0, 1], np.int32)
+    depth = oracle.tree_depths(parents)
+    inp = make_tree_sample("many", B, V, parents, depth, bf16=True, seed=24, temperatures=(0.8, 1.2),
+                           zipf=0.0, target_sigma=1.5)
+    ws = rsv.Workspace(dev).get(B, len(parents), V)
+    got = _run(inp, dev, seed=3, workspace=ws)
+    _compare(got, _oracle(inp, seed=3), "many sequences")
+    assert int(ws.count_nonzero().item()) == 0
+
+
+def test_named_workload_full_size(dev):
+    inp = workloads.make_extra("tree_sample_bf16_llama")
+    got = _run(inp, dev, seed=inp.seed, offset=inp.offset)
+    ref = _oracle(inp, seed=inp.seed, offset=inp.offset)
+    _compare(got, ref, "tree_sample_bf16_llama")
+    assert np.all(ref["path_len"] >= 1)

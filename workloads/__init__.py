@@ -18,6 +18,11 @@ The five named workloads (``CONFIGS``) are:
   chain_bf16_llama B=256, gamma=8, V=128256, bf16, T in {0, 0.7, 1.0}, Zipf boost
   onehot_bf16_qwen B=512, gamma=6, V=152064, bf16, one-hot draft, T=1.0
   tree_bf16_llama  B=32,  N=65 nodes (root + 4 + 16 + 44), V=128256, bf16, greedy
+and, for sampled tree verification (multi-round rejection sampling):
+  tree_sample_bf16_llama  the same tree, B=32, V=128256, bf16, T in {0.7, 1.0}:
+      target as chain_bf16_llama's, draft row of each inner node = target +
+      N(0, sigma_b^2), sigma_b ~ U[0.2, 2]; children drawn i.i.d. from q at
+      their parent.
 """
 from __future__ import annotations
 
@@ -30,6 +35,7 @@ import numpy as np
 CONFIGS = ["chain_f32_small", "chain_bf16_peaked", "chain_bf16_llama", "onehot_bf16_qwen",
            "tree_bf16_llama"]
 CONFIG_INDEX = {name: k for k, name in enumerate(CONFIGS)}
+EXTRA = ["tree_sample_bf16_llama"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -110,6 +116,41 @@ class TreeInputs:
 
     def algorithmic_bytes(self) -> int:
         return self.B * self.N * self.V * self.target.itemsize
+
+
+@dataclass
+class TreeSampleInputs:
+    name: str
+    target: np.ndarray        # [B, N, V]
+    draft: np.ndarray         # [B, N, V]; row v: q at node v (zeros at leaves: never read)
+    parents: np.ndarray       # [N] int32
+    depth: np.ndarray         # [N] int32
+    node_tokens: np.ndarray   # [B, N] int32
+    temperature: np.ndarray   # [B] float32
+    max_depth: int
+    seed: int = 0
+    offset: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.node_tokens.shape[0]
+
+    @property
+    def N(self):
+        return self.node_tokens.shape[1]
+
+    @property
+    def V(self):
+        return self.target.shape[2]
+
+    def inner_nodes(self) -> int:
+        return int(len(set(int(p) for p in self.parents[1:])))
+
+    def algorithmic_bytes(self) -> int:
+        """Every inner node's target and draft row once, plus one row per
+        sequence for its final draw."""
+        return self.B * (2 * self.inner_nodes() + 1) * self.V * self.target.itemsize
 
 
 def _seq_rng(seed: int, b: int) -> np.random.Generator:
@@ -236,6 +277,42 @@ def make_tree(name: str, B: int, V: int, parents: np.ndarray, depth: np.ndarray,
                       tokens, int(np.max(depth)))
 
 
+def make_tree_sample(name: str, B: int, V: int, parents: np.ndarray, depth: np.ndarray, *, bf16: bool,
+                     seed: int, temperatures=(0.7, 1.0), target_sigma: float = 3.0, zipf: float = 1.1,
+                     draft_sigma=(0.2, 2.0), workers=None) -> TreeSampleInputs:
+    """Sampled-tree inputs: children are i.i.d. draws from q at their parent."""
+    N = len(parents)
+    dt = np.uint16 if bf16 else np.float32
+    target = np.empty((B, N, V), dt)
+    draft = np.zeros((B, N, V), dt)
+    tokens = np.empty((B, N), np.int32)
+    temp = np.empty(B, np.float32)
+    inner = sorted(set(int(p) for p in parents[1:]))
+
+    def one(b):
+        rng = _seq_rng(seed, b)
+        T = float(temperatures[b % len(temperatures)])
+        temp[b] = T
+        sig = rng.uniform(*draft_sigma) if isinstance(draft_sigma, tuple) else float(draft_sigma)
+        for v in range(N):
+            t = rng.standard_normal(V, dtype=np.float32) * np.float32(target_sigma)
+            if zipf:
+                rank = rng.permutation(V).astype(np.float32) + 1.0
+                t = t - np.float32(zipf) * np.log(rank)
+            target[b, v] = round_bf16(t) if bf16 else t
+            if v in inner:
+                d = t + rng.standard_normal(V, dtype=np.float32) * np.float32(sig)
+                draft[b, v] = round_bf16(d) if bf16 else d
+        tokens[b, 0] = int(rng.integers(V))
+        q_vals = stored_values(draft[b])
+        for c in range(1, N):
+            tokens[b, c] = _draw_from_logits(rng, q_vals[parents[c]], T)
+
+    _parallel(one, B, workers)
+    return TreeSampleInputs(name, target, draft, np.asarray(parents, np.int32), np.asarray(depth, np.int32),
+                            tokens, temp, int(np.max(depth)), meta={"V": V})
+
+
 def make(name: str, workers=None):
     """One of the five named workloads at full size (generator seed 1000 + k)."""
     k = CONFIG_INDEX[name]
@@ -256,6 +333,15 @@ def make(name: str, workers=None):
     if name == "tree_bf16_llama":
         parents, depth = _c5_tree()
         return make_tree(name, 32, 128256, parents, depth, bf16=True, seed=seed, workers=workers)
+    raise KeyError(name)
+
+
+def make_extra(name: str, workers=None):
+    """Workloads of the rows beyond the five configurations (seed 2000 + k)."""
+    seed = 2000 + EXTRA.index(name)
+    if name == "tree_sample_bf16_llama":
+        parents, depth = _c5_tree()
+        return make_tree_sample(name, 32, 128256, parents, depth, bf16=True, seed=seed, workers=workers)
     raise KeyError(name)
 
 
