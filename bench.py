@@ -71,12 +71,17 @@ def cpu_baseline(inp, is_tree: bool, positions_per_step: int, threads: int | Non
     told otherwise, over the whole workload; repeated until about 10 s of CPU
     time or max_runs runs."""
     import oracle
+    import workloads
     threads = threads or min(16, os.cpu_count() or 1)
     times = []
     t_start = time.perf_counter()
     while len(times) < max_runs and (not times or time.perf_counter() - t_start < 10.0):
         t0 = time.perf_counter()
-        if is_tree:
+        if isinstance(inp, workloads.TreeSampleInputs):
+            oracle.verify_tree_sample(inp.target, inp.draft, inp.parents, inp.depth, inp.node_tokens,
+                                      inp.temperature, inp.max_depth, seed=inp.seed, offset=inp.offset,
+                                      nthreads=threads)
+        elif is_tree:
             oracle.verify_tree(inp.target, inp.parents, inp.depth, inp.node_tokens, inp.max_depth, nthreads=threads)
         else:
             oracle.verify_sample(inp.target, inp.draft, inp.draft_ids, inp.temperature, seed=inp.seed,
@@ -141,8 +146,9 @@ def main():
         copy_calibration(torch, dev, args.steps)
         return
     rsv.lib()
-    inp = workloads.make(args.workload)
+    inp = workloads.make_extra(args.workload) if args.workload in workloads.EXTRA else workloads.make(args.workload)
     is_tree = args.workload.startswith("tree")
+    sampled_tree = isinstance(inp, workloads.TreeSampleInputs)
     print("[bench] workload %s generated" % args.workload, file=sys.stderr, flush=True)
 
     # Two resident copies of the inputs, used alternately, so that no step
@@ -152,6 +158,8 @@ def main():
         if is_tree:
             copies.append(dict(t=to_dev(inp.target, torch, dev), par=torch.from_numpy(inp.parents).to(dev),
                                dep=torch.from_numpy(inp.depth).to(dev), tok=torch.from_numpy(inp.node_tokens).to(dev)))
+            if sampled_tree:
+                copies[-1].update(d=to_dev(inp.draft, torch, dev), temp=torch.from_numpy(inp.temperature).to(dev))
         else:
             copies.append(dict(t=to_dev(inp.target, torch, dev), d=to_dev(inp.draft, torch, dev),
                                ids=torch.from_numpy(inp.draft_ids).to(dev),
@@ -166,8 +174,13 @@ def main():
 
         def step(k):
             c = copies[k % 2]
-            rsv.spec_verify_tree(c["t"], c["par"], c["dep"], c["tok"], inp.max_depth, out_path=out[0],
-                                 out_path_len=out[1], out_bonus=out[2], workspace=wbuf)
+            if sampled_tree:
+                rsv.spec_verify_tree_sample(c["t"], c["d"], c["par"], c["dep"], c["tok"], c["temp"], inp.max_depth,
+                                            seed=inp.seed, offset=inp.offset, out_path=out[0], out_path_len=out[1],
+                                            out_token=out[2], workspace=wbuf)
+            else:
+                rsv.spec_verify_tree(c["t"], c["par"], c["dep"], c["tok"], inp.max_depth, out_path=out[0],
+                                     out_path_len=out[1], out_bonus=out[2], workspace=wbuf)
     else:
         B, G = inp.draft_ids.shape
         wbuf = ws.get(B, G + 1, inp.V)
@@ -213,6 +226,9 @@ def main():
     print("[bench] warm-cache steps and read ceiling done", file=sys.stderr, flush=True)
 
     ms_per_step = wall * 1e3 / args.steps
+    if sampled_tree:
+        # Data-dependent: the walk reads only the nodes on each sequence's path.
+        inp.paths = (out[0].cpu().numpy(), out[1].cpu().numpy())
     alg_bytes = inp.algorithmic_bytes()
     t_launch = float(np.mean(launch_ms)) * 1e-3
     achieved = alg_bytes / t_launch / 1e9
@@ -222,6 +238,13 @@ def main():
         cfg = {"workload": args.workload, "B": int(B), "nodes": int(inp.node_tokens.shape[1]), "V": int(inp.V),
                "input_dtype": str(inp.target.dtype).replace("uint16", "bf16"), "verify": "greedy tree"}
         extra = {}
+        if sampled_tree:
+            cfg["verify"] = "sampled tree (multi-round rejection sampling)"
+            cfg["temperatures"] = sorted(set(float(x) for x in inp.temperature))
+            plen = out[1].cpu().numpy()
+            extra = {"mean_accepted_depth": float(np.mean(plen[plen >= 1] - 1)),
+                     "algorithmic_bytes_note": "rows the walk must read: target and draft row of every inner "
+                                               "node on the accepted path, plus the leaf row of a bonus draw"}
     else:
         n = out[1].cpu().numpy()
         cfg = {"workload": args.workload, "B": int(B), "gamma": int(G), "V": int(inp.V),

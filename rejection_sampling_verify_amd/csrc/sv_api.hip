@@ -368,6 +368,8 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
   return sv::launch_tree(a, bf16, vec, (hipStream_t)stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+static_assert(SV_MAX_TREE_NODES == sv::kMaxTreeNodes, "LDS copies of a tree hold SV_MAX_TREE_NODES nodes");
+
 sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_row_stride, const void* draft_logits,
                                     int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* parents,
                                     const int32_t* depth, const int32_t* node_tokens, const float* temperature,
@@ -430,18 +432,21 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
   a.out_len = out_path_len;
   a.out_token = out_token;
   const bool vec = sv::aligned16(target_logits, c.t_stride) && sv::aligned16(draft_logits, c.d_stride);
-  // Walk: about 16K elements of a row per workgroup (whole streaming rounds),
+  // Walk: about 8K elements of a row per workgroup (whole streaming rounds),
   // and as many sequences per launch as keep every workgroup resident.
   const int unit = sv::kThreads * (bf16 ? 8 : 4);
-  const int w0 = std::max(1, (V + 16383) / 16384);
+  const int per_wg = std::max(unit, sv::env_int("SV_TREE_WLEN", 8192));
+  const int w0 = std::max(1, (V + per_wg - 1) / per_wg);
   a.wlen = ((V + w0 - 1) / w0 + unit - 1) / unit * unit;
+  // At most 256 workgroups per sequence (the leader stages one slot per thread).
+  const int min_wlen = ((V + 255) / 256 + unit - 1) / unit * unit;
+  a.wlen = std::max(a.wlen, min_wlen);
   a.W = (V + a.wlen - 1) / a.wlen;
   if (a.W > c.p2_stride) return SV_ERR_BAD_SHAPE;
   const long long resident = (long long)cus * sv::tree_walk_occupancy_cached(dev, bf16, vec);
   if (a.W > resident) return SV_ERR_BAD_SHAPE;
   const long long per_launch = std::max<long long>(1, resident / a.W);
   hipStream_t st = (hipStream_t)stream;
-  if (sv::launch_tree_sample_stats(a, bf16, vec, st) != hipSuccess) return SV_ERR_HIP;
   for (long long b0 = 0; b0 < B; b0 += per_launch) {
     a.b_base = (int32_t)b0;
     a.b_count = (int32_t)std::min<long long>(per_launch, B - b0);

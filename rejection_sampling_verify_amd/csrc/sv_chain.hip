@@ -1477,15 +1477,13 @@ __global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
 
 // ===========================================================================
 // Sampled trees: multi-round rejection sampling (the pages' "Tree Attention"
-// section). Two launches:
-//   stats: one item per (sequence, node with children, row kind, chunk): the
-//          chunk's (max, sum exp2) of the node's target row, or of its draft
-//          row (q at the node: the distribution its children were drawn from);
-//   walk:  W workgroups per sequence, each owning wlen elements of a row. The
-//          last of them to arrive after an action (the leader) takes the
-//          sequence's next decisions serially and publishes the next action;
-//          all W then carry it out on their part of the row: a residual-mass
-//          pass, or the final Gumbel-max draw.
+// section). One launch gives every sequence W workgroups, each owning wlen
+// elements of a row. The last of them to arrive after an action (the leader)
+// takes the sequence's next decisions serially and publishes the next action;
+// all W then carry it out on their part of the row: the (max, sum exp2) of a
+// node's target and draft rows when the walk reaches a node with children
+// (only the nodes on the walked path are read), a residual-mass pass, or the
+// final Gumbel-max draw.
 // After some rejections at a node the target distribution is
 // p' = (p - A q)_+ / B. It starts at A = 0, B = 1, and a rejection moves it to
 // A' = A + B, B' = sum_v (p - A' q)_+ (one pass over the row pair). This is the
@@ -1494,7 +1492,10 @@ __global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
 // residual draw of the chains with q scaled by A (log2 A folded into the draft
 // normalizer).
 // ===========================================================================
-enum TreeAction : uint32_t { TA_NONE = 0, TA_PASS = 1, TA_DRAW_RESIDUAL = 2, TA_DRAW_BONUS = 3, TA_DONE = 4 };
+
+enum TreeAction : uint32_t {
+  TA_NONE = 0, TA_PASS = 1, TA_DRAW_RESIDUAL = 2, TA_DRAW_BONUS = 3, TA_DONE = 4, TA_STATS = 5
+};
 
 // The action record, in the sequence's SeqState (dec[0] stored last):
 //   dec[0] = epoch << 40 | action << 32 | node
@@ -1529,43 +1530,30 @@ __device__ void tree_publish(const TreeSampleArgs& ta, int b, uint32_t epoch, ui
   xput64(&st->dec[0], ((uint64_t)(epoch + 1u) << 40) | ((uint64_t)action << 32) | (uint32_t)t.node);
 }
 
-// The j-th child (index order) of node v, or -1. Children follow their parent.
-__device__ int tree_child(const TreeSampleArgs& ta, int v, int j) {
+// The j-th child (index order) of node v, or -1. Children follow their
+// parent. par: the parent array, staged in LDS.
+__device__ int tree_child(const TreeSampleArgs& ta, const int32_t* par, int v, int j) {
   for (int c = v + 1; c < ta.N; ++c)
-    if (ta.parents[c] == v) {
+    if (par[c] == v) {
       if (j == 0) return c;
       --j;
     }
   return -1;
 }
 
-// Row normalizers of node v (log2 domain): its stats slots merged in chunk order.
-__device__ void tree_node_stats(const TreeSampleArgs& ta, int b, int v, float c2, float* zt2, float* zd2) {
-  LseState t, d;
-  t.M = d.M = -INFINITY;
-  t.s = d.s = 0.0f;
-  P1Slot* sl = ta.c.p1 + ((int64_t)b * ta.N + v) * ta.c.nchunks;
-  for (int k = 0; k < ta.c.nchunks; ++k) {
-    const uint64_t w0 = xget64(&sl[k].w0), w1 = xget64(&sl[k].w1);
-    LseState o;
-    o.M = hi_f(w0);
-    o.s = __uint_as_float(lo_u(w0));
-    t = lse_merge(t, o, c2);
-    o.M = hi_f(w1);
-    o.s = __uint_as_float(lo_u(w1));
-    d = lse_merge(d, o, c2);
-  }
-  *zt2 = t.M * c2 + fast_log2(t.s);
-  *zd2 = d.M * c2 + fast_log2(d.s);
-}
-
 // Thread 0 of the leader: the sequence's decisions up to its next action.
-// After a pass (prev = TA_PASS) the workgroups' partial masses are summed in
-// workgroup order and the target distribution is updated; then siblings are
-// tested (an accepted child becomes the node, and its children are tested in
-// turn) until a rejection needs the next pass, or the walk ends in a draw.
+// After a stats action the workgroups' (max, sum) pairs are merged in
+// workgroup order into the node's normalizers; after a pass (prev = TA_PASS)
+// the partial masses are summed in workgroup order and the target
+// distribution is updated. Then siblings are tested until an accepted child
+// with children needs its statistics, a rejection needs the next pass, or the
+// walk ends in a draw.
+// par and tok: the parents and this sequence's node tokens, staged in LDS;
+// part: the W workgroups' slots of the action just carried out, staged in
+// LDS (w0, w1 per workgroup).
 template <bool BF16>
-__device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32_t epoch, const uint64_t rec[4]) {
+__device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32_t epoch, const uint64_t rec[4],
+                          const int32_t* par, const int32_t* tok_s, const uint64_t (*part)[2]) {
   using E = Elem<BF16>;
   const ChainArgs& a = ta.c;
   const float T = a.temperature[b];
@@ -1602,23 +1590,39 @@ __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32
       return;
     }
     xput(&path[0], 0);
+    tree_publish(ta, b, epoch, tree_child(ta, par, 0, 0) >= 0 ? TA_STATS : TA_DRAW_BONUS, s);
+    return;
+  } else if (prev == TA_STATS) {
+    s = tree_state_of(rec);
     c2 = kLog2e / T;
-    if (tree_child(ta, 0, 0) >= 0) tree_node_stats(ta, b, 0, c2, &s.zt2, &s.zd2);
+    LseState t, d;
+    t.M = d.M = -INFINITY;
+    t.s = d.s = 0.0f;
+    for (int w = 0; w < ta.W; ++w) {
+      const uint64_t w0 = part[w][0], w1 = part[w][1];
+      LseState o;
+      o.M = hi_f(w0);
+      o.s = __uint_as_float(lo_u(w0));
+      t = lse_merge(t, o, c2);
+      o.M = hi_f(w1);
+      o.s = __uint_as_float(lo_u(w1));
+      d = lse_merge(d, o, c2);
+    }
+    s.zt2 = t.M * c2 + fast_log2(t.s);
+    s.zd2 = d.M * c2 + fast_log2(d.s);
   } else {
     s = tree_state_of(rec);
     c2 = kLog2e / T;
-    const P2Slot* sl = a.p2 + (int64_t)b * a.p2_stride;
     float S = 0.0f;
-    for (int w = 0; w < ta.W; ++w) S += __uint_as_float((uint32_t)xget64((uint64_t*)&sl[w].w0));
+    for (int w = 0; w < ta.W; ++w) S += __uint_as_float((uint32_t)part[w][0]);
     if (S > 0.0f) {  // (a residual of zero mass leaves p as it was)
       s.A = s.A + s.Bv;
       s.Bv = S;
     }
     s.round += 1;
   }
-  const int32_t* tok = ta.tokens + (int64_t)b * ta.N;
   for (int guard = 0; guard <= ta.N; ++guard) {
-    const int c = tree_child(ta, s.node, s.round);
+    const int c = tree_child(ta, par, s.node, s.round);
     if (c < 0) {
       // A leaf (no child tested) draws the bonus from p; a node whose
       // children were all rejected draws from its final residual (or from p
@@ -1626,7 +1630,7 @@ __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32
       tree_publish(ta, b, epoch, (s.round > 0 && s.A > 0.0f) ? TA_DRAW_RESIDUAL : TA_DRAW_BONUS, s);
       return;
     }
-    const int x = tok[c];
+    const int x = tok_s[c];
     const float lt = E::load(target_row(a, b, s.node), x), ld = E::load(draft_row(a, b, s.node), x);
     const float lp2 = __builtin_fmaf(lt, c2, -s.zt2), lq2 = __builtin_fmaf(ld, c2, -s.zd2);
     float acc;
@@ -1644,8 +1648,11 @@ __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32
       s.round = 0;
       s.A = 0.0f;
       s.Bv = 1.0f;
-      if (tree_child(ta, c, 0) >= 0) tree_node_stats(ta, b, c, c2, &s.zt2, &s.zd2);
-      continue;
+      s.zt2 = s.zd2 = 0.0f;
+      // The new node: its statistics first if it has children, else the
+      // bonus draw.
+      tree_publish(ta, b, epoch, tree_child(ta, par, c, 0) >= 0 ? TA_STATS : TA_DRAW_BONUS, s);
+      return;
     }
     tree_publish(ta, b, epoch, TA_PASS, s);  // the mass of (p - (A + B) q)_+ at this node
     return;
@@ -1717,50 +1724,12 @@ __device__ void tree_finish(const TreeSampleArgs& ta, int b, uint32_t action, Sm
     xput(&ta.out_len[b], (int)(uint32_t)sm.trec[3]);
   }
   __syncthreads();
-  const int nslots = ta.N * a.nchunks;
-  uint64_t* p1 = (uint64_t*)(a.p1 + (int64_t)b * nslots);
-  for (int k = threadIdx.x; k < 2 * nslots; k += kThreads) xput64(&p1[k], 0u);
   for (int k = threadIdx.x; k < 2 * ta.W; k += kThreads) xput64(&((uint64_t*)sl)[k], 0u);
   SeqState* st = a.seq + b;
   if (threadIdx.x < 4) xput64(&st->dec[threadIdx.x], 0u);
   if (threadIdx.x == 0) {
     xput(&st->lbest, 0u);
     xput(&st->p2_arrive, 0u);
-  }
-}
-
-// Stats launch: item (b, v, kind, c) in that order, c fastest.
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void tree_stats_kernel(TreeSampleArgs ta) {
-  __shared__ Smem sm;
-  const ChainArgs& a = ta.c;
-  const int C = a.nchunks;
-  int64_t r = blockIdx.x;
-  const int c = (int)(r % C);
-  r /= C;
-  const int kind = (int)(r % 2);
-  r /= 2;
-  const int v = (int)(r % ta.N);
-  const int b = (int)(r / ta.N);
-  const float T = a.temperature[b];
-  if (!(T > 0.0f) || T == INFINITY) return;
-  bool leaf = true;  // leaf rows are not needed: a leaf's bonus draw reads raw logits
-  for (int k = v + 1; k < ta.N; ++k)
-    if (ta.parents[k] == v) {
-      leaf = false;
-      break;
-    }
-  if (leaf) return;
-  const uint8_t* row = kind ? draft_row(a, b, v) : target_row(a, b, v);
-  const int lo = c * a.chunk, hi = min(a.V, lo + a.chunk);
-  const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && hi - lo == a.chunk;
-  Chunk<BF16, VEC> ch;
-  ch.load(row, lo, hi, a.kv);
-  const float c2 = kLog2e / T;
-  const LseState st = block_lse(fast ? lse_packed_bf16(ch.q, c2) : chunk_lse(ch, row, a.kv, c2), c2, sm, 0);
-  if (threadIdx.x == 0) {
-    P1Slot* dst = a.p1 + ((int64_t)b * ta.N + v) * C + c;
-    xput64(kind ? &dst->w1 : &dst->w0, pack(st.M, __float_as_uint(st.s)));
   }
 }
 
@@ -1776,6 +1745,13 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   if (b >= ta.b_base + ta.b_count) return;  // whole sequences only
   SeqState* st = a.seq + b;
   const int lo = w * ta.wlen, hi = min(a.V, lo + ta.wlen);
+  // The tree and this sequence's tokens in LDS: any workgroup may lead, and
+  // the leader walks them serially.
+  __shared__ int32_t s_par[kMaxTreeNodes], s_tok[kMaxTreeNodes];
+  for (int k = threadIdx.x; k < ta.N; k += kThreads) {
+    s_par[k] = ta.parents[k];
+    s_tok[k] = ta.tokens[(int64_t)b * ta.N + k];
+  }
   uint32_t epoch = 0, action = TA_NONE;
   float partial = 0.0f;
   P2Slot part;
@@ -1786,6 +1762,10 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
     if (threadIdx.x == 0) {
       P2Slot* slot = a.p2 + (int64_t)b * a.p2_stride + w;
       if (action == TA_PASS) xput64(&slot->w0, (uint64_t)__float_as_uint(partial));
+      if (action == TA_STATS) {
+        xput64(&slot->w0, part.w0);
+        xput64(&slot->w1, part.w1);
+      }
       if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) xput64(&slot->w0, part.w0);
       wait_vmem();
       const uint32_t old = atomicAdd(&st->p2_arrive, 1u);
@@ -1798,7 +1778,16 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
       if (last) tree_finish<BF16, VEC>(ta, b, action, sm);
       return;
     }
-    if (last && threadIdx.x == 0) tree_lead<BF16>(ta, b, action, epoch, sm.trec);
+    if (last) {
+      // The workgroups' slots, read in parallel.
+      const P2Slot* sl = a.p2 + (int64_t)b * a.p2_stride;
+      for (int k = threadIdx.x; k < ta.W; k += kThreads) {
+        sm.u.slot[k][0] = xget64((uint64_t*)&sl[k].w0);
+        sm.u.slot[k][1] = xget64((uint64_t*)&sl[k].w1);
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) tree_lead<BF16>(ta, b, action, epoch, sm.trec, s_par, s_tok, sm.u.slot);
+    }
     __syncthreads();
     // Wait for the next action (bounded).
     if (threadIdx.x == 0) {
@@ -1829,7 +1818,31 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
     action = (uint32_t)(sm.trec[0] >> 32) & 0xFFu;
     const TreeState t = tree_state_of(sm.trec);
     const float c2 = kLog2e / a.temperature[b];
-    if (action == TA_PASS) {
+    if (action == TA_STATS) {
+      // (max, sum exp2) of the node's target and draft rows over [lo, hi),
+      // in pieces of the launch's tile.
+      LseState lt, ld;
+      lt.M = ld.M = -INFINITY;
+      lt.s = ld.s = 0.0f;
+      for (int kind = 0; kind < 2; ++kind) {  // the target row, then the draft row
+        const uint8_t* row = kind ? draft_row(a, b, t.node) : target_row(a, b, t.node);
+        LseState acc;
+        acc.M = -INFINITY;
+        acc.s = 0.0f;
+        for (int lo2 = lo; lo2 < hi; lo2 += a.chunk) {
+          const int hi2 = min(hi, lo2 + a.chunk);
+          const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && hi2 - lo2 == a.chunk;
+          Chunk<BF16, VEC> ch;
+          ch.load(row, lo2, hi2, a.kv);
+          acc = lse_merge(acc, block_lse(fast ? lse_packed_bf16(ch.q, c2) : chunk_lse(ch, row, a.kv, c2), c2, sm, kind),
+                          c2);
+        }
+        if (kind) ld = acc;
+        else lt = acc;
+      }
+      part.w0 = pack(lt.M, __float_as_uint(lt.s));
+      part.w1 = pack(ld.M, __float_as_uint(ld.s));
+    } else if (action == TA_PASS) {
       const float zd2s = t.zd2 - fast_log2(t.A + t.Bv);
       partial = block_sum(residual_mass_part<BF16, VEC>(target_row(a, b, t.node), draft_row(a, b, t.node), lo, hi, c2,
                                                         t.zt2, zd2s),
@@ -1934,22 +1947,10 @@ int chain_occupancy(bool bf16, bool vec) {
 }
 
 template <bool BF16, bool VEC>
-hipError_t launch_tree_sample_stats_t(const TreeSampleArgs& a, hipStream_t stream) {
-  const long long grid = (long long)a.c.B * a.N * 2 * a.c.nchunks;
-  hipLaunchKernelGGL((tree_stats_kernel<BF16, VEC>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <bool BF16, bool VEC>
 hipError_t launch_tree_sample_walk_t(const TreeSampleArgs& a, hipStream_t stream) {
   const long long grid = (long long)a.b_count * a.W;
   hipLaunchKernelGGL((tree_walk_kernel<BF16, VEC>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
-}
-
-hipError_t launch_tree_sample_stats(const TreeSampleArgs& a, bool bf16, bool vec, hipStream_t stream) {
-  if (bf16) return vec ? launch_tree_sample_stats_t<true, true>(a, stream) : launch_tree_sample_stats_t<true, false>(a, stream);
-  return vec ? launch_tree_sample_stats_t<false, true>(a, stream) : launch_tree_sample_stats_t<false, false>(a, stream);
 }
 
 hipError_t launch_tree_sample_walk(const TreeSampleArgs& a, bool bf16, bool vec, hipStream_t stream) {

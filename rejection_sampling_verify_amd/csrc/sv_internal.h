@@ -202,7 +202,6 @@ int tree_occupancy(bool bf16, bool vec);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 int chain_occupancy(bool bf16, bool vec);
 int chain_p2_occupancy(bool bf16, bool vec);
-hipError_t launch_tree_sample_stats(const TreeSampleArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_tree_sample_walk(const TreeSampleArgs& a, bool bf16, bool vec, hipStream_t stream);
 int tree_sample_walk_occupancy(bool bf16, bool vec);
 

@@ -147,10 +147,25 @@ class TreeSampleInputs:
     def inner_nodes(self) -> int:
         return int(len(set(int(p) for p in self.parents[1:])))
 
+    paths: tuple | None = None  # (path [B, max_depth + 1], path_len [B]) of a verified step
+
     def algorithmic_bytes(self) -> int:
-        """Every inner node's target and draft row once, plus one row per
-        sequence for its final draw."""
-        return self.B * (2 * self.inner_nodes() + 1) * self.V * self.target.itemsize
+        """Rows a step must read at least once: the target and draft row of
+        every inner node on each sequence's accepted path, plus the leaf row
+        when the path ends at a leaf (its bonus draw). Needs self.paths; without
+        it, the bound for the deepest possible path of every sequence."""
+        inner = set(int(p) for p in self.parents[1:])
+        row = self.V * self.target.itemsize
+        if self.paths is None:
+            return self.B * (2 * (self.max_depth + 1)) * row
+        path, plen = self.paths
+        rows = 0
+        for b in range(self.B):
+            nodes = [int(v) for v in path[b, :max(int(plen[b]), 0)]]
+            rows += sum(2 for v in nodes if v in inner)
+            if nodes and nodes[-1] not in inner:
+                rows += 1
+        return rows * row
 
 
 def _seq_rng(seed: int, b: int) -> np.random.Generator:
