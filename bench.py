@@ -34,7 +34,7 @@ COPY_BYTES = 1 << 30
 DEFAULT_WORKLOAD = "chain_bf16_llama"
 KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_chain.hip", "rejection_sampling_verify_amd/csrc/sv_tree.hip",
                   "rejection_sampling_verify_amd/csrc/sv_device.h", "rejection_sampling_verify_amd/csrc/sv_internal.h",
-                  "rejection_sampling_verify_amd/csrc/sv_api.hip"]
+                  "rejection_sampling_verify_amd/csrc/sv_api.hip", "rejection_sampling_verify_amd/csrc/sv_kv.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -122,6 +122,82 @@ def copy_calibration(torch, dev, steps: int):
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": steps}), flush=True)
 
 
+def run_kv(args, torch, rsv, workloads, dev):
+    """KV-cache rollback after a tree verify step: one sv_kv_rollback call over
+    the resident K and V caches of every layer. Successive steps move the root
+    positions on by 64 (16 distinct sets, as decoding advances), so the rows a
+    step touches are not left in the caches by the step before."""
+    inp = workloads.make_extra(args.workload)
+    L, B, H, S, D = inp.shape
+    k = workloads.fill_kv_device(torch, torch.empty(inp.shape, dtype=torch.int16, device=dev), inp.seed, 0)
+    v = workloads.fill_kv_device(torch, torch.empty(inp.shape, dtype=torch.int16, device=dev), inp.seed, 1)
+    roots = [torch.from_numpy(inp.root + 64 * j).to(dev) for j in range(16)]
+    path = torch.from_numpy(inp.path).to(dev)
+    plen = torch.from_numpy(inp.path_len).to(dev)
+    out = torch.empty(B, dtype=torch.int32, device=dev)
+    print("[bench] workload %s resident" % args.workload, file=sys.stderr, flush=True)
+
+    def step(j):
+        rsv.sv_kv_rollback(k, v, roots[j % 16], path, plen, cache_len=out)
+
+    stream = torch.cuda.current_stream()
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        starts[j].record(stream)
+        step(j)
+        ends[j].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
+    ms_per_step = wall * 1e3 / args.steps
+    alg_bytes = inp.algorithmic_bytes()
+    achieved = alg_bytes / (float(np.mean(launch_ms)) * 1e-3) / 1e9
+    rec = {
+        "metric": "KV-cache rollback sequences/s (every layer's K and V moved to the accepted path)",
+        "value": B / (ms_per_step * 1e-3), "unit": "sequences/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "L": L, "B": B, "H": H, "S": S, "D": D, "cache_dtype": "bf16",
+                   "paths": "walks in the 65-node tree, 1 to 4 nodes"},
+        "moved_rows_per_layer_head": int(inp.moved_rows().sum()),
+        "algorithmic_bytes_per_step": int(alg_bytes),
+        "launch_ms": {"mean": float(np.mean(launch_ms)), "p10": float(np.percentile(launch_ms, 10)),
+                      "p50": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = kv_cpu_baseline(inp)
+    print(json.dumps(rec), flush=True)
+
+
+def kv_cpu_baseline(inp, max_runs: int = 5):
+    """The oracle on one layer of K and V for every sequence (numpy, one
+    thread), scaled to whole sequences (all layers)."""
+    from oracle import kv as okv
+    L, B, H, S, D = inp.shape
+    rng = np.random.default_rng(inp.seed)
+    kc = rng.integers(-32768, 32767, size=(1, B, H, S, D), dtype=np.int16)
+    vc = rng.integers(-32768, 32767, size=(1, B, H, S, D), dtype=np.int16)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_runs and time.perf_counter() - t_start < 10.0:
+        t0 = time.perf_counter()
+        okv.kv_rollback(kc, inp.root, inp.path, inp.path_len)
+        okv.kv_rollback(vc, inp.root, inp.path, inp.path_len)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": B / L / t, "unit": "sequences/s", "cores": 1, "kind": "oracle",
+            "sample": "one of %d layers, K and V, all %d sequences; %d run(s), median %.3f s" % (L, B, len(times), t)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +222,9 @@ def main():
         copy_calibration(torch, dev, args.steps)
         return
     rsv.lib()
+    if args.workload.startswith("kv_rollback"):
+        run_kv(args, torch, rsv, workloads, dev)
+        return
     inp = workloads.make_extra(args.workload) if args.workload in workloads.EXTRA else workloads.make(args.workload)
     is_tree = args.workload.startswith("tree")
     sampled_tree = isinstance(inp, workloads.TreeSampleInputs)

@@ -238,6 +238,34 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
                                     uint64_t offset, int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* sv_kv_rollback — rolls a KV cache back to the accepted tokens after a
+ * verify step ([SB] "KV-Cache Reuse and Rollback": a chain step crops every
+ * layer's cache to keep = T + n positions; a tree step keeps the accepted
+ * root-to-leaf path, gathered along the sequence dimension with the node
+ * positions as index).
+ *   k_cache, v_cache: device, each [L, B, H, S, D] contiguous elements of
+ *     elem_bytes (1, 2 or 4) bytes, 16-byte aligned; v_cache may be NULL.
+ *     Node i of sequence b's tree sits at position root_pos[b] + i; node 0,
+ *     the root, is the last committed token, whose entry the verify pass
+ *     wrote. A chain of gamma drafts is the tree 0 - 1 - ... - gamma.
+ *   path [B, P], path_len [B]: device, the verify step's accepted path (root
+ *     first), e.g. spec_verify_tree_sample's outputs; for a chain, path =
+ *     0 .. n and path_len = n + 1.
+ *   In place: for every layer, sequence and head, the entry at position
+ *   root_pos[b] + path[b][k] moves to root_pos[b] + k (k < path_len[b]);
+ *   positions before the root are untouched, those from the new length on
+ *   are left as they were. cache_len[b] (device, out) = root_pos[b] +
+ *   path_len[b], the number of valid positions (for a chain, T + n), or -1
+ *   when the path is not root-first, strictly increasing and inside the cache
+ *   (that sequence is left untouched).
+ * Returns SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE (a dimension < 0, S, D or P < 1,
+ * P > 1024, a row of D * elem_bytes bytes not a multiple of 16 or above 16 KiB), SV_ERR_BAD_DTYPE
+ * (elem_bytes), SV_ERR_BAD_ARG (a cache not 16-byte aligned) or SV_ERR_HIP;
+ * nothing is launched on an error, and nothing is written when L, B or H is 0. */
+sv_status_t sv_kv_rollback(void* k_cache, void* v_cache, int32_t elem_bytes, int32_t L, int32_t B, int32_t H,
+                           int32_t S, int32_t D, const int32_t* root_pos, const int32_t* path, int32_t P,
+                           const int32_t* path_len, int32_t* cache_len, void* stream);
+
 /*
  * Diagnostic entry points: the random primitives of the kernels, element by
  * element, so that they can be checked against their definitions. All arrays

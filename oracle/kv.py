@@ -20,8 +20,9 @@ import numpy as np
 def kv_rollback(cache: np.ndarray, root: np.ndarray, path: np.ndarray, path_len: np.ndarray):
     """Returns (new cache, new lengths). keep_idx = [0 .. root) + root + path[:len];
     positions from len(keep_idx) on are left as they were. A sequence with a
-    path that is not a valid gather (len < 1, a node before its predecessor, a
-    position past the end) is left unchanged and gets length -1."""
+    path that is not a valid gather (len < 1 or beyond the path array, a node
+    before its predecessor, a position past the end) is left unchanged and gets
+    length -1."""
     L, B, H, S, D = cache.shape
     out = cache.copy()
     new_len = np.empty(B, np.int32)
@@ -29,7 +30,7 @@ def kv_rollback(cache: np.ndarray, root: np.ndarray, path: np.ndarray, path_len:
         n = int(path_len[b])
         p = [int(x) for x in path[b, :max(n, 0)]]
         r = int(root[b])
-        ok = n >= 1 and p[0] == 0 and all(p[k] > p[k - 1] for k in range(1, n)) and 0 <= r and r + p[-1] < S
+        ok = 1 <= n <= path.shape[1] and p[0] == 0 and all(p[k] > p[k - 1] for k in range(1, n)) and 0 <= r and r + p[-1] < S
         if not ok:
             new_len[b] = -1
             continue

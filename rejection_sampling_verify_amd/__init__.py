@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     spec_verify_sample,
     spec_verify_tree,
     spec_verify_tree_sample,
+    sv_kv_rollback,
     sv_debug_noise,
     sv_debug_read_stream,
     sv_debug_wave_max,

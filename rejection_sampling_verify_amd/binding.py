@@ -22,7 +22,7 @@ SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
+           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
            "sv_debug_read_stream"]
 
 _lib = None
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_tree_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, u64, u64,
                                               P, P, P, P, sz, P]
         L.spec_verify_tree_sample.restype = ctypes.c_int
+        L.sv_kv_rollback.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
+        L.sv_kv_rollback.restype = ctypes.c_int
         L.sv_debug_philox.argtypes = [P, P, P, i32, P]
         L.sv_debug_philox.restype = ctypes.c_int
         L.sv_debug_noise.argtypes = [P, P, P, i32, P]
@@ -275,6 +277,32 @@ def spec_verify_tree_sample(target_logits, draft_logits, parents, depth, node_to
     if st != 0:
         raise SVError(st, "spec_verify_tree_sample")
     return out_path, out_path_len, out_token
+
+
+def sv_kv_rollback(k_cache, v_cache, root_pos, path, path_len, cache_len=None, stream=None):
+    """In-place KV-cache rollback to the accepted path. k_cache / v_cache:
+    contiguous device tensors [L, B, H, S, D] (v_cache may be None); root_pos
+    [B], path [B, P], path_len [B] int32. Returns cache_len [B] int32."""
+    import torch
+    if k_cache.dim() != 5 or not k_cache.is_contiguous():
+        raise ValueError("k_cache must be a contiguous [L, B, H, S, D] tensor")
+    L, B, H, S, D = k_cache.shape
+    if v_cache is not None and (tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype
+                                or not v_cache.is_contiguous()):
+        raise ValueError("v_cache must match k_cache")
+    _check_i32(root_pos, (B,), "root_pos")
+    _check_i32(path_len, (B,), "path_len")
+    if path.dim() != 2 or path.shape[0] != B:
+        raise ValueError("path must be [B, P]")
+    _check_i32(path, tuple(path.shape), "path")
+    if cache_len is None:
+        cache_len = torch.empty((B,), dtype=torch.int32, device=k_cache.device)
+    st = lib().sv_kv_rollback(_ptr(k_cache), _ptr(v_cache) if v_cache is not None else None, k_cache.element_size(),
+                              L, B, H, S, D, _ptr(root_pos), _ptr(path), int(path.shape[1]), _ptr(path_len),
+                              _ptr(cache_len), _stream(stream))
+    if st != 0:
+        raise SVError(st, "sv_kv_rollback")
+    return cache_len
 
 
 def sv_debug_philox(ctr, key, out=None, stream=None):

@@ -29,6 +29,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert set(names) >= {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample",
+                          "sv_kv_rollback",
                           "sv_workspace_bytes",
                           "sv_workspace_init", "sv_status_string", "sv_debug_philox", "sv_debug_noise",
                           "sv_debug_wave_max", "sv_debug_read_stream"}
@@ -130,3 +131,17 @@ def test_tree_sample_argument_validation(L):
     assert ts(ts=99) == 4 and ts(ds=99) == 4 and ts(off=1 << 31) == 4
     assert ts(wsb=10) == 5
     assert ts(B=0) == 0
+
+
+def test_kv_rollback_argument_validation(L):
+    f = _Fake(1 << 16)
+    P = f.ptr
+    kv = lambda **k: L.sv_kv_rollback(k.get("k", P), k.get("v", P), k.get("es", 2), k.get("L", 2), k.get("B", 2),
+                                      k.get("H", 2), k.get("S", 8), k.get("D", 64), k.get("root", P), P,
+                                      k.get("P", 4), P, k.get("out", P), None)
+    assert kv(k=None) == 1 and kv(root=None) == 1 and kv(out=None) == 1
+    assert kv(S=0) == 2 and kv(D=0) == 2 and kv(P=0) == 2 and kv(P=1025) == 2 and kv(L=-1) == 2
+    assert kv(D=7) == 2 and kv(D=8193) == 2 and kv(D=16384) == 2  # rows of 14 B; rows above 16 KiB
+    assert kv(es=3) == 3
+    assert kv(k=ctypes.c_void_p(P.value + 8)) == 4
+    assert kv(L=0) == 0 and kv(H=0) == 0

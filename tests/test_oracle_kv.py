@@ -40,3 +40,6 @@ def test_invalid_paths_are_left_alone():
     out, new_len = kv.kv_rollback(c, np.array([0, 0, 3]), path, np.array([0, 2, 2]))
     assert list(new_len) == [-1, -1, -1]  # empty path; root not first; past the end
     assert np.array_equal(out, c)
+    out, new_len = kv.kv_rollback(c, np.array([0, 0, 0]), path, np.array([4, 3, 1]))
+    assert list(new_len) == [-1, -1, 1]  # a length beyond the path array; a path with a -1 node
+    assert np.array_equal(out, c)

@@ -23,6 +23,11 @@ and, for sampled tree verification (multi-round rejection sampling):
       target as chain_bf16_llama's, draft row of each inner node = target +
       N(0, sigma_b^2), sigma_b ~ U[0.2, 2]; children drawn i.i.d. from q at
       their parent.
+and, for the KV-cache rollback after a verify step:
+  kv_rollback_bf16_llama  K and V caches [L=32, B=32, H=8, S=4096, D=128] bf16
+      (the KV layout of a 32-layer model with 8 KV heads of dimension 128),
+      root positions U[512, 3008), accepted paths drawn as walks in the same
+      65-node tree (a uniformly random child at each level, 1 to 4 nodes).
 """
 from __future__ import annotations
 
@@ -35,7 +40,7 @@ import numpy as np
 CONFIGS = ["chain_f32_small", "chain_bf16_peaked", "chain_bf16_llama", "onehot_bf16_qwen",
            "tree_bf16_llama"]
 CONFIG_INDEX = {name: k for k, name in enumerate(CONFIGS)}
-EXTRA = ["tree_sample_bf16_llama"]
+EXTRA = ["tree_sample_bf16_llama", "kv_rollback_bf16_llama"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -351,12 +356,123 @@ def make(name: str, workers=None):
     raise KeyError(name)
 
 
+@dataclass
+class KvRollbackInputs:
+    """A KV-cache rollback: caches of shape [L, B, H, S, D] with elements of
+    elem_bytes bytes (generated on demand: cache_host for small shapes,
+    fill_kv_device for resident ones), and per sequence the root position and
+    the accepted path (root first, node i at position root + i)."""
+    name: str
+    shape: tuple              # (L, B, H, S, D)
+    elem_bytes: int
+    root: np.ndarray          # [B] int32
+    path: np.ndarray          # [B, P] int32, -1 past path_len
+    path_len: np.ndarray      # [B] int32
+    seed: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.shape[1]
+
+    def int_dtype(self):
+        return {1: np.uint8, 2: np.int16, 4: np.int32}[self.elem_bytes]
+
+    def cache_host(self, which: int) -> np.ndarray:
+        """Random bit patterns (which = 0 for K, 1 for V)."""
+        rng = np.random.default_rng([self.seed, 77, which])
+        dt = self.int_dtype()
+        info = np.iinfo(dt)
+        return rng.integers(info.min, info.max, size=self.shape, dtype=dt, endpoint=True)
+
+    def moved_rows(self) -> np.ndarray:
+        """Per sequence, the path nodes whose row changes place (node k taken
+        from a node other than k)."""
+        return np.array([int(np.count_nonzero(self.path[b, :self.path_len[b]] != np.arange(self.path_len[b])))
+                         for b in range(self.B)], np.int64)
+
+    def algorithmic_bytes(self, with_v: bool = True) -> int:
+        """Each moved row read once and written once in every layer and head,
+        for K (and V), plus the root, path and length reads and the length
+        writes."""
+        L, B, H, S, D = self.shape
+        row = D * self.elem_bytes
+        moved = int(self.moved_rows().sum()) * L * H * row * 2 * (2 if with_v else 1)
+        return moved + self.path.nbytes + 3 * B * 4
+
+
+def fill_kv_device(torch, t, seed: int, which: int):
+    """Seeded random bits into a resident cache tensor (integer dtype)."""
+    g = torch.Generator(device=t.device)
+    g.manual_seed(seed * 16 + which)
+    t.random_(generator=g)
+    return t
+
+
+def _children(parents: np.ndarray):
+    ch = [[] for _ in range(len(parents))]
+    for v in range(1, len(parents)):
+        ch[int(parents[v])].append(v)
+    return ch
+
+
+def make_kv_rollback(name: str, L: int, B: int, H: int, S: int, D: int, *, elem_bytes: int, seed: int,
+                     kind: str = "tree", parents: np.ndarray | None = None, P: int | None = None,
+                     root_lo: int = 0, root_hi: int | None = None) -> KvRollbackInputs:
+    """kind 'tree': walks from the root of `parents`, a uniformly random child
+    at each level and 1 .. depth + 1 nodes; 'chain': the identity path 0 .. n
+    of a chain step, n uniform in [0, P); 'sparse': 0 followed by n - 1
+    increasing node indices below S - root (long paths), n uniform in [1, P].
+    Roots are uniform in [root_lo, root_hi) with root_hi defaulting to the
+    largest root that keeps every node of the path inside the cache."""
+    if kind == "tree":
+        ch = _children(parents)
+        depth = [0] * len(parents)
+        for v in range(1, len(parents)):
+            depth[v] = depth[int(parents[v])] + 1
+        P = max(depth) + 1
+        span = len(parents)
+    elif kind == "chain":
+        span = P
+    elif kind == "sparse":
+        span = S - root_lo if root_hi is None else S - root_hi + 1
+    else:
+        raise ValueError(kind)
+    hi = S - span + 1 if root_hi is None else root_hi
+    path = np.full((B, P), -1, np.int32)
+    plen = np.empty(B, np.int32)
+    root = np.empty(B, np.int32)
+    for b in range(B):
+        rng = _seq_rng(seed, b)
+        root[b] = int(rng.integers(root_lo, hi))
+        if kind == "tree":
+            nodes = [0]
+            n = int(rng.integers(1, P + 1))
+            while len(nodes) < n and ch[nodes[-1]]:
+                c = ch[nodes[-1]]
+                nodes.append(c[int(rng.integers(len(c)))])
+        elif kind == "chain":
+            nodes = list(range(int(rng.integers(0, P)) + 1))
+        else:
+            n = int(rng.integers(1, P + 1))
+            room = S - int(root[b])
+            n = min(n, room)
+            nodes = [0] + sorted(int(x) for x in rng.choice(np.arange(1, room), size=n - 1, replace=False))
+        path[b, :len(nodes)] = nodes
+        plen[b] = len(nodes)
+    return KvRollbackInputs(name, (L, B, H, S, D), elem_bytes, root, path, plen, seed=seed, meta={"kind": kind})
+
+
 def make_extra(name: str, workers=None):
     """Workloads of the rows beyond the five configurations (seed 2000 + k)."""
     seed = 2000 + EXTRA.index(name)
     if name == "tree_sample_bf16_llama":
         parents, depth = _c5_tree()
         return make_tree_sample(name, 32, 128256, parents, depth, bf16=True, seed=seed, workers=workers)
+    if name == "kv_rollback_bf16_llama":
+        parents, _ = _c5_tree()
+        return make_kv_rollback(name, 32, 32, 8, 4096, 128, elem_bytes=2, seed=seed, kind="tree", parents=parents,
+                                root_lo=512, root_hi=3008)
     raise KeyError(name)
 
 
