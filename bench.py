@@ -34,12 +34,14 @@ COPY_BYTES = 1 << 30
 DEFAULT_WORKLOAD = "chain_bf16_llama"
 KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_chain.hip", "rejection_sampling_verify_amd/csrc/sv_tree.hip",
                   "rejection_sampling_verify_amd/csrc/sv_device.h", "rejection_sampling_verify_amd/csrc/sv_internal.h",
-                  "rejection_sampling_verify_amd/csrc/sv_api.hip", "rejection_sampling_verify_amd/csrc/sv_kv.hip"]
+                  "rejection_sampling_verify_amd/csrc/sv_api.hip"]
+KV_KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_kv.hip"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str = DEFAULT_WORKLOAD) -> str:
+    """Hash of the sources of the kernels a workload runs (verify, or KV rollback)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KV_KERNEL_SOURCES if workload.startswith("kv_rollback") else KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -53,7 +55,7 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 

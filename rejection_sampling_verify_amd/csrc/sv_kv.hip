@@ -4,23 +4,23 @@
 // path's entries, gathered along the sequence dimension; a chain's path is the
 // identity, so a chain step only shortens the cache.
 //
-// One wavefront per (layer, sequence, head) slab of [positions, head_dim]. The
-// lanes check the path together, then move its rows as 16-byte vectors, a
-// chunk of rows at a time, every vector of a chunk read before any is written:
-// node k comes from node p_k >= k and the path increases, so the sources of
-// later chunks (rows p_j > p_k >= k) lie past every row an earlier chunk wrote,
-// and within a chunk the barrier orders the reads before the writes.
+// One workgroup per (layer, sequence), covering every head: the lanes check the
+// path together, then move its rows as 16-byte vectors, a chunk of (head, node,
+// vector) items at a time, every item of a chunk read before any is written.
+// Within one head node k comes from node p_k >= k and the path increases, so
+// the sources of later chunks (rows p_j > p_k >= k) lie past every row an
+// earlier chunk wrote there, and inside a chunk the barrier orders the reads
+// before the writes; heads are disjoint slabs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/spec_verify.h"
-#include "sv_internal.h"
 
 namespace sv {
 namespace {
 
 typedef uint32_t kv_u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kKvThreads = 64;      // one wavefront per slab
+constexpr int kKvThreads = 256;
 constexpr int kKvPerLane = 4;       // 16-byte vectors a lane holds per chunk (K and V each)
 constexpr int kKvMaxPath = 1024;    // path entries staged in LDS (a tree has at most SV_MAX_TREE_NODES nodes)
 constexpr int kKvMaxRowBytes = 16384;
@@ -28,7 +28,7 @@ constexpr int kKvMaxRowBytes = 16384;
 struct KvArgs {
   uint8_t* k;  // [L, B, H, S, D] elements of elem bytes
   uint8_t* v;  // same layout, or NULL
-  int32_t L, B, H, S;
+  int32_t B, H, S;
   int32_t vpr;              // 16-byte vectors per row (D * elem / 16)
   const int32_t* root;      // [B]
   const int32_t* path;      // [B, P]
@@ -39,52 +39,62 @@ struct KvArgs {
 
 __global__ __launch_bounds__(kKvThreads) void kv_rollback_kernel(KvArgs a) {
   extern __shared__ int32_t s_path[];  // [P]
-  const int64_t slab = blockIdx.x;     // (l, b, h), h fastest
-  const int h = (int)(slab % a.H);
-  const int b = (int)((slab / a.H) % a.B);
-  const int l = (int)(slab / ((int64_t)a.H * a.B));
-  const int lane = (int)threadIdx.x;
+  const int64_t lb = blockIdx.x;       // (l, b), b fastest
+  const int b = (int)(lb % a.B);
+  const int l = (int)(lb / a.B);
+  const int tid = (int)threadIdx.x;
+  // The whole path row is staged whatever its length, so that its loads and
+  // those of the length and the root share one trip to memory.
+  for (int k = tid; k < a.P; k += kKvThreads) s_path[k] = a.path[(int64_t)b * a.P + k];
   const int n = a.path_len[b];
   const int r = a.root[b];
+  __syncthreads();
   // The oracle's validity rule: root first, strictly increasing nodes, every
   // position inside the cache (which also keeps every node >= 0).
   int bad = !(n >= 1 && n <= a.P && r >= 0);
   if (!bad)
-    for (int k = lane; k < n; k += kKvThreads) s_path[k] = a.path[(int64_t)b * a.P + k];
-  __syncthreads();
-  if (!bad)
-    for (int k = lane; k < n; k += kKvThreads) {
+    for (int k = tid; k < n; k += kKvThreads) {
       const int p = s_path[k];
       bad |= !((k == 0 ? p == 0 : p > s_path[k - 1]) && (int64_t)r + p < a.S);
     }
   bad = __syncthreads_or(bad);
-  if (lane == 0 && l == 0 && h == 0) a.cache_len[b] = bad ? -1 : r + n;
+  if (tid == 0 && l == 0) a.cache_len[b] = bad ? -1 : r + n;
   if (bad) return;
   const int vpr = a.vpr;
+  const int per_head = n * vpr;
+  const int items = a.H * per_head;  // (head, node, vector), vector fastest; < 2^31 (checked on the host)
   const int64_t row_bytes = (int64_t)vpr * 16;
-  const int64_t slab_off = slab * a.S * row_bytes;
-  const int items = n * vpr;  // (node, vector) pairs, vector fastest
+  const int64_t head_bytes = (int64_t)a.S * row_bytes;
+  const int64_t lb_off = lb * a.H * head_bytes + (int64_t)r * row_bytes;
   for (int i0 = 0; i0 < items; i0 += kKvThreads * kKvPerLane) {
     kv_u32x4 qk[kKvPerLane], qv[kKvPerLane];
+    int64_t dst[kKvPerLane];
+    bool act[kKvPerLane];
 #pragma unroll
     for (int j = 0; j < kKvPerLane; ++j) {
-      const int i = i0 + j * kKvThreads + lane;
-      const int k = i / vpr;
-      if (i < items && s_path[k] != k) {
-        const int64_t src = slab_off + (int64_t)(r + s_path[k]) * row_bytes + (int64_t)(i - k * vpr) * 16;
-        qk[j] = *(const kv_u32x4*)(a.k + src);
-        if (a.v) qv[j] = *(const kv_u32x4*)(a.v + src);
+      const int i = i0 + j * kKvThreads + tid;
+      act[j] = false;
+      if (i < items) {
+        const int h = i / per_head;
+        const int rem = i - h * per_head;
+        const int k = rem / vpr;
+        const int64_t base = lb_off + h * head_bytes + (int64_t)(rem - k * vpr) * 16;
+        const int p = s_path[k];
+        act[j] = p != k;
+        dst[j] = base + (int64_t)k * row_bytes;
+        if (act[j]) {
+          const int64_t src = base + (int64_t)p * row_bytes;
+          qk[j] = *(const kv_u32x4*)(a.k + src);
+          if (a.v) qv[j] = *(const kv_u32x4*)(a.v + src);
+        }
       }
     }
     __syncthreads();  // the whole chunk is read before any of it is written
 #pragma unroll
     for (int j = 0; j < kKvPerLane; ++j) {
-      const int i = i0 + j * kKvThreads + lane;
-      const int k = i / vpr;
-      if (i < items && s_path[k] != k) {
-        const int64_t dst = slab_off + (int64_t)(r + k) * row_bytes + (int64_t)(i - k * vpr) * 16;
-        *(kv_u32x4*)(a.k + dst) = qk[j];
-        if (a.v) *(kv_u32x4*)(a.v + dst) = qv[j];
+      if (act[j]) {
+        *(kv_u32x4*)(a.k + dst[j]) = qk[j];
+        if (a.v) *(kv_u32x4*)(a.v + dst[j]) = qv[j];
       }
     }
     __syncthreads();
@@ -107,13 +117,12 @@ sv_status_t sv_kv_rollback(void* k_cache, void* v_cache, int32_t elem_bytes, int
   const int64_t row_bytes = (int64_t)D * elem_bytes;
   if (row_bytes % 16 != 0 || row_bytes > sv::kKvMaxRowBytes) return SV_ERR_BAD_SHAPE;
   if ((uintptr_t)k_cache % 16 != 0 || (uintptr_t)v_cache % 16 != 0) return SV_ERR_BAD_ARG;
-  const int64_t slabs = (int64_t)L * B * H;
-  if (slabs >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
-  if (slabs == 0) return SV_OK;
+  const int64_t groups = (int64_t)L * B;
+  if (groups >= (1ll << 31) || (int64_t)H * P * (row_bytes / 16) >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
+  if (groups == 0 || H == 0) return SV_OK;
   sv::KvArgs a;
   a.k = (uint8_t*)k_cache;
   a.v = (uint8_t*)v_cache;
-  a.L = L;
   a.B = B;
   a.H = H;
   a.S = S;
@@ -123,7 +132,7 @@ sv_status_t sv_kv_rollback(void* k_cache, void* v_cache, int32_t elem_bytes, int
   a.P = P;
   a.path_len = path_len;
   a.cache_len = cache_len;
-  hipLaunchKernelGGL(sv::kv_rollback_kernel, dim3((unsigned)slabs), dim3(sv::kKvThreads), P * sizeof(int32_t),
+  hipLaunchKernelGGL(sv::kv_rollback_kernel, dim3((unsigned)groups), dim3(sv::kKvThreads), P * sizeof(int32_t),
                      (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
