@@ -36,12 +36,16 @@ KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_chain.hip", "rejection_
                   "rejection_sampling_verify_amd/csrc/sv_device.h", "rejection_sampling_verify_amd/csrc/sv_internal.h",
                   "rejection_sampling_verify_amd/csrc/sv_api.hip"]
 KV_KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_kv.hip"]
+NGRAM_KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_ngram.hip"]
 
 
 def kernel_source_hash(workload: str = DEFAULT_WORKLOAD) -> str:
-    """Hash of the sources of the kernels a workload runs (verify, or KV rollback)."""
+    """Hash of the sources of the kernels a workload runs (verify, KV rollback
+    or n-gram drafting)."""
     h = hashlib.sha256()
-    for rel in KV_KERNEL_SOURCES if workload.startswith("kv_rollback") else KERNEL_SOURCES:
+    srcs = (KV_KERNEL_SOURCES if workload.startswith("kv_rollback") else
+            NGRAM_KERNEL_SOURCES if workload.startswith("ngram") else KERNEL_SOURCES)
+    for rel in srcs:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -180,6 +184,74 @@ def run_kv(args, torch, rsv, workloads, dev):
     print(json.dumps(rec), flush=True)
 
 
+def run_ngram(args, torch, rsv, workloads, dev):
+    """Prompt-lookup drafting: one sv_ngram_draft call over the batch of token
+    histories. The histories (33.5 MB) would sit in the 256 MB MALL if one copy
+    were reused, so 16 resident copies are used in turn."""
+    inp = workloads.make_extra(args.workload)
+    copies = [torch.from_numpy(inp.tokens).to(dev) for _ in range(16)]
+    lengths = torch.from_numpy(inp.lengths).to(dev)
+    B, gamma = inp.B, inp.gamma
+    out = (torch.empty((B, gamma), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+           torch.empty(B, dtype=torch.int32, device=dev))
+    print("[bench] workload %s resident" % args.workload, file=sys.stderr, flush=True)
+
+    def step(j):
+        rsv.sv_ngram_draft(copies[j % 16], lengths, inp.ngram, gamma, inp.pad, out_draft=out[0], out_count=out[1],
+                           out_match=out[2])
+
+    stream = torch.cuda.current_stream()
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        starts[j].record(stream)
+        step(j)
+        ends[j].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
+    ms_per_step = wall * 1e3 / args.steps
+    match = out[2].cpu().numpy()
+    alg_bytes = inp.algorithmic_bytes(match)
+    achieved = alg_bytes / (float(np.mean(launch_ms)) * 1e-3) / 1e9
+    rec = {
+        "metric": "n-gram (prompt-lookup) drafts/s: one-hot gamma-token proposals per second",
+        "value": B / (ms_per_step * 1e-3), "unit": "drafts/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": [int(inp.lengths.min()), int(inp.lengths.max())],
+                   "stride": int(inp.tokens.shape[1]), "ngram": inp.ngram, "gamma": gamma,
+                   "pad_with_last": bool(inp.pad), "V": inp.meta["V"]},
+        "matched_fraction": float(np.mean(match >= 0)),
+        "algorithmic_bytes_per_step": int(alg_bytes),
+        "algorithmic_bytes_note": "each sequence's tokens from its match's start to its end (all of them "
+                                  "without a match), plus lengths and outputs",
+        "launch_ms": {"mean": float(np.mean(launch_ms)), "p10": float(np.percentile(launch_ms, 10)),
+                      "p50": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        from oracle import ngram as og
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < 3 and time.perf_counter() - t_start < 10.0:
+            t1 = time.perf_counter()
+            og.ngram_draft(inp.tokens, inp.lengths, inp.ngram, gamma, inp.pad)
+            times.append(time.perf_counter() - t1)
+        t = float(np.median(times))
+        rec["cpu_baseline"] = {"value": B / t, "unit": "drafts/s", "cores": 1, "kind": "oracle",
+                               "sample": "the whole workload (one step), %d run(s), median %.3f s, Python loops"
+                                         % (len(times), t)}
+    print(json.dumps(rec), flush=True)
+
+
 def kv_cpu_baseline(inp, max_runs: int = 5):
     """The oracle on one layer of K and V for every sequence (numpy, one
     thread), scaled to whole sequences (all layers)."""
@@ -226,6 +298,9 @@ def main():
     rsv.lib()
     if args.workload.startswith("kv_rollback"):
         run_kv(args, torch, rsv, workloads, dev)
+        return
+    if args.workload.startswith("ngram"):
+        run_ngram(args, torch, rsv, workloads, dev)
         return
     inp = workloads.make_extra(args.workload) if args.workload in workloads.EXTRA else workloads.make(args.workload)
     is_tree = args.workload.startswith("tree")

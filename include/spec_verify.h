@@ -238,6 +238,35 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
                                     uint64_t offset, int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* sv_ngram_draft — prompt-lookup / n-gram drafting: one-hot draft proposals
+ * copied from earlier in each sequence ("7.6 Speculative Decoding", Exercise
+ * 4; "Self-Speculative Decoding", "Copying, verified against plain greedy").
+ * The last `ngram` tokens of sequence b are looked up at the earlier start
+ * positions T - ngram - 1 down to 0; the most recent match i gives the
+ * proposal tokens[b][i + ngram ...].
+ *   tokens [B, stride] int32, lengths [B] int32: device. Row b holds
+ *     lengths[b] tokens; entries from there to the stride are never read.
+ *   ngram: 1 .. 16 (1 is the exercise's last-token key; the lookup page uses
+ *     3). gamma >= 1: tokens proposed.
+ *   pad_with_last = 1 (the exercise): always gamma tokens; positions past the
+ *     end of the sequence, and all of them when there is no match (or the
+ *     sequence is shorter than ngram + 1), propose the last token again. The
+ *     output is a fixed-length one-hot draft (spec_verify_sample with
+ *     draft_logits NULL).
+ *   pad_with_last = 0 (the lookup page): the continuation, cut at the end of
+ *     the sequence; no proposal without a match.
+ *   out_draft [B, gamma] (device, out): the proposal, -1 past out_count[b].
+ *   out_count [B] (device, out): tokens proposed, or -1 for an invalid length
+ *     (below 0, above the stride, or 0 with pad_with_last = 1).
+ *   out_match [B] (device, out, may be NULL): the match's start i, or -1.
+ * Returns SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE (B < 0, stride < 1 or above
+ * 2^31 - 1, ngram outside 1 .. 16, gamma < 1), SV_ERR_BAD_ARG (pad_with_last
+ * not 0 or 1) or SV_ERR_HIP; nothing is launched on an error, and nothing is
+ * written when B is 0. */
+sv_status_t sv_ngram_draft(const int32_t* tokens, int64_t stride, const int32_t* lengths, int32_t B, int32_t ngram,
+                           int32_t gamma, int32_t pad_with_last, int32_t* out_draft, int32_t* out_count,
+                           int32_t* out_match, void* stream);
+
 /* sv_kv_rollback — rolls a KV cache back to the accepted tokens after a
  * verify step ([SB] "KV-Cache Reuse and Rollback": a chain step crops every
  * layer's cache to keep = T + n positions; a tree step keeps the accepted

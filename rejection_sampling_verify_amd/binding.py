@@ -22,7 +22,7 @@ SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
+           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback", "sv_ngram_draft", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
            "sv_debug_read_stream"]
 
 _lib = None
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_tree_sample.restype = ctypes.c_int
         L.sv_kv_rollback.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
         L.sv_kv_rollback.restype = ctypes.c_int
+        L.sv_ngram_draft.argtypes = [P, i64, P, i32, i32, i32, i32, P, P, P, P]
+        L.sv_ngram_draft.restype = ctypes.c_int
         L.sv_debug_philox.argtypes = [P, P, P, i32, P]
         L.sv_debug_philox.restype = ctypes.c_int
         L.sv_debug_noise.argtypes = [P, P, P, i32, P]
@@ -284,11 +286,11 @@ def sv_kv_rollback(k_cache, v_cache, root_pos, path, path_len, cache_len=None, s
     contiguous device tensors [L, B, H, S, D] (v_cache may be None); root_pos
     [B], path [B, P], path_len [B] int32. Returns cache_len [B] int32."""
     import torch
-    if k_cache.dim() != 5 or not k_cache.is_contiguous():
-        raise ValueError("k_cache must be a contiguous [L, B, H, S, D] tensor")
+    if k_cache.dim() != 5 or not k_cache.is_contiguous() or not k_cache.is_cuda:
+        raise ValueError("k_cache must be a contiguous [L, B, H, S, D] CUDA tensor")
     L, B, H, S, D = k_cache.shape
     if v_cache is not None and (tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype
-                                or not v_cache.is_contiguous()):
+                                or not v_cache.is_contiguous() or not v_cache.is_cuda):
         raise ValueError("v_cache must match k_cache")
     _check_i32(root_pos, (B,), "root_pos")
     _check_i32(path_len, (B,), "path_len")
@@ -303,6 +305,36 @@ def sv_kv_rollback(k_cache, v_cache, root_pos, path, path_len, cache_len=None, s
     if st != 0:
         raise SVError(st, "sv_kv_rollback")
     return cache_len
+
+
+def sv_ngram_draft(tokens, lengths, ngram, gamma, pad_with_last=True, out_draft=None, out_count=None,
+                   out_match=None, stream=None):
+    """Prompt-lookup drafting. tokens: device int32 [B, stride] (rows may be a
+    strided view with unit element stride); lengths: int32 [B]. Returns
+    (draft [B, gamma], count [B], match [B])."""
+    import torch
+    if tokens.dim() != 2 or tokens.dtype != torch.int32 or tokens.stride(1) != 1 or not tokens.is_cuda:
+        raise ValueError("tokens must be an int32 [B, stride] CUDA tensor with contiguous rows")
+    B = tokens.shape[0]
+    _check_i32(lengths, (B,), "lengths")
+    dev = tokens.device
+    if out_draft is None:
+        out_draft = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_match is None:
+        out_match = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check_i32(out_draft, (B, gamma), "out_draft")
+    _check_i32(out_count, (B,), "out_count")
+    _check_i32(out_match, (B,), "out_match")
+    stride = tokens.stride(0) if B > 1 else tokens.shape[1]
+    if stride < tokens.shape[1]:
+        raise ValueError("rows of tokens overlap")
+    st = lib().sv_ngram_draft(_ptr(tokens), stride, _ptr(lengths), B, int(ngram), int(gamma), int(bool(pad_with_last)),
+                              _ptr(out_draft), _ptr(out_count), _ptr(out_match), _stream(stream))
+    if st != 0:
+        raise SVError(st, "sv_ngram_draft")
+    return out_draft, out_count, out_match
 
 
 def sv_debug_philox(ctr, key, out=None, stream=None):

@@ -29,7 +29,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert set(names) >= {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample",
-                          "sv_kv_rollback",
+                          "sv_kv_rollback", "sv_ngram_draft",
                           "sv_workspace_bytes",
                           "sv_workspace_init", "sv_status_string", "sv_debug_philox", "sv_debug_noise",
                           "sv_debug_wave_max", "sv_debug_read_stream"}
@@ -145,3 +145,16 @@ def test_kv_rollback_argument_validation(L):
     assert kv(es=3) == 3
     assert kv(k=ctypes.c_void_p(P.value + 8)) == 4
     assert kv(L=0) == 0 and kv(H=0) == 0
+
+
+def test_ngram_argument_validation(L):
+    f = _Fake(1 << 12)
+    P = f.ptr
+    ng = lambda **k: L.sv_ngram_draft(k.get("tok", P), k.get("stride", 64), k.get("len", P), k.get("B", 2),
+                                      k.get("n", 3), k.get("g", 4), k.get("pad", 1), k.get("d", P), k.get("c", P),
+                                      None, None)
+    assert ng(tok=None) == 1 and ng(len=None) == 1 and ng(d=None) == 1 and ng(c=None) == 1
+    assert ng(B=-1) == 2 and ng(stride=0) == 2 and ng(stride=1 << 31) == 2
+    assert ng(n=0) == 2 and ng(n=17) == 2 and ng(g=0) == 2
+    assert ng(pad=2) == 4
+    assert ng(B=0) == 0

@@ -28,6 +28,11 @@ and, for the KV-cache rollback after a verify step:
       (the KV layout of a 32-layer model with 8 KV heads of dimension 128),
       root positions U[512, 3008), accepted paths drawn as walks in the same
       65-node tree (a uniformly random child at each level, 1 to 4 nodes).
+and, for prompt-lookup drafting:
+  ngram_draft_qwen  B=512 token histories of T ~ U[2048, 16384] tokens over
+      V=152064 (row stride 16384), ngram=3, gamma=6, padded to gamma with the
+      last token (the one-hot drafts of onehot_bf16_qwen); text is Zipf(1.1)
+      with copies of earlier spans, and half the sequences end inside a copy.
 """
 from __future__ import annotations
 
@@ -40,7 +45,7 @@ import numpy as np
 CONFIGS = ["chain_f32_small", "chain_bf16_peaked", "chain_bf16_llama", "onehot_bf16_qwen",
            "tree_bf16_llama"]
 CONFIG_INDEX = {name: k for k, name in enumerate(CONFIGS)}
-EXTRA = ["tree_sample_bf16_llama", "kv_rollback_bf16_llama"]
+EXTRA = ["tree_sample_bf16_llama", "kv_rollback_bf16_llama", "ngram_draft_qwen"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -463,6 +468,79 @@ def make_kv_rollback(name: str, L: int, B: int, H: int, S: int, D: int, *, elem_
     return KvRollbackInputs(name, (L, B, H, S, D), elem_bytes, root, path, plen, seed=seed, meta={"kind": kind})
 
 
+@dataclass
+class NgramInputs:
+    """Token histories for n-gram drafting: tokens [B, stride] int32 (row b
+    holds lengths[b] tokens, the rest -1), and the drafter's settings."""
+    name: str
+    tokens: np.ndarray
+    lengths: np.ndarray
+    ngram: int
+    gamma: int
+    pad: bool
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.tokens.shape[0]
+
+    def algorithmic_bytes(self, match: np.ndarray) -> int:
+        """Per sequence, the tokens from the match's start to the end (all of
+        them without a match: a right-to-left scan has to read that far), the
+        length, and the outputs (gamma + 2 words)."""
+        n = 0
+        for b in range(self.B):
+            T = int(self.lengths[b])
+            n += 4 * (T - int(match[b]) if match[b] >= 0 else T) + 4 * (self.gamma + 3)
+        return n
+
+
+def _zipf_sampler(V: int, s: float):
+    w = np.arange(1, V + 1, dtype=np.float64) ** -s
+    cdf = np.cumsum(w)
+    cdf /= cdf[-1]
+    return lambda rng, size: np.minimum(np.searchsorted(cdf, rng.random(size)), V - 1).astype(np.int32)
+
+
+def make_ngram(name: str, B: int, V: int, T_range, *, ngram: int, gamma: int, pad: bool, seed: int,
+               stride: int | None = None, zipf: float = 1.1, copy_prob: float = 0.15, tail_copy: float = 0.5):
+    """Zipf(zipf) text over V with copies: pieces of 16-256 fresh tokens, or
+    (probability copy_prob, once 64 tokens exist) a copy of 8-128 earlier
+    tokens from a uniform earlier start; with probability tail_copy the last
+    c ~ U[ngram, 48] tokens are replaced by a copy of an earlier span, so the
+    tail n-gram has an earlier occurrence. A per-sequence shift of the ids
+    makes the frequent ids differ between sequences."""
+    draw = _zipf_sampler(V, zipf)
+    lo, hi = T_range
+    stride = stride or hi
+    tokens = np.full((B, stride), -1, np.int32)
+    lengths = np.empty(B, np.int32)
+    for b in range(B):
+        rng = _seq_rng(seed, b)
+        T = int(rng.integers(lo, hi + 1))
+        seq = np.empty(T + 256, np.int32)
+        n = 0
+        while n < T:
+            if n >= 64 and rng.random() < copy_prob:
+                c = int(rng.integers(8, 129))
+                src = int(rng.integers(0, n - 8))
+                c = min(c, n - src)
+                seq[n:n + c] = seq[src:src + c]
+            else:
+                c = int(rng.integers(16, 257))
+                seq[n:n + c] = draw(rng, c)
+            n += c
+        seq = seq[:T]
+        if T > 2 * 48 and rng.random() < tail_copy:
+            c = int(rng.integers(ngram, 49))
+            src = int(rng.integers(0, T - 2 * c))
+            seq[T - c:] = seq[src:src + c].copy()
+        shift = int(rng.integers(V))
+        tokens[b, :T] = (seq.astype(np.int64) + shift) % V
+        lengths[b] = T
+    return NgramInputs(name, tokens, lengths, ngram, gamma, pad, meta={"V": V, "seed": seed})
+
+
 def make_extra(name: str, workers=None):
     """Workloads of the rows beyond the five configurations (seed 2000 + k)."""
     seed = 2000 + EXTRA.index(name)
@@ -473,6 +551,8 @@ def make_extra(name: str, workers=None):
         parents, _ = _c5_tree()
         return make_kv_rollback(name, 32, 32, 8, 4096, 128, elem_bytes=2, seed=seed, kind="tree", parents=parents,
                                 root_lo=512, root_hi=3008)
+    if name == "ngram_draft_qwen":
+        return make_ngram(name, 512, 152064, (2048, 16384), ngram=3, gamma=6, pad=True, seed=seed)
     raise KeyError(name)
 
 
