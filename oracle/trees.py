@@ -52,3 +52,38 @@ def longest_valid_path(parents, tokens, argmax_of):
             if len(path) > len(best) or (len(path) == len(best) and end < best[-1]):
                 best = path
     return best
+
+
+def tree_is_valid(parents) -> bool:
+    """The order build_tree_attn asks for: the root first (parent -1), and
+    every other node's parent an earlier node."""
+    return len(parents) >= 1 and parents[0] == -1 and all(0 <= parents[i] < i for i in range(1, len(parents)))
+
+
+def tree_attn_batch(parents: np.ndarray, offsets=None, packed: bool = False):
+    """Batched build_tree_attn. parents: [B, N] (one tree per sequence) or [N]
+    (with offsets giving B). Returns (mask [B, N, N] uint8, or [B, N, ceil(N/32)]
+    uint32 words with bit j % 32 of word j // 32 for column j; position ids
+    [B, N] int32 = offset + depth). A sequence whose tree is not in that order
+    gets an all-zero mask and position ids -1."""
+    parents = np.asarray(parents)
+    if parents.ndim == 1:
+        B = 1 if offsets is None else len(offsets)
+        parents = np.broadcast_to(parents, (B, parents.shape[0]))
+    B, N = parents.shape
+    offsets = np.zeros(B, np.int64) if offsets is None else np.asarray(offsets, np.int64)
+    mask = np.zeros((B, N, N), np.uint8)
+    pos = np.full((B, N), -1, np.int32)
+    for b in range(B):
+        par = [int(x) for x in parents[b]]
+        if not tree_is_valid(par):
+            continue
+        mask[b] = ancestor_mask(par)
+        pos[b] = np.asarray(depths(par), np.int64) + offsets[b]
+    if not packed:
+        return mask, pos
+    W = (N + 31) // 32
+    words = np.zeros((B, N, W), np.uint32)
+    for j in range(N):
+        words[:, :, j // 32] |= mask[:, :, j].astype(np.uint32) << np.uint32(j % 32)
+    return words, pos
