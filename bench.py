@@ -37,14 +37,16 @@ KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_chain.hip", "rejection_
                   "rejection_sampling_verify_amd/csrc/sv_api.hip"]
 KV_KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_kv.hip"]
 NGRAM_KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_ngram.hip"]
+TREE_MASK_KERNEL_SOURCES = ["rejection_sampling_verify_amd/csrc/sv_treemask.hip"]
 
 
 def kernel_source_hash(workload: str = DEFAULT_WORKLOAD) -> str:
-    """Hash of the sources of the kernels a workload runs (verify, KV rollback
-    or n-gram drafting)."""
+    """Hash of the sources of the kernels a workload runs (verify, KV rollback,
+    n-gram drafting or the tree mask)."""
     h = hashlib.sha256()
     srcs = (KV_KERNEL_SOURCES if workload.startswith("kv_rollback") else
-            NGRAM_KERNEL_SOURCES if workload.startswith("ngram") else KERNEL_SOURCES)
+            NGRAM_KERNEL_SOURCES if workload.startswith("ngram") else
+            TREE_MASK_KERNEL_SOURCES if workload.startswith("tree_mask") else KERNEL_SOURCES)
     for rel in srcs:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
@@ -252,6 +254,67 @@ def run_ngram(args, torch, rsv, workloads, dev):
     print(json.dumps(rec), flush=True)
 
 
+def run_tree_mask(args, torch, rsv, workloads, dev):
+    """Tree attention mask and position ids for a batch of per-sequence trees:
+    one sv_tree_mask call (bool mask and position ids)."""
+    inp = workloads.make_extra(args.workload)
+    B, N = inp.B, inp.N
+    par = torch.from_numpy(inp.parents).to(dev)
+    off = torch.from_numpy(inp.offsets).to(dev)
+    out_mask = torch.empty((B, N, N), dtype=torch.bool, device=dev)
+    out_pos = torch.empty((B, N), dtype=torch.int32, device=dev)
+    print("[bench] workload %s resident" % args.workload, file=sys.stderr, flush=True)
+
+    def step(j):
+        rsv.sv_tree_mask(par, off, out_mask=out_mask, out_position_ids=out_pos)
+
+    stream = torch.cuda.current_stream()
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        starts[j].record(stream)
+        step(j)
+        ends[j].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
+    ms_per_step = wall * 1e3 / args.steps
+    alg_bytes = inp.algorithmic_bytes()
+    achieved = alg_bytes / (float(np.mean(launch_ms)) * 1e-3) / 1e9
+    rec = {
+        "metric": "tree attention masks/s (ancestor mask and depth position ids per sequence)",
+        "value": B / (ms_per_step * 1e-3), "unit": "masks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "nodes": N, "mask": "bool [B, N, N]",
+                   "trees": "one per sequence, breadth-first, 1 to 4 children per node"},
+        "algorithmic_bytes_per_step": int(alg_bytes),
+        "launch_ms": {"mean": float(np.mean(launch_ms)), "p10": float(np.percentile(launch_ms, 10)),
+                      "p50": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        from oracle import trees
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < 20 and time.perf_counter() - t_start < 10.0:
+            t1 = time.perf_counter()
+            trees.tree_attn_batch(inp.parents, inp.offsets)
+            times.append(time.perf_counter() - t1)
+        t = float(np.median(times))
+        rec["cpu_baseline"] = {"value": B / t, "unit": "masks/s", "cores": 1, "kind": "oracle",
+                               "sample": "the whole workload (one step), %d run(s), median %.4f s, Python loops"
+                                         % (len(times), t)}
+    print(json.dumps(rec), flush=True)
+
+
 def kv_cpu_baseline(inp, max_runs: int = 5):
     """The oracle on one layer of K and V for every sequence (numpy, one
     thread), scaled to whole sequences (all layers)."""
@@ -301,6 +364,9 @@ def main():
         return
     if args.workload.startswith("ngram"):
         run_ngram(args, torch, rsv, workloads, dev)
+        return
+    if args.workload.startswith("tree_mask"):
+        run_tree_mask(args, torch, rsv, workloads, dev)
         return
     inp = workloads.make_extra(args.workload) if args.workload in workloads.EXTRA else workloads.make(args.workload)
     is_tree = args.workload.startswith("tree")

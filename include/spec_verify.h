@@ -238,6 +238,30 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
                                     uint64_t offset, int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* sv_tree_mask — the attention mask and position ids of a token tree packed
+ * into one forward pass ("7.6 Speculative Decoding", "Tree Attention:
+ * Verifying Many Candidates at Once", build_tree_attn; "Self-Speculative
+ * Decoding", "Verifying a tree instead of a line"): node i may attend to node
+ * j iff j is i or one of its ancestors, and node i's position id is its depth
+ * plus the sequence's offset.
+ *   parents: device int32, N entries per sequence, rows parents_stride apart
+ *     (0: one tree for every sequence). parents[0] = -1 (the root), and every
+ *     other parent is an earlier node.
+ *   position_offset [B]: device int32 or NULL (0), e.g. the root's position
+ *     in the sequence so that ids continue the committed prefix.
+ *   out_mask [B, N, N]: device bytes, 1 = may attend (torch.bool's layout), or
+ *     NULL. out_mask_bits [B, N, ceil(N / 32)]: device 32-bit words, column j
+ *     at bit j % 32 of word j / 32, or NULL. out_position_ids [B, N]: device
+ *     int32 or NULL. At least one output.
+ *   A sequence whose tree breaks the order gets an all-zero mask and position
+ *   ids -1.
+ * Returns SV_ERR_NULL_ARG (parents, or every output, NULL), SV_ERR_BAD_SHAPE
+ * (B < 0, N outside 1 .. 1024, a stride below N other than 0) or SV_ERR_HIP;
+ * nothing is launched on an error, and nothing is written when B is 0. */
+sv_status_t sv_tree_mask(const int32_t* parents, int64_t parents_stride, int32_t B, int32_t N,
+                         const int32_t* position_offset, uint8_t* out_mask, uint32_t* out_mask_bits,
+                         int32_t* out_position_ids, void* stream);
+
 /* sv_ngram_draft — prompt-lookup / n-gram drafting: one-hot draft proposals
  * copied from earlier in each sequence ("7.6 Speculative Decoding", Exercise
  * 4; "Self-Speculative Decoding", "Copying, verified against plain greedy").

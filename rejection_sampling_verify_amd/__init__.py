@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     spec_verify_tree_sample,
     sv_kv_rollback,
     sv_ngram_draft,
+    sv_tree_mask,
     sv_debug_noise,
     sv_debug_read_stream,
     sv_debug_wave_max,

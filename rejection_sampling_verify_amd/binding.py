@@ -22,7 +22,7 @@ SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback", "sv_ngram_draft", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
+           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback", "sv_ngram_draft", "sv_tree_mask", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
            "sv_debug_read_stream"]
 
 _lib = None
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.sv_kv_rollback.restype = ctypes.c_int
         L.sv_ngram_draft.argtypes = [P, i64, P, i32, i32, i32, i32, P, P, P, P]
         L.sv_ngram_draft.restype = ctypes.c_int
+        L.sv_tree_mask.argtypes = [P, i64, i32, i32, P, P, P, P, P]
+        L.sv_tree_mask.restype = ctypes.c_int
         L.sv_debug_philox.argtypes = [P, P, P, i32, P]
         L.sv_debug_philox.restype = ctypes.c_int
         L.sv_debug_noise.argtypes = [P, P, P, i32, P]
@@ -335,6 +337,46 @@ def sv_ngram_draft(tokens, lengths, ngram, gamma, pad_with_last=True, out_draft=
     if st != 0:
         raise SVError(st, "sv_ngram_draft")
     return out_draft, out_count, out_match
+
+
+def sv_tree_mask(parents, position_offset=None, B=None, mask=True, packed=False, position_ids=True,
+                 out_mask=None, out_position_ids=None, stream=None):
+    """Tree attention mask and position ids. parents: device int32 [B, N] (one
+    tree per sequence; an expanded view shares one) or [N] (one tree, B from
+    position_offset or the B argument). Returns (mask, position_ids): mask is
+    bool [B, N, N], or with packed=True int32 words [B, N, ceil(N / 32)]
+    holding the bits; either is None when not asked for."""
+    import torch
+    if parents.dtype != torch.int32 or not parents.is_cuda or parents.dim() not in (1, 2) or parents.stride(-1) != 1:
+        raise ValueError("parents must be an int32 CUDA tensor [B, N] or [N] with contiguous rows")
+    N = parents.shape[-1]
+    if parents.dim() == 2:
+        B = parents.shape[0]
+        stride = parents.stride(0) if B > 1 else N
+    else:
+        B = B if B is not None else (position_offset.shape[0] if position_offset is not None else 1)
+        stride = 0
+    if position_offset is not None:
+        _check_i32(position_offset, (B,), "position_offset")
+    dev = parents.device
+    if mask and out_mask is None:
+        out_mask = (torch.empty((B, N, (N + 31) // 32), dtype=torch.int32, device=dev) if packed
+                    else torch.empty((B, N, N), dtype=torch.bool, device=dev))
+    if position_ids and out_position_ids is None:
+        out_position_ids = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if out_position_ids is not None:
+        _check_i32(out_position_ids, (B, N), "out_position_ids")
+    if out_mask is not None:
+        want = (B, N, (N + 31) // 32) if packed else (B, N, N)
+        if tuple(out_mask.shape) != want or not out_mask.is_contiguous() or not out_mask.is_cuda or \
+                out_mask.element_size() != (4 if packed else 1):
+            raise ValueError("out_mask must be a contiguous CUDA tensor of shape %s" % (want,))
+    st = lib().sv_tree_mask(_ptr(parents), stride, B, N, _ptr(position_offset),
+                            None if packed else _ptr(out_mask), _ptr(out_mask) if packed else None,
+                            _ptr(out_position_ids), _stream(stream))
+    if st != 0:
+        raise SVError(st, "sv_tree_mask")
+    return out_mask, out_position_ids
 
 
 def sv_debug_philox(ctr, key, out=None, stream=None):

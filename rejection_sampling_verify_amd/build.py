@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "librsv_hip.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["sv_api.hip", "sv_chain.hip", "sv_tree.hip", "sv_debug.hip", "sv_kv.hip", "sv_ngram.hip"]
+SOURCES = ["sv_api.hip", "sv_chain.hip", "sv_tree.hip", "sv_debug.hip", "sv_kv.hip", "sv_ngram.hip", "sv_treemask.hip"]
 ARCH = os.environ.get("SV_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions are kept off: only plain fp32 VALU code is emitted.

@@ -29,7 +29,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = _declared()
     assert set(names) >= {"spec_verify_sample", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample",
-                          "sv_kv_rollback", "sv_ngram_draft",
+                          "sv_kv_rollback", "sv_ngram_draft", "sv_tree_mask",
                           "sv_workspace_bytes",
                           "sv_workspace_init", "sv_status_string", "sv_debug_philox", "sv_debug_noise",
                           "sv_debug_wave_max", "sv_debug_read_stream"}
@@ -158,3 +158,13 @@ def test_ngram_argument_validation(L):
     assert ng(n=0) == 2 and ng(n=17) == 2 and ng(g=0) == 2
     assert ng(pad=2) == 4
     assert ng(B=0) == 0
+
+
+def test_tree_mask_argument_validation(L):
+    f = _Fake(1 << 12)
+    P = f.ptr
+    tm = lambda **k: L.sv_tree_mask(k.get("par", P), k.get("stride", 8), k.get("B", 2), k.get("N", 8), None,
+                                    k.get("m", P), k.get("bits", None), k.get("pos", None), None)
+    assert tm(par=None) == 1 and tm(m=None) == 1
+    assert tm(B=-1) == 2 and tm(N=0) == 2 and tm(N=1025) == 2 and tm(stride=-1) == 2 and tm(stride=7) == 2
+    assert tm(B=0) == 0 and tm(B=0, stride=0) == 0

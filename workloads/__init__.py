@@ -33,6 +33,10 @@ and, for prompt-lookup drafting:
       V=152064 (row stride 16384), ngram=3, gamma=6, padded to gamma with the
       last token (the one-hot drafts of onehot_bf16_qwen); text is Zipf(1.1)
       with copies of earlier spans, and half the sequences end inside a copy.
+and, for the tree attention mask and position ids:
+  tree_mask_b256  B=256 sequences, each with its own 65-node tree (breadth-first,
+      1 to 4 children per node, as dynamic trees are), position offsets
+      U[512, 4096) (the root's place in the sequence), bool mask.
 """
 from __future__ import annotations
 
@@ -45,7 +49,7 @@ import numpy as np
 CONFIGS = ["chain_f32_small", "chain_bf16_peaked", "chain_bf16_llama", "onehot_bf16_qwen",
            "tree_bf16_llama"]
 CONFIG_INDEX = {name: k for k, name in enumerate(CONFIGS)}
-EXTRA = ["tree_sample_bf16_llama", "kv_rollback_bf16_llama", "ngram_draft_qwen"]
+EXTRA = ["tree_sample_bf16_llama", "kv_rollback_bf16_llama", "ngram_draft_qwen", "tree_mask_b256"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -541,6 +545,56 @@ def make_ngram(name: str, B: int, V: int, T_range, *, ngram: int, gamma: int, pa
     return NgramInputs(name, tokens, lengths, ngram, gamma, pad, meta={"V": V, "seed": seed})
 
 
+def random_tree(rng, N: int, branching=(1, 4)) -> np.ndarray:
+    """A breadth-first tree of N nodes (parents before children): each node of
+    a level gets branching[0] .. branching[1] children until N nodes exist."""
+    parents = [-1]
+    frontier = [0]
+    while len(parents) < N:
+        nxt = []
+        for p in frontier:
+            for _ in range(int(rng.integers(branching[0], branching[1] + 1))):
+                if len(parents) < N:
+                    parents.append(p)
+                    nxt.append(len(parents) - 1)
+        frontier = nxt or [len(parents) - 1]
+    return np.array(parents, np.int32)
+
+
+@dataclass
+class TreeMaskInputs:
+    name: str
+    parents: np.ndarray   # [B, N] int32
+    offsets: np.ndarray   # [B] int32
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.parents.shape[0]
+
+    @property
+    def N(self):
+        return self.parents.shape[1]
+
+    def algorithmic_bytes(self, packed: bool = False) -> int:
+        """Parents and offsets read; mask (bytes, or packed words) and
+        position ids written."""
+        B, N = self.parents.shape
+        mask = B * N * ((N + 31) // 32) * 4 if packed else B * N * N
+        return B * N * 4 + B * 4 + mask + B * N * 4
+
+
+def make_tree_mask(name: str, B: int, N: int, *, seed: int, branching=(1, 4), offset_range=(512, 4096),
+                   chain: bool = False) -> TreeMaskInputs:
+    parents = np.empty((B, N), np.int32)
+    offsets = np.empty(B, np.int32)
+    for b in range(B):
+        rng = _seq_rng(seed, b)
+        parents[b] = np.arange(-1, N - 1, dtype=np.int32) if chain else random_tree(rng, N, branching)
+        offsets[b] = int(rng.integers(offset_range[0], offset_range[1]))
+    return TreeMaskInputs(name, parents, offsets)
+
+
 def make_extra(name: str, workers=None):
     """Workloads of the rows beyond the five configurations (seed 2000 + k)."""
     seed = 2000 + EXTRA.index(name)
@@ -553,6 +607,8 @@ def make_extra(name: str, workers=None):
                                 root_lo=512, root_hi=3008)
     if name == "ngram_draft_qwen":
         return make_ngram(name, 512, 152064, (2048, 16384), ngram=3, gamma=6, pad=True, seed=seed)
+    if name == "tree_mask_b256":
+        return make_tree_mask(name, 256, 65, seed=seed)
     raise KeyError(name)
 
 
