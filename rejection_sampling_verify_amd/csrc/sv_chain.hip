@@ -1530,15 +1530,28 @@ __device__ void tree_publish(const TreeSampleArgs& ta, int b, uint32_t epoch, ui
   xput64(&st->dec[0], ((uint64_t)(epoch + 1u) << 40) | ((uint64_t)action << 32) | (uint32_t)t.node);
 }
 
-// The j-th child (index order) of node v, or -1. Children follow their
-// parent. par: the parent array, staged in LDS.
-__device__ int tree_child(const TreeSampleArgs& ta, const int32_t* par, int v, int j) {
-  for (int c = v + 1; c < ta.N; ++c)
-    if (par[c] == v) {
-      if (j == 0) return c;
-      --j;
+// All threads: the children of node v in index order into kids[0 .. *nkids)
+// (an ordered compaction of the parent array, staged in LDS). wcnt: one word
+// per wave of scratch in LDS.
+__device__ void tree_children(int N, const int32_t* par, int v, int32_t* kids, int32_t* nkids, int32_t* wcnt) {
+  const int lane = (int)(threadIdx.x & 63), wv = (int)(threadIdx.x >> 6);
+  int base = 0;
+  for (int k0 = 0; k0 < N; k0 += kThreads) {
+    const int k = k0 + (int)threadIdx.x;
+    const bool f = k < N && par[k] == v;
+    const uint64_t m = __ballot(f);
+    if (lane == 0) wcnt[wv] = __popcll(m);
+    __syncthreads();
+    int off = base, tot = 0;
+    for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+      if (w2 < wv) off += wcnt[w2];
+      tot += wcnt[w2];
     }
-  return -1;
+    if (f) kids[off + __popcll(m & ((1ull << lane) - 1ull))] = k;
+    base += tot;
+    __syncthreads();  // wcnt is written again next round
+  }
+  if (threadIdx.x == 0) *nkids = base;
 }
 
 // Thread 0 of the leader: the sequence's decisions up to its next action.
@@ -1548,12 +1561,15 @@ __device__ int tree_child(const TreeSampleArgs& ta, const int32_t* par, int v, i
 // distribution is updated. Then siblings are tested until an accepted child
 // with children needs its statistics, a rejection needs the next pass, or the
 // walk ends in a draw.
-// par and tok: the parents and this sequence's node tokens, staged in LDS;
-// part: the W workgroups' slots of the action just carried out, staged in
-// LDS (w0, w1 per workgroup).
+// In LDS: kids[0 .. nkids), the children of the node the decisions start
+// from, in index order; haskid, whether each node has children; tok_s, this
+// sequence's node tokens; part, the W workgroups' slots of the action just
+// carried out (w0, w1 per workgroup). tree_bad, tok_bad: the checks of the
+// tree and of the tokens, made by the whole workgroup while staging them.
 template <bool BF16>
 __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32_t epoch, const uint64_t rec[4],
-                          const int32_t* par, const int32_t* tok_s, const uint64_t (*part)[2]) {
+                          const int32_t* kids, int nkids, const uint8_t* haskid, const int32_t* tok_s,
+                          const uint64_t (*part)[2], int tree_bad, int tok_bad) {
   using E = Elem<BF16>;
   const ChainArgs& a = ta.c;
   const float T = a.temperature[b];
@@ -1561,17 +1577,9 @@ __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32
   float c2 = 0.0f;
   if (prev == TA_NONE) {
     int code = 0;
-    bool tree_ok = ta.parents[0] == -1 && ta.depth[0] == 0;
-    for (int c = 1; c < ta.N && tree_ok; ++c) {
-      const int pc = ta.parents[c];
-      tree_ok = pc >= 0 && pc < c && ta.depth[c] == ta.depth[pc] + 1 && ta.depth[c] <= ta.max_depth;
-    }
-    const int32_t* tok = ta.tokens + (int64_t)b * ta.N;
-    bool tok_ok = true;
-    for (int c = 1; c < ta.N; ++c) tok_ok = tok_ok && tok[c] >= 0 && tok[c] < a.V;
-    if (!tree_ok) code = -3;
+    if (tree_bad) code = -3;
     else if (!(T > 0.0f) || T == INFINITY) code = -2;
-    else if (!tok_ok) code = -1;
+    else if (tok_bad) code = -1;
     // Outputs are written with device-coherent stores: later leaders of this
     // sequence may run on other XCDs, and plain stores to one line from two
     // L2s would be written back in either order.
@@ -1590,7 +1598,7 @@ __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32
       return;
     }
     xput(&path[0], 0);
-    tree_publish(ta, b, epoch, tree_child(ta, par, 0, 0) >= 0 ? TA_STATS : TA_DRAW_BONUS, s);
+    tree_publish(ta, b, epoch, haskid[0] ? TA_STATS : TA_DRAW_BONUS, s);
     return;
   } else if (prev == TA_STATS) {
     s = tree_state_of(rec);
@@ -1622,7 +1630,7 @@ __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32
     s.round += 1;
   }
   for (int guard = 0; guard <= ta.N; ++guard) {
-    const int c = tree_child(ta, par, s.node, s.round);
+    const int c = s.round < nkids ? kids[s.round] : -1;
     if (c < 0) {
       // A leaf (no child tested) draws the bonus from p; a node whose
       // children were all rejected draws from its final residual (or from p
@@ -1651,7 +1659,7 @@ __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32
       s.zt2 = s.zd2 = 0.0f;
       // The new node: its statistics first if it has children, else the
       // bonus draw.
-      tree_publish(ta, b, epoch, tree_child(ta, par, c, 0) >= 0 ? TA_STATS : TA_DRAW_BONUS, s);
+      tree_publish(ta, b, epoch, haskid[c] ? TA_STATS : TA_DRAW_BONUS, s);
       return;
     }
     tree_publish(ta, b, epoch, TA_PASS, s);  // the mass of (p - (A + B) q)_+ at this node
@@ -1747,11 +1755,30 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   const int lo = w * ta.wlen, hi = min(a.V, lo + ta.wlen);
   // The tree and this sequence's tokens in LDS: any workgroup may lead, and
   // the leader walks them serially.
-  __shared__ int32_t s_par[kMaxTreeNodes], s_tok[kMaxTreeNodes];
+  // The checks of the tree (root first at depth 0; every other parent an
+  // earlier node, one level up; no node deeper than max_depth) and of the
+  // tokens, one node per lane.
+  __shared__ int32_t s_par[kMaxTreeNodes], s_tok[kMaxTreeNodes], s_kids[kMaxTreeNodes];
+  __shared__ uint8_t s_haskid[kMaxTreeNodes];
+  __shared__ int32_t s_nkids, s_wcnt[kThreads / 64];
+  int tree_bad = 0, tok_bad = 0;
   for (int k = threadIdx.x; k < ta.N; k += kThreads) {
-    s_par[k] = ta.parents[k];
-    s_tok[k] = ta.tokens[(int64_t)b * ta.N + k];
+    const int pk = ta.parents[k], dk = ta.depth[k], xk = ta.tokens[(int64_t)b * ta.N + k];
+    s_par[k] = pk;
+    s_tok[k] = xk;
+    s_haskid[k] = 0;
+    if (k == 0) {
+      tree_bad |= pk != -1 || dk != 0;
+    } else {
+      tree_bad |= !(pk >= 0 && pk < k) || dk > ta.max_depth || dk != ta.depth[pk >= 0 && pk < k ? pk : 0] + 1;
+      tok_bad |= xk < 0 || xk >= a.V;
+    }
   }
+  tree_bad = __syncthreads_or(tree_bad);
+  tok_bad = __syncthreads_or(tok_bad);
+  for (int k = 1 + (int)threadIdx.x; k < ta.N; k += kThreads)
+    if (s_par[k] >= 0 && s_par[k] < ta.N) s_haskid[s_par[k]] = 1;
+  __syncthreads();
   uint32_t epoch = 0, action = TA_NONE;
   float partial = 0.0f;
   P2Slot part;
@@ -1785,8 +1812,11 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
         sm.u.slot[k][0] = xget64((uint64_t*)&sl[k].w0);
         sm.u.slot[k][1] = xget64((uint64_t*)&sl[k].w1);
       }
+      // The children of the node the decisions start from.
+      tree_children(ta.N, s_par, action == TA_NONE ? 0 : (int)(uint32_t)sm.trec[0], s_kids, &s_nkids, s_wcnt);
       __syncthreads();
-      if (threadIdx.x == 0) tree_lead<BF16>(ta, b, action, epoch, sm.trec, s_par, s_tok, sm.u.slot);
+      if (threadIdx.x == 0)
+        tree_lead<BF16>(ta, b, action, epoch, sm.trec, s_kids, s_nkids, s_haskid, s_tok, sm.u.slot, tree_bad, tok_bad);
     }
     __syncthreads();
     // Wait for the next action (bounded).
