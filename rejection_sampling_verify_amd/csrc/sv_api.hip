@@ -428,6 +428,10 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
   a.tokens = node_tokens;
   a.N = N;
   a.max_depth = max_depth;
+  // The walk's second buffer of workgroup parts: the greedy tree's slots,
+  // unused here (B * N * nchunks 8-byte slots hold B * nchunks 16-byte parts
+  // for N >= 2; a one-node tree never needs the second buffer).
+  a.slot2 = (sv::P2Slot*)(ws + L.tree_slot);
   a.out_path = out_path;
   a.out_len = out_path_len;
   a.out_token = out_token;

@@ -71,7 +71,6 @@ struct Smem {
   ArgMax rg[kMaxGamma];
   int32_t acc[kMaxGamma];
   Decision dec;
-  uint64_t trec[4];  // sampled trees: the sequence's current action record
 };
 
 // Block-wide log-sum-exp merge: within a wave the maximum first, then every
@@ -1478,12 +1477,15 @@ __global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
 // ===========================================================================
 // Sampled trees: multi-round rejection sampling (the pages' "Tree Attention"
 // section). One launch gives every sequence W workgroups, each owning wlen
-// elements of a row. The last of them to arrive after an action (the leader)
-// takes the sequence's next decisions serially and publishes the next action;
-// all W then carry it out on their part of the row: the (max, sum exp2) of a
-// node's target and draft rows when the walk reaches a node with children
-// (only the nodes on the walked path are read), a residual-mass pass, or the
-// final Gumbel-max draw.
+// elements of a row. After an action every workgroup waits until all W have
+// arrived with their parts, then takes the sequence's next decisions itself
+// from the same parts (so all reach the same state; one of them writes the
+// outputs) and carries out the next action on its part of the row: the
+// (max, sum exp2) of a node's target and draft rows when the walk reaches a
+// node with children (only the nodes on the walked path are read), a
+// residual-mass pass, or the final Gumbel-max draw. The parts of successive
+// actions alternate between two slot buffers, since a workgroup can start
+// the next action while another still reads the parts of the last.
 // After some rejections at a node the target distribution is
 // p' = (p - A q)_+ / B. It starts at A = 0, B = 1, and a rejection moves it to
 // A' = A + B, B' = sum_v (p - A' q)_+ (one pass over the row pair). This is the
@@ -1497,38 +1499,13 @@ enum TreeAction : uint32_t {
   TA_NONE = 0, TA_PASS = 1, TA_DRAW_RESIDUAL = 2, TA_DRAW_BONUS = 3, TA_DONE = 4, TA_STATS = 5
 };
 
-// The action record, in the sequence's SeqState (dec[0] stored last):
-//   dec[0] = epoch << 40 | action << 32 | node
-//   dec[1] = A bits << 32 | B bits
-//   dec[2] = zt2 bits << 32 | zd2 bits   (the node's log2-domain normalizers)
-//   dec[3] = round << 32 | path length   (round: the sibling last tested)
+// The walk's state: the node, the sibling last tested (round), the path
+// length, the target distribution's (A, B) and the node's log2-domain
+// normalizers.
 struct TreeState {
   int node, round, len;
   float A, Bv, zt2, zd2;
 };
-
-__device__ __forceinline__ TreeState tree_state_of(const uint64_t rec[4]) {
-  TreeState t;
-  t.node = (int)(uint32_t)rec[0];
-  t.A = hi_f(rec[1]);
-  t.Bv = __uint_as_float(lo_u(rec[1]));
-  t.zt2 = hi_f(rec[2]);
-  t.zd2 = __uint_as_float(lo_u(rec[2]));
-  t.round = (int)(rec[3] >> 32);
-  t.len = (int)(uint32_t)rec[3];
-  return t;
-}
-
-// Thread 0: publishes the next action (payload first, then the word the
-// other workgroups wait on).
-__device__ void tree_publish(const TreeSampleArgs& ta, int b, uint32_t epoch, uint32_t action, const TreeState& t) {
-  SeqState* st = ta.c.seq + b;
-  xput64(&st->dec[1], pack(t.A, __float_as_uint(t.Bv)));
-  xput64(&st->dec[2], pack(t.zt2, __float_as_uint(t.zd2)));
-  xput64(&st->dec[3], ((uint64_t)(uint32_t)t.round << 32) | (uint32_t)t.len);
-  wait_vmem();
-  xput64(&st->dec[0], ((uint64_t)(epoch + 1u) << 40) | ((uint64_t)action << 32) | (uint32_t)t.node);
-}
 
 // All threads: the children of node v in index order into kids[0 .. *nkids)
 // (an ordered compaction of the parent array, staged in LDS). wcnt: one word
@@ -1554,55 +1531,56 @@ __device__ void tree_children(int N, const int32_t* par, int v, int32_t* kids, i
   if (threadIdx.x == 0) *nkids = base;
 }
 
-// Thread 0 of the leader: the sequence's decisions up to its next action.
-// After a stats action the workgroups' (max, sum) pairs are merged in
-// workgroup order into the node's normalizers; after a pass (prev = TA_PASS)
-// the partial masses are summed in workgroup order and the target
-// distribution is updated. Then siblings are tested until an accepted child
-// with children needs its statistics, a rejection needs the next pass, or the
-// walk ends in a draw.
-// In LDS: kids[0 .. nkids), the children of the node the decisions start
-// from, in index order; haskid, whether each node has children; tok_s, this
-// sequence's node tokens; part, the W workgroups' slots of the action just
-// carried out (w0, w1 per workgroup). tree_bad, tok_bad: the checks of the
-// tree and of the tokens, made by the whole workgroup while staging them.
+// Thread 0 of every workgroup: the sequence's decisions after the action
+// `prev` (TA_NONE: before the first) up to its next action, which it returns;
+// s, the state, is updated in place. After a stats action the workgroups'
+// (max, sum) pairs are merged in workgroup order into the node's normalizers;
+// after a pass the partial masses are summed in workgroup order and the target
+// distribution is updated. Then the next sibling is tested: an accepted child
+// with children needs its statistics, a rejection the next pass, and the walk
+// otherwise ends in a draw. Only the workgroup with `writer` set writes the
+// outputs.
+// In LDS: kids[0 .. nkids), the children of s.node in index order; haskid,
+// whether each node has children; tok_s, this sequence's node tokens; part,
+// the W workgroups' parts of the action just carried out (w0, w1 per
+// workgroup). tree_bad, tok_bad: the checks of the tree and of the tokens,
+// made by the whole workgroup while staging them.
 template <bool BF16>
-__device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32_t epoch, const uint64_t rec[4],
-                          const int32_t* kids, int nkids, const uint8_t* haskid, const int32_t* tok_s,
-                          const uint64_t (*part)[2], int tree_bad, int tok_bad) {
+__device__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, TreeState& s, const int32_t* kids,
+                                int nkids, const uint8_t* haskid, const int32_t* tok_s, const uint64_t (*part)[2],
+                                int tree_bad, int tok_bad, bool writer) {
   using E = Elem<BF16>;
   const ChainArgs& a = ta.c;
   const float T = a.temperature[b];
-  TreeState s;
-  float c2 = 0.0f;
+  const float c2 = kLog2e / T;
+  int32_t* path = ta.out_path + (int64_t)b * (ta.max_depth + 1);
+  auto to_node = [&](int v) {
+    s.node = v;
+    s.round = 0;
+    s.A = 0.0f;
+    s.Bv = 1.0f;
+    s.zt2 = s.zd2 = 0.0f;
+  };
   if (prev == TA_NONE) {
     int code = 0;
     if (tree_bad) code = -3;
     else if (!(T > 0.0f) || T == INFINITY) code = -2;
     else if (tok_bad) code = -1;
-    // Outputs are written with device-coherent stores: later leaders of this
-    // sequence may run on other XCDs, and plain stores to one line from two
-    // L2s would be written back in either order.
-    int32_t* path = ta.out_path + (int64_t)b * (ta.max_depth + 1);
-    for (int k = 0; k <= ta.max_depth; ++k) xput(&path[k], -1);
-    xput(&ta.out_token[b], -1);
-    s.node = 0;
-    s.round = 0;
-    s.len = 1;
-    s.A = 0.0f;
-    s.Bv = 1.0f;
-    s.zt2 = s.zd2 = 0.0f;
-    if (code != 0) {
-      xput(&ta.out_len[b], code);
-      tree_publish(ta, b, epoch, TA_DONE, s);
-      return;
+    // Outputs are written with device-coherent stores: the workgroup that
+    // finishes the sequence may run on another XCD, and plain stores to one
+    // line from two L2s would be written back in either order.
+    if (writer) {
+      for (int k = 0; k <= ta.max_depth; ++k) xput(&path[k], -1);
+      xput(&ta.out_token[b], -1);
+      if (code != 0) xput(&ta.out_len[b], code);
+      else xput(&path[0], 0);
     }
-    xput(&path[0], 0);
-    tree_publish(ta, b, epoch, haskid[0] ? TA_STATS : TA_DRAW_BONUS, s);
-    return;
-  } else if (prev == TA_STATS) {
-    s = tree_state_of(rec);
-    c2 = kLog2e / T;
+    to_node(0);
+    s.len = 1;
+    if (code != 0) return TA_DONE;
+    return haskid[0] ? TA_STATS : TA_DRAW_BONUS;
+  }
+  if (prev == TA_STATS) {
     LseState t, d;
     t.M = d.M = -INFINITY;
     t.s = d.s = 0.0f;
@@ -1619,8 +1597,6 @@ __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32
     s.zt2 = t.M * c2 + fast_log2(t.s);
     s.zd2 = d.M * c2 + fast_log2(d.s);
   } else {
-    s = tree_state_of(rec);
-    c2 = kLog2e / T;
     float S = 0.0f;
     for (int w = 0; w < ta.W; ++w) S += __uint_as_float((uint32_t)part[w][0]);
     if (S > 0.0f) {  // (a residual of zero mass leaves p as it was)
@@ -1629,42 +1605,33 @@ __device__ void tree_lead(const TreeSampleArgs& ta, int b, uint32_t prev, uint32
     }
     s.round += 1;
   }
-  for (int guard = 0; guard <= ta.N; ++guard) {
-    const int c = s.round < nkids ? kids[s.round] : -1;
-    if (c < 0) {
-      // A leaf (no child tested) draws the bonus from p; a node whose
-      // children were all rejected draws from its final residual (or from p
-      // if no residual had mass).
-      tree_publish(ta, b, epoch, (s.round > 0 && s.A > 0.0f) ? TA_DRAW_RESIDUAL : TA_DRAW_BONUS, s);
-      return;
-    }
-    const int x = tok_s[c];
-    const float lt = E::load(target_row(a, b, s.node), x), ld = E::load(draft_row(a, b, s.node), x);
-    const float lp2 = __builtin_fmaf(lt, c2, -s.zt2), lq2 = __builtin_fmaf(ld, c2, -s.zd2);
-    float acc;
-    if (s.A == 0.0f && s.Bv == 1.0f) {
-      acc = fast_exp2(fminf(0.0f, lp2 - lq2));  // min(1, p/q), as the chains compute it
-    } else {
-      const float p = fast_exp2(lp2), q = fast_exp2(lq2);
-      acc = q > 0.0f ? fminf(1.0f, fmaxf(0.0f, p - s.A * q) / (s.Bv * q)) : 1.0f;
-    }
-    const Words4 wu = philox10((uint32_t)s.round, (uint32_t)s.node, (uint32_t)b, a.ctr_accept, a.key0, a.key1);
-    if (uniform_accept(wu.w[0]) < acc) {
-      if (s.len <= ta.max_depth) xput(&ta.out_path[(int64_t)b * (ta.max_depth + 1) + s.len], c);
-      s.len += 1;
-      s.node = c;
-      s.round = 0;
-      s.A = 0.0f;
-      s.Bv = 1.0f;
-      s.zt2 = s.zd2 = 0.0f;
-      // The new node: its statistics first if it has children, else the
-      // bonus draw.
-      tree_publish(ta, b, epoch, haskid[c] ? TA_STATS : TA_DRAW_BONUS, s);
-      return;
-    }
-    tree_publish(ta, b, epoch, TA_PASS, s);  // the mass of (p - (A + B) q)_+ at this node
-    return;
+  const int c = s.round < nkids ? kids[s.round] : -1;
+  if (c < 0) {
+    // A leaf (no child tested) draws the bonus from p; a node whose children
+    // were all rejected draws from its final residual (or from p if no
+    // residual had mass).
+    return (s.round > 0 && s.A > 0.0f) ? TA_DRAW_RESIDUAL : TA_DRAW_BONUS;
   }
+  const int x = tok_s[c];
+  const float lt = E::load(target_row(a, b, s.node), x), ld = E::load(draft_row(a, b, s.node), x);
+  const float lp2 = __builtin_fmaf(lt, c2, -s.zt2), lq2 = __builtin_fmaf(ld, c2, -s.zd2);
+  float acc;
+  if (s.A == 0.0f && s.Bv == 1.0f) {
+    acc = fast_exp2(fminf(0.0f, lp2 - lq2));  // min(1, p/q), as the chains compute it
+  } else {
+    const float p = fast_exp2(lp2), q = fast_exp2(lq2);
+    acc = q > 0.0f ? fminf(1.0f, fmaxf(0.0f, p - s.A * q) / (s.Bv * q)) : 1.0f;
+  }
+  const Words4 wu = philox10((uint32_t)s.round, (uint32_t)s.node, (uint32_t)b, a.ctr_accept, a.key0, a.key1);
+  if (uniform_accept(wu.w[0]) < acc) {
+    if (writer && s.len <= ta.max_depth) xput(&path[s.len], c);
+    s.len += 1;
+    to_node(c);
+    // The new node: its statistics first if it has children, else the bonus
+    // draw.
+    return haskid[c] ? TA_STATS : TA_DRAW_BONUS;
+  }
+  return TA_PASS;  // the mass of (p - (A + B) q)_+ at this node
 }
 
 // This workgroup's part of sum_v (p(v) - A q(v))_+ over [lo, hi), with the
@@ -1710,31 +1677,36 @@ __device__ float residual_mass_part(const uint8_t* rt, const uint8_t* rd, int lo
   return s;
 }
 
-// The last workgroup after the final action: the drawn token (workgroup
+// The last workgroup to arrive after the draw: the drawn token (workgroup
 // parts merged in workgroup order, lowest index on ties), the outputs, and the
-// sequence's workspace returned to zero.
+// sequence's workspace returned to zero. parts: the draw's slot buffer;
+// both_buffers: whether earlier actions used the other one too.
 template <bool BF16, bool VEC>
-__device__ void tree_finish(const TreeSampleArgs& ta, int b, uint32_t action, Smem& sm) {
+__device__ void tree_finish(const TreeSampleArgs& ta, int b, int len, const P2Slot* parts, bool both_buffers,
+                            Smem& sm) {
   const ChainArgs& a = ta.c;
-  P2Slot* sl = a.p2 + (int64_t)b * a.p2_stride;
-  if (threadIdx.x == 0 && action != TA_DONE) {
+  if (threadIdx.x == 0) {
     ArgMax m;
     m.v = -INFINITY;
     m.i = -1;
     for (int w = 0; w < ta.W; ++w) {
-      const uint64_t w0 = xget64(&sl[w].w0);
+      const uint64_t w0 = xget64((uint64_t*)&parts[w].w0);
       ArgMax o;
       o.v = hi_f(w0);
       o.i = (int)lo_u(w0);
       m = argmax_merge(m, o);
     }
     xput(&ta.out_token[b], m.i);
-    xput(&ta.out_len[b], (int)(uint32_t)sm.trec[3]);
+    xput(&ta.out_len[b], len);
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < 2 * ta.W; k += kThreads) xput64(&((uint64_t*)sl)[k], 0u);
+  uint64_t* s0 = (uint64_t*)(a.p2 + (int64_t)b * a.p2_stride);
+  uint64_t* s1 = (uint64_t*)(ta.slot2 + (int64_t)b * a.p2_stride);
+  for (int k = threadIdx.x; k < 2 * ta.W; k += kThreads) {
+    xput64(&s0[k], 0u);
+    if (both_buffers) xput64(&s1[k], 0u);
+  }
   SeqState* st = a.seq + b;
-  if (threadIdx.x < 4) xput64(&st->dec[threadIdx.x], 0u);
   if (threadIdx.x == 0) {
     xput(&st->lbest, 0u);
     xput(&st->p2_arrive, 0u);
@@ -1753,14 +1725,14 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   if (b >= ta.b_base + ta.b_count) return;  // whole sequences only
   SeqState* st = a.seq + b;
   const int lo = w * ta.wlen, hi = min(a.V, lo + ta.wlen);
-  // The tree and this sequence's tokens in LDS: any workgroup may lead, and
-  // the leader walks them serially.
-  // The checks of the tree (root first at depth 0; every other parent an
-  // earlier node, one level up; no node deeper than max_depth) and of the
-  // tokens, one node per lane.
+  // The tree and this sequence's tokens in LDS, with the checks of the tree
+  // (root first at depth 0; every other parent an earlier node, one level
+  // up; no node deeper than max_depth) and of the tokens, one node per lane.
   __shared__ int32_t s_par[kMaxTreeNodes], s_tok[kMaxTreeNodes], s_kids[kMaxTreeNodes];
   __shared__ uint8_t s_haskid[kMaxTreeNodes];
   __shared__ int32_t s_nkids, s_wcnt[kThreads / 64];
+  __shared__ TreeState s_state;
+  __shared__ uint32_t s_action;
   int tree_bad = 0, tok_bad = 0;
   for (int k = threadIdx.x; k < ta.N; k += kThreads) {
     const int pk = ta.parents[k], dk = ta.depth[k], xk = ta.tokens[(int64_t)b * ta.N + k];
@@ -1779,75 +1751,23 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   for (int k = 1 + (int)threadIdx.x; k < ta.N; k += kThreads)
     if (s_par[k] >= 0 && s_par[k] < ta.N) s_haskid[s_par[k]] = 1;
   __syncthreads();
-  uint32_t epoch = 0, action = TA_NONE;
-  float partial = 0.0f;
-  P2Slot part;
-  part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
-  part.w1 = 0u;
-  for (int iter = 0; iter <= ta.N + 2; ++iter) {
-    // Arrive with this workgroup's part of the action just carried out.
-    if (threadIdx.x == 0) {
-      P2Slot* slot = a.p2 + (int64_t)b * a.p2_stride + w;
-      if (action == TA_PASS) xput64(&slot->w0, (uint64_t)__float_as_uint(partial));
-      if (action == TA_STATS) {
-        xput64(&slot->w0, part.w0);
-        xput64(&slot->w1, part.w1);
-      }
-      if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) xput64(&slot->w0, part.w0);
-      wait_vmem();
-      const uint32_t old = atomicAdd(&st->p2_arrive, 1u);
-      sm.flag_last = (old + 1u == (uint32_t)ta.W) ? 1u : 0u;
-      if (sm.flag_last) xput(&st->p2_arrive, 0u);
-    }
-    __syncthreads();
-    const bool last = sm.flag_last != 0u;
-    if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS || action == TA_DONE) {
-      if (last) tree_finish<BF16, VEC>(ta, b, action, sm);
-      return;
-    }
-    if (last) {
-      // The workgroups' slots, read in parallel.
-      const P2Slot* sl = a.p2 + (int64_t)b * a.p2_stride;
-      for (int k = threadIdx.x; k < ta.W; k += kThreads) {
-        sm.u.slot[k][0] = xget64((uint64_t*)&sl[k].w0);
-        sm.u.slot[k][1] = xget64((uint64_t*)&sl[k].w1);
-      }
-      // The children of the node the decisions start from.
-      tree_children(ta.N, s_par, action == TA_NONE ? 0 : (int)(uint32_t)sm.trec[0], s_kids, &s_nkids, s_wcnt);
-      __syncthreads();
-      if (threadIdx.x == 0)
-        tree_lead<BF16>(ta, b, action, epoch, sm.trec, s_kids, s_nkids, s_haskid, s_tok, sm.u.slot, tree_bad, tok_bad);
-    }
-    __syncthreads();
-    // Wait for the next action (bounded).
-    if (threadIdx.x == 0) {
-      uint64_t r0 = xget64(&st->dec[0]);
-      uint32_t spins = 0;
-      sm.stalled = 0u;
-      while ((uint32_t)(r0 >> 40) == epoch) {
-        if (++spins > a.spin_limit || ((spins & 255u) == 0u && xget(&a.done[1]) != 0u)) {
-          atomicOr(&a.done[1], 1u);
-          xput(&ta.out_len[b], -4);
-          sm.stalled = 1u;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-        r0 = xget64(&st->dec[0]);
-      }
-      sm.trec[0] = r0;
-      if (!sm.stalled) {
-        sm.trec[1] = xget64(&st->dec[1]);
-        sm.trec[2] = xget64(&st->dec[2]);
-        sm.trec[3] = xget64(&st->dec[3]);
-      }
-      sm.lkey = 0u;
-    }
-    __syncthreads();
-    if (sm.stalled) return;
-    epoch += 1u;
-    action = (uint32_t)(sm.trec[0] >> 32) & 0xFFu;
-    const TreeState t = tree_state_of(sm.trec);
-    const float c2 = kLog2e / a.temperature[b];
+  // The first decisions need no part of any workgroup.
+  if (threadIdx.x == 0) {
+    TreeState s0;
+    s_action = tree_decide<BF16>(ta, b, TA_NONE, s0, s_kids, 0, s_haskid, s_tok, nullptr, tree_bad, tok_bad, w == 0);
+    s_state = s0;
+    sm.lkey = 0u;
+  }
+  __syncthreads();
+  uint32_t action = s_action;
+  if (action == TA_DONE) return;  // a bad input: nothing was touched
+  const float c2 = kLog2e / a.temperature[b];
+  for (uint32_t epoch = 0; epoch <= (uint32_t)ta.N + 2u; ++epoch) {
+    const TreeState t = s_state;
+    float partial = 0.0f;
+    P2Slot part;
+    part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
+    part.w1 = 0u;
     if (action == TA_STATS) {
       // (max, sum exp2) of the node's target and draft rows over [lo, hi),
       // in pieces of the launch's tile.
@@ -1877,7 +1797,7 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
       partial = block_sum(residual_mass_part<BF16, VEC>(target_row(a, b, t.node), draft_row(a, b, t.node), lo, hi, c2,
                                                         t.zt2, zd2s),
                           sm);
-    } else if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) {
+    } else {
       Decision d;
       d.kind = KIND_SAMPLED;
       d.n = 0;
@@ -1899,6 +1819,58 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
         else gumbel_chunk<BF16, VEC, P2_BONUS>(a, b, d, lo, hi, sm, &part);
       }
     }
+    // Arrive with this workgroup's part (buffer epoch & 1): the arrival counter
+    // only grows during the walk, W per action.
+    P2Slot* parts = ((epoch & 1u) ? ta.slot2 : a.p2) + (int64_t)b * a.p2_stride;
+    const uint32_t want = (uint32_t)ta.W * (epoch + 1u);
+    if (threadIdx.x == 0) {
+      if (action == TA_PASS) {
+        xput64(&parts[w].w0, (uint64_t)__float_as_uint(partial));
+      } else {
+        xput64(&parts[w].w0, part.w0);
+        xput64(&parts[w].w1, part.w1);
+      }
+      wait_vmem();
+      const uint32_t old = atomicAdd(&st->p2_arrive, 1u);
+      sm.flag_last = (old + 1u == want) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) {
+      if (sm.flag_last) tree_finish<BF16, VEC>(ta, b, t.len, parts, epoch > 0u, sm);
+      return;
+    }
+    // Wait until all W have arrived (bounded).
+    if (threadIdx.x == 0) {
+      uint32_t spins = 0;
+      sm.stalled = 0u;
+      while (xget(&st->p2_arrive) < want) {
+        if (++spins > a.spin_limit || ((spins & 255u) == 0u && xget(&a.done[1]) != 0u)) {
+          atomicOr(&a.done[1], 1u);
+          xput(&ta.out_len[b], -4);
+          sm.stalled = 1u;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    if (sm.stalled) return;
+    // Every workgroup: the parts (read in parallel), the node's children, and
+    // the same decisions.
+    for (int k = threadIdx.x; k < ta.W; k += kThreads) {
+      sm.u.slot[k][0] = xget64((uint64_t*)&parts[k].w0);
+      sm.u.slot[k][1] = xget64((uint64_t*)&parts[k].w1);
+    }
+    tree_children(ta.N, s_par, t.node, s_kids, &s_nkids, s_wcnt);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      TreeState s1 = s_state;
+      s_action = tree_decide<BF16>(ta, b, action, s1, s_kids, s_nkids, s_haskid, s_tok, sm.u.slot, 0, 0, w == 0);
+      s_state = s1;
+      sm.lkey = 0u;
+    }
+    __syncthreads();
+    action = s_action;
   }
 }
 
