@@ -442,7 +442,7 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
   const int per_wg = std::max(unit, sv::env_int("SV_TREE_WLEN", 8192));
   const int w0 = std::max(1, (V + per_wg - 1) / per_wg);
   a.wlen = ((V + w0 - 1) / w0 + unit - 1) / unit * unit;
-  // At most 256 workgroups per sequence (the leader stages one slot per thread).
+  // At most 256 workgroups per sequence (each stages the parts, one per thread).
   const int min_wlen = ((V + 255) / 256 + unit - 1) / unit * unit;
   a.wlen = std::max(a.wlen, min_wlen);
   a.W = (V + a.wlen - 1) / a.wlen;

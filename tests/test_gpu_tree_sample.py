@@ -181,3 +181,25 @@ def test_named_workload_full_size(dev):
     ref = _oracle(inp, seed=inp.seed, offset=inp.offset)
     _compare(got, ref, "tree_sample_bf16_llama")
     assert np.all(ref["path_len"] >= 1)
+
+
+@pytest.mark.parametrize("N,V", [(1, 1000), (2, 1000), (2, 700), (3, 2048)])
+def test_smallest_trees_and_vocabularies(dev, N, V):
+    """A root alone (a bonus draw, one action) and the smallest trees with a
+    child, at vocabularies of one workgroup part: the walk's second slot
+    buffer sits in the greedy tree's slot area, which holds it exactly from
+    N = 2 on and is never used by a one-node tree."""
+    import rejection_sampling_verify_amd as rsv
+    B = 40
+    parents = np.arange(-1, N - 1, dtype=np.int32)
+    depth = np.arange(N, dtype=np.int32)
+    inp = make_tree_sample("small_%d_%d" % (N, V), B, V, parents, depth, bf16=True, seed=30 + N, temperatures=(0.8, 1.2),
+                           zipf=0.0, target_sigma=1.5, draft_sigma=(0.2, 1.0))
+    ws = rsv.Workspace(dev).get(B, N, V)
+    for s in (0, 5):
+        got = _run(inp, dev, seed=s, workspace=ws)
+        ref = _oracle(inp, seed=s)
+        _compare(got, ref, "N=%d V=%d seed %d" % (N, V, s))
+        assert int(ws.count_nonzero().item()) == 0
+    if N == 1:
+        assert np.all(got["path_len"] == 1)
