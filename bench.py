@@ -12,6 +12,13 @@ same run (the library's read yardstick over a 2 GiB buffer) and the call's
 fraction of it, and a warm-cache launch time (the same input copy every step,
 labelled as such; the timed steps alternate two copies).
 
+Other workloads (--workload): the four other verify configurations
+(chain_f32_small, chain_bf16_peaked, onehot_bf16_qwen, tree_bf16_llama),
+sampled trees (tree_sample_bf16_llama), and the steps around the verify, each
+with its own metric and the same roofline / cpu_baseline fields:
+kv_rollback_bf16_llama (sequences rolled back per second), ngram_draft_qwen
+(drafts per second) and tree_mask_b256 (masks per second).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
