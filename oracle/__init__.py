@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_int]
         L.or_verify_tree.restype = ctypes.c_int
         L.or_verify_tree_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, P, P, i32, i32, i32, i32,
-                                            u64, u64, P, P, P, P, P, P, P, ctypes.c_int]
+                                            u64, u64, i32, P, P, P, P, P, P, P, ctypes.c_int]
         L.or_verify_tree_sample.restype = ctypes.c_int
         L.or_tree_depths.argtypes = [P, i32, P]
         L.or_tree_depths.restype = ctypes.c_int
@@ -198,13 +198,16 @@ def verify_tree(target, parents, depth, node_tokens, max_depth, V=None, nthreads
 
 
 def verify_tree_sample(target, draft, parents, depth, node_tokens, temperature, max_depth, seed=0, offset=0,
-                       V=None, nthreads=None) -> dict:
+                       V=None, nthreads=None, without_replacement=False) -> dict:
     """Sampled tree verification by multi-round rejection sampling ([SB] "Tree
     Attention"). target and draft are [B, N, Vs] (draft row v: q at node v,
     from which v's children were drawn). Returns path [B, max_depth + 1],
     path_len [B] (nodes on the path, or a negative code), token [B] (the bonus
     or replacement token after the path), top_gap, flags, rejections and
-    margin (the smallest |u - a| over the siblings tested) [B]."""
+    margin (the smallest |u - a| over the siblings tested) [B].
+    without_replacement: siblings were drawn without replacement, so each
+    round's q is q over the tokens not drawn yet, renormalized (the page's
+    variant); siblings must then carry distinct tokens (else code -1)."""
     tok = np.ascontiguousarray(node_tokens, dtype=np.int32)
     B, N = tok.shape
     V, tstride = _rows(target, N, V)
@@ -222,7 +225,8 @@ def verify_tree_sample(target, draft, parents, depth, node_tokens, temperature, 
     nt = nthreads or os.cpu_count() or 1
     rc = lib().or_verify_tree_sample(_ptr(target), tstride, _ptr(draft), dstride, _logits_dtype(target),
                                      _ptr(par), _ptr(dep), _ptr(tok), _ptr(temp), B, N, V, max_depth,
-                                     seed, offset, _ptr(out["path"]), _ptr(out["path_len"]), _ptr(out["token"]),
+                                     seed, offset, int(bool(without_replacement)), _ptr(out["path"]),
+                                     _ptr(out["path_len"]), _ptr(out["token"]),
                                      _ptr(out["top_gap"]), _ptr(out["flags"]), _ptr(out["rejections"]),
                                      _ptr(out["margin"]), nt)
     if rc != 0:

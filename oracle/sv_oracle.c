@@ -518,7 +518,7 @@ static void or_softmax(const void* base, int dtype, int64_t stride, int64_t r, i
 static void or_tree_sample_one(const void* target, int64_t tstride, const void* draft,
                                int64_t dstride, int dtype, const int32_t* parents,
                                const int32_t* tok, double T, int32_t b, int32_t N, int32_t V,
-                               int32_t max_depth, uint64_t seed, uint64_t offset, double* y,
+                               int32_t max_depth, uint64_t seed, uint64_t offset, int wor, double* y,
                                double* P, double* Q, int32_t* path, int32_t* out_len,
                                int32_t* out_token, double* top_gap, int32_t* flags,
                                int32_t* rejections, double* margin) {
@@ -565,6 +565,14 @@ static void or_tree_sample_one(const void* target, int64_t tstride, const void* 
       } else {
         fl |= OR_FLAG_FALLBACK;
       }
+      if (wor) {
+        /* Siblings drawn without replacement: the next one came from q over
+         * the tokens not drawn yet, renormalized. */
+        const double left = 1.0 - Q[x];
+        Q[x] = 0.0;
+        if (left > 0.0)
+          for (int32_t v = 0; v < V; ++v) Q[v] /= left;
+      }
     }
     if (next < 0) {
       /* Every child rejected: the replacement token from the final residual
@@ -590,9 +598,9 @@ int or_verify_tree_sample(const void* target, int64_t tstride, const void* draft
                           int dtype, const int32_t* parents, const int32_t* depth,
                           const int32_t* node_tokens, const float* temperature, int32_t B,
                           int32_t N, int32_t V, int32_t max_depth, uint64_t seed, uint64_t offset,
-                          int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
-                          double* top_gap, int32_t* flags, int32_t* rejections, double* margin,
-                          int nthreads) {
+                          int32_t without_replacement, int32_t* out_path, int32_t* out_path_len,
+                          int32_t* out_token, double* top_gap, int32_t* flags, int32_t* rejections,
+                          double* margin, int nthreads) {
   if (!target || !draft || !parents || !depth || !node_tokens || !temperature || !out_path ||
       !out_path_len || !out_token)
     return 1;
@@ -625,14 +633,19 @@ int or_verify_tree_sample(const void* target, int64_t tstride, const void* draft
         continue;
       }
       int bad = 0;
-      for (int32_t c = 1; c < N; ++c)
+      for (int32_t c = 1; c < N; ++c) {
         if (tok[c] < 0 || tok[c] >= V) bad = 1;
+        /* Without replacement, siblings carry distinct tokens. */
+        if (without_replacement)
+          for (int32_t s2 = 1; s2 < c; ++s2)
+            if (parents[s2] == parents[c] && tok[s2] == tok[c]) bad = 1;
+      }
       if (bad) {
         out_path_len[b] = OR_SEQ_BAD_TOKEN;
         continue;
       }
       or_tree_sample_one(target, tstride, draft, dstride, dtype, parents, tok, T, b, N, V,
-                         max_depth, seed, offset, y, P, Q, path, &out_path_len[b], &out_token[b],
+                         max_depth, seed, offset, without_replacement != 0, y, P, Q, path, &out_path_len[b], &out_token[b],
                          top_gap ? &top_gap[b] : NULL, flags ? &flags[b] : NULL,
                          rejections ? &rejections[b] : NULL, margin ? &margin[b] : NULL);
     }

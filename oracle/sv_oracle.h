@@ -74,9 +74,9 @@ int or_verify_tree_sample(const void* target, int64_t tstride, const void* draft
                           int dtype, const int32_t* parents, const int32_t* depth,
                           const int32_t* node_tokens, const float* temperature, int32_t B,
                           int32_t N, int32_t V, int32_t max_depth, uint64_t seed, uint64_t offset,
-                          int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
-                          double* top_gap, int32_t* flags, int32_t* rejections, double* margin,
-                          int nthreads);
+                          int32_t without_replacement, int32_t* out_path, int32_t* out_path_len,
+                          int32_t* out_token, double* top_gap, int32_t* flags, int32_t* rejections,
+                          double* margin, int nthreads);
 
 int or_tree_depths(const int32_t* parents, int32_t N, int32_t* depth_out);
 

@@ -176,3 +176,125 @@ def test_bad_inputs_are_marked():
     bad_tree = oracle.verify_tree_sample(t, t.copy(), np.array([-1, 0, 0], np.int32), np.array([0, 1, 2], np.int32),
                                          tok, np.ones(B, np.float32), 2)
     assert np.all(bad_tree["path_len"] == -3)
+
+
+# ---------------------------------------------------------------------------
+# Siblings drawn without replacement: each round's q is q over the tokens not
+# drawn yet, renormalized (the page's variant).
+# ---------------------------------------------------------------------------
+
+def _rule_law_wor(p, q, k):
+    """Exact law of (round of acceptance or None, emitted token) for k
+    siblings drawn from q without replacement, enumerating every ordered draw
+    of distinct tokens with rational arithmetic. Written from the rule's
+    statement, independently of the C oracle."""
+    V = len(p)
+
+    def renorm_without(qj, x):
+        left = 1 - qj[x]
+        return [Fraction(0) if t == x else (v / left if left > 0 else v) for t, v in enumerate(qj)]
+
+    law = {}
+    for xs in itertools.permutations(range(V), k):
+        # probability of this ordered draw
+        w = Fraction(1)
+        qj = list(q)
+        for x in xs:
+            w *= qj[x]
+            qj = renorm_without(qj, x)
+        if w == 0:
+            continue
+        # the rule along it
+        pj, qj = list(p), list(q)
+        still = Fraction(1)
+        for j, x in enumerate(xs):
+            a = min(Fraction(1), pj[x] / qj[x])
+            law[(j, x)] = law.get((j, x), Fraction(0)) + w * still * a
+            still *= 1 - a
+            r = [max(u - v, Fraction(0)) for u, v in zip(pj, qj)]
+            z = sum(r)
+            if z > 0:
+                pj = [u / z for u in r]
+            qj = renorm_without(qj, x)
+        for t in range(V):
+            law[(None, t)] = law.get((None, t), Fraction(0)) + w * still * pj[t]
+    return law
+
+
+def test_without_replacement_rule_is_lossless_by_exact_enumeration():
+    cases = [
+        ([Fraction(3, 10), Fraction(5, 10), Fraction(2, 10)], [Fraction(1, 2), Fraction(1, 4), Fraction(1, 4)]),
+        ([Fraction(1, 8), Fraction(1, 8), Fraction(1, 4), Fraction(1, 2)],
+         [Fraction(4, 10), Fraction(3, 10), Fraction(2, 10), Fraction(1, 10)]),
+    ]
+    for p, q in cases:
+        for k in range(1, len(p) + 1):
+            law = _rule_law_wor(p, q, k)
+            assert sum(law.values()) == 1
+            emitted = [sum(v for (j, t), v in law.items() if t == s) for s in range(len(p))]
+            assert emitted == p, (p, q, k, emitted)
+    # with one sibling the two rules coincide
+    p, q = cases[0]
+    assert _rule_law_wor(p, q, 1) == _rule_law(p, q, 1)
+
+
+def _one_node_batch_wor(rng, lp, lq, k, B, V):
+    N = k + 1
+    target = np.broadcast_to(np.asarray(lp, np.float32), (B, N, V)).copy()
+    draft = np.broadcast_to(np.asarray(lq, np.float32), (B, N, V)).copy()
+    q = np.exp(np.asarray(lq, np.float64))
+    q /= q.sum()
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        tok[b, 1:] = rng.choice(V, size=k, replace=False, p=q)
+    parents = np.array([-1] + [0] * k, np.int32)
+    depth = np.array([0] + [1] * k, np.int32)
+    return target, draft, parents, depth, tok
+
+
+def test_oracle_without_replacement_emits_p_and_the_rule_rounds_chi_square():
+    rng = np.random.default_rng(12)
+    V, k, B = 4, 3, 60000
+    lp = np.log(np.array([0.1, 0.2, 0.3, 0.4]))
+    lq = np.log(np.array([0.4, 0.3, 0.2, 0.1]))
+    target, draft, parents, depth, tok = _one_node_batch_wor(rng, lp, lq, k, B, V)
+    o = oracle.verify_tree_sample(target, draft, parents, depth, tok, np.ones(B, np.float32), 1, seed=6,
+                                  without_replacement=True)
+    p64 = np.exp(np.float64(target[0, 0])) / np.exp(np.float64(target[0, 0])).sum()
+    q64 = np.exp(np.float64(draft[0, 0])) / np.exp(np.float64(draft[0, 0])).sum()
+    first = np.where(o["path_len"] >= 2, tok[np.arange(B), np.maximum(o["path"][:, 1], 0)], o["token"])
+    assert stats.chisquare(np.bincount(first, minlength=V), p64 * B).pvalue > 1e-3
+    rounds = np.where(o["path_len"] >= 2, o["path"][:, 1] - 1, k)
+    law = _rule_law_wor([Fraction(float(x)) for x in p64], [Fraction(float(x)) for x in q64], k)
+    exp_r = np.array([float(sum(v for (j, t), v in law.items() if j == r)) for r in range(k)] +
+                     [float(sum(v for (j, t), v in law.items() if j is None))])
+    assert stats.chisquare(np.bincount(rounds, minlength=k + 1), exp_r * B).pvalue > 1e-3
+    # the i.i.d. rule's round law differs here, so the test tells the two apart
+    law_iid = _rule_law([Fraction(float(x)) for x in p64], [Fraction(float(x)) for x in q64], k)
+    assert abs(float(law_iid.get((None, 0), 0)) - float(law.get((None, 0), 0))) > 1e-3 or \
+        abs(sum(float(v) for (j, t), v in law_iid.items() if j == 1) -
+            sum(float(v) for (j, t), v in law.items() if j == 1)) > 1e-3
+
+
+def test_without_replacement_single_children_and_duplicates():
+    """One child per node: the same outputs as the i.i.d. rule. Duplicate
+    sibling tokens are a bad input without replacement."""
+    rng = np.random.default_rng(13)
+    B, V = 16, 50
+    parents = np.array([-1, 0, 1, 2], np.int32)
+    depth = oracle.tree_depths(parents)
+    t = rng.normal(0, 2, (B, 4, V)).astype(np.float32)
+    d = (t + rng.normal(0, 1, (B, 4, V))).astype(np.float32)
+    tok = rng.integers(0, V, (B, 4)).astype(np.int32)
+    a = oracle.verify_tree_sample(t, d, parents, depth, tok, np.ones(B, np.float32), 3, seed=2)
+    b = oracle.verify_tree_sample(t, d, parents, depth, tok, np.ones(B, np.float32), 3, seed=2,
+                                  without_replacement=True)
+    assert all(np.array_equal(a[key], b[key]) for key in ("path", "path_len", "token"))
+    par2 = np.array([-1, 0, 0], np.int32)
+    tok2 = np.array([[0, 5, 5], [0, 5, 6]], np.int32)
+    t2 = rng.normal(0, 1, (2, 3, V)).astype(np.float32)
+    r = oracle.verify_tree_sample(t2, t2.copy(), par2, oracle.tree_depths(par2), tok2, np.ones(2, np.float32), 1,
+                                  without_replacement=True)
+    assert r["path_len"][0] == -1 and r["path_len"][1] >= 1
+    r = oracle.verify_tree_sample(t2, t2.copy(), par2, oracle.tree_depths(par2), tok2, np.ones(2, np.float32), 1)
+    assert r["path_len"][0] >= 1  # with replacement, repeats are fine
