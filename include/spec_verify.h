@@ -222,6 +222,12 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
  *     node v is word 0 of counter (j, v, b, 2 offset); the noise of a draw at
  *     node v is that of position v. A tree shaped like a chain therefore
  *     verifies exactly as spec_verify_sample verifies the chain.
+ *   siblings_without_replacement: 0 when a node's children were drawn i.i.d.
+ *     from q; 1 when they were drawn without replacement ([SB] "Tree
+ *     Attention": q renormalized over the remaining candidates). Then the
+ *     j-th sibling's round uses q over the tokens not drawn before it,
+ *     renormalized, both in its accept test and in the residual after a
+ *     rejection, and siblings must carry distinct tokens (else code -1).
  *   Outputs (device): out_path [B, max_depth + 1] (accepted nodes from the
  *     root, -1 padded), out_path_len [B] (nodes on the path; -1 a node token
  *     out of range, -2 a temperature not > 0, -3 an invalid tree, -4 a bounded
@@ -229,14 +235,15 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
  *   workspace: sv_workspace_bytes(B, N, V) bytes, as for spec_verify_tree.
  * Returns SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE (B, N, V or max_depth out of
  * range, or a vocabulary too long for one launch), SV_ERR_BAD_DTYPE,
- * SV_ERR_BAD_ARG (a stride < V, offset >= 2^31), SV_ERR_WORKSPACE or
- * SV_ERR_HIP; nothing is launched on an error. */
+ * SV_ERR_BAD_ARG (a stride < V, offset >= 2^31, siblings_without_replacement
+ * not 0 or 1), SV_ERR_WORKSPACE or SV_ERR_HIP; nothing is launched on an error. */
 sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_row_stride, const void* draft_logits,
                                     int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* parents,
                                     const int32_t* depth, const int32_t* node_tokens, const float* temperature,
                                     int32_t B, int32_t N, int32_t V, int32_t max_depth, uint64_t seed,
-                                    uint64_t offset, int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
-                                    void* workspace, size_t workspace_bytes, void* stream);
+                                    uint64_t offset, int32_t siblings_without_replacement, int32_t* out_path,
+                                    int32_t* out_path_len, int32_t* out_token, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* sv_tree_mask — the attention mask and position ids of a token tree packed
  * into one forward pass ("7.6 Speculative Decoding", "Tree Attention:

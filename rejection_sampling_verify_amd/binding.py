@@ -62,7 +62,7 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_tree.argtypes = [P, i64, ctypes.c_int, P, P, P, i32, i32, i32, i32, P, P, P, P, sz, P]
         L.spec_verify_tree.restype = ctypes.c_int
         L.spec_verify_tree_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, u64, u64,
-                                              P, P, P, P, sz, P]
+                                              i32, P, P, P, P, sz, P]
         L.spec_verify_tree_sample.restype = ctypes.c_int
         L.sv_kv_rollback.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
         L.sv_kv_rollback.restype = ctypes.c_int
@@ -249,7 +249,7 @@ def spec_verify_tree(target_logits, parents, depth, node_tokens, max_depth: int,
 
 def spec_verify_tree_sample(target_logits, draft_logits, parents, depth, node_tokens, temperature, max_depth: int,
                             seed: int = 0, offset: int = 0, out_path=None, out_path_len=None, out_token=None,
-                            workspace=None, V: int | None = None, stream=None):
+                            workspace=None, V: int | None = None, stream=None, without_replacement: bool = False):
     """Sampled tree verification (multi-round rejection sampling). target and
     draft logits [B, N, V] (draft row v: q at node v), temperature [B] > 0.
     Returns (out_path [B, max_depth+1], out_path_len [B], out_token [B])."""
@@ -276,7 +276,8 @@ def spec_verify_tree_sample(target_logits, draft_logits, parents, depth, node_to
         workspace = Workspace(dev).get(B, N, V)
     st = lib().spec_verify_tree_sample(_ptr(target_logits), ts, _ptr(draft_logits), ds, _dtype_code(target_logits),
                                        _ptr(parents), _ptr(depth), _ptr(node_tokens), _ptr(temperature), B, N, V,
-                                       max_depth, seed, offset, _ptr(out_path), _ptr(out_path_len), _ptr(out_token),
+                                       max_depth, seed, offset, int(bool(without_replacement)), _ptr(out_path),
+                                       _ptr(out_path_len), _ptr(out_token),
                                        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
         raise SVError(st, "spec_verify_tree_sample")

@@ -374,8 +374,9 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
                                     int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* parents,
                                     const int32_t* depth, const int32_t* node_tokens, const float* temperature,
                                     int32_t B, int32_t N, int32_t V, int32_t max_depth, uint64_t seed,
-                                    uint64_t offset, int32_t* out_path, int32_t* out_path_len, int32_t* out_token,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+                                    uint64_t offset, int32_t siblings_without_replacement, int32_t* out_path,
+                                    int32_t* out_path_len, int32_t* out_token, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   if (!target_logits || !draft_logits || !parents || !depth || !node_tokens || !temperature || !out_path ||
       !out_path_len || !out_token)
     return SV_ERR_NULL_ARG;
@@ -385,6 +386,7 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
   if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_BAD_DTYPE;
   if (target_row_stride < V || draft_row_stride < V) return SV_ERR_BAD_ARG;
   if (offset >= (1ull << 31)) return SV_ERR_BAD_ARG;
+  if (siblings_without_replacement != 0 && siblings_without_replacement != 1) return SV_ERR_BAD_ARG;
   const size_t need = sv_workspace_bytes(B, N, V);
   const sv_status_t ws_ok = sv::check_workspace(workspace, workspace_bytes, need);
   if (ws_ok != SV_OK) return ws_ok;
@@ -432,6 +434,7 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
   // unused here (B * N * nchunks 8-byte slots hold B * nchunks 16-byte parts
   // for N >= 2; a one-node tree never needs the second buffer).
   a.slot2 = (sv::P2Slot*)(ws + L.tree_slot);
+  a.wor = siblings_without_replacement;
   a.out_path = out_path;
   a.out_len = out_path_len;
   a.out_token = out_token;

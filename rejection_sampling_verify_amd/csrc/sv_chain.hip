@@ -722,14 +722,24 @@ __device__ void pass1_item(const ChainArgs& a, int b, int r, Smem& sm) {
 // ---------------------------------------------------------------------------
 // Pass 2: one chunk of the row a decided sequence draws its last token from.
 // ---------------------------------------------------------------------------
+// Whether idx is one of the n entries of list l (a short list in LDS).
+__device__ __forceinline__ bool in_list(const int32_t* l, int n, int idx) {
+  for (int i = 0; i < n; ++i)
+    if (l[i] == idx) return true;
+  return false;
+}
+
 // One chunk of a Gumbel-max draw, specialised on what the score of an element
 // is (MODE = P2_RESIDUAL: ln(p - q) where p > q; P2_RESIDUAL_ONEHOT: l/T for
 // v != x; P2_BONUS: l/T). For each 16-byte vector the lane forms the Philox
 // words and the pruning test of its elements; the exact score and noise are
 // evaluated only when some element survives (rare once the bound has risen),
-// lowest index first. Vectors are prefetched three deep.
-template <bool BF16, bool VEC, int MODE>
-__device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm, P2Slot* out) {
+// lowest index first. Vectors are prefetched three deep. EXCL: the excl[0 .. nexcl)
+// elements take no part (sampled trees whose siblings were drawn without
+// replacement).
+template <bool BF16, bool VEC, int MODE, bool EXCL = false>
+__device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm, P2Slot* out,
+                             const int32_t* excl = nullptr, int nexcl = 0) {
   using E = Elem<BF16>;
   constexpr int EV = E::kPerVec;
   constexpr bool residual = (MODE == P2_RESIDUAL);
@@ -769,6 +779,7 @@ __device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int 
   };
   // Pruning test; r is the residual bound from accumulate().
   auto test = [&](float lt, float r, uint32_t w, int idx) -> bool {
+    if (EXCL && in_list(excl, nexcl, idx)) return false;
     if (residual) return r > 0.0f && may_win_lin(w, r * scale);
     if (onehot && idx == xex) return false;
     return may_win_log2(w, __builtin_fmaf(lt, c2, nL2));  // log2 exp(l/T - L)
@@ -920,9 +931,9 @@ __device__ __forceinline__ void set_phase_priority(int rnd, int rounds) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-template <int MODE, bool BETA>
+template <int MODE, bool BETA, bool EXCL = false>
 __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm,
-                                  P2Slot* out) {
+                                  P2Slot* out, const int32_t* excl = nullptr, int nexcl = 0) {
   using E = Elem<true>;
   constexpr bool residual = (MODE == P2_RESIDUAL);
   constexpr bool onehot = (MODE == P2_RESIDUAL_ONEHOT);
@@ -1011,6 +1022,7 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
         } else {
           k = (onehot && base + e == xex) ? -INFINITY : el(qt0, e);
         }
+        if (EXCL && in_list(excl, nexcl, base + e)) k = -INFINITY;
         if (k > key) {
           key = k;
           ke = e;
@@ -1100,6 +1112,7 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
         } else {
           k = (e != xrel) && may_win_bits(w, __builtin_fmaf(el(qt0, e), c2s, log_bias));
         }
+        if (EXCL && k && in_list(excl, nexcl, base + e)) k = false;
         if (k) {
           const float tot = total(el(qt0, e), residual ? el(qd0, e) : 0.0f, w);
           best_push(bst, tot, base + e);
@@ -1157,6 +1170,7 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
       } else {
         keep = !(onehot && idx == xex);
       }
+      if (EXCL && keep && in_list(excl, nexcl, idx)) keep = false;
       if (keep) best_push(bst, total(lt, ld, w), idx);
     }
   }
@@ -1505,6 +1519,16 @@ enum TreeAction : uint32_t {
 struct TreeState {
   int node, round, len;
   float A, Bv, zt2, zd2;
+  float An;  // A for the pass after a rejection
+  float qd;  // without replacement: q's mass on the siblings drawn so far
+};
+
+// Without replacement, per sibling i rejected at the current node: its token,
+// its p and q, and F, the value of (p - A q)_+ it keeps once drawn (it leaves
+// q, so later rounds no longer subtract from it).
+struct TreeDrawn {
+  int32_t* x;
+  float *p, *q, *F;
 };
 
 // All threads: the children of node v in index order into kids[0 .. *nkids)
@@ -1544,11 +1568,16 @@ __device__ void tree_children(int N, const int32_t* par, int v, int32_t* kids, i
 // whether each node has children; tok_s, this sequence's node tokens; part,
 // the W workgroups' parts of the action just carried out (w0, w1 per
 // workgroup). tree_bad, tok_bad: the checks of the tree and of the tokens,
-// made by the whole workgroup while staging them.
+// made by the whole workgroup while staging them. dr: the siblings drawn at
+// the current node (without replacement only).
+// Without replacement, round j's q is q s over the tokens not drawn yet, with
+// s = 1 / (1 - mass of the drawn ones): a rejection moves A to A + B s, and the
+// drawn tokens keep the values F they had then (the pass's sum is corrected
+// for them with their gathered logits).
 template <bool BF16>
 __device__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, TreeState& s, const int32_t* kids,
                                 int nkids, const uint8_t* haskid, const int32_t* tok_s, const uint64_t (*part)[2],
-                                int tree_bad, int tok_bad, bool writer) {
+                                int tree_bad, int tok_bad, bool writer, const TreeDrawn& dr) {
   using E = Elem<BF16>;
   const ChainArgs& a = ta.c;
   const float T = a.temperature[b];
@@ -1559,6 +1588,8 @@ __device__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, 
     s.round = 0;
     s.A = 0.0f;
     s.Bv = 1.0f;
+    s.An = 0.0f;
+    s.qd = 0.0f;
     s.zt2 = s.zd2 = 0.0f;
   };
   if (prev == TA_NONE) {
@@ -1599,10 +1630,14 @@ __device__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, 
   } else {
     float S = 0.0f;
     for (int w = 0; w < ta.W; ++w) S += __uint_as_float((uint32_t)part[w][0]);
+    const int r = s.round;  // the sibling just rejected
+    if (ta.wor)
+      for (int i = 0; i < r; ++i) S += dr.F[i] - fmaxf(0.0f, dr.p[i] - s.An * dr.q[i]);
     if (S > 0.0f) {  // (a residual of zero mass leaves p as it was)
-      s.A = s.A + s.Bv;
+      s.A = s.An;
       s.Bv = S;
     }
+    if (ta.wor) dr.F[r] = fmaxf(0.0f, dr.p[r] - s.A * dr.q[r]);
     s.round += 1;
   }
   const int c = s.round < nkids ? kids[s.round] : -1;
@@ -1615,12 +1650,13 @@ __device__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, 
   const int x = tok_s[c];
   const float lt = E::load(target_row(a, b, s.node), x), ld = E::load(draft_row(a, b, s.node), x);
   const float lp2 = __builtin_fmaf(lt, c2, -s.zt2), lq2 = __builtin_fmaf(ld, c2, -s.zd2);
+  const float p = fast_exp2(lp2), q = fast_exp2(lq2);
+  const float sfac = (ta.wor && s.qd > 0.0f) ? 1.0f / (1.0f - s.qd) : 1.0f;
   float acc;
-  if (s.A == 0.0f && s.Bv == 1.0f) {
+  if (s.A == 0.0f && s.Bv == 1.0f && sfac == 1.0f) {
     acc = fast_exp2(fminf(0.0f, lp2 - lq2));  // min(1, p/q), as the chains compute it
   } else {
-    const float p = fast_exp2(lp2), q = fast_exp2(lq2);
-    acc = q > 0.0f ? fminf(1.0f, fmaxf(0.0f, p - s.A * q) / (s.Bv * q)) : 1.0f;
+    acc = q > 0.0f ? fminf(1.0f, fmaxf(0.0f, p - s.A * q) / (s.Bv * q * sfac)) : 1.0f;
   }
   const Words4 wu = philox10((uint32_t)s.round, (uint32_t)s.node, (uint32_t)b, a.ctr_accept, a.key0, a.key1);
   if (uniform_accept(wu.w[0]) < acc) {
@@ -1631,7 +1667,14 @@ __device__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, 
     // draw.
     return haskid[c] ? TA_STATS : TA_DRAW_BONUS;
   }
-  return TA_PASS;  // the mass of (p - (A + B) q)_+ at this node
+  if (ta.wor) {
+    dr.x[s.round] = x;
+    dr.p[s.round] = p;
+    dr.q[s.round] = q;
+    s.qd += q;
+  }
+  s.An = s.A + s.Bv * sfac;
+  return TA_PASS;  // the mass of (p - A' q)_+ at this node, A' = s.An
 }
 
 // This workgroup's part of sum_v (p(v) - A q(v))_+ over [lo, hi), with the
@@ -1681,9 +1724,12 @@ __device__ float residual_mass_part(const uint8_t* rt, const uint8_t* rd, int lo
 // parts merged in workgroup order, lowest index on ties), the outputs, and the
 // sequence's workspace returned to zero. parts: the draw's slot buffer;
 // both_buffers: whether earlier actions used the other one too.
+// ndrawn > 0 (a residual draw without replacement): the siblings drawn before
+// the last one took no part in the row's draw; each competes with its kept
+// value F instead (ln F plus its noise, keyed as the row's).
 template <bool BF16, bool VEC>
 __device__ void tree_finish(const TreeSampleArgs& ta, int b, int len, const P2Slot* parts, bool both_buffers,
-                            Smem& sm) {
+                            int node, int ndrawn, const TreeDrawn& dr, Smem& sm) {
   const ChainArgs& a = ta.c;
   if (threadIdx.x == 0) {
     ArgMax m;
@@ -1694,6 +1740,15 @@ __device__ void tree_finish(const TreeSampleArgs& ta, int b, int len, const P2Sl
       ArgMax o;
       o.v = hi_f(w0);
       o.i = (int)lo_u(w0);
+      m = argmax_merge(m, o);
+    }
+    for (int i = 0; i < ndrawn; ++i) {
+      if (!(dr.F[i] > 0.0f)) continue;
+      const int x = dr.x[i];
+      ArgMax o;
+      o.v = logf(dr.F[i]) +
+            gumbel(word_at(philox10((uint32_t)x >> 2, (uint32_t)node, (uint32_t)b, a.ctr_noise, a.key0, a.key1), x & 3));
+      o.i = x;
       m = argmax_merge(m, o);
     }
     xput(&ta.out_token[b], m.i);
@@ -1733,6 +1788,13 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   __shared__ int32_t s_nkids, s_wcnt[kThreads / 64];
   __shared__ TreeState s_state;
   __shared__ uint32_t s_action;
+  __shared__ int32_t s_dx[kMaxTreeNodes];
+  __shared__ float s_dp[kMaxTreeNodes], s_dq[kMaxTreeNodes], s_dF[kMaxTreeNodes];
+  TreeDrawn dr;
+  dr.x = s_dx;
+  dr.p = s_dp;
+  dr.q = s_dq;
+  dr.F = s_dF;
   int tree_bad = 0, tok_bad = 0;
   for (int k = threadIdx.x; k < ta.N; k += kThreads) {
     const int pk = ta.parents[k], dk = ta.depth[k], xk = ta.tokens[(int64_t)b * ta.N + k];
@@ -1751,10 +1813,17 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   for (int k = 1 + (int)threadIdx.x; k < ta.N; k += kThreads)
     if (s_par[k] >= 0 && s_par[k] < ta.N) s_haskid[s_par[k]] = 1;
   __syncthreads();
+  if (ta.wor) {
+    // Without replacement, siblings carry distinct tokens.
+    int dup = 0;
+    for (int k = 1 + (int)threadIdx.x; k < ta.N; k += kThreads)
+      for (int k2 = 1; k2 < k; ++k2) dup |= s_par[k2] == s_par[k] && s_tok[k2] == s_tok[k];
+    tok_bad |= __syncthreads_or(dup);
+  }
   // The first decisions need no part of any workgroup.
   if (threadIdx.x == 0) {
     TreeState s0;
-    s_action = tree_decide<BF16>(ta, b, TA_NONE, s0, s_kids, 0, s_haskid, s_tok, nullptr, tree_bad, tok_bad, w == 0);
+    s_action = tree_decide<BF16>(ta, b, TA_NONE, s0, s_kids, 0, s_haskid, s_tok, nullptr, tree_bad, tok_bad, w == 0, dr);
     s_state = s0;
     sm.lkey = 0u;
   }
@@ -1793,7 +1862,7 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
       part.w0 = pack(lt.M, __float_as_uint(lt.s));
       part.w1 = pack(ld.M, __float_as_uint(ld.s));
     } else if (action == TA_PASS) {
-      const float zd2s = t.zd2 - fast_log2(t.A + t.Bv);
+      const float zd2s = t.zd2 - fast_log2(t.An);
       partial = block_sum(residual_mass_part<BF16, VEC>(target_row(a, b, t.node), draft_row(a, b, t.node), lo, hi, c2,
                                                         t.zt2, zd2s),
                           sm);
@@ -1811,11 +1880,16 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
       d.a_row = 0.0f;
       d.tok = -1;
       d.mode = action == TA_DRAW_RESIDUAL ? P2_RESIDUAL : P2_BONUS;
+      // Without replacement, the siblings drawn before the last one keep
+      // their own values: they are drawn apart, at the finish.
+      const int nx = (ta.wor && action == TA_DRAW_RESIDUAL) ? t.round - 1 : 0;
       if (BF16 && VEC) {
-        if (action == TA_DRAW_RESIDUAL) gumbel_chunk_bf16<P2_RESIDUAL, false>(a, b, d, lo, hi, sm, &part);
+        if (nx > 0) gumbel_chunk_bf16<P2_RESIDUAL, false, true>(a, b, d, lo, hi, sm, &part, s_dx, nx);
+        else if (action == TA_DRAW_RESIDUAL) gumbel_chunk_bf16<P2_RESIDUAL, false>(a, b, d, lo, hi, sm, &part);
         else gumbel_chunk_bf16<P2_BONUS, false>(a, b, d, lo, hi, sm, &part);
       } else {
-        if (action == TA_DRAW_RESIDUAL) gumbel_chunk<BF16, VEC, P2_RESIDUAL>(a, b, d, lo, hi, sm, &part);
+        if (nx > 0) gumbel_chunk<BF16, VEC, P2_RESIDUAL, true>(a, b, d, lo, hi, sm, &part, s_dx, nx);
+        else if (action == TA_DRAW_RESIDUAL) gumbel_chunk<BF16, VEC, P2_RESIDUAL>(a, b, d, lo, hi, sm, &part);
         else gumbel_chunk<BF16, VEC, P2_BONUS>(a, b, d, lo, hi, sm, &part);
       }
     }
@@ -1836,7 +1910,10 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
     }
     __syncthreads();
     if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) {
-      if (sm.flag_last) tree_finish<BF16, VEC>(ta, b, t.len, parts, epoch > 0u, sm);
+      if (sm.flag_last) {
+        const int nx = (ta.wor && action == TA_DRAW_RESIDUAL) ? t.round - 1 : 0;
+        tree_finish<BF16, VEC>(ta, b, t.len, parts, epoch > 0u, t.node, nx > 0 ? nx : 0, dr, sm);
+      }
       return;
     }
     // Wait until all W have arrived (bounded).
@@ -1865,7 +1942,7 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
     __syncthreads();
     if (threadIdx.x == 0) {
       TreeState s1 = s_state;
-      s_action = tree_decide<BF16>(ta, b, action, s1, s_kids, s_nkids, s_haskid, s_tok, sm.u.slot, 0, 0, w == 0);
+      s_action = tree_decide<BF16>(ta, b, action, s1, s_kids, s_nkids, s_haskid, s_tok, sm.u.slot, 0, 0, w == 0, dr);
       s_state = s1;
       sm.lkey = 0u;
     }

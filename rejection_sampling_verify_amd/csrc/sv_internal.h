@@ -123,6 +123,7 @@ struct TreeSampleArgs {
   int32_t W, wlen;         // walk: workgroups per sequence, elements per workgroup
   int32_t b_base, b_count; // walk: the sequences of this launch
   P2Slot* slot2;           // walk: the second buffer of workgroup parts, [B, c.p2_stride] (N >= 2)
+  int32_t wor;             // siblings drawn without replacement (q renormalized over the tokens not drawn yet)
   int32_t* out_path;       // [B, max_depth + 1]
   int32_t* out_len;        // [B]
   int32_t* out_token;      // [B]

@@ -123,12 +123,12 @@ def test_tree_sample_argument_validation(L):
     ts = lambda **k: L.spec_verify_tree_sample(k.get("t", P), k.get("ts", 100), k.get("d", P), k.get("ds", 100),
                                                k.get("dt", 1), k.get("par", P), P, P, k.get("temp", P),
                                                k.get("B", 2), k.get("N", 5), k.get("V", 100), k.get("md", 3),
-                                               0, k.get("off", 0), P, P, P, k.get("ws", P), k.get("wsb", f.nbytes),
-                                               None)
+                                               0, k.get("off", 0), k.get("wor", 0), P, P, P, k.get("ws", P),
+                                               k.get("wsb", f.nbytes), None)
     assert ts(d=None) == 1 and ts(temp=None) == 1 and ts(par=None) == 1
     assert ts(N=0) == 2 and ts(N=1025) == 2 and ts(md=5) == 2 and ts(md=-1) == 2 and ts(B=-1) == 2
     assert ts(dt=2) == 3
-    assert ts(ts=99) == 4 and ts(ds=99) == 4 and ts(off=1 << 31) == 4
+    assert ts(ts=99) == 4 and ts(ds=99) == 4 and ts(off=1 << 31) == 4 and ts(wor=2) == 4
     assert ts(wsb=10) == 5
     assert ts(B=0) == 0
 

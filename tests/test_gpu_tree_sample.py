@@ -33,7 +33,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _run(inp, dev, seed=0, offset=0, workspace=None, temperature=None, parents=None, tokens=None):
+def _run(inp, dev, seed=0, offset=0, workspace=None, temperature=None, parents=None, tokens=None, wor=False):
     import rejection_sampling_verify_amd as rsv
     t = to_dev(inp.target, torch, dev)
     d = to_dev(inp.draft, torch, dev)
@@ -42,7 +42,7 @@ def _run(inp, dev, seed=0, offset=0, workspace=None, temperature=None, parents=N
     tok = torch.from_numpy(inp.node_tokens if tokens is None else tokens).to(dev)
     temp = torch.from_numpy(inp.temperature if temperature is None else temperature).to(dev)
     path, plen, token = rsv.spec_verify_tree_sample(t, d, par, dep, tok, temp, inp.max_depth, seed=seed,
-                                                    offset=offset, workspace=workspace)
+                                                    offset=offset, workspace=workspace, without_replacement=wor)
     torch.cuda.synchronize()
     return {"path": path.cpu().numpy(), "path_len": plen.cpu().numpy(), "token": token.cpu().numpy()}
 
@@ -65,11 +65,11 @@ def _compare(got, ref, label):
     return excused
 
 
-def _oracle(inp, seed=0, offset=0, temperature=None, parents=None, tokens=None):
+def _oracle(inp, seed=0, offset=0, temperature=None, parents=None, tokens=None, wor=False):
     return oracle.verify_tree_sample(inp.target, inp.draft, inp.parents if parents is None else parents, inp.depth,
                                      inp.node_tokens if tokens is None else tokens,
                                      inp.temperature if temperature is None else temperature, inp.max_depth,
-                                     seed=seed, offset=offset)
+                                     seed=seed, offset=offset, without_replacement=wor)
 
 
 def _random_tree(rng, N, branching=(1, 4)):
@@ -203,3 +203,46 @@ def test_smallest_trees_and_vocabularies(dev, N, V):
         assert int(ws.count_nonzero().item()) == 0
     if N == 1:
         assert np.all(got["path_len"] == 1)
+
+
+# Siblings drawn without replacement: each round's q is q over the tokens not
+# drawn yet, renormalized; drawn siblings keep their residual values.
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_tree_sample_without_replacement_parity(dev, name):
+    B, N, V, bf16, temps, seed = CASES[name]
+    rng = np.random.default_rng(seed + 100)
+    parents, depth = _random_tree(rng, N)
+    inp = make_tree_sample(name + "_wor", B, V, parents, depth, bf16=bf16, seed=seed + 100, temperatures=temps,
+                           target_sigma=2.0, zipf=0.0 if not bf16 else 1.1, draft_sigma=(0.3, 1.5),
+                           without_replacement=True)
+    for s_, off in ((0, 0), (9, 4)):
+        got = _run(inp, dev, seed=s_, offset=off, wor=True)
+        ref = _oracle(inp, seed=s_, offset=off, wor=True)
+        _compare(got, ref, "%s without replacement seed %d" % (name, s_))
+    assert np.any(ref["rejections"] >= 2)  # drawn siblings kept apart in passes and draws
+
+
+def test_without_replacement_full_size_and_rules(dev):
+    """The 65-node workload's shape with siblings drawn without replacement;
+    duplicate siblings are a bad token only in this mode; one child per node
+    verifies as with replacement."""
+    import rejection_sampling_verify_amd as rsv
+    parents, depth = workloads.tree_c5_structure()
+    inp = make_tree_sample("c5_wor", 32, 128256, parents, depth, bf16=True, seed=2100, without_replacement=True)
+    ws = rsv.Workspace(dev).get(32, len(parents), 128256)
+    got = _run(inp, dev, seed=1, workspace=ws, wor=True)
+    _compare(got, _oracle(inp, seed=1, wor=True), "c5 without replacement")
+    assert int(ws.count_nonzero().item()) == 0
+    tok = inp.node_tokens.copy()
+    tok[3, 2] = tok[3, 1]  # two children of the root with one token
+    got = _run(inp, dev, seed=1, tokens=tok, wor=True)
+    assert got["path_len"][3] == -1
+    _compare(got, _oracle(inp, seed=1, tokens=tok, wor=True), "duplicate siblings")
+    got_iid = _run(inp, dev, seed=1, tokens=tok)
+    assert got_iid["path_len"][3] >= 1
+    chain = make_tree_sample("chain_wor", 16, 3000, np.arange(-1, 5, dtype=np.int32), np.arange(6, dtype=np.int32),
+                             bf16=True, seed=2101, temperatures=(0.8, 1.2), without_replacement=True)
+    a = _run(chain, dev, seed=3)
+    b = _run(chain, dev, seed=3, wor=True)
+    assert all(np.array_equal(a[k], b[k]) for k in ("path", "path_len", "token"))

@@ -308,8 +308,10 @@ def make_tree(name: str, B: int, V: int, parents: np.ndarray, depth: np.ndarray,
 
 def make_tree_sample(name: str, B: int, V: int, parents: np.ndarray, depth: np.ndarray, *, bf16: bool,
                      seed: int, temperatures=(0.7, 1.0), target_sigma: float = 3.0, zipf: float = 1.1,
-                     draft_sigma=(0.2, 2.0), workers=None) -> TreeSampleInputs:
-    """Sampled-tree inputs: children are i.i.d. draws from q at their parent."""
+                     draft_sigma=(0.2, 2.0), workers=None, without_replacement: bool = False) -> TreeSampleInputs:
+    """Sampled-tree inputs: children are i.i.d. draws from q at their parent,
+    or (without_replacement) a draw without replacement in index order: the
+    top-k of the Gumbel-perturbed draft scores, in order of perturbed score."""
     N = len(parents)
     dt = np.uint16 if bf16 else np.float32
     target = np.empty((B, N, V), dt)
@@ -334,6 +336,14 @@ def make_tree_sample(name: str, B: int, V: int, parents: np.ndarray, depth: np.n
                 draft[b, v] = round_bf16(d) if bf16 else d
         tokens[b, 0] = int(rng.integers(V))
         q_vals = stored_values(draft[b])
+        if without_replacement:
+            for v in inner:
+                kids = [c for c in range(1, N) if parents[c] == v]
+                y = q_vals[v].astype(np.float64) / T + rng.gumbel(size=V)
+                order = np.argsort(-y, kind="stable")[:len(kids)]
+                for c, x in zip(kids, order):
+                    tokens[b, c] = int(x)
+            return
         for c in range(1, N):
             tokens[b, c] = _draw_from_logits(rng, q_vals[parents[c]], T)
 
