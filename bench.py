@@ -95,7 +95,8 @@ def cpu_baseline(inp, is_tree: bool, positions_per_step: int, threads: int | Non
         if isinstance(inp, workloads.TreeSampleInputs):
             oracle.verify_tree_sample(inp.target, inp.draft, inp.parents, inp.depth, inp.node_tokens,
                                       inp.temperature, inp.max_depth, seed=inp.seed, offset=inp.offset,
-                                      nthreads=threads)
+                                      nthreads=threads,
+                                      without_replacement=inp.meta.get("without_replacement", False))
         elif is_tree:
             oracle.verify_tree(inp.target, inp.parents, inp.depth, inp.node_tokens, inp.max_depth, nthreads=threads)
         else:
@@ -406,7 +407,8 @@ def main():
             if sampled_tree:
                 rsv.spec_verify_tree_sample(c["t"], c["d"], c["par"], c["dep"], c["tok"], c["temp"], inp.max_depth,
                                             seed=inp.seed, offset=inp.offset, out_path=out[0], out_path_len=out[1],
-                                            out_token=out[2], workspace=wbuf)
+                                            out_token=out[2], workspace=wbuf,
+                                            without_replacement=inp.meta.get("without_replacement", False))
             else:
                 rsv.spec_verify_tree(c["t"], c["par"], c["dep"], c["tok"], inp.max_depth, out_path=out[0],
                                      out_path_len=out[1], out_bonus=out[2], workspace=wbuf)
@@ -469,6 +471,8 @@ def main():
         extra = {}
         if sampled_tree:
             cfg["verify"] = "sampled tree (multi-round rejection sampling)"
+            if inp.meta.get("without_replacement"):
+                cfg["verify"] += ", siblings drawn without replacement"
             cfg["temperatures"] = sorted(set(float(x) for x in inp.temperature))
             plen = out[1].cpu().numpy()
             extra = {"mean_accepted_depth": float(np.mean(plen[plen >= 1] - 1)),

@@ -23,6 +23,8 @@ and, for sampled tree verification (multi-round rejection sampling):
       target as chain_bf16_llama's, draft row of each inner node = target +
       N(0, sigma_b^2), sigma_b ~ U[0.2, 2]; children drawn i.i.d. from q at
       their parent.
+  tree_sample_wor_bf16_llama  the same, with each node's children drawn
+      without replacement (the top-k of the Gumbel-perturbed draft scores).
 and, for the KV-cache rollback after a verify step:
   kv_rollback_bf16_llama  K and V caches [L=32, B=32, H=8, S=4096, D=128] bf16
       (the KV layout of a 32-layer model with 8 KV heads of dimension 128),
@@ -49,7 +51,8 @@ import numpy as np
 CONFIGS = ["chain_f32_small", "chain_bf16_peaked", "chain_bf16_llama", "onehot_bf16_qwen",
            "tree_bf16_llama"]
 CONFIG_INDEX = {name: k for k, name in enumerate(CONFIGS)}
-EXTRA = ["tree_sample_bf16_llama", "kv_rollback_bf16_llama", "ngram_draft_qwen", "tree_mask_b256"]
+EXTRA = ["tree_sample_bf16_llama", "kv_rollback_bf16_llama", "ngram_draft_qwen", "tree_mask_b256",
+         "tree_sample_wor_bf16_llama"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -349,7 +352,7 @@ def make_tree_sample(name: str, B: int, V: int, parents: np.ndarray, depth: np.n
 
     _parallel(one, B, workers)
     return TreeSampleInputs(name, target, draft, np.asarray(parents, np.int32), np.asarray(depth, np.int32),
-                            tokens, temp, int(np.max(depth)), meta={"V": V})
+                            tokens, temp, int(np.max(depth)), meta={"V": V, "without_replacement": without_replacement})
 
 
 def make(name: str, workers=None):
@@ -619,6 +622,10 @@ def make_extra(name: str, workers=None):
         return make_ngram(name, 512, 152064, (2048, 16384), ngram=3, gamma=6, pad=True, seed=seed)
     if name == "tree_mask_b256":
         return make_tree_mask(name, 256, 65, seed=seed)
+    if name == "tree_sample_wor_bf16_llama":
+        parents, depth = _c5_tree()
+        return make_tree_sample(name, 32, 128256, parents, depth, bf16=True, seed=seed, workers=workers,
+                                without_replacement=True)
     raise KeyError(name)
 
 
