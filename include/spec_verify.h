@@ -269,6 +269,19 @@ sv_status_t sv_tree_mask(const int32_t* parents, int64_t parents_stride, int32_t
                          const int32_t* position_offset, uint8_t* out_mask, uint32_t* out_mask_bits,
                          int32_t* out_position_ids, void* stream);
 
+/* sv_kv_rollback_layers — sv_kv_rollback for caches kept as one tensor per
+ * layer (the page's key_cache[l] / value_cache[l]).
+ *   k_layers, v_layers: DEVICE arrays of L device pointers, each to a
+ *     contiguous, 16-byte aligned [B, H, S, D] cache of elem_bytes elements
+ *     (the caller's to keep valid for the call); v_layers may be NULL.
+ *   Everything else, the in-place move and the status codes are as for
+ *   sv_kv_rollback (the layer pointers themselves cannot be checked on the
+ *   host: a misaligned one is the caller's error). */
+sv_status_t sv_kv_rollback_layers(void* const* k_layers, void* const* v_layers, int32_t elem_bytes, int32_t L,
+                                  int32_t B, int32_t H, int32_t S, int32_t D, const int32_t* root_pos,
+                                  const int32_t* path, int32_t P, const int32_t* path_len, int32_t* cache_len,
+                                  void* stream);
+
 /* sv_ngram_draft — prompt-lookup / n-gram drafting: one-hot draft proposals
  * copied from earlier in each sequence ("7.6 Speculative Decoding", Exercise
  * 4; "Self-Speculative Decoding", "Copying, verified against plain greedy").

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     spec_verify_tree,
     spec_verify_tree_sample,
     sv_kv_rollback,
+    sv_kv_rollback_layers,
     sv_ngram_draft,
     sv_tree_mask,
     sv_debug_noise,

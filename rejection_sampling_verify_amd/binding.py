@@ -22,7 +22,7 @@ SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback", "sv_ngram_draft", "sv_tree_mask", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
+           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback", "sv_kv_rollback_layers", "sv_ngram_draft", "sv_tree_mask", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
            "sv_debug_read_stream"]
 
 _lib = None
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_tree_sample.restype = ctypes.c_int
         L.sv_kv_rollback.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
         L.sv_kv_rollback.restype = ctypes.c_int
+        L.sv_kv_rollback_layers.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
+        L.sv_kv_rollback_layers.restype = ctypes.c_int
         L.sv_ngram_draft.argtypes = [P, i64, P, i32, i32, i32, i32, P, P, P, P]
         L.sv_ngram_draft.restype = ctypes.c_int
         L.sv_tree_mask.argtypes = [P, i64, i32, i32, P, P, P, P, P]
@@ -307,6 +309,40 @@ def sv_kv_rollback(k_cache, v_cache, root_pos, path, path_len, cache_len=None, s
                               _ptr(cache_len), _stream(stream))
     if st != 0:
         raise SVError(st, "sv_kv_rollback")
+    return cache_len
+
+
+def sv_kv_rollback_layers(k_layers, v_layers, root_pos, path, path_len, cache_len=None, stream=None):
+    """sv_kv_rollback for caches kept as one tensor per layer: k_layers (and
+    v_layers, or None) are lists of contiguous device tensors [B, H, S, D],
+    all of one shape and dtype, 16-byte aligned. Returns cache_len [B]."""
+    import torch
+    if not k_layers:
+        raise ValueError("k_layers must hold at least one layer")
+    ref = k_layers[0]
+    layers = list(k_layers) + (list(v_layers) if v_layers is not None else [])
+    if v_layers is not None and len(v_layers) != len(k_layers):
+        raise ValueError("v_layers must have as many layers as k_layers")
+    for t in layers:
+        if (t.dim() != 4 or tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype or not t.is_contiguous()
+                or not t.is_cuda or t.data_ptr() % 16 != 0):
+            raise ValueError("every layer must be a contiguous, 16-byte aligned CUDA tensor of one shape and dtype")
+    B, H, S, D = ref.shape
+    _check_i32(root_pos, (B,), "root_pos")
+    _check_i32(path_len, (B,), "path_len")
+    if path.dim() != 2 or path.shape[0] != B:
+        raise ValueError("path must be [B, P]")
+    _check_i32(path, tuple(path.shape), "path")
+    dev = ref.device
+    kp = torch.tensor([t.data_ptr() for t in k_layers], dtype=torch.int64, device=dev)
+    vp = torch.tensor([t.data_ptr() for t in v_layers], dtype=torch.int64, device=dev) if v_layers is not None else None
+    if cache_len is None:
+        cache_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = lib().sv_kv_rollback_layers(_ptr(kp), _ptr(vp), ref.element_size(), len(k_layers), B, H, S, D,
+                                     _ptr(root_pos), _ptr(path), int(path.shape[1]), _ptr(path_len), _ptr(cache_len),
+                                     _stream(stream))
+    if st != 0:
+        raise SVError(st, "sv_kv_rollback_layers")
     return cache_len
 
 

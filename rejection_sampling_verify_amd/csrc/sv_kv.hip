@@ -26,8 +26,10 @@ constexpr int kKvMaxPath = 1024;    // path entries staged in LDS (a tree has at
 constexpr int kKvMaxRowBytes = 16384;
 
 struct KvArgs {
-  uint8_t* k;  // [L, B, H, S, D] elements of elem bytes
+  uint8_t* k;  // [L, B, H, S, D] elements of elem bytes (stacked layers)
   uint8_t* v;  // same layout, or NULL
+  const uint64_t* k_layers;  // or: device array of L pointers to [B, H, S, D] caches
+  const uint64_t* v_layers;  // same, or NULL
   int32_t B, H, S;
   int32_t vpr;              // 16-byte vectors per row (D * elem / 16)
   const int32_t* root;      // [B]
@@ -37,6 +39,9 @@ struct KvArgs {
   int32_t* cache_len;       // [B] out
 };
 
+// LAYERS: each layer's cache is its own allocation, found in k_layers /
+// v_layers; else the layers are stacked in k / v.
+template <bool LAYERS>
 __global__ __launch_bounds__(kKvThreads) void kv_rollback_kernel(KvArgs a) {
   extern __shared__ int32_t s_path[];  // [P]
   const int64_t lb = blockIdx.x;       // (l, b), b fastest
@@ -65,7 +70,14 @@ __global__ __launch_bounds__(kKvThreads) void kv_rollback_kernel(KvArgs a) {
   const int items = a.H * per_head;  // (head, node, vector), vector fastest; < 2^31 (checked on the host)
   const int64_t row_bytes = (int64_t)vpr * 16;
   const int64_t head_bytes = (int64_t)a.S * row_bytes;
-  const int64_t lb_off = lb * a.H * head_bytes + (int64_t)r * row_bytes;
+  uint8_t* kbase = a.k;
+  uint8_t* vbase = a.v;
+  int64_t lb_off = lb * a.H * head_bytes + (int64_t)r * row_bytes;
+  if (LAYERS) {
+    kbase = (uint8_t*)a.k_layers[l];
+    vbase = a.v_layers ? (uint8_t*)a.v_layers[l] : nullptr;
+    lb_off = (int64_t)b * a.H * head_bytes + (int64_t)r * row_bytes;
+  }
   for (int i0 = 0; i0 < items; i0 += kKvThreads * kKvPerLane) {
     kv_u32x4 qk[kKvPerLane], qv[kKvPerLane];
     int64_t dst[kKvPerLane];
@@ -84,8 +96,8 @@ __global__ __launch_bounds__(kKvThreads) void kv_rollback_kernel(KvArgs a) {
         dst[j] = base + (int64_t)k * row_bytes;
         if (act[j]) {
           const int64_t src = base + (int64_t)p * row_bytes;
-          qk[j] = *(const kv_u32x4*)(a.k + src);
-          if (a.v) qv[j] = *(const kv_u32x4*)(a.v + src);
+          qk[j] = *(const kv_u32x4*)(kbase + src);
+          if (vbase) qv[j] = *(const kv_u32x4*)(vbase + src);
         }
       }
     }
@@ -93,8 +105,8 @@ __global__ __launch_bounds__(kKvThreads) void kv_rollback_kernel(KvArgs a) {
 #pragma unroll
     for (int j = 0; j < kKvPerLane; ++j) {
       if (act[j]) {
-        *(kv_u32x4*)(a.k + dst[j]) = qk[j];
-        if (a.v) *(kv_u32x4*)(a.v + dst[j]) = qv[j];
+        *(kv_u32x4*)(kbase + dst[j]) = qk[j];
+        if (vbase) *(kv_u32x4*)(vbase + dst[j]) = qv[j];
       }
     }
     __syncthreads();
@@ -104,37 +116,66 @@ __global__ __launch_bounds__(kKvThreads) void kv_rollback_kernel(KvArgs a) {
 }  // namespace
 }  // namespace sv
 
+namespace {
+
+// Checks shared by both entry points, then the launch.
+sv_status_t kv_launch(sv::KvArgs a, int32_t elem_bytes, int32_t L, int32_t B, int32_t H, int32_t S, int32_t D,
+                      int32_t P, bool layers, void* stream) {
+  if (!a.root || !a.path || !a.path_len || !a.cache_len) return SV_ERR_NULL_ARG;
+  if (L < 0 || B < 0 || H < 0 || S < 1 || D < 1 || P < 1 || P > sv::kKvMaxPath) return SV_ERR_BAD_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return SV_ERR_BAD_DTYPE;
+  // Rows move as 16-byte vectors: a row is a whole number of them.
+  const int64_t row_bytes = (int64_t)D * elem_bytes;
+  if (row_bytes % 16 != 0 || row_bytes > sv::kKvMaxRowBytes) return SV_ERR_BAD_SHAPE;
+  const int64_t groups = (int64_t)L * B;
+  if (groups >= (1ll << 31) || (int64_t)H * P * (row_bytes / 16) >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
+  if (groups == 0 || H == 0) return SV_OK;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.vpr = (int32_t)(row_bytes / 16);
+  a.P = P;
+  const dim3 grid((unsigned)groups), block(sv::kKvThreads);
+  if (layers)
+    hipLaunchKernelGGL(sv::kv_rollback_kernel<true>, grid, block, P * sizeof(int32_t), (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(sv::kv_rollback_kernel<false>, grid, block, P * sizeof(int32_t), (hipStream_t)stream, a);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 sv_status_t sv_kv_rollback(void* k_cache, void* v_cache, int32_t elem_bytes, int32_t L, int32_t B, int32_t H,
                            int32_t S, int32_t D, const int32_t* root_pos, const int32_t* path, int32_t P,
                            const int32_t* path_len, int32_t* cache_len, void* stream) {
-  if (!k_cache || !root_pos || !path || !path_len || !cache_len) return SV_ERR_NULL_ARG;
-  if (L < 0 || B < 0 || H < 0 || S < 1 || D < 1 || P < 1 || P > sv::kKvMaxPath) return SV_ERR_BAD_SHAPE;
-  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4) return SV_ERR_BAD_DTYPE;
-  // Rows move as 16-byte vectors: a row is a whole number of them and the
-  // caches are 16-byte aligned.
-  const int64_t row_bytes = (int64_t)D * elem_bytes;
-  if (row_bytes % 16 != 0 || row_bytes > sv::kKvMaxRowBytes) return SV_ERR_BAD_SHAPE;
+  if (!k_cache) return SV_ERR_NULL_ARG;
+  // The caches are 16-byte aligned.
   if ((uintptr_t)k_cache % 16 != 0 || (uintptr_t)v_cache % 16 != 0) return SV_ERR_BAD_ARG;
-  const int64_t groups = (int64_t)L * B;
-  if (groups >= (1ll << 31) || (int64_t)H * P * (row_bytes / 16) >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
-  if (groups == 0 || H == 0) return SV_OK;
-  sv::KvArgs a;
+  sv::KvArgs a = {};
   a.k = (uint8_t*)k_cache;
   a.v = (uint8_t*)v_cache;
-  a.B = B;
-  a.H = H;
-  a.S = S;
-  a.vpr = (int32_t)(row_bytes / 16);
   a.root = root_pos;
   a.path = path;
-  a.P = P;
   a.path_len = path_len;
   a.cache_len = cache_len;
-  hipLaunchKernelGGL(sv::kv_rollback_kernel, dim3((unsigned)groups), dim3(sv::kKvThreads), P * sizeof(int32_t),
-                     (hipStream_t)stream, a);
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+  return kv_launch(a, elem_bytes, L, B, H, S, D, P, false, stream);
+}
+
+sv_status_t sv_kv_rollback_layers(void* const* k_layers, void* const* v_layers, int32_t elem_bytes, int32_t L,
+                                  int32_t B, int32_t H, int32_t S, int32_t D, const int32_t* root_pos,
+                                  const int32_t* path, int32_t P, const int32_t* path_len, int32_t* cache_len,
+                                  void* stream) {
+  if (!k_layers) return SV_ERR_NULL_ARG;
+  sv::KvArgs a = {};
+  a.k_layers = (const uint64_t*)k_layers;
+  a.v_layers = (const uint64_t*)v_layers;
+  a.root = root_pos;
+  a.path = path;
+  a.path_len = path_len;
+  a.cache_len = cache_len;
+  return kv_launch(a, elem_bytes, L, B, H, S, D, P, true, stream);
 }
 
 }  // extern "C"

@@ -145,6 +145,9 @@ def test_kv_rollback_argument_validation(L):
     assert kv(es=3) == 3
     assert kv(k=ctypes.c_void_p(P.value + 8)) == 4
     assert kv(L=0) == 0 and kv(H=0) == 0
+    kl = lambda **k: L.sv_kv_rollback_layers(k.get("k", P), None, 2, 2, 2, 2, 8, k.get("D", 64), k.get("root", P), P, 4,
+                                             P, P, None)
+    assert kl(k=None) == 1 and kl(root=None) == 1 and kl(D=7) == 2
 
 
 def test_ngram_argument_validation(L):

@@ -137,3 +137,27 @@ def test_kv_rollback_named_workload_full_size(dev):
     print("[kv parity] full size: %d slabs ok, moved rows per layer-head %d" % (len(slabs),
                                                                             int(inp.moved_rows().sum())),
           flush=True)
+
+
+def test_kv_rollback_per_layer_tensors(dev):
+    """Caches kept as one tensor per layer (the page's key_cache[l]): the same
+    result as the oracle on the stacked layers."""
+    import rejection_sampling_verify_amd as rsv
+    inp = make_kv_rollback("layers", 3, 7, 2, 96, 64, elem_bytes=2, seed=33, kind="tree", parents=_tree())
+    k_host, v_host = inp.cache_host(0), inp.cache_host(1)
+    ks = [torch.from_numpy(k_host[l].copy()).to(dev) for l in range(3)]
+    vs = [torch.from_numpy(v_host[l].copy()).to(dev) for l in range(3)]
+    n = rsv.sv_kv_rollback_layers(ks, vs, torch.from_numpy(inp.root).to(dev), torch.from_numpy(inp.path).to(dev),
+                                  torch.from_numpy(inp.path_len).to(dev))
+    torch.cuda.synchronize()
+    ref_k, ref_len = okv.kv_rollback(k_host, inp.root, inp.path, inp.path_len)
+    ref_v, _ = okv.kv_rollback(v_host, inp.root, inp.path, inp.path_len)
+    assert np.array_equal(n.cpu().numpy(), ref_len)
+    assert np.array_equal(np.stack([x.cpu().numpy() for x in ks]), ref_k)
+    assert np.array_equal(np.stack([x.cpu().numpy() for x in vs]), ref_v)
+    ks2 = [torch.from_numpy(k_host[l].copy()).to(dev) for l in range(3)]
+    rsv.sv_kv_rollback_layers(ks2, None, torch.from_numpy(inp.root).to(dev), torch.from_numpy(inp.path).to(dev),
+                              torch.from_numpy(inp.path_len).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(np.stack([x.cpu().numpy() for x in ks2]), ref_k)
+    print("[kv parity] per-layer tensors ok", flush=True)
