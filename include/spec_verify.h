@@ -247,8 +247,8 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
 
 /* sv_tree_mask — the attention mask and position ids of a token tree packed
  * into one forward pass ("7.6 Speculative Decoding", "Tree Attention:
- * Verifying Many Candidates at Once", build_tree_attn; "Self-Speculative
- * Decoding", "Verifying a tree instead of a line"): node i may attend to node
+ * Verifying Many Candidates at Once", build_tree_attn; "Medusa, EAGLE and
+ * self-speculation", "Verifying a tree instead of a line"): node i may attend to node
  * j iff j is i or one of its ancestors, and node i's position id is its depth
  * plus the sequence's offset.
  *   parents: device int32, N entries per sequence, rows parents_stride apart
@@ -284,7 +284,7 @@ sv_status_t sv_kv_rollback_layers(void* const* k_layers, void* const* v_layers, 
 
 /* sv_ngram_draft — prompt-lookup / n-gram drafting: one-hot draft proposals
  * copied from earlier in each sequence ("7.6 Speculative Decoding", Exercise
- * 4; "Self-Speculative Decoding", "Copying, verified against plain greedy").
+ * 4; "Medusa, EAGLE and self-speculation", "Copying, verified against plain greedy").
  * The last `ngram` tokens of sequence b are looked up at the earlier start
  * positions T - ngram - 1 down to 0; the most recent match i gives the
  * proposal tokens[b][i + ngram ...].

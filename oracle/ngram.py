@@ -7,7 +7,7 @@ Two definitions on the pages:
   past the end of the sequence, or every position when there is no earlier
   occurrence, proposes the last token again. Always gamma tokens, each with a
   one-hot q.
-- "Self-Speculative Decoding", "Copying, verified against plain greedy"
+- "Medusa, EAGLE and self-speculation", "Copying, verified against plain greedy"
   (`lookup_draft`): the key is the last `ngram` tokens; scan the earlier
   start positions from right to left for the same n-gram and propose what
   followed it, at most k tokens and fewer where the sequence ends; no proposal

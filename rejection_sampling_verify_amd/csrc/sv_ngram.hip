@@ -1,6 +1,6 @@
 // sv_ngram.hip — prompt-lookup / n-gram drafting on the device ("7.6
 // Speculative Decoding: Draft Models, Medusa, EAGLE & Lookahead", Exercise 4;
-// "Self-Speculative Decoding", "Copying, verified against plain greedy"): the
+// "Medusa, EAGLE and self-speculation", "Copying, verified against plain greedy"): the
 // last `ngram` tokens of each sequence are looked up at earlier start positions,
 // most recent first, and the tokens that followed the match are proposed; the
 // proposals are one-hot drafts for the verify step.

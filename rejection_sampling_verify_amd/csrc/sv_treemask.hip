@@ -1,7 +1,7 @@
 // sv_treemask.hip — tree attention mask and position ids from parent pointers
 // ("7.6 Speculative Decoding: Draft Models, Medusa, EAGLE & Lookahead", "Tree
-// Attention: Verifying Many Candidates at Once", build_tree_attn; "Self-
-// Speculative Decoding", "Verifying a tree instead of a line"): node i may
+// Attention: Verifying Many Candidates at Once", build_tree_attn; "Medusa,
+// EAGLE and self-speculation", "Verifying a tree instead of a line"): node i may
 // attend to node j iff j is i or one of its ancestors, and node i's position
 // id is its depth, so that one packed forward pass scores every path of the
 // tree as if each were a contiguous sequence.
