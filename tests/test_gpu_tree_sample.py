@@ -246,3 +246,17 @@ def test_without_replacement_full_size_and_rules(dev):
     a = _run(chain, dev, seed=3)
     b = _run(chain, dev, seed=3, wor=True)
     assert all(np.array_equal(a[k], b[k]) for k in ("path", "path_len", "token"))
+
+
+@pytest.mark.parametrize("wor", [False, True])
+def test_largest_tree(dev, wor):
+    """A tree of the largest size (1024 nodes), in both sibling modes: the
+    walk's LDS arrays, child lists and duplicate check at their limit."""
+    B, N, V = 4, 1024, 3000
+    rng = np.random.default_rng(40)
+    parents, depth = _random_tree(rng, N, branching=(2, 6))
+    inp = make_tree_sample("n1024", B, V, parents, depth, bf16=True, seed=41, temperatures=(0.9,), zipf=0.0,
+                           target_sigma=1.5, draft_sigma=(0.3, 1.0), without_replacement=wor)
+    got = _run(inp, dev, seed=2, wor=wor)
+    _compare(got, _oracle(inp, seed=2, wor=wor), "N=1024 wor=%d" % wor)
+    assert np.all(got["path_len"] >= 1)
