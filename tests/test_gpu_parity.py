@@ -339,3 +339,14 @@ def test_named_workload_full_size(dev, name):
     _report(name, s)
     n = got["n"]
     print("[parity] %s mean accepted %.3f, emitted/step %.3f" % (name, n.mean(), n.mean() + 1), flush=True)
+
+
+def test_tree_largest(dev):
+    """The greedy tree walk at the largest tree (1024 nodes): deep paths
+    (children carry their parent's argmax often), bit-exact."""
+    rng = np.random.default_rng(44)
+    parents = workloads.random_tree(rng, 1024, (2, 6))
+    depth = np.array(oracle.tree_depths(parents), np.int32)
+    inp = make_tree("t1024", 6, 2000, parents, depth, bf16=True, seed=45, hit=0.9)
+    ref = _check_tree(inp, dev)
+    assert ref["path_len"].max() >= 4
