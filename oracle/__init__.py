@@ -26,6 +26,7 @@ DTYPE_BF16 = 1
 SEQ_BAD_TOKEN = -1
 SEQ_BAD_TEMPERATURE = -2
 SEQ_BAD_TREE = -3
+SEQ_BAD_LOGITS = -5
 FLAG_KNIFE_EDGE = 1
 FLAG_FALLBACK = 2
 KNIFE_EDGE = 1e-5

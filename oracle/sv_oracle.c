@@ -210,6 +210,18 @@ static void or_fill_bad(int32_t* out_tokens, int32_t gamma, int32_t* out_n, int3
   *out_n = code;
 }
 
+/* Whether softmax(row / T) is a probability distribution: some entry above
+ * -inf, and none NaN or +inf. (-inf entries are tokens of probability 0.) */
+static int or_row_has_softmax(const void* base, int dtype, int64_t stride, int64_t r, int32_t V) {
+  int finite = 0;
+  for (int32_t v = 0; v < V; ++v) {
+    const double l = or_decode(base, dtype, r * stride + v);
+    if (isnan(l) || l == INFINITY) return 0;
+    if (l > -INFINITY) finite = 1;
+  }
+  return finite;
+}
+
 /* Sampled verification of one sequence. Steps follow [SB] speculative_step:
  * (1) normalize target and draft rows with the temperature, (2) walk the
  * drafts left to right, accepting x_i with probability min(1, p_i(x_i)/q_i(x_i)),
@@ -305,6 +317,9 @@ static void or_sample_one(const void* target, int64_t tstride, const void* draft
   out_tokens[n] = top.v1;
   for (int32_t i = n + 1; i <= gamma; ++i) out_tokens[i] = -1;
   *out_n = n;
+  /* A draw over a row without a finite entry (only the bonus row can be one:
+   * the rows scored above were checked) has nothing to draw. */
+  if (top.v1 < 0) or_fill_bad(out_tokens, gamma, out_n, OR_SEQ_BAD_LOGITS);
   if (d) {
     or_set(d->residual_mass, b, beta);
     or_set(d->top_gap, b, or_top2_gap(&top));
@@ -355,8 +370,17 @@ int or_verify_sample(const void* target, int64_t tstride, const void* draft, int
         or_greedy_one(target, tstride, dtype, ids, b, gamma, V, yp, tok, &out_n[b],
                       d ? d->accept_prob : NULL);
       } else {
-        or_sample_one(target, tstride, draft, dstride, dtype, ids, T, b, gamma, V, seed, offset,
-                      u_override, yp, yq, tok, &out_n[b], d);
+        /* Every row the accept tests read must define a distribution. */
+        int rows_ok = 1;
+        for (int32_t i = 0; i < gamma && rows_ok; ++i) {
+          rows_ok &= or_row_has_softmax(target, dtype, tstride, (int64_t)b * (gamma + 1) + i, V);
+          if (draft) rows_ok &= or_row_has_softmax(draft, dtype, dstride, (int64_t)b * gamma + i, V);
+        }
+        if (!rows_ok)
+          or_fill_bad(tok, gamma, &out_n[b], OR_SEQ_BAD_LOGITS);
+        else
+          or_sample_one(target, tstride, draft, dstride, dtype, ids, T, b, gamma, V, seed, offset,
+                        u_override, yp, yq, tok, &out_n[b], d);
       }
     }
     free(yp);

@@ -17,6 +17,7 @@
 #define OR_SEQ_BAD_TOKEN (-1)
 #define OR_SEQ_BAD_TEMPERATURE (-2)
 #define OR_SEQ_BAD_TREE (-3)
+#define OR_SEQ_BAD_LOGITS (-5) /* a sampled sequence's row has no probability distribution */
 
 /* flags[b] bits */
 #define OR_FLAG_KNIFE_EDGE 1 /* some tested position had |u - a| < OR_KNIFE_EDGE */

@@ -583,3 +583,150 @@ def test_accept_test_is_strict():
     r = oracle.verify_sample(tgt, dft, ids, np.ones(2, np.float32), u_override=u)
     assert r["accept_prob"][0, 0] == 0.0 and r["n"][0] == 0
     assert r["accept_prob"][1, 0] == 1.0 and r["n"][1] == 1
+
+
+def _tokens_histogram(col):
+    obs = {}
+    for v in col:
+        obs[(int(v),)] = obs.get((int(v),), 0) + 1
+    return obs
+
+
+def test_empty_residual_falls_back_to_p():
+    """An empty residual (p <= q everywhere, reachable only when p = q up to
+    rounding) makes the repository's fallback draw the correction from p at
+    the rejected row, with the same noise. Pinned two ways: q = p exactly with
+    a forced rejection (u = 1 is not below a = 1), and an input where the
+    drafted token's draft logit differs by an amount no fp64 sum can hold
+    (so p and q agree bit for bit everywhere else and a is about e^-60). The
+    draws must follow p of the rejected row, not of another row."""
+    rng = np.random.default_rng(31)
+    V, B, T = 10, 100000, 0.9
+    rows = rng.normal(0, 1.0, (3, V)).astype(np.float32)
+    # q = p on row 1, forced rejection there after an accepted row 0.
+    tgt = np.broadcast_to(rows, (B, 3, V)).copy()
+    dft = np.broadcast_to(rows[:2], (B, 2, V)).copy()
+    ids = np.broadcast_to(np.array([[3, 5]], np.int32), (B, 2)).copy()
+    u = np.broadcast_to(np.array([[0.0, 1.0]]), (B, 2)).copy()
+    r = oracle.verify_sample(tgt, dft, ids, np.full(B, T, np.float32), seed=5, u_override=u)
+    assert np.all(r["n"] == 1)
+    assert np.all(r["flags"] & oracle.FLAG_FALLBACK)
+    assert np.all(r["residual_mass"] == 0.0)
+    p1 = _softmax64(rows[1], T)
+    assert _chi2_pvalue(_tokens_histogram(r["tokens"][:, 1]), {(v,): p1[v] for v in range(V)}, B) > 1e-4
+    # The row the draw reads is the rejected one: row 2's law is rejected.
+    p2 = _softmax64(rows[2], T)
+    assert _chi2_pvalue(_tokens_histogram(r["tokens"][:, 1]), {(v,): p2[v] for v in range(V)}, B) < 1e-9
+    # Rounding construction with the accept uniforms of the generator.
+    x = 4
+    tgt2 = np.broadcast_to(rows[:2], (B, 2, V)).copy()
+    dft2 = np.broadcast_to(rows[:1], (B, 1, V)).copy()
+    tgt2[:, 0, x] = -100.0
+    dft2[:, 0, x] = -40.0
+    ids2 = np.full((B, 1), x, np.int32)
+    r2 = oracle.verify_sample(tgt2, dft2, ids2, np.full(B, 1.0, np.float32), seed=6)
+    assert np.all(r2["n"] == 0) and np.all(r2["flags"] & oracle.FLAG_FALLBACK)
+    assert np.all(r2["accept_prob"][:, 0] < 1e-25)
+    p0 = _softmax64(tgt2[0, 0], 1.0)
+    expect = {(v,): p0[v] for v in range(V) if p0[v] > 1e-12}
+    assert _chi2_pvalue(_tokens_histogram(r2["tokens"][:, 0]), expect, B) > 1e-4
+
+
+def test_tree_zero_mass_residual_leaves_p():
+    """Sampled trees: after a rejection whose residual has zero mass (the same
+    rounding construction as for chains: the child's draft logit is below what
+    an fp64 sum can hold, so p and q agree elsewhere), the target distribution
+    stays p; with every child rejected the token is then a draw from p at the
+    node."""
+    rng = np.random.default_rng(32)
+    V, B, T = 10, 60000, 1.0
+    parents = np.array([-1, 0], np.int32)
+    depth = np.array([0, 1], np.int32)
+    row = rng.normal(0, 1.0, V).astype(np.float32)
+    x = 7
+    tgt = np.broadcast_to(np.stack([row, row]), (B, 2, V)).copy()
+    dft = tgt.copy()
+    tgt[:, 0, x] = -100.0
+    dft[:, 0, x] = -40.0
+    tok = np.zeros((B, 2), np.int32)
+    tok[:, 1] = x
+    r = oracle.verify_tree_sample(tgt, dft, parents, depth, tok, np.full(B, T, np.float32), 1, seed=9)
+    assert np.all(r["path_len"] == 1) and np.all(r["rejections"] == 1)
+    assert np.all(r["flags"] & oracle.FLAG_FALLBACK)
+    p0 = _softmax64(tgt[0, 0], T)
+    expect = {(v,): p0[v] for v in range(V) if p0[v] > 1e-12}
+    assert _chi2_pvalue(_tokens_histogram(r["token"]), expect, B) > 1e-4
+
+
+def test_masked_entries_have_probability_zero():
+    """-inf logits are tokens of probability 0 ([SB] "A From-Scratch
+    Implementation" asks for care when a probability is tiny): the accept
+    probability and log-normalizer equal those of the vocabulary with the
+    masked entries removed; a drafted token with p(x) = 0 gets a = 0, one with
+    q(x) = 0 gets a = 1, and a row with one finite entry is one-hot there."""
+    rng = np.random.default_rng(33)
+    V, Vr = 12, 8
+    keep = np.array([0, 1, 3, 4, 6, 7, 9, 11])
+    tgt = rng.normal(0, 1.5, (1, 3, V)).astype(np.float32)
+    dft = rng.normal(0, 1.5, (1, 2, V)).astype(np.float32)
+    masked = np.setdiff1d(np.arange(V), keep)
+    tgt[:, :, masked] = -np.inf
+    dft[:, :, masked] = -np.inf
+    ids = np.array([[keep[2], keep[5]]], np.int32)
+    T = np.array([0.8], np.float32)
+    full = oracle.verify_sample(tgt, dft, ids, T, seed=1)
+    red = oracle.verify_sample(np.ascontiguousarray(tgt[:, :, keep]), np.ascontiguousarray(dft[:, :, keep]),
+                               np.array([[2, 5]], np.int32), T, seed=1)
+    assert np.allclose(full["accept_prob"], red["accept_prob"], rtol=0, atol=1e-15)
+    assert np.allclose(full["logz_target"], red["logz_target"], rtol=0, atol=1e-15)
+    assert np.allclose(full["logz_draft"], red["logz_draft"], rtol=0, atol=1e-15)
+    # p(x) = 0 and q(x) = 0.
+    t2 = rng.normal(0, 1.0, (2, 2, V)).astype(np.float32)
+    d2 = rng.normal(0, 1.0, (2, 1, V)).astype(np.float32)
+    t2[0, 0, 5] = -np.inf
+    d2[1, 0, 6] = -np.inf
+    r = oracle.verify_sample(t2, d2, np.array([[5], [6]], np.int32), np.ones(2, np.float32),
+                             u_override=np.array([[0.0], [1.0 - 2.0 ** -24]]))
+    assert r["accept_prob"][0, 0] == 0.0 and r["n"][0] == 0 and r["tokens"][0, 0] != 5
+    assert r["accept_prob"][1, 0] == 1.0 and r["n"][1] == 1
+    # One finite entry: p is one-hot, its token is always accepted and the
+    # bonus row's single finite entry is always drawn.
+    t3 = np.full((4, 2, V), -np.inf, np.float32)
+    t3[:, 0, 2] = 1.5
+    t3[:, 1, 9] = -3.0
+    d3 = rng.normal(0, 1.0, (4, 1, V)).astype(np.float32)
+    r3 = oracle.verify_sample(t3, d3, np.full((4, 1), 2, np.int32), np.ones(4, np.float32), seed=3)
+    assert np.all(r3["n"] == 1) and np.all(r3["tokens"][:, 1] == 9)
+    assert np.all(r3["logz_target"][:, 0] == 1.5)
+
+
+def test_rows_without_a_distribution_are_reported():
+    """The repository's contract for sampled sequences: every row the accept
+    tests read must define softmax(row / T) (an entry above -inf, none NaN or
+    +inf), and a bonus row must have a finite entry to draw from; otherwise the
+    sequence gets code -5 and tokens -1. Greedy sequences take the argmax of
+    anything but NaN (+inf is the largest value)."""
+    rng = np.random.default_rng(34)
+    V = 16
+    B = 6
+    tgt = rng.normal(0, 1.0, (B, 3, V)).astype(np.float32)
+    dft = rng.normal(0, 1.0, (B, 2, V)).astype(np.float32)
+    tgt[0, 1, 3] = np.inf          # target row 1
+    dft[1, 0, 4] = np.nan          # draft row 0
+    tgt[2, 0, :] = -np.inf         # a row with no finite entry
+    tgt[3, 2, :] = -np.inf         # bonus row without a finite entry
+    tgt[4, 2, 5] = np.inf          # +inf in the bonus row only
+    ids = rng.integers(0, V, size=(B, 2)).astype(np.int32)
+    u = np.zeros((B, 2))           # accept every scored draft
+    r = oracle.verify_sample(tgt, dft, ids, np.ones(B, np.float32), seed=2, u_override=u)
+    assert r["n"].tolist()[:4] == [oracle.SEQ_BAD_LOGITS] * 4
+    assert np.all(r["tokens"][:4] == -1)
+    # +inf in the bonus row: the row's law puts all mass on it.
+    assert r["n"][4] == 2 and r["tokens"][4, 2] == 5
+    assert r["n"][5] == 2
+    # Greedy: +inf is the argmax, lowest index among equal values.
+    g = tgt.copy()
+    g[0, 0, :] = -np.inf
+    g[0, 0, [6, 9]] = np.inf
+    rg = oracle.verify_sample(g, None, np.array([[6, 1]] * B, np.int32), np.zeros(B, np.float32))
+    assert rg["n"][0] >= 1 and rg["tokens"][0, 0] == 6

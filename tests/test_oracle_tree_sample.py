@@ -5,10 +5,12 @@ No GPU. The pages' rule: test the children of a node one by one against the
 current target distribution p, replacing p by the normalized residual
 (p - q)_+ after each rejection, and draw the replacement from the final
 residual when every child is rejected; each round is the single-candidate rule,
-so the emitted token is distributed exactly as p. Siblings are read as i.i.d.
-draws from the draft distribution q at their parent (the plainest reading;
-the pages also mention renormalizing q when siblings are drawn without
-replacement, which this library does not do).
+so the emitted token is distributed exactly as p. By default siblings are
+read as i.i.d. draws from the draft distribution q at their parent (the
+plainest reading). The pages also mention siblings drawn without
+replacement, where q is renormalized over the candidates left; the oracle
+and the library implement that variant too (without_replacement=True), and
+it is pinned below by its own exact enumeration.
 """
 import itertools
 from fractions import Fraction
