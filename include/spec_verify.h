@@ -25,6 +25,22 @@
  *           (b * rows_per_seq + i) * row_stride. Rows whose byte address is a
  *           multiple of 16 take the vectorized path; others are read element by
  *           element (correct, slower).
+ * Values.   A logit is any finite value, -inf or +inf, never NaN. -inf marks
+ *           a token of probability 0 (a masked entry). Sampled rows are
+ *           computed in fp32 from l / T: log-probabilities carry an absolute
+ *           rounding error of about |l| / T * 2^-24, so very large positive
+ *           logits (|l| / T in the thousands and up) cost accuracy, and l / T
+ *           must stay below 2^126 / log2(e). Greedy verification
+ *           (temperature 0, spec_verify_greedy, spec_verify_tree) takes the
+ *           argmax of any such row, +inf being the largest value. For a
+ *           sampled sequence of spec_verify_sample, every row the accept tests
+ *           read (target and draft rows 0 .. gamma-1) must define softmax(l / T):
+ *           some entry above -inf and none +inf; a NaN anywhere in them is also
+ *           caught. A sequence breaking this gets SV_SEQ_BAD_LOGITS, as does
+ *           one whose bonus row (read only when every draft is accepted) has no
+ *           entry above -inf; a +inf in the bonus row is drawn (the lowest index
+ *           among several). spec_verify_tree_sample requires finite or -inf
+ *           entries with at least one finite entry per row it reads.
  * Errors.   The return value reports host-side argument validation (done before
  *           any HIP call, so nothing is enqueued on failure) and launch
  *           failures (SV_ERR_HIP). Problems that only the device can see are
@@ -38,7 +54,7 @@
  *           one workspace race.
  * Random.   Randomness is counter-based Philox4x32-10 (Salmon et al., SC'11)
  *           with key = (seed low 32 bits, seed high 32 bits) and counter words
- *           (c0, c1, c2, c3) = (c0, position, sequence b, 2*offset + stream):
+ *           (c0, c1, c2, c3) = (c0, position, seq_base + b, 2*offset + stream):
  *             stream 0, c0 = 0       : accept uniform of position i = word 0;
  *             stream 1, c0 = v / 4   : Gumbel noise of vocab entry v = word v%4.
  *           A word w maps to u = (w >> 8) * 2^-24 (accept test, u in [0,1)) or
@@ -64,7 +80,8 @@ typedef enum {
   SV_ERR_NULL_ARG = 1,   /* a required pointer is NULL                         */
   SV_ERR_BAD_SHAPE = 2,  /* B, gamma/N, V or max_depth out of range            */
   SV_ERR_BAD_DTYPE = 3,  /* dtype is not an sv_dtype_t value                   */
-  SV_ERR_BAD_ARG = 4,    /* row stride < V, offset >= 2^31, misaligned workspace */
+  SV_ERR_BAD_ARG = 4,    /* row stride < V, offset >= 2^31, seq_base + B > 2^32,
+                          * misaligned workspace                             */
   SV_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than sv_workspace_bytes  */
   SV_ERR_HIP = 6         /* a HIP runtime call or kernel launch failed         */
 } sv_status_t;
@@ -83,6 +100,8 @@ typedef enum {
                                      * workspace is then left dirty and must be
                                      * re-initialized (sv_workspace_init) before
                                      * its next use                               */
+#define SV_SEQ_BAD_LOGITS (-5)      /* a sampled sequence's row defines no
+                                     * distribution (see "Values" above)         */
 
 /* Optional diagnostics of spec_verify_sample; the struct and each field may
  * be NULL. All are device arrays of fp32. */
@@ -144,19 +163,41 @@ const char* sv_status_string(sv_status_t status);
  * draft_ids      [B, gamma] int32.
  * temperature    [B] fp32 (device).
  * seed, offset   Philox key and per-step counter word (offset < 2^31).
+ * seq_base       counter word 2 of sequence b is seq_base + b (seq_base + B
+ *                <= 2^32): a batch split over several calls (or GPUs) gives
+ *                each call its first sequence's global index, and the split
+ *                calls reproduce the single call bit for bit.
  * out_tokens     [B, gamma+1] int32: x_0 .. x_{n-1}, then the correction or
  *                bonus token, then -1 padding.
- * out_num_accepted [B] int32: n in [0, gamma], or an SV_SEQ_* code (< 0).
+ * out_num_accepted [B] int32: n in [0, gamma], or an SV_SEQ_* code (< 0):
+ *                SV_SEQ_BAD_TEMPERATURE, SV_SEQ_BAD_TOKEN or SV_SEQ_BAD_LOGITS
+ *                (the first that applies), or SV_SEQ_INTERNAL.
  * diag           optional diagnostics (see sv_diag_t), may be NULL.
  */
 sv_status_t spec_verify_sample(const void* target_logits, int64_t target_row_stride,
                                const void* draft_logits, int64_t draft_row_stride,
                                sv_dtype_t dtype, const int32_t* draft_ids,
                                const float* temperature, int32_t B, int32_t gamma,
-                               int32_t V, uint64_t seed, uint64_t offset,
+                               int32_t V, uint64_t seed, uint64_t offset, uint32_t seq_base,
                                int32_t* out_tokens, int32_t* out_num_accepted,
                                const sv_diag_t* diag, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* sv_debug_sample_tiled — spec_verify_sample with its tiling fixed by the
+ * caller instead of chosen by the library (for tests that check that results
+ * do not depend on the tiling; no operation of the pages). p1_vectors: 16-byte
+ * vectors per thread in a pass-1 chunk (1, 2, 4 or 8; 0 = chosen); p2_chunks:
+ * pass-2 chunks per drawn row (0 = chosen; capped at one per four streaming
+ * rounds). Everything else is as for spec_verify_sample; SV_ERR_BAD_ARG for
+ * other tiling values. */
+sv_status_t sv_debug_sample_tiled(const void* target_logits, int64_t target_row_stride,
+                                  const void* draft_logits, int64_t draft_row_stride,
+                                  sv_dtype_t dtype, const int32_t* draft_ids,
+                                  const float* temperature, int32_t B, int32_t gamma, int32_t V,
+                                  uint64_t seed, uint64_t offset, uint32_t seq_base,
+                                  int32_t* out_tokens, int32_t* out_num_accepted,
+                                  const sv_diag_t* diag, void* workspace, size_t workspace_bytes,
+                                  void* stream, int32_t p1_vectors, int32_t p2_chunks);
 
 /*
  * spec_verify_greedy — argmax-match verification of a batch of chains.
@@ -217,8 +258,8 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
  *   parents, depth: device [N], a tree in parent-before-child order rooted at
  *     node 0 (as for spec_verify_tree); node_tokens: device [B, N], token of
  *     each node (node 0's is not read); temperature: device [B], each > 0.
- *   seed, offset: Philox key and per-step counter word, as for
- *     spec_verify_sample. The accept uniform of the j-th sibling tested under
+ *   seed, offset, seq_base: Philox key, per-step counter word and the
+ *     global index of the first sequence, as for spec_verify_sample. The accept uniform of the j-th sibling tested under
  *     node v is word 0 of counter (j, v, b, 2 offset); the noise of a draw at
  *     node v is that of position v. A tree shaped like a chain therefore
  *     verifies exactly as spec_verify_sample verifies the chain.
@@ -235,13 +276,14 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
  *   workspace: sv_workspace_bytes(B, N, V) bytes, as for spec_verify_tree.
  * Returns SV_ERR_NULL_ARG, SV_ERR_BAD_SHAPE (B, N, V or max_depth out of
  * range, or a vocabulary too long for one launch), SV_ERR_BAD_DTYPE,
- * SV_ERR_BAD_ARG (a stride < V, offset >= 2^31, siblings_without_replacement
- * not 0 or 1), SV_ERR_WORKSPACE or SV_ERR_HIP; nothing is launched on an error. */
+ * SV_ERR_BAD_ARG (a stride < V, offset >= 2^31, seq_base + B > 2^32,
+ * siblings_without_replacement not 0 or 1), SV_ERR_WORKSPACE or SV_ERR_HIP; nothing is launched on an error. */
 sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_row_stride, const void* draft_logits,
                                     int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* parents,
                                     const int32_t* depth, const int32_t* node_tokens, const float* temperature,
                                     int32_t B, int32_t N, int32_t V, int32_t max_depth, uint64_t seed,
-                                    uint64_t offset, int32_t siblings_without_replacement, int32_t* out_path,
+                                    uint64_t offset, uint32_t seq_base, int32_t siblings_without_replacement,
+                                    int32_t* out_path,
                                     int32_t* out_path_len, int32_t* out_token, void* workspace,
                                     size_t workspace_bytes, void* stream);
 

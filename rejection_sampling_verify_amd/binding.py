@@ -7,6 +7,7 @@ kernels.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -20,10 +21,12 @@ SV_SEQ_BAD_TOKEN = -1
 SV_SEQ_BAD_TEMPERATURE = -2
 SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
+SV_SEQ_BAD_LOGITS = -5
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
-           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback", "sv_kv_rollback_layers", "sv_ngram_draft", "sv_tree_mask", "sv_debug_philox", "sv_debug_noise", "sv_debug_wave_max",
-           "sv_debug_read_stream"]
+           "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback",
+           "sv_kv_rollback_layers", "sv_ngram_draft", "sv_tree_mask", "sv_debug_philox", "sv_debug_noise",
+           "sv_debug_wave_max", "sv_debug_read_stream", "sv_debug_sample_tiled"]
 
 _lib = None
 
@@ -54,15 +57,18 @@ def lib() -> ctypes.CDLL:
         L.sv_workspace_init.restype = ctypes.c_int
         L.sv_status_string.argtypes = [ctypes.c_int]
         L.sv_status_string.restype = ctypes.c_char_p
-        L.spec_verify_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, i32, i32, i32, u64, u64, P, P,
+        u32 = ctypes.c_uint32
+        L.spec_verify_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, i32, i32, i32, u64, u64, u32, P, P,
                                          ctypes.POINTER(_Diag), P, sz, P]
         L.spec_verify_sample.restype = ctypes.c_int
+        L.sv_debug_sample_tiled.argtypes = L.spec_verify_sample.argtypes + [i32, i32]
+        L.sv_debug_sample_tiled.restype = ctypes.c_int
         L.spec_verify_greedy.argtypes = [P, i64, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P]
         L.spec_verify_greedy.restype = ctypes.c_int
         L.spec_verify_tree.argtypes = [P, i64, ctypes.c_int, P, P, P, i32, i32, i32, i32, P, P, P, P, sz, P]
         L.spec_verify_tree.restype = ctypes.c_int
         L.spec_verify_tree_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, u64, u64,
-                                              i32, P, P, P, P, sz, P]
+                                              u32, i32, P, P, P, P, sz, P]
         L.spec_verify_tree_sample.restype = ctypes.c_int
         L.sv_kv_rollback.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
         L.sv_kv_rollback.restype = ctypes.c_int
@@ -101,6 +107,15 @@ def _stream(stream=None):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(stream):
+    """Allocations made inside belong to `stream` (the caller's side stream, if
+    any): torch fills them on it, and its caching allocator reuses their
+    memory only after the work queued there, which includes the kernels that
+    use them."""
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def _ptr(t):
@@ -158,7 +173,7 @@ def _check_i32(t, shape, name):
 
 def spec_verify_sample(target_logits, draft_logits, draft_ids, temperature, seed: int = 0, offset: int = 0,
                        out_tokens=None, out_num_accepted=None, diag: dict | None = None, workspace=None,
-                       V: int | None = None, stream=None):
+                       V: int | None = None, stream=None, seq_base: int = 0, tiling: tuple | None = None):
     """Sampled (temperature > 0) / greedy (temperature == 0) verification.
 
     target_logits [B, gamma+1, V'] and draft_logits [B, gamma, V'] (or None for a
@@ -166,6 +181,9 @@ def spec_verify_sample(target_logits, draft_logits, draft_ids, temperature, seed
     temperature [B] float32. Returns (out_tokens [B, gamma+1], out_num_accepted [B]).
     diag: optional dict of preallocated float32 tensors with keys accept_prob,
     logz_target, logz_draft ([B, gamma]) and residual_mass ([B]).
+    seq_base: global index of the first sequence (Philox counter word 2).
+    tiling: (p1_vectors, p2_chunks) to fix the tiling through the debug entry
+    point sv_debug_sample_tiled (results must not depend on it).
     """
     import torch
     B, gamma = draft_ids.shape
@@ -179,21 +197,25 @@ def spec_verify_sample(target_logits, draft_logits, draft_ids, temperature, seed
         if draft_logits.dtype != target_logits.dtype:
             raise ValueError("draft and target logits must share a dtype")
         ds = _row_stride(draft_logits, gamma, V)
-    if out_tokens is None:
-        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=target_logits.device)
-    if out_num_accepted is None:
-        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=target_logits.device)
+    with _on(stream):
+        if out_tokens is None:
+            out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=target_logits.device)
+        if out_num_accepted is None:
+            out_num_accepted = torch.empty((B,), dtype=torch.int32, device=target_logits.device)
+        if workspace is None:
+            workspace = Workspace(target_logits.device).get(B, gamma + 1, V)
     d = None
     if diag:
         d = _Diag(*[diag[k].data_ptr() if diag.get(k) is not None else None
                     for k in ("accept_prob", "logz_target", "logz_draft", "residual_mass")])
-    if workspace is None:
-        workspace = Workspace(target_logits.device).get(B, gamma + 1, V)
-    st = lib().spec_verify_sample(_ptr(target_logits), ts, _ptr(draft_logits), ds, _dtype_code(target_logits),
-                                  _ptr(draft_ids), _ptr(temperature), B, gamma, V, seed, offset,
-                                  _ptr(out_tokens), _ptr(out_num_accepted),
-                                  ctypes.byref(d) if d is not None else None,
-                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    args = (_ptr(target_logits), ts, _ptr(draft_logits), ds, _dtype_code(target_logits),
+            _ptr(draft_ids), _ptr(temperature), B, gamma, V, seed, offset, seq_base,
+            _ptr(out_tokens), _ptr(out_num_accepted), ctypes.byref(d) if d is not None else None,
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if tiling is None:
+        st = lib().spec_verify_sample(*args)
+    else:
+        st = lib().sv_debug_sample_tiled(*args, int(tiling[0]), int(tiling[1]))
     if st != 0:
         raise SVError(st, "spec_verify_sample")
     return out_tokens, out_num_accepted
@@ -207,12 +229,13 @@ def spec_verify_greedy(target_logits, draft_ids, out_tokens=None, out_num_accept
     V = int(target_logits.shape[2]) if V is None else int(V)
     _check_i32(draft_ids, (B, gamma), "draft_ids")
     ts = _row_stride(target_logits, gamma + 1, V)
-    if out_tokens is None:
-        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=target_logits.device)
-    if out_num_accepted is None:
-        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=target_logits.device)
-    if workspace is None:
-        workspace = Workspace(target_logits.device).get(B, gamma + 1, V)
+    with _on(stream):
+        if out_tokens is None:
+            out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=target_logits.device)
+        if out_num_accepted is None:
+            out_num_accepted = torch.empty((B,), dtype=torch.int32, device=target_logits.device)
+        if workspace is None:
+            workspace = Workspace(target_logits.device).get(B, gamma + 1, V)
     st = lib().spec_verify_greedy(_ptr(target_logits), ts, _dtype_code(target_logits), _ptr(draft_ids), B, gamma,
                                   V, _ptr(out_tokens), _ptr(out_num_accepted), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream))
@@ -232,14 +255,15 @@ def spec_verify_tree(target_logits, parents, depth, node_tokens, max_depth: int,
     _check_i32(depth, (N,), "depth")
     ts = _row_stride(target_logits, N, V)
     dev = target_logits.device
-    if out_path is None:
-        out_path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
-    if out_path_len is None:
-        out_path_len = torch.empty((B,), dtype=torch.int32, device=dev)
-    if out_bonus is None:
-        out_bonus = torch.empty((B,), dtype=torch.int32, device=dev)
-    if workspace is None:
-        workspace = Workspace(dev).get(B, N, V)
+    with _on(stream):
+        if out_path is None:
+            out_path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+        if out_path_len is None:
+            out_path_len = torch.empty((B,), dtype=torch.int32, device=dev)
+        if out_bonus is None:
+            out_bonus = torch.empty((B,), dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = Workspace(dev).get(B, N, V)
     st = lib().spec_verify_tree(_ptr(target_logits), ts, _dtype_code(target_logits), _ptr(parents), _ptr(depth),
                                 _ptr(node_tokens), B, N, V, max_depth, _ptr(out_path), _ptr(out_path_len),
                                 _ptr(out_bonus), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -251,7 +275,8 @@ def spec_verify_tree(target_logits, parents, depth, node_tokens, max_depth: int,
 
 def spec_verify_tree_sample(target_logits, draft_logits, parents, depth, node_tokens, temperature, max_depth: int,
                             seed: int = 0, offset: int = 0, out_path=None, out_path_len=None, out_token=None,
-                            workspace=None, V: int | None = None, stream=None, without_replacement: bool = False):
+                            workspace=None, V: int | None = None, stream=None, without_replacement: bool = False,
+                            seq_base: int = 0):
     """Sampled tree verification (multi-round rejection sampling). target and
     draft logits [B, N, V] (draft row v: q at node v), temperature [B] > 0.
     Returns (out_path [B, max_depth+1], out_path_len [B], out_token [B])."""
@@ -268,17 +293,18 @@ def spec_verify_tree_sample(target_logits, draft_logits, parents, depth, node_to
     ts = _row_stride(target_logits, N, V)
     ds = _row_stride(draft_logits, N, V)
     dev = target_logits.device
-    if out_path is None:
-        out_path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
-    if out_path_len is None:
-        out_path_len = torch.empty((B,), dtype=torch.int32, device=dev)
-    if out_token is None:
-        out_token = torch.empty((B,), dtype=torch.int32, device=dev)
-    if workspace is None:
-        workspace = Workspace(dev).get(B, N, V)
+    with _on(stream):
+        if out_path is None:
+            out_path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+        if out_path_len is None:
+            out_path_len = torch.empty((B,), dtype=torch.int32, device=dev)
+        if out_token is None:
+            out_token = torch.empty((B,), dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = Workspace(dev).get(B, N, V)
     st = lib().spec_verify_tree_sample(_ptr(target_logits), ts, _ptr(draft_logits), ds, _dtype_code(target_logits),
                                        _ptr(parents), _ptr(depth), _ptr(node_tokens), _ptr(temperature), B, N, V,
-                                       max_depth, seed, offset, int(bool(without_replacement)), _ptr(out_path),
+                                       max_depth, seed, offset, seq_base, int(bool(without_replacement)), _ptr(out_path),
                                        _ptr(out_path_len), _ptr(out_token),
                                        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
@@ -303,7 +329,8 @@ def sv_kv_rollback(k_cache, v_cache, root_pos, path, path_len, cache_len=None, s
         raise ValueError("path must be [B, P]")
     _check_i32(path, tuple(path.shape), "path")
     if cache_len is None:
-        cache_len = torch.empty((B,), dtype=torch.int32, device=k_cache.device)
+        with _on(stream):
+            cache_len = torch.empty((B,), dtype=torch.int32, device=k_cache.device)
     st = lib().sv_kv_rollback(_ptr(k_cache), _ptr(v_cache) if v_cache is not None else None, k_cache.element_size(),
                               L, B, H, S, D, _ptr(root_pos), _ptr(path), int(path.shape[1]), _ptr(path_len),
                               _ptr(cache_len), _stream(stream))
@@ -334,10 +361,12 @@ def sv_kv_rollback_layers(k_layers, v_layers, root_pos, path, path_len, cache_le
         raise ValueError("path must be [B, P]")
     _check_i32(path, tuple(path.shape), "path")
     dev = ref.device
-    kp = torch.tensor([t.data_ptr() for t in k_layers], dtype=torch.int64, device=dev)
-    vp = torch.tensor([t.data_ptr() for t in v_layers], dtype=torch.int64, device=dev) if v_layers is not None else None
-    if cache_len is None:
-        cache_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    with _on(stream):
+        kp = torch.tensor([t.data_ptr() for t in k_layers], dtype=torch.int64, device=dev)
+        vp = (torch.tensor([t.data_ptr() for t in v_layers], dtype=torch.int64, device=dev)
+              if v_layers is not None else None)
+        if cache_len is None:
+            cache_len = torch.empty((B,), dtype=torch.int32, device=dev)
     st = lib().sv_kv_rollback_layers(_ptr(kp), _ptr(vp), ref.element_size(), len(k_layers), B, H, S, D,
                                      _ptr(root_pos), _ptr(path), int(path.shape[1]), _ptr(path_len), _ptr(cache_len),
                                      _stream(stream))
@@ -357,12 +386,13 @@ def sv_ngram_draft(tokens, lengths, ngram, gamma, pad_with_last=True, out_draft=
     B = tokens.shape[0]
     _check_i32(lengths, (B,), "lengths")
     dev = tokens.device
-    if out_draft is None:
-        out_draft = torch.empty((B, gamma), dtype=torch.int32, device=dev)
-    if out_count is None:
-        out_count = torch.empty((B,), dtype=torch.int32, device=dev)
-    if out_match is None:
-        out_match = torch.empty((B,), dtype=torch.int32, device=dev)
+    with _on(stream):
+        if out_draft is None:
+            out_draft = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+        if out_count is None:
+            out_count = torch.empty((B,), dtype=torch.int32, device=dev)
+        if out_match is None:
+            out_match = torch.empty((B,), dtype=torch.int32, device=dev)
     _check_i32(out_draft, (B, gamma), "out_draft")
     _check_i32(out_count, (B,), "out_count")
     _check_i32(out_match, (B,), "out_match")
@@ -396,11 +426,12 @@ def sv_tree_mask(parents, position_offset=None, B=None, mask=True, packed=False,
     if position_offset is not None:
         _check_i32(position_offset, (B,), "position_offset")
     dev = parents.device
-    if mask and out_mask is None:
-        out_mask = (torch.empty((B, N, (N + 31) // 32), dtype=torch.int32, device=dev) if packed
-                    else torch.empty((B, N, N), dtype=torch.bool, device=dev))
-    if position_ids and out_position_ids is None:
-        out_position_ids = torch.empty((B, N), dtype=torch.int32, device=dev)
+    with _on(stream):
+        if mask and out_mask is None:
+            out_mask = (torch.empty((B, N, (N + 31) // 32), dtype=torch.int32, device=dev) if packed
+                        else torch.empty((B, N, N), dtype=torch.bool, device=dev))
+        if position_ids and out_position_ids is None:
+            out_position_ids = torch.empty((B, N), dtype=torch.int32, device=dev)
     if out_position_ids is not None:
         _check_i32(out_position_ids, (B, N), "out_position_ids")
     if out_mask is not None:

@@ -45,31 +45,27 @@ std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kMaxDevices][12];
 std::atomic<int> g_tree_occ[kMaxDevices][4];
 
-int env_int(const char* name, int dflt) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  return std::atoi(s);
-}
-
 struct Tiling {
   int kv, chunk, nchunks;
 };
 
+// Pass-1 items a launch should hold at least, so that small batches still
+// spread over the whole GPU.
+constexpr long long kTargetItems = 4096;
+
 // Chunk length: as long as possible (8 vectors per thread) while the pass-1
-// item count stays at or above the target, so that small batches still spread
-// over the whole GPU.
-Tiling pick_tiling(long long rows, int32_t V, bool bf16) {
+// item count stays at or above the target. forced_kv (a power of two up to 8)
+// fixes the vectors per thread instead; 0 picks them.
+Tiling pick_tiling(long long rows, int32_t V, bool bf16, int forced_kv = 0) {
   const int ev = bf16 ? 8 : 4;
-  const long long target = env_int("SV_TARGET_ITEMS", 4096);
   int kv = kMaxVecsPerThread;
-  int forced = env_int("SV_KV", 0);
-  if (forced >= 1 && forced <= kMaxVecsPerThread && (forced & (forced - 1)) == 0) {
-    kv = forced;
+  if (forced_kv >= 1 && forced_kv <= kMaxVecsPerThread && (forced_kv & (forced_kv - 1)) == 0) {
+    kv = forced_kv;
   } else {
     while (kv > 1) {
       const long long chunk = (long long)kThreads * ev * kv;
       const long long items = rows * ((V + chunk - 1) / chunk);
-      if (items >= target) break;
+      if (items >= kTargetItems) break;
       kv >>= 1;
     }
   }
@@ -92,20 +88,8 @@ bool device_info(int* dev, int* cus) {
   return true;
 }
 
-// Resident workgroups per CU of the chain / tree kernels, queried once per
-// device and configuration.
-int occupancy(int dev, bool bf16, bool vec) {
-  const int k = (bf16 ? 2 : 0) + (vec ? 1 : 0);
-  int n = g_occ[dev][k].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    n = chain_occupancy(bf16, vec);
-    if (n <= 0) n = 1;
-    g_occ[dev][k].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
-// Resident workgroups per CU of the second of the two chain launches.
+// Resident workgroups per CU of the pass-2 launch, queried once per device
+// and configuration.
 int p2_occupancy(int dev, bool bf16, bool vec) {
   const int k = 4 + (bf16 ? 2 : 0) + (vec ? 1 : 0);
   int n = g_occ[dev][k].load(std::memory_order_relaxed);
@@ -150,17 +134,20 @@ sv_status_t check_workspace(void* ws, size_t bytes, size_t need) {
   return SV_OK;
 }
 
+// forced_kv, forced_p2: the debug entry point's fixed tiling (0: chosen here).
 sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, int64_t d_stride,
                       sv_dtype_t dtype, const int32_t* ids, const float* temperature, int32_t B,
-                      int32_t gamma, int32_t V, uint64_t seed, uint64_t offset, int32_t* out_tokens,
-                      int32_t* out_n, const sv_diag_t* diag, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      int32_t gamma, int32_t V, uint64_t seed, uint64_t offset, uint32_t seq_base,
+                      int32_t* out_tokens, int32_t* out_n, const sv_diag_t* diag, void* workspace,
+                      size_t workspace_bytes, void* stream, int forced_kv = 0, int forced_p2 = 0) {
   if (!target || !ids || !out_tokens || !out_n) return SV_ERR_NULL_ARG;
   if (B < 0 || B > SV_MAX_BATCH || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > (1 << 30))
     return SV_ERR_BAD_SHAPE;
   if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_BAD_DTYPE;
   if (t_stride < V || (draft && d_stride < V)) return SV_ERR_BAD_ARG;
   if (offset >= (1ull << 31)) return SV_ERR_BAD_ARG;
+  if (forced_kv < 0 || forced_p2 < 0) return SV_ERR_BAD_ARG;
+  if ((uint64_t)seq_base + (uint64_t)B > (1ull << 32)) return SV_ERR_BAD_ARG;
   const size_t need = sv_workspace_bytes(B, gamma + 1, V);
   const sv_status_t ws_ok = check_workspace(workspace, workspace_bytes, need);
   if (ws_ok != SV_OK) return ws_ok;
@@ -169,7 +156,7 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   const bool bf16 = (dtype == SV_DTYPE_BF16);
   const int es = bf16 ? 2 : 4;
   const bool vec = aligned16(target, t_stride * es) && (!draft || aligned16(draft, d_stride * es));
-  const Tiling tl = pick_tiling((long long)B * gamma * (draft ? 2 : 1), V, bf16);
+  const Tiling tl = pick_tiling((long long)B * gamma * (draft ? 2 : 1), V, bf16, forced_kv);
   const WsLayout L = ws_layout(B, gamma + 1, max_chunks(V));
   uint8_t* ws = (uint8_t*)workspace;
 
@@ -191,27 +178,17 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   a.chunk = tl.chunk;
   a.nchunks = tl.nchunks;
   a.kv = tl.kv;
-  // Pass-2 chunks. The fused launch sizes them for about two resident
-  // workgroups per (sequence, chunk) over the whole GPU. The second of two
-  // launches sizes them on the device, once the number of sequences with a
-  // pending draw is known: as many chunks per row as fill one resident
-  // wave of its workgroups. Either way a chunk is at least four streaming
-  // units long (one unit: one vector per thread).
+  // Pass-2 chunks: the second launch sizes them on the device, once the
+  // number of sequences with a pending draw is known, as many per row as fill
+  // one resident wave of its workgroups, each at least four streaming units
+  // long (one unit: one vector per thread).
   {
     const int unit = kThreads * (bf16 ? 8 : 4);
     const long long cap = std::max<long long>(1, (V + 4 * unit - 1) / (4 * unit));
-    const int forced = env_int("SV_P2_CHUNKS", 0);
-    const long long resident = (long long)cus * occupancy(dev, bf16, vec);
-    long long c2 = forced > 0 ? forced : (2 * resident + B - 1) / B;
-    c2 = std::max<long long>(1, std::min<long long>(c2, cap));
-    long long len = (V + c2 - 1) / c2;
-    len = (len + unit - 1) / unit * unit;
-    a.p2_chunk = (int32_t)len;
-    a.p2_nchunks = (int32_t)((V + len - 1) / len);
     a.p2_stride = max_chunks(V);
     a.p2_unit = unit;
     a.p2_cap = (int32_t)cap;
-    a.p2_force = forced > 0 ? (int32_t)std::min<long long>(forced, cap) : 0;
+    a.p2_force = forced_p2 > 0 ? (int32_t)std::min<long long>(forced_p2, cap) : 0;
     const long long resident2 = (long long)cus * p2_occupancy(dev, bf16, vec);
     const long long grid2 = a.p2_force > 0 ? (long long)B * a.p2_force : std::max<long long>(resident2, B);
     if (grid2 >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
@@ -221,6 +198,7 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   a.key1 = (uint32_t)(seed >> 32);
   a.ctr_accept = (uint32_t)(2u * (uint32_t)offset);
   a.ctr_noise = (uint32_t)(2u * (uint32_t)offset + 1u);
+  a.seq_base = seq_base;
   a.out_tokens = out_tokens;
   a.out_n = out_n;
   if (diag) {
@@ -234,35 +212,15 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   a.p1 = (P1Slot*)(ws + L.p1);
   a.p2 = (P2Slot*)(ws + L.p2);
   a.work = (uint32_t*)(ws + L.work);
-  // Two launches by default (measured faster on MI355X: pass 1 keeps eight
-  // waves per SIMD streaming); one fused launch on request.
-  a.fused = env_int("SV_FUSED", 0) ? 1 : 0;
   a.spin_limit = 1u << 22;
-  // Lags of the fused launch: about one resident GPU of workgroups between
-  // the pass-1 items of a sequence and its decision, so that the decision
-  // rarely waits, and half as many again before its pass-2 items, which
-  // wait for the decision.
   const long long n1 = (long long)gamma * tl.nchunks * (draft ? 2 : 1);
-  const long long per = n1 + 1 + a.p2_nchunks;
-  const long long resident = (long long)cus * occupancy(dev, bf16, vec);
-  const long long lag = (resident + per - 1) / per + 1;
-  a.lag = (int32_t)std::min<long long>(lag, 1 << 20);
-  a.lag2 = (int32_t)std::min<long long>(lag + (lag + 1) / 2, 1 << 20);
-  const int forced_lag = env_int("SV_LAG", -1), forced_lag2 = env_int("SV_LAG2", -1);
-  if (forced_lag >= 0) a.lag = std::min(forced_lag, 1 << 20);
-  if (forced_lag2 >= 0) a.lag2 = a.lag + std::min(forced_lag2, 1 << 20);
-  if (a.lag2 < a.lag) a.lag2 = a.lag;
-  if ((long long)(B + a.lag2) * per >= (1ll << 31) || (long long)B * (n1 + 1) >= (1ll << 31))
-    return SV_ERR_BAD_SHAPE;
+  if ((long long)B * (n1 + 1) >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
 
+  // Two launches: pass 1 over every (sequence, position, chunk) followed by
+  // the decisions, then pass 2.
   hipStream_t s = (hipStream_t)stream;
-  if (a.fused) {
-    if (launch_chain(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
-  } else {
-    // Two launches: pass 1 over every (sequence, position, chunk), then pass 2.
-    if (launch_chain_p1(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
-    if (launch_chain_p2(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
-  }
+  if (launch_chain_p1(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_chain_p2(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 
@@ -298,18 +256,33 @@ const char* sv_status_string(sv_status_t status) {
 sv_status_t spec_verify_sample(const void* target_logits, int64_t target_row_stride, const void* draft_logits,
                                int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* draft_ids,
                                const float* temperature, int32_t B, int32_t gamma, int32_t V, uint64_t seed,
-                               uint64_t offset, int32_t* out_tokens, int32_t* out_num_accepted,
+                               uint64_t offset, uint32_t seq_base, int32_t* out_tokens, int32_t* out_num_accepted,
                                const sv_diag_t* diag, void* workspace, size_t workspace_bytes, void* stream) {
   if (!temperature) return SV_ERR_NULL_ARG;
   return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, dtype, draft_ids,
-                       temperature, B, gamma, V, seed, offset, out_tokens, out_num_accepted, diag, workspace,
-                       workspace_bytes, stream);
+                       temperature, B, gamma, V, seed, offset, seq_base, out_tokens, out_num_accepted, diag,
+                       workspace, workspace_bytes, stream);
+}
+
+sv_status_t sv_debug_sample_tiled(const void* target_logits, int64_t target_row_stride, const void* draft_logits,
+                                  int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* draft_ids,
+                                  const float* temperature, int32_t B, int32_t gamma, int32_t V, uint64_t seed,
+                                  uint64_t offset, uint32_t seq_base, int32_t* out_tokens,
+                                  int32_t* out_num_accepted, const sv_diag_t* diag, void* workspace,
+                                  size_t workspace_bytes, void* stream, int32_t p1_vectors, int32_t p2_chunks) {
+  if (!temperature) return SV_ERR_NULL_ARG;
+  if (p1_vectors < 0 || p1_vectors > sv::kMaxVecsPerThread || (p1_vectors & (p1_vectors - 1)) != 0 ||
+      p2_chunks < 0)
+    return SV_ERR_BAD_ARG;
+  return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, dtype, draft_ids,
+                       temperature, B, gamma, V, seed, offset, seq_base, out_tokens, out_num_accepted, diag,
+                       workspace, workspace_bytes, stream, p1_vectors, p2_chunks);
 }
 
 sv_status_t spec_verify_greedy(const void* target_logits, int64_t target_row_stride, sv_dtype_t dtype,
                                const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
                                int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
-  return sv::run_chain(target_logits, target_row_stride, nullptr, 0, dtype, draft_ids, nullptr, B, gamma, V, 0, 0,
+  return sv::run_chain(target_logits, target_row_stride, nullptr, 0, dtype, draft_ids, nullptr, B, gamma, V, 0, 0, 0,
                        out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes, stream);
 }
 
@@ -354,7 +327,6 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
   a.done = (uint32_t*)(ws + L.done);
   a.slot = (sv::TreeSlot*)(ws + L.tree_slot);
   const bool vec = sv::aligned16(target_logits, a.t_stride);
-  a.fused = sv::env_int("SV_FUSED", 1) ? 1 : 0;
   a.spin_limit = 1u << 22;
   int dev = 0, cus = 0;
   if (!sv::device_info(&dev, &cus)) return SV_ERR_HIP;
@@ -363,8 +335,6 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
   const long long n1 = (long long)N * tl.nchunks;
   const long long resident = (long long)cus * sv::tree_occupancy_cached(dev, bf16, vec);
   a.lag = (int32_t)std::min<long long>((resident + n1 - 1) / n1 + 1, 1 << 20);
-  const int forced_lag = sv::env_int("SV_LAG", -1);
-  if (forced_lag >= 0) a.lag = forced_lag;
   return sv::launch_tree(a, bf16, vec, (hipStream_t)stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -374,7 +344,8 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
                                     int64_t draft_row_stride, sv_dtype_t dtype, const int32_t* parents,
                                     const int32_t* depth, const int32_t* node_tokens, const float* temperature,
                                     int32_t B, int32_t N, int32_t V, int32_t max_depth, uint64_t seed,
-                                    uint64_t offset, int32_t siblings_without_replacement, int32_t* out_path,
+                                    uint64_t offset, uint32_t seq_base, int32_t siblings_without_replacement,
+                                    int32_t* out_path,
                                     int32_t* out_path_len, int32_t* out_token, void* workspace,
                                     size_t workspace_bytes, void* stream) {
   if (!target_logits || !draft_logits || !parents || !depth || !node_tokens || !temperature || !out_path ||
@@ -387,6 +358,7 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
   if (target_row_stride < V || draft_row_stride < V) return SV_ERR_BAD_ARG;
   if (offset >= (1ull << 31)) return SV_ERR_BAD_ARG;
   if (siblings_without_replacement != 0 && siblings_without_replacement != 1) return SV_ERR_BAD_ARG;
+  if ((uint64_t)seq_base + (uint64_t)B > (1ull << 32)) return SV_ERR_BAD_ARG;
   const size_t need = sv_workspace_bytes(B, N, V);
   const sv_status_t ws_ok = sv::check_workspace(workspace, workspace_bytes, need);
   if (ws_ok != SV_OK) return ws_ok;
@@ -420,6 +392,7 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
   c.key1 = (uint32_t)(seed >> 32);
   c.ctr_accept = (uint32_t)(2u * (uint32_t)offset);
   c.ctr_noise = (uint32_t)(2u * (uint32_t)offset + 1u);
+  c.seq_base = seq_base;
   c.done = (uint32_t*)(ws + L.done);
   c.seq = (sv::SeqState*)(ws + L.seq);
   c.p1 = (sv::P1Slot*)(ws + L.p1);
@@ -442,7 +415,7 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
   // Walk: about 8K elements of a row per workgroup (whole streaming rounds),
   // and as many sequences per launch as keep every workgroup resident.
   const int unit = sv::kThreads * (bf16 ? 8 : 4);
-  const int per_wg = std::max(unit, sv::env_int("SV_TREE_WLEN", 8192));
+  const int per_wg = std::max(unit, 8192);
   const int w0 = std::max(1, (V + per_wg - 1) / per_wg);
   a.wlen = ((V + w0 - 1) / w0 + unit - 1) / unit * unit;
   // At most 256 workgroups per sequence (each stages the parts, one per thread).

@@ -19,19 +19,12 @@
 //     Gumbel-max (or argmax) over chunk c of the row the decision names. The
 //     last pass-2 item of b to finish merges the partials and writes the last
 //     token.
-// By default two launches run them: every pass-1 item followed by the
-// decision items (which wait, boundedly, for slots of items dispatched before
-// them), then pass 2, which finds every decision taken; pass 1 then runs at
-// eight waves per SIMD and keeps the most row chunks in flight. One fused
-// launch is also available: workgroup ids are laid out in groups, group g
-// holding the pass-1 items of sequence g, the decision item of sequence g - Ld
-// and the pass-2 items of sequence g - L2 (L2 >= Ld; ids naming no sequence
-// exit at once), so that the decisions and pass 2 of earlier sequences run
-// while later ones stream pass 1. The dispatcher starts workgroups in id
-// order, so whatever an item waits for has a smaller id and is already
-// running; every wait is bounded regardless. Merges run in fixed chunk order,
-// so results do not depend on the launch layout or on which item finishes
-// last.
+// Two launches run them: every pass-1 item followed by the decision items
+// (which wait, boundedly, for slots of items dispatched before them), then
+// pass 2, which finds every decision taken; pass 1 then runs at eight waves
+// per SIMD and keeps the most row chunks in flight. Merges run in fixed chunk
+// order, so results do not depend on the launch layout or on which item
+// finishes last.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -39,7 +32,14 @@ namespace sv {
 
 namespace {
 
-enum SeqKind { KIND_BAD_T = 0, KIND_GREEDY = 1, KIND_SAMPLED = 2, KIND_BAD_ID = 3, KIND_STALLED = 4 };
+enum SeqKind {
+  KIND_BAD_T = 0,
+  KIND_GREEDY = 1,
+  KIND_SAMPLED = 2,
+  KIND_BAD_ID = 3,
+  KIND_STALLED = 4,
+  KIND_BAD_LOGITS = 5  // a row of a sampled sequence defines no distribution
+};
 
 // The decision of one sequence, as every pass-2 item of it computes it.
 struct Decision {
@@ -338,10 +338,44 @@ __device__ __forceinline__ LseState lse_packed_bf16(u32x4 (&q)[kMaxVecsPerThread
 // Argmax of the chunk [lo, lo + chunk) (lowest index among equal values): the
 // block maximum first, then the lowest index holding it, searched only by the
 // threads that hold it.
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_i16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Whether this thread holds a positive element the packed-f16 maximum cannot
+// see: +inf, a NaN with the sign bit clear, or a value of 2^121 or more (bit
+// patterns from 0x7C00 up). Positive bf16 values order like their patterns
+// read as signed 16-bit integers, so one packed integer maximum finds them.
+__device__ __forceinline__ bool has_huge_positive_bf16(const u32x4 (&q)[kMaxVecsPerThread]) {
+  uint32_t m0 = 0x80008000u, m1 = 0x80008000u;
+#pragma unroll
+  for (int k = 0; k < kMaxVecsPerThread; ++k) {
+    m0 = pk_max_i16(m0, q[k][0]);
+    m1 = pk_max_i16(m1, q[k][1]);
+    m0 = pk_max_i16(m0, q[k][2]);
+    m1 = pk_max_i16(m1, q[k][3]);
+  }
+  const uint32_t m = pk_max_i16(m0, m1);
+  return (int16_t)(m & 0xFFFFu) >= 0x7C00 || (int16_t)(m >> 16) >= 0x7C00;
+}
+
+// Returns index 0x7FFFFFFF when the packed search cannot decide the chunk:
+// a positive element it cannot see (see has_huge_positive_bf16), or a chunk
+// whose maximum reads as -inf (every element -inf, or some at or below
+// -2^121). The caller then scans the chunk element by element.
 __device__ __forceinline__ ArgMax argmax_packed_bf16(u32x4 (&q)[kMaxVecsPerThread], int lo, Smem& sm) {
-  const float m = packed_max_bf16(q);
+  float m = packed_max_bf16(q);
+  if (has_huge_positive_bf16(q)) m = INFINITY;
   opaque(q);
   const float bm = block_max(m, sm);
+  if (bm == INFINITY || bm == -INFINITY) {
+    ArgMax r;
+    r.v = bm;
+    r.i = 0x7FFFFFFF;
+    return r;
+  }
   int idx = 0x7FFFFFFF;
   if (m == bm) {
 #pragma unroll
@@ -490,7 +524,7 @@ __device__ void write_decision(const ChainArgs& a, int b, Smem& sm) {
 }
 
 template <bool BF16>
-__device__ void decide(const ChainArgs& a, int b, Smem& sm) {
+__device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
   const int G = a.gamma, C = a.nchunks, tid = threadIdx.x;
   const int32_t* ids = a.ids + (int64_t)b * G;
   float T;
@@ -512,7 +546,9 @@ __device__ void decide(const ChainArgs& a, int b, Smem& sm) {
     sm.rg[tid].v = -INFINITY;
     sm.rg[tid].i = -1;
   }
-  if (tid == 0) sm.stalled = 0u;
+  // A workspace left dirty by a call whose bounded wait gave up (its control
+  // word still set) decides nothing: the sequence reports SV_SEQ_INTERNAL.
+  if (tid == 0) sm.stalled = (xload(&a.done[1]) != 0u) ? 1u : 0u;
   __syncthreads();
   if (kind != KIND_BAD_T) {
     // Wait for every slot (also when a drafted id turns out to be invalid, so
@@ -574,22 +610,29 @@ __device__ void decide(const ChainArgs& a, int b, Smem& sm) {
   if (sm.stalled) kind = KIND_STALLED;
 
   // Accept tests, one thread per position.
+  if (tid == 0) sm.flag_last = 0u;  // set below if some row has no distribution
+  __syncthreads();
   if (tid < G && kind == KIND_SAMPLED) {
     const float z2t = sm.rt[tid].M * c2 + fast_log2(sm.rt[tid].s);
     const float lp2 = __builtin_fmaf(glt, c2, -z2t);
     float z2d = NAN, lq2 = 0.0f;
+    bool finite = __builtin_isfinite(z2t);
     if (a.draft != nullptr) {
       z2d = sm.rd[tid].M * c2 + fast_log2(sm.rd[tid].s);
       lq2 = __builtin_fmaf(gld, c2, -z2d);
+      finite = finite && __builtin_isfinite(z2d);
     }
+    // A row with no entry above -inf, or with +inf or NaN, has no softmax.
+    if (!finite) atomicOr(&sm.flag_last, 1u);
     const float acc_p = fast_exp2(fminf(0.0f, lp2 - lq2));
-    const Words4 w = philox10(0u, (uint32_t)tid, (uint32_t)b, a.ctr_accept, a.key0, a.key1);
+    const Words4 w = philox10(0u, (uint32_t)tid, a.seq_base + (uint32_t)b, a.ctr_accept, a.key0, a.key1);
     sm.acc[tid] = (uniform_accept(w.w[0]) < acc_p) ? 1 : 0;
     sm.rt[tid].M = z2t;  // from here on: the row normalizers and a_i
     sm.rd[tid].M = z2d;
     sm.rt[tid].s = acc_p;
   }
   __syncthreads();
+  if (kind == KIND_SAMPLED && sm.flag_last) kind = KIND_BAD_LOGITS;
   if (tid == 0) {
     Decision d;
     d.kind = kind;
@@ -608,6 +651,8 @@ __device__ void decide(const ChainArgs& a, int b, Smem& sm) {
       d.n = -1;
     } else if (kind == KIND_STALLED) {
       d.n = -4;
+    } else if (kind == KIND_BAD_LOGITS) {
+      d.n = -5;
     } else if (kind == KIND_GREEDY) {
       d.n = G;
       for (int i = 0; i < G; ++i)
@@ -645,11 +690,11 @@ __device__ void decide(const ChainArgs& a, int b, Smem& sm) {
   __syncthreads();
   write_decision(a, b, sm);
   // Publish the record for the pass-2 items: the payload, then (once it has
-  // landed) the word they wait on. With two launches only a sequence with a
-  // pending draw has pass-2 items; it is appended to the work list.
+  // landed) the word that marks it complete. Only a sequence with a pending
+  // draw has pass-2 items; it is appended to the work list.
   if (tid == 0) {
     const Decision& d = sm.dec;
-    if (a.fused || d.mode != P2_NONE) {
+    if (d.mode != P2_NONE) {
       SeqState* st = a.seq + b;
       xput64(&st->dec[1], pack(d.zt2, __float_as_uint(d.zd2)));
       xput64(&st->dec[2], pack(d.c2, __float_as_uint(d.invT)));
@@ -657,7 +702,7 @@ __device__ void decide(const ChainArgs& a, int b, Smem& sm) {
       wait_vmem();
       xput64(&st->dec[0], kRecPublished | ((uint64_t)(uint32_t)d.row << 32) | ((uint32_t)(d.n + 64) << 8) | d.mode);
     }
-    if (!a.fused && d.mode != P2_NONE) {
+    if (d.mode != P2_NONE) {
       const uint32_t idx = atomicAdd(&a.done[kDoneNWork], 1u);
       if (idx < (uint32_t)a.B) xput(&a.work[idx], (uint32_t)b);
       else atomicOr(&a.done[1], 1u);  // a list left over from an aborted call
@@ -675,7 +720,7 @@ __device__ __forceinline__ int p1_items_per_seq(const ChainArgs& a) {
 }
 
 template <bool BF16, bool VEC>
-__device__ void pass1_item(const ChainArgs& a, int b, int r, Smem& sm) {
+__device__ __forceinline__ void pass1_item(const ChainArgs& a, int b, int r, Smem& sm) {
   const int GC = a.gamma * a.nchunks;
   const bool draft_item = r >= GC;  // item of a dense draft row
   if (draft_item) r -= GC;
@@ -697,13 +742,21 @@ __device__ void pass1_item(const ChainArgs& a, int b, int r, Smem& sm) {
   if (kind == KIND_GREEDY) {
     ArgMax m;
     if (fast) m = argmax_packed_bf16(ch.q, lo, sm);
-    // (The packed search can miss only for subnormal maxima flushed by the
-    // f16 comparison; then the plain scan decides.)
+    // The plain scan decides where the packed search cannot: elements outside
+    // the f16 reading's range (see argmax_packed_bf16), or a maximum flushed
+    // as an f16 subnormal.
     if (!fast || m.i == 0x7FFFFFFF) m = block_argmax(chunk_argmax(ch, row, a.kv), sm);
     w0 = pack(m.v, (uint32_t)(m.i + 1));
   } else {
     const float c2 = kLog2e / T;
-    const LseState st = block_lse(fast ? lse_packed_bf16(ch.q, c2) : chunk_lse(ch, row, a.kv, c2), c2, sm, 0);
+    LseState st = block_lse(fast ? lse_packed_bf16(ch.q, c2) : chunk_lse(ch, row, a.kv, c2), c2, sm, 0);
+    // The packed maximum skips elements of magnitude 2^121 or more, +inf and
+    // NaN. A skipped element above the maximum overflows the sum (+inf or
+    // NaN), and a chunk whose every element is skipped or -inf reads as -inf:
+    // in both cases the plain scan takes the chunk again. (If the row has no
+    // distribution, its statistics stay non-finite and the decision reports
+    // the sequence.)
+    if (fast && (!(st.s <= 3.0e38f) || st.M == -INFINITY)) st = block_lse(chunk_lse(ch, row, a.kv, c2), c2, sm, 0);
     const uint64_t w = pack(st.M, __float_as_uint(st.s));
     if (draft_item) w1 = w;
     else w0 = w;
@@ -748,7 +801,7 @@ __device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int 
   const uint8_t* rd = residual ? draft_row(a, b, dec.row) : nullptr;
   const float c2 = dec.c2, invT = dec.invT, zt2 = dec.zt2, zd2 = dec.zd2;
   const int xex = dec.x;
-  const uint32_t crow = (uint32_t)dec.row, cseq = (uint32_t)b;
+  const uint32_t crow = (uint32_t)dec.row, cseq = a.seq_base + (uint32_t)b;
   const uint32_t ctr3 = a.ctr_noise, k0 = a.key0, k1 = a.key1;
   Best bst;
   bst.s = -INFINITY;
@@ -897,42 +950,47 @@ __device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int 
   out->w1 = pack(bsum, (uint32_t)bany);
 }
 
-// How many rounds ahead (0 or 1) the bf16 Gumbel loop loads its vectors. With
-// few waves per SIMD, as at the end of the pass or for small batches, a
-// round's load latency is otherwise exposed; the lead costs 4 registers per
-// row read.
-#ifndef SV_P2_DEPTH
-#define SV_P2_DEPTH 1
-#endif
-constexpr int kP2Depth = SV_P2_DEPTH;
-static_assert(kP2Depth == 0 || kP2Depth == 1, "lead of 0 or 1 round");
-
-// One chunk of a Gumbel-max draw over 16-byte-aligned bf16 rows. Each lane
-// takes one 8-element vector per round (prefetched a round ahead), forms the
-// Philox words of its two 4-element blocks and a cheap, conservative pruning
-// test; only the survivors get their exact score and noise. The first round
-// seeds the wave's threshold L with the exact total of its highest-scoring
-// element. L is wave-uniform and rises whenever a survivor beats it, or
-// another wave of the workgroup (through LDS) or another workgroup of the
-// same row (through the sequence record, read one round late) reports a
-// higher total.
 // Wave priority from progress through a chunk: 3 in its first quarter of
 // rounds, down to 0 in its last. The pass-2 workgroups of a launch start
 // together with equal work, and a SIMD otherwise issues its oldest wave
 // first, so those dispatched last would finish last by far; a wave that is
 // ahead now yields to those behind it. (Wave priority only, set with
-// s_setprio; the queues and streams keep their default priority.)
-__device__ __forceinline__ void set_phase_priority(int rnd, int rounds) {
-  const int ph = (4 * rnd) / rounds;
-  if (rnd > 0 && ph == (4 * (rnd - 1)) / rounds) return;
-  if (ph == 0) __builtin_amdgcn_s_setprio(3);
-  else if (ph == 1) __builtin_amdgcn_s_setprio(2);
-  else if (ph == 2) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-}
+// s_setprio; the queues and streams keep their default priority.) The
+// rounds at which the level drops are computed once per chunk.
+struct PhaseTable {
+  int r1, r2, r3;  // first round of the second, third and fourth quarter
+  __device__ __forceinline__ explicit PhaseTable(int rounds) {
+    r1 = (rounds + 3) / 4;          // smallest r with 4 r >= rounds
+    r2 = (2 * rounds + 3) / 4;
+    r3 = (3 * rounds + 3) / 4;
+  }
+  __device__ __forceinline__ void set(int rnd) const {
+    if (rnd != 0 && rnd != r1 && rnd != r2 && rnd != r3) return;
+    const int ph = (rnd >= r1) + (rnd >= r2) + (rnd >= r3);
+    if (ph == 0) __builtin_amdgcn_s_setprio(3);
+    else if (ph == 1) __builtin_amdgcn_s_setprio(2);
+    else if (ph == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
+};
 
+// One chunk of a Gumbel-max draw over 16-byte-aligned bf16 rows. Each lane
+// takes one 8-element vector per round, loaded two rounds ahead (three
+// vector buffers that rotate by unrolling the loop three times, so that no
+// register move waits for a load in flight), forms the Philox words of its
+// two 4-element blocks and a cheap, conservative pruning test; only the
+// survivors get their exact score and noise. The first round seeds the
+// wave's threshold L with the exact total of its highest-scoring element. L
+// is wave-uniform and rises whenever a survivor beats it, or another wave of
+// the workgroup (through LDS) or another workgroup of the same row (through
+// the sequence record, read once every three rounds) reports a higher total.
+// The residual's bulk test bounds its score by log2 p alone (ln (p - q) <=
+// ln p), reading only the target vector; the tighter bound on log2 (p - q)
+// and the candidacy test p > q are applied only in waves where some element
+// passes the first test (about one wave-round in a hundred at the large
+// workloads).
 template <int MODE, bool BETA, bool EXCL = false>
-__device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm,
+__device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm,
                                   P2Slot* out, const int32_t* excl = nullptr, int nexcl = 0) {
   using E = Elem<true>;
   constexpr bool residual = (MODE == P2_RESIDUAL);
@@ -941,7 +999,7 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
   const uint8_t* rd = residual ? draft_row(a, b, dec.row) : nullptr;
   const float c2 = dec.c2, invT = dec.invT, zt2 = dec.zt2, zd2 = dec.zd2;
   const int xex = dec.x;
-  const uint32_t crow = (uint32_t)dec.row, cseq = (uint32_t)b;
+  const uint32_t crow = (uint32_t)dec.row, cseq = a.seq_base + (uint32_t)b;
   const uint32_t ctr3 = a.ctr_noise, k0 = a.key0, k1 = a.key1;
   const int lane = (int)(threadIdx.x & 63);
   Best bst;
@@ -955,7 +1013,6 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
   constexpr bool want_beta = residual && BETA;
   float Lpost = -INFINITY;  // the largest total this wave has reported
   uint32_t* const gkey = &a.seq[b].lbest;
-  uint32_t gnext = 0u;      // the sequence's key, loaded a round ahead
   auto set_L = [&](float l) {
     L = l;
     nL2 = -L * kLog2e;
@@ -978,32 +1035,36 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
   };
   // Bounds of the fast test for the current L: the pattern of n is compared
   // with b 2^23 + log_bias, b an upper bound on the score in log2 units (l c2
-  // for the bonus draws). log_bias stays finite (no threshold yet: everything
-  // passes), so that b = -inf (p <= q) always fails.
-  float c2s = 0.0f, log_bias = 0x1p120f;
+  // for the bonus draws, l c2 - zt2 = log2 p for the residual's bulk test).
+  // log_bias stays finite (no threshold yet: everything passes), so that
+  // b = -inf always fails. The residual's bulk bias carries zt2 and 2^-11 of
+  // slack on top of the exact test's 2^-12, which covers its two extra
+  // roundings: the bulk test then passes every element the exact one does.
+  float c2s = 0.0f, log_bias = 0x1p120f, bulk_bias = 0x1p120f;
   auto set_bounds = [&]() {
     c2s = c2 * 0x1p23f;
     log_bias = __builtin_fminf((nL2 + (33.0f + 127.0f + 0x1p-12f)) * 0x1p23f, 0x1p120f);
+    bulk_bias = residual ? __builtin_fminf((nL2 - zt2 + (33.0f + 127.0f + 0x1p-12f + 0x1p-11f)) * 0x1p23f, 0x1p120f)
+                         : log_bias;
   };
   set_bounds();
   const int nfull = (hi - lo) / 8;
-  constexpr int D = kP2Depth;
-  u32x4 qt[D + 1], qd[D + 1];  // qt[0], qd[0]: this round's vectors
   const int vi0 = (int)threadIdx.x;
+  // A lane past the last whole vector loads the last one again (discarded),
+  // so that every load is issued by the whole wave.
   auto fetch = [&](int vi, u32x4& qt, u32x4& qd) {
-    if (vi < nfull) {
-      qt = load_vec_stream(rt + (int64_t)(lo + vi * 8) * 2);
-      if (residual) qd = load_vec_stream(rd + (int64_t)(lo + vi * 8) * 2);
-    }
+    const int v = min(vi, nfull - 1);
+    qt = load_vec_stream(rt + (int64_t)(lo + v * 8) * 2);
+    if (residual) qd = load_vec_stream(rd + (int64_t)(lo + v * 8) * 2);
   };
-#pragma unroll
-  for (int j = 0; j < (D > 0 ? D : 1); ++j) fetch(vi0 + j * kThreads, qt[j], qd[j]);
+  const int rounds = (nfull + kThreads - 1) / kThreads;  // same for every lane
+  u32x4 qa, qb, qc, da, db, dc;
+  if (rounds > 0) fetch(vi0, qa, da);
+  if (rounds > 1) fetch(vi0 + kThreads, qb, db);
   // The first vectors have landed before the loop (vmcnt(0)): inside it the
-  // compiler then waits only for the vectors of the round it works on, not for
-  // the prefetches of the next.
+  // compiler then waits only for the vectors of the round it works on, not
+  // for the loads of the next two.
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  const u32x4& qt0 = qt[0];  // the seed's vectors
-  const u32x4& qd0 = qd[0];
   {
     // Seed L: every lane's highest-scoring element of its first vector gets
     // its exact total, and L starts at the largest of them over the
@@ -1017,10 +1078,10 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
       for (int e = 0; e < 8; ++e) {
         float k;
         if (residual) {
-          const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
+          const float lp2 = __builtin_fmaf(el(qa, e), c2, -zt2), lq2 = __builtin_fmaf(el(da, e), c2, -zd2);
           k = lp2 > lq2 ? residual_log2_bound(lp2, lq2) : -INFINITY;
         } else {
-          k = (onehot && base + e == xex) ? -INFINITY : el(qt0, e);
+          k = (onehot && base + e == xex) ? -INFINITY : el(qa, e);
         }
         if (EXCL && in_list(excl, nexcl, base + e)) k = -INFINITY;
         if (k > key) {
@@ -1035,8 +1096,8 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e == ke) {
-          klt = el(qt0, e);
-          if (residual) kld = el(qd0, e);
+          klt = el(qa, e);
+          if (residual) kld = el(da, e);
         }
       const int kidx = base + ke;
       t0 = total(klt, kld, word_at(philox10((uint32_t)kidx >> 2, crow, cseq, ctr3, k0, k1), kidx & 3));
@@ -1053,16 +1114,16 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
       set_bounds();
     }
   }
-  const int rounds = (nfull + kThreads - 1) / kThreads;  // same for every lane
-  // One round over vectors qt0/qd0, starting the load of round rnd + D into
-  // qn/dn. (A deeper lead would need the loop unrolled, to rotate buffers
-  // without moves that wait for the loads, and costs more registers than the
-  // waves it would save.)
-  auto round = [&](int rnd, const u32x4& qt0, const u32x4& qd0, u32x4& qn, u32x4& dn) {
+  const PhaseTable phase(rounds);
+  // One round over the vectors qt0 / qd0 (whose loads were issued two rounds
+  // earlier).
+  auto round = [&](int rnd, const u32x4& qt0, const u32x4& qd0) __attribute__((always_inline)) {
+    // The three unrolled rounds are scheduled one after the other: left to
+    // interleave them, the compiler would hold three rounds' Philox words
+    // at once and lose occupancy.
+    __builtin_amdgcn_sched_barrier(0);
+    phase.set(rnd);
     const int vi = vi0 + rnd * kThreads;
-    // The sequence's best total, read now and used at the end of the round.
-    const uint32_t gk = xload(gkey);
-    if (D > 0) fetch(vi + D * kThreads, qn, dn);
     const bool have = vi < nfull;
     const int base = lo + vi * 8;
     // The Philox words first: they do not wait for the vectors.
@@ -1077,23 +1138,14 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
         beta += lp2 > lq2 ? fast_exp2(lp2) - fast_exp2(lq2) : 0.0f;
       }
     }
-    // The fast test of element e: its threshold t for the bit-pattern test
-    // of its noise word. For the residual it uses the bound on log2 (p - q)
-    // without first asking whether p > q (for p <= q the bound is at most
-    // log2 p - 100, which the survivor path then discards), and for one-hot
-    // draws it does not exclude the draft token (the survivor path does).
-    auto fast_t = [&](int e) -> float {
-      if (residual) {
-        const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
-        return __builtin_fmaf(residual_log2_bound(lp2, lq2), 0x1p23f, log_bias);
-      }
-      return __builtin_fmaf(el(qt0, e), c2s, log_bias);
-    };
+    // The bulk test of element e (target vector only). It does not exclude
+    // the one-hot draft token or ask whether p > q: the survivor path does.
     // Only whether some lane of the wave has a survivor is kept: the
     // verdicts are lane masks OR-ed on the scalar unit.
     uint64_t surv = 0ull;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) surv |= lanes_may_win((e < 4) ? wa.w[e & 3] : wb.w[e & 3], fast_t(e));
+    for (int e = 0; e < 8; ++e)
+      surv |= lanes_may_win((e < 4) ? wa.w[e & 3] : wb.w[e & 3], __builtin_fmaf(el(qt0, e), c2s, bulk_bias));
     surv &= __builtin_amdgcn_ballot_w64(have);
     if (surv != 0ull && have) {
       // One-hot: the draft token is excluded (xrel: its place in this vector,
@@ -1131,27 +1183,37 @@ __device__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec,
       Lpost = Ln;
     }
     const uint32_t lk = __builtin_amdgcn_readfirstlane(__hip_atomic_load(&sm.lkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-    Ln = fmaxf(Ln, fmaxf(key_total(lk), key_total(__builtin_amdgcn_readfirstlane(gk))));
+    Ln = fmaxf(Ln, key_total(lk));
     if (Ln > L) {
       set_L(Ln);
       set_bounds();
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  if (D == 0) {
-#pragma unroll 1
-    for (int rnd = 0; rnd < rounds; ++rnd) {
-      set_phase_priority(rnd, rounds);
-      if (rnd > 0) fetch(vi0 + rnd * kThreads, qt[0], qd[0]);
-      round(rnd, qt[0], qd[0], qt[0], qd[0]);
+  // The sequence's best total from the other workgroups of the row: loaded
+  // before the first of three rounds' vector loads and read after the third
+  // round, whose vectors were loaded after it (loads complete in order, so it
+  // costs no wait of its own).
+  auto take_global = [&](uint32_t gk) {
+    const float g = key_total(__builtin_amdgcn_readfirstlane(gk));
+    if (g > L) {
+      set_L(g);
+      set_bounds();
     }
-  } else {
+  };
 #pragma unroll 1
-    for (int rnd = 0; rnd < rounds; ++rnd) {
-      set_phase_priority(rnd, rounds);
-      round(rnd, qt[0], qd[0], qt[1], qd[1]);
-      qt[0] = qt[1];
-      if (residual) qd[0] = qd[1];
-    }
+  for (int rnd = 0; rnd < rounds; rnd += 2) {
+    const uint32_t gk = xload(gkey);
+    if (rnd + 2 < rounds) fetch(vi0 + (rnd + 2) * kThreads, qc, dc);
+    round(rnd, qa, da);
+    if (rnd + 1 >= rounds) break;
+    qa = qb;
+    if (residual) da = db;
+    if (rnd + 3 < rounds) fetch(vi0 + (rnd + 3) * kThreads, qb, db);
+    round(rnd + 1, qa, da);
+    qa = qc;
+    if (residual) da = dc;
+    take_global(gk);
   }
   // Elements past the last whole vector, one by one.
   const int tail_lo = lo + nfull * 8;
@@ -1294,7 +1356,14 @@ __device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks
       beta = 0.0f;
     }
     if (threadIdx.x == 0) {
-      a.out_tokens[(int64_t)b * (G + 1) + d.n] = m.i;
+      if (m.i >= 0) {
+        a.out_tokens[(int64_t)b * (G + 1) + d.n] = m.i;
+      } else {
+        // Nothing to draw from: a row with no entry above -inf (only the bonus
+        // row can be one, the others passed the decision's check).
+        for (int k = 0; k <= G; ++k) a.out_tokens[(int64_t)b * (G + 1) + k] = -1;
+        a.out_n[b] = -5;
+      }
       // One-hot draft: (p - delta_x)_+ has mass 1 - p(x) exactly.
       if (a.d_beta && d.mode == P2_RESIDUAL) a.d_beta[b] = beta;
       if (a.d_beta && d.mode == P2_RESIDUAL_ONEHOT) a.d_beta[b] = 1.0f - d.a_row;
@@ -1308,51 +1377,29 @@ __device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks
   if (threadIdx.x == 0) {
     xput(&a.seq[b].p2_arrive, 0u);
     xput(&a.seq[b].lbest, 0u);
-    if (!a.fused) {
-      // Every item on the work list has read it once all draws are done: the
-      // last sequence to finish returns the list to empty.
-      xput(&a.work[sm.unit[4]], 0u);
-      const uint32_t fin = atomicAdd(&a.done[kDoneNFinal], 1u) + 1u;
-      if (fin == sm.nwork) {
-        xput(&a.done[kDoneNWork], 0u);
-        xput(&a.done[kDoneNFinal], 0u);
-      }
+    // Every item on the work list has read it once all draws are done: the
+    // last sequence to finish returns the list to empty.
+    xput(&a.work[sm.unit[4]], 0u);
+    const uint32_t fin = atomicAdd(&a.done[kDoneNFinal], 1u) + 1u;
+    if (fin == sm.nwork) {
+      xput(&a.done[kDoneNWork], 0u);
+      xput(&a.done[kDoneNFinal], 0u);
     }
   }
 }
 
-// Reads the decision record of b (thread 0; bounded wait in the fused
-// launch). Returns false if the wait gave up.
+// Reads the decision record of b (thread 0). The first launch has completed,
+// so the record is complete: its four words in one round trip. Returns false
+// if it was never published (a wait of the first launch gave up).
 __device__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
   uint64_t* rec = a.seq[b].dec;
-  uint64_t d0, d1 = 0u, d2 = 0u, d3 = 0u;
-  if (!a.fused) {
-    // Two launches: the first has completed, so the record is complete; its
-    // four words in one round trip.
-    d0 = xget64(&rec[0]);
-    d1 = xget64(&rec[1]);
-    d2 = xget64(&rec[2]);
-    d3 = xget64(&rec[3]);
-    if (!(d0 & kRecPublished)) return false;
-  } else {
-    // Fused: wait for the word stored last, then read the others.
-    d0 = xget64(&rec[0]);
-  }
-  uint32_t spins = 0;
-  while (!(d0 & kRecPublished)) {
-    // Give up after spin_limit rounds, or soon after any other wait of this
-    // call gave up.
-    if (++spins > a.spin_limit || ((spins & 255u) == 0u && xget(&a.done[1]) != 0u)) {
-      atomicOr(&a.done[1], 1u);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(2);
-    d0 = xget64(&rec[0]);
-  }
-  if (a.fused) {
-    d1 = xget64(&rec[1]);
-    d2 = xget64(&rec[2]);
-    d3 = xget64(&rec[3]);
+  const uint64_t d0 = xget64(&rec[0]);
+  const uint64_t d1 = xget64(&rec[1]);
+  const uint64_t d2 = xget64(&rec[2]);
+  const uint64_t d3 = xget64(&rec[3]);
+  if (!(d0 & kRecPublished)) {
+    atomicOr(&a.done[1], 1u);
+    return false;
   }
   Decision d;
   d.kind = KIND_SAMPLED;  // not used by pass 2
@@ -1372,7 +1419,7 @@ __device__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
 }
 
 template <bool BF16, bool VEC, bool BETA>
-__device__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p2_nchunks, Smem& sm) {
+__device__ __forceinline__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p2_nchunks, Smem& sm) {
   if (threadIdx.x == 0) {
     Decision d;
     const bool ok = read_decision(a, b, &d);
@@ -1413,28 +1460,9 @@ __device__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p
 }
 
 // ---------------------------------------------------------------------------
-// Launch layouts.
+// Launches.
 // ---------------------------------------------------------------------------
-// Fused: group g = [pass-1 items of g][decision of g - lag_d][pass-2 items of
-// g - lag_2], for g in [0, B + lag_2).
-template <bool BF16, bool VEC, bool BETA>
-__global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
-  __shared__ Smem sm;
-  const int n1 = p1_items_per_seq(a), per = n1 + 1 + a.p2_nchunks;
-  const int g = (int)(blockIdx.x / (uint32_t)per);
-  const int r = (int)(blockIdx.x % (uint32_t)per);
-  if (r < n1) {
-    if (g < a.B) pass1_item<BF16, VEC>(a, g, r, sm);
-  } else if (r == n1) {
-    const int b = g - a.lag;
-    if (b >= 0 && b < a.B) decide<BF16>(a, b, sm);
-  } else {
-    const int b = g - a.lag2;
-    if (b >= 0 && b < a.B) pass2_item<BF16, VEC, BETA>(a, b, r - n1 - 1, a.p2_chunk, a.p2_nchunks, sm);
-  }
-}
-
-// Split, first launch: every pass-1 item, then one decision item per
+// First launch: every pass-1 item, then one decision item per
 // sequence (all pass-1 items have been dispatched before any decision).
 // Eight waves per SIMD: pass 1 is bound by how many row chunks are in flight.
 template <bool BF16, bool VEC>
@@ -1451,7 +1479,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   }
 }
 
-// Split, second launch: every decision is taken and the sequences with a
+// Second launch: every decision is taken and the sequences with a
 // pending draw are on the work list. Their rows are cut into as many chunks
 // as fill the launch's workgroups (one resident wave of them), and workgroup
 // u takes chunk u mod n of list entry u / n; the others have nothing to do.
@@ -1534,7 +1562,7 @@ struct TreeDrawn {
 // All threads: the children of node v in index order into kids[0 .. *nkids)
 // (an ordered compaction of the parent array, staged in LDS). wcnt: one word
 // per wave of scratch in LDS.
-__device__ void tree_children(int N, const int32_t* par, int v, int32_t* kids, int32_t* nkids, int32_t* wcnt) {
+__device__ __forceinline__ void tree_children(int N, const int32_t* par, int v, int32_t* kids, int32_t* nkids, int32_t* wcnt) {
   const int lane = (int)(threadIdx.x & 63), wv = (int)(threadIdx.x >> 6);
   int base = 0;
   for (int k0 = 0; k0 < N; k0 += kThreads) {
@@ -1575,7 +1603,7 @@ __device__ void tree_children(int N, const int32_t* par, int v, int32_t* kids, i
 // drawn tokens keep the values F they had then (the pass's sum is corrected
 // for them with their gathered logits).
 template <bool BF16>
-__device__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, TreeState& s, const int32_t* kids,
+__device__ __forceinline__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, TreeState& s, const int32_t* kids,
                                 int nkids, const uint8_t* haskid, const int32_t* tok_s, const uint64_t (*part)[2],
                                 int tree_bad, int tok_bad, bool writer, const TreeDrawn& dr) {
   using E = Elem<BF16>;
@@ -1658,7 +1686,7 @@ __device__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, 
   } else {
     acc = q > 0.0f ? fminf(1.0f, fmaxf(0.0f, p - s.A * q) / (s.Bv * q * sfac)) : 1.0f;
   }
-  const Words4 wu = philox10((uint32_t)s.round, (uint32_t)s.node, (uint32_t)b, a.ctr_accept, a.key0, a.key1);
+  const Words4 wu = philox10((uint32_t)s.round, (uint32_t)s.node, a.seq_base + (uint32_t)b, a.ctr_accept, a.key0, a.key1);
   if (uniform_accept(wu.w[0]) < acc) {
     if (writer && s.len <= ta.max_depth) xput(&path[s.len], c);
     s.len += 1;
@@ -1680,7 +1708,7 @@ __device__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, 
 // This workgroup's part of sum_v (p(v) - A q(v))_+ over [lo, hi), with the
 // factor A folded into the draft normalizer (zd2s = zd2 - log2 A).
 template <bool BF16, bool VEC>
-__device__ float residual_mass_part(const uint8_t* rt, const uint8_t* rd, int lo, int hi, float c2, float zt2,
+__device__ __forceinline__ float residual_mass_part(const uint8_t* rt, const uint8_t* rd, int lo, int hi, float c2, float zt2,
                                     float zd2s) {
   using E = Elem<BF16>;
   constexpr int EV = E::kPerVec;
@@ -1728,7 +1756,7 @@ __device__ float residual_mass_part(const uint8_t* rt, const uint8_t* rd, int lo
 // the last one took no part in the row's draw; each competes with its kept
 // value F instead (ln F plus its noise, keyed as the row's).
 template <bool BF16, bool VEC>
-__device__ void tree_finish(const TreeSampleArgs& ta, int b, int len, const P2Slot* parts, bool both_buffers,
+__device__ __forceinline__ void tree_finish(const TreeSampleArgs& ta, int b, int len, const P2Slot* parts, bool both_buffers,
                             int node, int ndrawn, const TreeDrawn& dr, Smem& sm) {
   const ChainArgs& a = ta.c;
   if (threadIdx.x == 0) {
@@ -1747,7 +1775,7 @@ __device__ void tree_finish(const TreeSampleArgs& ta, int b, int len, const P2Sl
       const int x = dr.x[i];
       ArgMax o;
       o.v = logf(dr.F[i]) +
-            gumbel(word_at(philox10((uint32_t)x >> 2, (uint32_t)node, (uint32_t)b, a.ctr_noise, a.key0, a.key1), x & 3));
+            gumbel(word_at(philox10((uint32_t)x >> 2, (uint32_t)node, a.seq_base + (uint32_t)b, a.ctr_noise, a.key0, a.key1), x & 3));
       o.i = x;
       m = argmax_merge(m, o);
     }
@@ -1957,17 +1985,6 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t nwords) {
 }
 
 template <bool BF16, bool VEC>
-hipError_t launch_chain_t(const ChainArgs& a, hipStream_t stream) {
-  const long long n1 = (long long)a.gamma * a.nchunks * (a.draft != nullptr ? 2 : 1);
-  const long long grid = (long long)(a.B + a.lag2) * (n1 + 1 + a.p2_nchunks);
-  if (a.d_beta)
-    hipLaunchKernelGGL((chain_kernel<BF16, VEC, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((chain_kernel<BF16, VEC, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <bool BF16, bool VEC>
 hipError_t launch_chain_p1_t(const ChainArgs& a, hipStream_t stream) {
   const long long n1 = (long long)a.gamma * a.nchunks * (a.draft != nullptr ? 2 : 1);
   hipLaunchKernelGGL((chain_p1_kernel<BF16, VEC>), dim3((unsigned)(a.B * (n1 + 1))), dim3(kThreads), 0, stream, a);
@@ -1984,19 +2001,7 @@ hipError_t launch_chain_p2_t(const ChainArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool BF16, bool VEC>
-int occupancy_t() {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chain_kernel<BF16, VEC, false>, kThreads, 0) != hipSuccess) n = 0;
-  return n;
-}
-
 }  // namespace
-
-hipError_t launch_chain(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream) {
-  if (bf16) return vec ? launch_chain_t<true, true>(a, stream) : launch_chain_t<true, false>(a, stream);
-  return vec ? launch_chain_t<false, true>(a, stream) : launch_chain_t<false, false>(a, stream);
-}
 
 hipError_t launch_chain_p1(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream) {
   if (bf16) return vec ? launch_chain_p1_t<true, true>(a, stream) : launch_chain_p1_t<true, false>(a, stream);
@@ -2018,11 +2023,6 @@ int p2_occupancy_t() {
 int chain_p2_occupancy(bool bf16, bool vec) {
   if (bf16) return vec ? p2_occupancy_t<true, true>() : p2_occupancy_t<true, false>();
   return vec ? p2_occupancy_t<false, true>() : p2_occupancy_t<false, false>();
-}
-
-int chain_occupancy(bool bf16, bool vec) {
-  if (bf16) return vec ? occupancy_t<true, true>() : occupancy_t<true, false>();
-  return vec ? occupancy_t<false, true>() : occupancy_t<false, false>();
 }
 
 template <bool BF16, bool VEC>

@@ -80,15 +80,15 @@ struct ChainArgs {
   int32_t chunk;    // elements per pass-1 chunk
   int32_t nchunks;  // pass-1 chunks per row
   int32_t kv;       // 16-byte vectors per thread per pass-1 chunk (<= kMaxVecsPerThread)
-  int32_t p2_chunk;    // fused launch: elements per pass-2 chunk
-  int32_t p2_nchunks;  // fused launch: pass-2 chunks per row
   int32_t p2_stride;   // pass-2 slots per sequence (>= any chunk count)
-  int32_t p2_grid;     // two launches: workgroups of the second launch
-  int32_t p2_cap;      // two launches: most pass-2 chunks per row
-  int32_t p2_force;    // two launches: chunks per row when > 0 (else sized to fill p2_grid)
+  int32_t p2_grid;     // workgroups of the pass-2 launch
+  int32_t p2_cap;      // most pass-2 chunks per row
+  int32_t p2_force;    // pass-2 chunks per row when > 0 (debug entry point only;
+                       // else sized to fill p2_grid)
   int32_t p2_unit;     // pass-2 chunk lengths are multiples of this
   uint32_t key0, key1;
   uint32_t ctr_accept, ctr_noise;  // counter word 3 of the two Philox streams
+  uint32_t seq_base;  // counter word 2 of sequence b is seq_base + b
   int32_t* out_tokens;
   int32_t* out_n;
   float* d_accept;
@@ -101,12 +101,8 @@ struct ChainArgs {
   SeqState* seq;      // [B]
   P1Slot* p1;         // [B, gamma, nchunks]
   P2Slot* p2;         // [B, p2_stride]
-  uint32_t* work;     // [B] two launches: sequences with pass-2 work, in the
-                      // order their decisions were taken
-  int32_t lag;        // fused launch: the decision of sequence k follows the
-                      // pass-1 items of k + lag,
-  int32_t lag2;       // and its pass-2 items those of k + lag2 (lag2 >= lag)
-  int32_t fused;      // one launch for both passes
+  uint32_t* work;     // [B] sequences with pass-2 work, in the order their
+                      // decisions were taken
   uint32_t spin_limit;
 };
 
@@ -143,7 +139,6 @@ struct TreeArgs {
   uint32_t* done;         // as in ChainArgs
   TreeSlot* slot;         // [B, N, nchunks]
   int32_t lag;            // the decision of sequence k follows the items of k + lag
-  int32_t fused;          // items and decisions in one launch
   uint32_t spin_limit;
 };
 
@@ -196,13 +191,11 @@ WsLayout ws_layout(int32_t B, int32_t rows, int32_t nchunks);
 int32_t max_chunks(int32_t V);
 
 // Launchers (host). Return hipSuccess or the first HIP error.
-hipError_t launch_chain(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_chain_p1(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_chain_p2(const ChainArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_tree(const TreeArgs& a, bool bf16, bool vec, hipStream_t stream);
 int tree_occupancy(bool bf16, bool vec);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
-int chain_occupancy(bool bf16, bool vec);
 int chain_p2_occupancy(bool bf16, bool vec);
 hipError_t launch_tree_sample_walk(const TreeSampleArgs& a, bool bf16, bool vec, hipStream_t stream);
 int tree_sample_walk_occupancy(bool bf16, bool vec);

@@ -125,9 +125,13 @@ __device__ void tree_decide(const TreeArgs& a, int b, TreeSmem& sm) {
   if (tid == 0) {
     sm.bad_tree = 0;
     sm.bad_tok = 0;
-    sm.stalled = 0;
+    // A workspace left dirty by a call whose bounded wait gave up decides
+    // nothing: every sequence reports SV_SEQ_INTERNAL.
+    sm.stalled = (xload(&a.done[1]) != 0u) ? 1 : 0;
     sm.maxdep = 0;
   }
+  // The flags are cleared before any wave can set one.
+  __syncthreads();
   // The tree description first: its loads overlap the slot polling below.
   for (int node = tid; node < N; node += kThreads) {
     sm.par[node] = (int16_t)max(-1, min(a.parents[node], kMaxTreeNodes));
@@ -240,32 +244,10 @@ __global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
     tree_decide(a, k, sm);
 }
 
-// The two kinds as separate launches.
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void tree_items_kernel(TreeArgs a) {
-  __shared__ TreeSmem sm;
-  const int per_seq = a.N * a.nchunks;
-  const int b = blockIdx.x / per_seq;
-  const int r = blockIdx.x % per_seq;
-  tree_item<BF16, VEC>(a, b, r / a.nchunks, r % a.nchunks, sm);
-}
-
-__global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeArgs a) {
-  __shared__ TreeSmem sm;
-  tree_decide(a, blockIdx.x, sm);
-}
-
 template <bool BF16, bool VEC>
 hipError_t launch_tree_t(const TreeArgs& a, hipStream_t stream) {
   const long long items = (long long)a.B * a.N * a.nchunks;
-  if (a.fused) {
-    hipLaunchKernelGGL((tree_kernel<BF16, VEC>), dim3((unsigned)(items + a.B)), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((tree_items_kernel<BF16, VEC>), dim3((unsigned)items), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tree_decide_kernel, dim3((unsigned)a.B), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((tree_kernel<BF16, VEC>), dim3((unsigned)(items + a.B)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
                           "sv_kv_rollback", "sv_ngram_draft", "sv_tree_mask",
                           "sv_workspace_bytes",
                           "sv_workspace_init", "sv_status_string", "sv_debug_philox", "sv_debug_noise",
-                          "sv_debug_wave_max", "sv_debug_read_stream"}
+                          "sv_debug_wave_max", "sv_debug_read_stream", "sv_debug_sample_tiled"}
     out = subprocess.run(["nm", "-D", "--defined-only", rsv.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     missing = [n for n in names if n not in exported]
@@ -68,11 +68,15 @@ class _Fake:
 def _sample(L, **kw):
     f = _Fake(1 << 20)
     args = dict(target=f.ptr, ts=1000, draft=f.ptr, ds=1000, dtype=1, ids=f.ptr, temp=f.ptr, B=4, gamma=3,
-                V=1000, seed=0, offset=0, tok=f.ptr, n=f.ptr, diag=None, ws=f.ptr, wsb=f.nbytes, stream=None)
+                V=1000, seed=0, offset=0, base=0, tok=f.ptr, n=f.ptr, diag=None, ws=f.ptr, wsb=f.nbytes,
+                stream=None, tiling=None)
     args.update(kw)
-    return L.spec_verify_sample(args["target"], args["ts"], args["draft"], args["ds"], args["dtype"], args["ids"],
-                                args["temp"], args["B"], args["gamma"], args["V"], args["seed"], args["offset"],
-                                args["tok"], args["n"], args["diag"], args["ws"], args["wsb"], args["stream"])
+    common = (args["target"], args["ts"], args["draft"], args["ds"], args["dtype"], args["ids"], args["temp"],
+              args["B"], args["gamma"], args["V"], args["seed"], args["offset"], args["base"], args["tok"],
+              args["n"], args["diag"], args["ws"], args["wsb"], args["stream"])
+    if args["tiling"] is not None:
+        return L.sv_debug_sample_tiled(*common, *args["tiling"])
+    return L.spec_verify_sample(*common)
 
 
 def test_sample_argument_validation(L):
@@ -84,6 +88,9 @@ def test_sample_argument_validation(L):
     assert _sample(L, dtype=7) == 3
     assert _sample(L, ts=999) == 4 and _sample(L, ds=10) == 4
     assert _sample(L, offset=1 << 31) == 4
+    assert _sample(L, base=(1 << 32) - 3) == 4 and _sample(L, base=(1 << 32) - 4, B=0) == 0
+    assert _sample(L, tiling=(3, 0)) == 4 and _sample(L, tiling=(16, 0)) == 4 and _sample(L, tiling=(0, -1)) == 4
+    assert _sample(L, tiling=(2, 5), B=0) == 0
     assert _sample(L, ws=None) == 5 and _sample(L, wsb=100) == 5
     f = _Fake(1 << 20)
     assert _sample(L, ws=ctypes.c_void_p(f.ptr.value + 16)) == 4  # misaligned workspace
@@ -123,12 +130,14 @@ def test_tree_sample_argument_validation(L):
     ts = lambda **k: L.spec_verify_tree_sample(k.get("t", P), k.get("ts", 100), k.get("d", P), k.get("ds", 100),
                                                k.get("dt", 1), k.get("par", P), P, P, k.get("temp", P),
                                                k.get("B", 2), k.get("N", 5), k.get("V", 100), k.get("md", 3),
-                                               0, k.get("off", 0), k.get("wor", 0), P, P, P, k.get("ws", P),
+                                               0, k.get("off", 0), k.get("base", 0), k.get("wor", 0), P, P, P,
+                                               k.get("ws", P),
                                                k.get("wsb", f.nbytes), None)
     assert ts(d=None) == 1 and ts(temp=None) == 1 and ts(par=None) == 1
     assert ts(N=0) == 2 and ts(N=1025) == 2 and ts(md=5) == 2 and ts(md=-1) == 2 and ts(B=-1) == 2
     assert ts(dt=2) == 3
     assert ts(ts=99) == 4 and ts(ds=99) == 4 and ts(off=1 << 31) == 4 and ts(wor=2) == 4
+    assert ts(base=(1 << 32) - 1) == 4
     assert ts(wsb=10) == 5
     assert ts(B=0) == 0
 
@@ -171,3 +180,11 @@ def test_tree_mask_argument_validation(L):
     assert tm(par=None) == 1 and tm(m=None) == 1
     assert tm(B=-1) == 2 and tm(N=0) == 2 and tm(N=1025) == 2 and tm(stride=-1) == 2 and tm(stride=7) == 2
     assert tm(B=0) == 0 and tm(B=0, stride=0) == 0
+
+
+def test_library_reads_no_environment(L):
+    """Tuning is fixed in the library or passed explicitly (sv_debug_sample_tiled):
+    the library imports no environment lookup."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", rsv.LIB_PATH], capture_output=True, text=True).stdout
+    imported = set(line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip())
+    assert not imported & {"getenv", "secure_getenv", "__secure_getenv"}

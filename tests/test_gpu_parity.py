@@ -128,63 +128,47 @@ def test_bad_inputs_per_sequence(dev):
     compare_chain(got, ref, label="bad")
 
 
-def test_deterministic_and_grid_invariant(dev, monkeypatch):
-    """Bitwise identical outputs across runs and launch layouts (two launches,
-    or one fused launch with any lags), and oracle-exact at any chunking."""
+def test_deterministic_and_grid_invariant(dev):
+    """Bitwise identical outputs across runs and tilings (pass-2 chunks per
+    row forced through the debug entry point), and oracle-exact at any pass-1
+    chunk length."""
     inp = make_chain("grid", 40, 6, 70001, bf16=True, seed=24, target_sigma=3.0, draft_sigma=(0.3, 1.5),
                      temperatures=(0.0, 0.7, 1.0))
     base = run_sample(inp, torch, dev)
     ref = oracle_sample(inp)
     compare_chain(base, ref, label="grid base")
-    F = {"SV_FUSED": "1"}
-    variants = [F, {**F, "SV_LAG": "0"}, {**F, "SV_LAG": "1"}, {**F, "SV_LAG": "3"}, {**F, "SV_LAG": "100000"},
-                {"SV_FUSED": "0", "SV_LAG": "0"}, {**F, "SV_LAG": "0", "SV_LAG2": "0"},
-                {**F, "SV_LAG": "1", "SV_LAG2": "9"}, {"SV_P2_CHUNKS": "1"}, {"SV_P2_CHUNKS": "3"},
-                {**F, "SV_P2_CHUNKS": "7"}, {"SV_P2_CHUNKS": "1000"}, {}]
-    for env in variants:
-        for k in ("SV_GRID", "SV_FUSED", "SV_LAG", "SV_LAG2", "SV_P2_CHUNKS"):
-            monkeypatch.delenv(k, raising=False)
-        for k, v in env.items():
-            monkeypatch.setenv(k, v)
-        got = run_sample(inp, torch, dev)
+    for tiling in ((0, 1), (0, 3), (0, 7), (0, 1000), (0, 5), None):
+        got = run_sample(inp, torch, dev, tiling=tiling)
         for key in ("tokens", "n", "accept_prob", "logz_target", "logz_draft"):
-            assert np.array_equal(got[key], base[key], equal_nan=True), (env, key)
+            assert np.array_equal(got[key], base[key], equal_nan=True), (tiling, key)
         # the residual mass is summed over pass-2 chunks: their count changes rounding only
         np.testing.assert_allclose(got["residual_mass"], base["residual_mass"], rtol=0, atol=1e-6)
-    for k in ("SV_GRID", "SV_FUSED", "SV_LAG", "SV_LAG2", "SV_P2_CHUNKS"):
-        monkeypatch.delenv(k, raising=False)
     # a different chunk length changes only rounding: still oracle-exact
-    for kv in ("1", "2", "8"):
-        monkeypatch.setenv("SV_KV", kv)
-        compare_chain(run_sample(inp, torch, dev), ref, label="kv " + kv)
-    monkeypatch.delenv("SV_KV", raising=False)
+    for kv in (1, 2, 8):
+        compare_chain(run_sample(inp, torch, dev, tiling=(kv, 0)), ref, label="kv %d" % kv)
 
 
-def test_onehot_launch_layouts(dev, monkeypatch):
-    """One-hot drafts at mixed accept lengths: one fused launch with any lags
-    and two launches give identical, oracle-exact outputs and leave the
-    workspace zero."""
+def test_onehot_tilings(dev):
+    """One-hot drafts at mixed accept lengths: every tiling gives identical,
+    oracle-exact outputs and leaves the workspace zero."""
     import rejection_sampling_verify_amd as rsv
     inp = make_chain("onehot_layouts", 48, 5, 30011, bf16=True, seed=25, target_sigma=6.0,
                      temperatures=(0.6, 1.0), one_hot=True, onehot_hit=0.85)
     ref = oracle_sample(inp)
     ws = rsv.Workspace(dev).get(48, 6, 30011)
     base = None
-    for env in ({"SV_FUSED": "1"}, {"SV_FUSED": "0"}, {"SV_FUSED": "1", "SV_LAG": "0", "SV_LAG2": "0"},
-                {"SV_FUSED": "1", "SV_LAG": "2", "SV_LAG2": "7"}, {"SV_FUSED": "1", "SV_LAG": "100000"}):
-        for k in ("SV_FUSED", "SV_LAG", "SV_LAG2"):
-            monkeypatch.delenv(k, raising=False)
-        for k, v in env.items():
-            monkeypatch.setenv(k, v)
-        got = run_sample(inp, torch, dev, workspace=ws)
-        compare_chain(got, ref, label="onehot %s" % env)
+    for tiling in (None, (0, 1), (0, 2), (0, 3), (0, 100), (4, 0), (1, 7)):
+        got = run_sample(inp, torch, dev, workspace=ws, tiling=tiling)
+        compare_chain(got, ref, label="onehot %s" % (tiling,))
         if base is None:
             base = got
-        for key in ("tokens", "n", "accept_prob", "logz_target", "residual_mass"):
-            assert np.array_equal(got[key], base[key], equal_nan=True), (env, key)
+        # Pass-2 chunking changes nothing; a pass-1 chunk length changes only
+        # the rounding of the row statistics (oracle-exact above).
+        keys = ("tokens", "n", "accept_prob", "logz_target", "residual_mass") if tiling is None or tiling[0] == 0 \
+            else ("tokens", "n")
+        for key in keys:
+            assert np.array_equal(got[key], base[key], equal_nan=True), (tiling, key)
         assert int(ws.count_nonzero().item()) == 0
-    for k in ("SV_FUSED", "SV_LAG", "SV_LAG2"):
-        monkeypatch.delenv(k, raising=False)
     assert set(np.unique(base["n"])) >= {0, 1, 2, 5}
 
 
@@ -202,7 +186,7 @@ def test_workspace_reuse_across_shapes(dev):
 
 
 @pytest.mark.parametrize("name", ["chain_bf16_peaked", "chain_bf16_llama", "onehot_bf16_qwen"])
-def test_without_diagnostics(dev, monkeypatch, name):
+def test_without_diagnostics(dev, name):
     """The call without diagnostic outputs (the kernels that skip the residual
     mass, as the benchmark runs them) gives the same ids and lengths as the
     call with them, at the default and at forced pass-2 chunk counts, and
@@ -210,15 +194,11 @@ def test_without_diagnostics(dev, monkeypatch, name):
     inp = workloads.make(name)
     ref = oracle_sample(inp)
     with_diag = run_sample(inp, torch, dev)
-    for chunks in (None, "1", "5"):
-        monkeypatch.delenv("SV_P2_CHUNKS", raising=False)
-        if chunks:
-            monkeypatch.setenv("SV_P2_CHUNKS", chunks)
-        got = run_sample(inp, torch, dev, diag=False)
+    for chunks in (None, 1, 5):
+        got = run_sample(inp, torch, dev, diag=False, tiling=None if chunks is None else (0, chunks))
         assert np.array_equal(got["n"], with_diag["n"]), (name, chunks)
         assert np.array_equal(got["tokens"], with_diag["tokens"]), (name, chunks)
         compare_chain(got, ref, check_diag=False, label="%s no diagnostics" % name)
-    monkeypatch.delenv("SV_P2_CHUNKS", raising=False)
 
 
 def test_more_sequences_than_resident_workgroups(dev):
@@ -286,9 +266,9 @@ def test_tree_chain_shaped_equals_greedy(dev):
         assert bonus[b].item() == gtok[b, n]
 
 
-def test_tree_fp32_and_launch_layouts(dev, monkeypatch):
-    """fp32 trees, and identical results for one fused launch with any lag or
-    two launches; every call returns its workspace to zero."""
+def test_tree_fp32_repeatable(dev):
+    """fp32 trees; repeated calls on one workspace give identical results and
+    each returns the workspace to zero."""
     import rejection_sampling_verify_amd as rsv
     parents, depth = workloads.tree_c5_structure()
     inp = make_tree("tl", 24, 20011, parents, depth, bf16=False, seed=43, hit=0.6)
@@ -297,19 +277,13 @@ def test_tree_fp32_and_launch_layouts(dev, monkeypatch):
     t = to_dev(inp.target, torch, dev)
     args = (t, torch.from_numpy(inp.parents).to(dev), torch.from_numpy(inp.depth).to(dev),
             torch.from_numpy(inp.node_tokens).to(dev), inp.max_depth)
-    for env in ({"SV_FUSED": "0"}, {"SV_LAG": "0"}, {"SV_LAG": "1"}, {"SV_LAG": "100000"}, {}):
-        for k in ("SV_FUSED", "SV_LAG"):
-            monkeypatch.delenv(k, raising=False)
-        for k, v in env.items():
-            monkeypatch.setenv(k, v)
+    for rep in range(3):
         path, plen, bonus = rsv.spec_verify_tree(*args, workspace=ws)
         torch.cuda.synchronize()
-        assert np.array_equal(plen.cpu().numpy(), base["path_len"]), env
-        assert np.array_equal(path.cpu().numpy(), base["path"]), env
-        assert np.array_equal(bonus.cpu().numpy(), base["bonus"]), env
-        assert int(ws.count_nonzero().item()) == 0, env
-    for k in ("SV_FUSED", "SV_LAG"):
-        monkeypatch.delenv(k, raising=False)
+        assert np.array_equal(plen.cpu().numpy(), base["path_len"]), rep
+        assert np.array_equal(path.cpu().numpy(), base["path"]), rep
+        assert np.array_equal(bonus.cpu().numpy(), base["bonus"]), rep
+        assert int(ws.count_nonzero().item()) == 0, rep
 
 
 def test_tree_malformed(dev):

@@ -47,7 +47,7 @@ def _run(inp, dev, seed=0, offset=0, workspace=None, temperature=None, parents=N
     return {"path": path.cpu().numpy(), "path_len": plen.cpu().numpy(), "token": token.cpu().numpy()}
 
 
-def _compare(got, ref, label):
+def _compare(got, ref, label, allow_excused=0):
     B = ref["path_len"].shape[0]
     excused = []
     for b in range(B):
@@ -62,6 +62,8 @@ def _compare(got, ref, label):
         excused.append(b)
     print("[tree-sample parity] %s B=%d excused=%d rejections=%s" % (label, B, len(excused),
           np.bincount(np.maximum(ref["rejections"], 0)).tolist()), flush=True)
+    # At the fixed seeds of the tests nothing is excused.
+    assert len(excused) == allow_excused, "%s: excused %s, expected %d" % (label, excused, allow_excused)
     return excused
 
 
