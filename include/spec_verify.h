@@ -83,10 +83,13 @@ typedef enum {
   SV_ERR_BAD_ARG = 4,    /* row stride < V, offset >= 2^31, seq_base + B > 2^32,
                           * misaligned workspace                             */
   SV_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than sv_workspace_bytes  */
-  SV_ERR_HIP = 6         /* a HIP runtime call or kernel launch failed         */
+  SV_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed         */
+  SV_ERR_SCRATCH_LIMIT = 7 /* spec_verify_sample_noalloc: the call needs more
+                          * than SV_NOALLOC_SCRATCH_BYTES of scratch          */
 } sv_status_t;
 
 /* Limits checked on the host. */
+#define SV_NOALLOC_SCRATCH_BYTES (32u << 20) /* static scratch of spec_verify_sample_noalloc, per GPU */
 #define SV_MAX_GAMMA 16
 #define SV_MAX_TREE_NODES 1024
 #define SV_MAX_BATCH (1 << 20)
@@ -182,6 +185,28 @@ sv_status_t spec_verify_sample(const void* target_logits, int64_t target_row_str
                                int32_t* out_tokens, int32_t* out_num_accepted,
                                const sv_diag_t* diag, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* spec_verify_sample_noalloc — spec_verify_sample for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It takes no workspace: its scratch is a
+ * static device array of SV_NOALLOC_SCRATCH_BYTES (32 MiB) that the library
+ * holds on every GPU it runs on until the process ends, and it calls no
+ * hipMalloc, hipFree or allocating routine. Each call first zeroes the part
+ * it uses (sv_workspace_bytes(B, gamma + 1, V) bytes, with a fill kernel on
+ * `stream`), so a call that follows an aborted one starts clean. All calls on
+ * one GPU share that array: calls that overlap on one GPU (different streams,
+ * or host threads) race and must be ordered by the caller. The caller still
+ * owns every input and output. Arguments, outputs and errors are those of
+ * spec_verify_sample, plus SV_ERR_SCRATCH_LIMIT when the call needs more than
+ * SV_NOALLOC_SCRATCH_BYTES (for example B = 512, gamma = 6, V = 152064 needs
+ * about 13 MiB). */
+sv_status_t spec_verify_sample_noalloc(const void* target_logits, int64_t target_row_stride,
+                                       const void* draft_logits, int64_t draft_row_stride,
+                                       sv_dtype_t dtype, const int32_t* draft_ids,
+                                       const float* temperature, int32_t B, int32_t gamma, int32_t V,
+                                       uint64_t seed, uint64_t offset, uint32_t seq_base,
+                                       int32_t* out_tokens, int32_t* out_num_accepted,
+                                       const sv_diag_t* diag, void* stream);
 
 /* sv_debug_sample_tiled — spec_verify_sample with its tiling fixed by the
  * caller instead of chosen by the library (for tests that check that results

@@ -11,6 +11,9 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     SV_DTYPE_BF16,
     SV_DTYPE_F32,
+    SV_ERR_SCRATCH_LIMIT,
+    SV_NOALLOC_SCRATCH_BYTES,
+    SV_SEQ_BAD_LOGITS,
     SV_SEQ_BAD_TEMPERATURE,
     SV_SEQ_BAD_TOKEN,
     SV_SEQ_BAD_TREE,
@@ -21,6 +24,7 @@ from .binding import (  # noqa: F401
     lib,
     spec_verify_greedy,
     spec_verify_sample,
+    spec_verify_sample_noalloc,
     spec_verify_tree,
     spec_verify_tree_sample,
     sv_kv_rollback,

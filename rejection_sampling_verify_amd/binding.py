@@ -22,11 +22,13 @@ SV_SEQ_BAD_TEMPERATURE = -2
 SV_SEQ_BAD_TREE = -3
 SV_SEQ_INTERNAL = -4
 SV_SEQ_BAD_LOGITS = -5
+SV_ERR_SCRATCH_LIMIT = 7
+SV_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTS = ["sv_workspace_bytes", "sv_workspace_init", "sv_status_string", "spec_verify_sample",
            "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_sample", "sv_kv_rollback",
            "sv_kv_rollback_layers", "sv_ngram_draft", "sv_tree_mask", "sv_debug_philox", "sv_debug_noise",
-           "sv_debug_wave_max", "sv_debug_read_stream", "sv_debug_sample_tiled"]
+           "sv_debug_wave_max", "sv_debug_read_stream", "sv_debug_sample_tiled", "spec_verify_sample_noalloc"]
 
 _lib = None
 
@@ -63,6 +65,9 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_sample.restype = ctypes.c_int
         L.sv_debug_sample_tiled.argtypes = L.spec_verify_sample.argtypes + [i32, i32]
         L.sv_debug_sample_tiled.restype = ctypes.c_int
+        L.spec_verify_sample_noalloc.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, i32, i32, i32, u64, u64, u32,
+                                                 P, P, ctypes.POINTER(_Diag), P]
+        L.spec_verify_sample_noalloc.restype = ctypes.c_int
         L.spec_verify_greedy.argtypes = [P, i64, ctypes.c_int, P, i32, i32, i32, P, P, P, sz, P]
         L.spec_verify_greedy.restype = ctypes.c_int
         L.spec_verify_tree.argtypes = [P, i64, ctypes.c_int, P, P, P, i32, i32, i32, i32, P, P, P, P, sz, P]
@@ -218,6 +223,32 @@ def spec_verify_sample(target_logits, draft_logits, draft_ids, temperature, seed
         st = lib().sv_debug_sample_tiled(*args, int(tiling[0]), int(tiling[1]))
     if st != 0:
         raise SVError(st, "spec_verify_sample")
+    return out_tokens, out_num_accepted
+
+
+def spec_verify_sample_noalloc(target_logits, draft_logits, draft_ids, temperature, out_tokens, out_num_accepted,
+                               seed: int = 0, offset: int = 0, seq_base: int = 0, diag: dict | None = None,
+                               V: int | None = None, stream=None):
+    """spec_verify_sample through the allocation-free entry point: no workspace
+    (the library's static scratch on this GPU), and outputs preallocated by
+    the caller, so that the call allocates nothing."""
+    B, gamma = draft_ids.shape
+    V = int(target_logits.shape[2]) if V is None else int(V)
+    _check_i32(draft_ids, (B, gamma), "draft_ids")
+    _check_i32(out_tokens, (B, gamma + 1), "out_tokens")
+    _check_i32(out_num_accepted, (B,), "out_num_accepted")
+    ts = _row_stride(target_logits, gamma + 1, V)
+    ds = 0 if draft_logits is None else _row_stride(draft_logits, gamma, V)
+    d = None
+    if diag:
+        d = _Diag(*[diag[k].data_ptr() if diag.get(k) is not None else None
+                    for k in ("accept_prob", "logz_target", "logz_draft", "residual_mass")])
+    st = lib().spec_verify_sample_noalloc(_ptr(target_logits), ts, _ptr(draft_logits), ds,
+                                          _dtype_code(target_logits), _ptr(draft_ids), _ptr(temperature), B, gamma,
+                                          V, seed, offset, seq_base, _ptr(out_tokens), _ptr(out_num_accepted),
+                                          ctypes.byref(d) if d is not None else None, _stream(stream))
+    if st != 0:
+        raise SVError(st, "spec_verify_sample_noalloc")
     return out_tokens, out_num_accepted
 
 

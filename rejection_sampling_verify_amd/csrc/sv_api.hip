@@ -134,20 +134,31 @@ sv_status_t check_workspace(void* ws, size_t bytes, size_t need) {
   return SV_OK;
 }
 
-// forced_kv, forced_p2: the debug entry point's fixed tiling (0: chosen here).
-sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, int64_t d_stride,
-                      sv_dtype_t dtype, const int32_t* ids, const float* temperature, int32_t B,
-                      int32_t gamma, int32_t V, uint64_t seed, uint64_t offset, uint32_t seq_base,
-                      int32_t* out_tokens, int32_t* out_n, const sv_diag_t* diag, void* workspace,
-                      size_t workspace_bytes, void* stream, int forced_kv = 0, int forced_p2 = 0) {
+// Host-side validation of the chain entry points' arguments (no HIP call).
+sv_status_t check_chain_args(const void* target, int64_t t_stride, const void* draft, int64_t d_stride,
+                             sv_dtype_t dtype, const int32_t* ids, int32_t B, int32_t gamma, int32_t V,
+                             uint64_t offset, uint32_t seq_base, const int32_t* out_tokens, const int32_t* out_n) {
   if (!target || !ids || !out_tokens || !out_n) return SV_ERR_NULL_ARG;
   if (B < 0 || B > SV_MAX_BATCH || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > (1 << 30))
     return SV_ERR_BAD_SHAPE;
   if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_BAD_DTYPE;
   if (t_stride < V || (draft && d_stride < V)) return SV_ERR_BAD_ARG;
   if (offset >= (1ull << 31)) return SV_ERR_BAD_ARG;
-  if (forced_kv < 0 || forced_p2 < 0) return SV_ERR_BAD_ARG;
   if ((uint64_t)seq_base + (uint64_t)B > (1ull << 32)) return SV_ERR_BAD_ARG;
+  return SV_OK;
+}
+
+// forced_kv, forced_p2: the debug entry point's fixed tiling (0: chosen here).
+sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, int64_t d_stride,
+                      sv_dtype_t dtype, const int32_t* ids, const float* temperature, int32_t B,
+                      int32_t gamma, int32_t V, uint64_t seed, uint64_t offset, uint32_t seq_base,
+                      int32_t* out_tokens, int32_t* out_n, const sv_diag_t* diag, void* workspace,
+                      size_t workspace_bytes, void* stream, int forced_kv = 0, int forced_p2 = 0,
+                      bool clear_workspace = false) {
+  const sv_status_t args_ok =
+      check_chain_args(target, t_stride, draft, d_stride, dtype, ids, B, gamma, V, offset, seq_base, out_tokens, out_n);
+  if (args_ok != SV_OK) return args_ok;
+  if (forced_kv < 0 || forced_p2 < 0) return SV_ERR_BAD_ARG;
   const size_t need = sv_workspace_bytes(B, gamma + 1, V);
   const sv_status_t ws_ok = check_workspace(workspace, workspace_bytes, need);
   if (ws_ok != SV_OK) return ws_ok;
@@ -219,9 +230,30 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   // Two launches: pass 1 over every (sequence, position, chunk) followed by
   // the decisions, then pass 2.
   hipStream_t s = (hipStream_t)stream;
+  // The allocation-free variant's scratch keeps the last call's contents:
+  // the range this call uses is zeroed first (a fill kernel).
+  if (clear_workspace && launch_fill_zero(workspace, need, s) != hipSuccess) return SV_ERR_HIP;
   if (launch_chain_p1(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
   if (launch_chain_p2(a, bf16, vec, s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
+}
+
+// Scratch memory of the allocation-free entry point: a file-scope device
+// array, one copy per GPU, held until the process ends. Host code never uses
+// the array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current and kept here.
+constexpr size_t kScratchBytes = SV_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+void* scratch_address(int dev) {
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
 }
 
 }  // namespace
@@ -249,6 +281,7 @@ const char* sv_status_string(sv_status_t status) {
     case SV_ERR_BAD_ARG: return "bad stride, offset or alignment";
     case SV_ERR_WORKSPACE: return "workspace missing or too small";
     case SV_ERR_HIP: return "HIP runtime or launch failure";
+    case SV_ERR_SCRATCH_LIMIT: return "call needs more than the allocation-free entry point's scratch memory";
   }
   return "unknown status";
 }
@@ -277,6 +310,29 @@ sv_status_t sv_debug_sample_tiled(const void* target_logits, int64_t target_row_
   return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, dtype, draft_ids,
                        temperature, B, gamma, V, seed, offset, seq_base, out_tokens, out_num_accepted, diag,
                        workspace, workspace_bytes, stream, p1_vectors, p2_chunks);
+}
+
+sv_status_t spec_verify_sample_noalloc(const void* target_logits, int64_t target_row_stride,
+                                       const void* draft_logits, int64_t draft_row_stride, sv_dtype_t dtype,
+                                       const int32_t* draft_ids, const float* temperature, int32_t B,
+                                       int32_t gamma, int32_t V, uint64_t seed, uint64_t offset,
+                                       uint32_t seq_base, int32_t* out_tokens, int32_t* out_num_accepted,
+                                       const sv_diag_t* diag, void* stream) {
+  if (!temperature) return SV_ERR_NULL_ARG;
+  const sv_status_t args_ok = sv::check_chain_args(target_logits, target_row_stride, draft_logits, draft_row_stride,
+                                                   dtype, draft_ids, B, gamma, V, offset, seq_base, out_tokens,
+                                                   out_num_accepted);
+  if (args_ok != SV_OK) return args_ok;
+  const size_t need = sv_workspace_bytes(B, gamma + 1, V);
+  if (need > sv::kScratchBytes) return SV_ERR_SCRATCH_LIMIT;
+  if (B == 0) return SV_OK;
+  int dev = 0, cus = 0;
+  if (!sv::device_info(&dev, &cus)) return SV_ERR_HIP;
+  void* ws = sv::scratch_address(dev);
+  if (ws == nullptr) return SV_ERR_HIP;
+  return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, dtype, draft_ids,
+                       temperature, B, gamma, V, seed, offset, seq_base, out_tokens, out_num_accepted, diag, ws,
+                       need, stream, 0, 0, /*clear_workspace=*/true);
 }
 
 sv_status_t spec_verify_greedy(const void* target_logits, int64_t target_row_stride, sv_dtype_t dtype,

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in range(7):
+    for code in range(8):
         assert rsv.sv_status_string(code)
     assert rsv.sv_status_string(99) == "unknown status"
 
@@ -188,3 +188,19 @@ def test_library_reads_no_environment(L):
     out = subprocess.run(["nm", "-D", "--undefined-only", rsv.LIB_PATH], capture_output=True, text=True).stdout
     imported = set(line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip())
     assert not imported & {"getenv", "secure_getenv", "__secure_getenv"}
+
+
+def test_noalloc_argument_validation(L):
+    """The allocation-free entry point refuses, before any HIP call, a call
+    whose scratch need exceeds its static array, and validates like
+    spec_verify_sample otherwise."""
+    f = _Fake(1 << 16)
+    P = f.ptr
+    na = lambda **k: L.spec_verify_sample_noalloc(k.get("t", P), k.get("ts", 1000), None, 0, k.get("dt", 1), P,
+                                                  k.get("temp", P), k.get("B", 4), k.get("G", 3), k.get("V", 1000),
+                                                  0, k.get("off", 0), 0, P, P, None, None)
+    assert na(B=4096, G=16, V=152064, ts=152064) == rsv.SV_ERR_SCRATCH_LIMIT
+    assert na(temp=None) == 1 and na(t=None) == 1
+    assert na(G=0) == 2 and na(dt=5) == 3 and na(ts=10) == 4 and na(off=1 << 31) == 4
+    assert na(B=0) == 0
+    assert "scratch" in rsv.sv_status_string(rsv.SV_ERR_SCRATCH_LIMIT)
