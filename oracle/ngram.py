@@ -36,24 +36,21 @@ def ngram_draft_one(seq, ngram: int, gamma: int, pad: bool):
     T = len(seq)
     if T == 0:
         return (None, -1) if pad else ([], -1)
+    # The key is the n-gram that ends the sequence, starting at T - ngram. An
+    # earlier occurrence starts at some i < T - ngram (it may overlap the key);
+    # every start is compared token by token, in increasing order, and a later
+    # match replaces an earlier one, so the most recent occurrence is kept.
+    key = T - ngram
     match = -1
-    if T >= ngram + 1:
-        tail = seq[T - ngram:]
-        for i in range(T - ngram - 1, -1, -1):
-            if seq[i:i + ngram] == tail:
-                match = i
-                break
-    last = seq[-1]
-    draft = []
-    for k in range(gamma):
-        pos = match + ngram + k
-        if match != -1 and pos < T:
-            draft.append(seq[pos])
-        elif pad:
-            draft.append(last)
-        else:
-            break
-    return draft, match
+    for i in range(max(key, 0)):
+        if all(seq[i + j] == seq[key + j] for j in range(ngram)):
+            match = i
+    # The proposal is what followed the occurrence, at most gamma tokens.
+    follow = seq[match + ngram:match + ngram + gamma] if match >= 0 else []
+    if pad:
+        # The exercise's fill: the last token wherever the copy runs short.
+        return follow + [seq[-1]] * (gamma - len(follow)), match
+    return follow, match
 
 
 def ngram_draft(tokens: np.ndarray, lengths: np.ndarray, ngram: int, gamma: int, pad: bool):

@@ -124,6 +124,19 @@ int tree_occupancy_cached(int dev, bool bf16, bool vec) {
   return n;
 }
 
+// The raw value of an enum argument: callers through the C ABI may pass any
+// int, and a C++ load of an enum value outside its listed range is undefined,
+// so it is validated as an int.
+template <typename E>
+int raw_value(const E& e) {
+  int v;
+  static_assert(sizeof(E) == sizeof(int), "enum arguments are int-sized");
+  std::memcpy(&v, &e, sizeof(v));
+  return v;
+}
+
+bool dtype_ok(int dt) { return dt == SV_DTYPE_F32 || dt == SV_DTYPE_BF16; }
+
 bool aligned16(const void* p, int64_t stride_bytes) {
   return ((uintptr_t)p % 16 == 0) && (stride_bytes % 16 == 0);
 }
@@ -136,12 +149,12 @@ sv_status_t check_workspace(void* ws, size_t bytes, size_t need) {
 
 // Host-side validation of the chain entry points' arguments (no HIP call).
 sv_status_t check_chain_args(const void* target, int64_t t_stride, const void* draft, int64_t d_stride,
-                             sv_dtype_t dtype, const int32_t* ids, int32_t B, int32_t gamma, int32_t V,
+                             int dtype, const int32_t* ids, int32_t B, int32_t gamma, int32_t V,
                              uint64_t offset, uint32_t seq_base, const int32_t* out_tokens, const int32_t* out_n) {
   if (!target || !ids || !out_tokens || !out_n) return SV_ERR_NULL_ARG;
   if (B < 0 || B > SV_MAX_BATCH || gamma < 1 || gamma > SV_MAX_GAMMA || V < 1 || V > (1 << 30))
     return SV_ERR_BAD_SHAPE;
-  if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_BAD_DTYPE;
+  if (!dtype_ok(dtype)) return SV_ERR_BAD_DTYPE;
   if (t_stride < V || (draft && d_stride < V)) return SV_ERR_BAD_ARG;
   if (offset >= (1ull << 31)) return SV_ERR_BAD_ARG;
   if ((uint64_t)seq_base + (uint64_t)B > (1ull << 32)) return SV_ERR_BAD_ARG;
@@ -150,7 +163,7 @@ sv_status_t check_chain_args(const void* target, int64_t t_stride, const void* d
 
 // forced_kv, forced_p2: the debug entry point's fixed tiling (0: chosen here).
 sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, int64_t d_stride,
-                      sv_dtype_t dtype, const int32_t* ids, const float* temperature, int32_t B,
+                      int dtype, const int32_t* ids, const float* temperature, int32_t B,
                       int32_t gamma, int32_t V, uint64_t seed, uint64_t offset, uint32_t seq_base,
                       int32_t* out_tokens, int32_t* out_n, const sv_diag_t* diag, void* workspace,
                       size_t workspace_bytes, void* stream, int forced_kv = 0, int forced_p2 = 0,
@@ -273,7 +286,11 @@ sv_status_t sv_workspace_init(void* workspace, size_t workspace_bytes, void* str
 }
 
 const char* sv_status_string(sv_status_t status) {
-  switch (status) {
+  // Callers through the C ABI may pass any int: the code is read as the raw
+  // value (a C++ load of an enum outside its listed range is undefined).
+  int code;
+  std::memcpy(&code, &status, sizeof(code));
+  switch (code) {
     case SV_OK: return "success";
     case SV_ERR_NULL_ARG: return "a required pointer is NULL";
     case SV_ERR_BAD_SHAPE: return "batch, draft length, node count, vocabulary or depth out of range";
@@ -292,7 +309,7 @@ sv_status_t spec_verify_sample(const void* target_logits, int64_t target_row_str
                                uint64_t offset, uint32_t seq_base, int32_t* out_tokens, int32_t* out_num_accepted,
                                const sv_diag_t* diag, void* workspace, size_t workspace_bytes, void* stream) {
   if (!temperature) return SV_ERR_NULL_ARG;
-  return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, dtype, draft_ids,
+  return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, sv::raw_value(dtype), draft_ids,
                        temperature, B, gamma, V, seed, offset, seq_base, out_tokens, out_num_accepted, diag,
                        workspace, workspace_bytes, stream);
 }
@@ -307,7 +324,7 @@ sv_status_t sv_debug_sample_tiled(const void* target_logits, int64_t target_row_
   if (p1_vectors < 0 || p1_vectors > sv::kMaxVecsPerThread || (p1_vectors & (p1_vectors - 1)) != 0 ||
       p2_chunks < 0)
     return SV_ERR_BAD_ARG;
-  return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, dtype, draft_ids,
+  return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, sv::raw_value(dtype), draft_ids,
                        temperature, B, gamma, V, seed, offset, seq_base, out_tokens, out_num_accepted, diag,
                        workspace, workspace_bytes, stream, p1_vectors, p2_chunks);
 }
@@ -320,7 +337,7 @@ sv_status_t spec_verify_sample_noalloc(const void* target_logits, int64_t target
                                        const sv_diag_t* diag, void* stream) {
   if (!temperature) return SV_ERR_NULL_ARG;
   const sv_status_t args_ok = sv::check_chain_args(target_logits, target_row_stride, draft_logits, draft_row_stride,
-                                                   dtype, draft_ids, B, gamma, V, offset, seq_base, out_tokens,
+                                                   sv::raw_value(dtype), draft_ids, B, gamma, V, offset, seq_base, out_tokens,
                                                    out_num_accepted);
   if (args_ok != SV_OK) return args_ok;
   const size_t need = sv_workspace_bytes(B, gamma + 1, V);
@@ -330,7 +347,7 @@ sv_status_t spec_verify_sample_noalloc(const void* target_logits, int64_t target
   if (!sv::device_info(&dev, &cus)) return SV_ERR_HIP;
   void* ws = sv::scratch_address(dev);
   if (ws == nullptr) return SV_ERR_HIP;
-  return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, dtype, draft_ids,
+  return sv::run_chain(target_logits, target_row_stride, draft_logits, draft_row_stride, sv::raw_value(dtype), draft_ids,
                        temperature, B, gamma, V, seed, offset, seq_base, out_tokens, out_num_accepted, diag, ws,
                        need, stream, 0, 0, /*clear_workspace=*/true);
 }
@@ -338,7 +355,8 @@ sv_status_t spec_verify_sample_noalloc(const void* target_logits, int64_t target
 sv_status_t spec_verify_greedy(const void* target_logits, int64_t target_row_stride, sv_dtype_t dtype,
                                const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
                                int32_t* out_num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
-  return sv::run_chain(target_logits, target_row_stride, nullptr, 0, dtype, draft_ids, nullptr, B, gamma, V, 0, 0, 0,
+  return sv::run_chain(target_logits, target_row_stride, nullptr, 0, sv::raw_value(dtype), draft_ids, nullptr, B, gamma,
+                       V, 0, 0, 0,
                        out_tokens, out_num_accepted, nullptr, workspace, workspace_bytes, stream);
 }
 
@@ -351,7 +369,7 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
   if (B < 0 || B > SV_MAX_BATCH || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > (1 << 30) || max_depth < 0 ||
       max_depth >= N)
     return SV_ERR_BAD_SHAPE;
-  if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_BAD_DTYPE;
+  if (!sv::dtype_ok(sv::raw_value(dtype))) return SV_ERR_BAD_DTYPE;
   if (target_row_stride < V) return SV_ERR_BAD_ARG;
   const size_t need = sv_workspace_bytes(B, N, V);
   const sv_status_t ws_ok = sv::check_workspace(workspace, workspace_bytes, need);
@@ -410,7 +428,7 @@ sv_status_t spec_verify_tree_sample(const void* target_logits, int64_t target_ro
   if (B < 0 || B > SV_MAX_BATCH || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > (1 << 30) || max_depth < 0 ||
       max_depth >= N)
     return SV_ERR_BAD_SHAPE;
-  if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_BAD_DTYPE;
+  if (!sv::dtype_ok(sv::raw_value(dtype))) return SV_ERR_BAD_DTYPE;
   if (target_row_stride < V || draft_row_stride < V) return SV_ERR_BAD_ARG;
   if (offset >= (1ull << 31)) return SV_ERR_BAD_ARG;
   if (siblings_without_replacement != 0 && siblings_without_replacement != 1) return SV_ERR_BAD_ARG;

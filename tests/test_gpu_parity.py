@@ -315,6 +315,25 @@ def test_named_workload_full_size(dev, name):
     print("[parity] %s mean accepted %.3f, emitted/step %.3f" % (name, n.mean(), n.mean() + 1), flush=True)
 
 
+def test_tree_deepest_paths(dev):
+    """1024-node trees at full depth: a chain-shaped tree (depth 1023) whose
+    every child carries its parent's argmax, so the accepted path runs to the
+    last node, and a deep, narrow random tree (1 or 2 children per node)."""
+    N = 1024
+    chain = np.arange(-1, N - 1, dtype=np.int32)
+    depth = np.array(oracle.tree_depths(chain), np.int32)
+    inp = make_tree("chain1024", 3, 2000, chain, depth, bf16=True, seed=46, hit=1.0)
+    ref = _check_tree(inp, dev)
+    assert np.all(ref["path_len"] == N)
+    rng = np.random.default_rng(47)
+    narrow = workloads.random_tree(rng, N, (1, 2))
+    depth = np.array(oracle.tree_depths(narrow), np.int32)
+    assert depth.max() >= 9
+    inp = make_tree("narrow1024", 4, 3001, narrow, depth, bf16=False, seed=48, hit=0.97)
+    ref = _check_tree(inp, dev)
+    assert ref["path_len"].max() >= 6
+
+
 def test_tree_largest(dev):
     """The greedy tree walk at the largest tree (1024 nodes): deep paths
     (children carry their parent's argmax often), bit-exact."""

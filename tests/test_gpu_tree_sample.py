@@ -262,3 +262,27 @@ def test_largest_tree(dev, wor):
     got = _run(inp, dev, seed=2, wor=wor)
     _compare(got, _oracle(inp, seed=2, wor=wor), "N=1024 wor=%d" % wor)
     assert np.all(got["path_len"] >= 1)
+
+
+@pytest.mark.parametrize("wor", [False, True])
+def test_deepest_paths(dev, wor):
+    """1024-node trees at full depth, both sibling rules: a chain-shaped tree
+    (depth 1023) with q = p at every node, so every child is accepted and the
+    walk takes 1023 steps to the last node (the walk's step bound and path
+    writes at their limit), and a deep, narrow random tree (1 or 2 children
+    per node)."""
+    N = 1024
+    chain = np.arange(-1, N - 1, dtype=np.int32)
+    depth = np.array(oracle.tree_depths(chain), np.int32)
+    inp = make_tree_sample("chain1024", 2, 1500, chain, depth, bf16=True, seed=49, temperatures=(1.0,), zipf=0.0,
+                           target_sigma=1.5, draft_sigma=(0.0, 0.0), without_replacement=wor)
+    got = _run(inp, dev, seed=3, wor=wor)
+    _compare(got, _oracle(inp, seed=3, wor=wor), "chain N=1024 wor=%d" % wor)
+    assert np.all(got["path_len"] == N)
+    rng = np.random.default_rng(50)
+    parents, depth = _random_tree(rng, N, branching=(1, 2))
+    inp = make_tree_sample("narrow1024", 3, 2000, parents, depth, bf16=False, seed=51, temperatures=(0.8, 1.0),
+                           zipf=0.0, target_sigma=1.0, draft_sigma=(0.1, 0.4), without_replacement=wor)
+    got = _run(inp, dev, seed=4, wor=wor)
+    _compare(got, _oracle(inp, seed=4, wor=wor), "narrow N=1024 wor=%d" % wor)
+    assert got["path_len"].max() >= 4
