@@ -6,11 +6,13 @@ logits, temperatures drawn from {0, 0.7, 1.0}), inputs resident in HBM. Prints
 one JSON line: verified positions/s (B * gamma per step) as `value`, the
 logit-read bandwidth against the HBM roofline of one verify call (the kernels
 it launches back to back on one stream, timed with HIP events on that stream),
-and the CPU oracle timed on the host as a baseline (all host threads, and one).
+and the CPU oracle timed on the host as a baseline (every host thread the
+process may use, and one).
 Beside the roofline it reports the GPU's streaming-read rate measured in the
 same run (the library's read yardstick over a 2 GiB buffer) and the call's
 fraction of it, and a warm-cache launch time (the same input copy every step,
-labelled as such; the timed steps alternate two copies).
+labelled as such; the timed steps rotate over copies of the inputs that
+together exceed the 256 MB MALL).
 
 Other workloads (--workload): the four other verify configurations
 (chain_f32_small, chain_bf16_peaked, onehot_bf16_qwen, tree_bf16_llama),
@@ -81,13 +83,35 @@ def to_dev(a, torch, dev):
     return torch.from_numpy(a).to(dev)
 
 
+def host_threads() -> int:
+    """The host threads this process may use: the CPUs it is allowed to run on,
+    within the OpenMP thread budget of its environment when one is set (a GPU
+    host shares its cores between its GPUs' jobs that way)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    budget = os.environ.get("OMP_NUM_THREADS", "")
+    if budget.isdigit() and int(budget) > 0:
+        n = min(n, int(budget))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, is_tree: bool, positions_per_step: int, threads: int | None = None, max_runs: int = 3):
-    """The oracle as it stands, on all host threads (capped at 16) unless
-    told otherwise, over the whole workload; repeated until about 10 s of CPU
-    time or max_runs runs."""
+    """The oracle as it stands, on every host thread this process may use
+    unless told otherwise, over the whole workload; repeated until about 10 s
+    of CPU time or max_runs runs."""
     import oracle
     import workloads
-    threads = threads or min(16, os.cpu_count() or 1)
+    threads = threads or host_threads()
     times = []
     t_start = time.perf_counter()
     while len(times) < max_runs and (not times or time.perf_counter() - t_start < 10.0):
@@ -105,7 +129,9 @@ def cpu_baseline(inp, is_tree: bool, positions_per_step: int, threads: int | Non
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     return {"value": positions_per_step / t, "unit": "verified positions/s", "cores": threads, "kind": "oracle",
-            "sample": "the whole workload (one step), %d run(s), median %.3f s, fp64 plain loops" % (len(times), t)}
+            "sample": "the whole workload (one step), %d run(s), median %.3f s, fp64 plain loops" % (len(times), t),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
 def read_ceiling(torch, dev, rsv, nbytes: int = 2 << 30, launches: int = 10):
@@ -381,10 +407,14 @@ def main():
     sampled_tree = isinstance(inp, workloads.TreeSampleInputs)
     print("[bench] workload %s generated" % args.workload, file=sys.stderr, flush=True)
 
-    # Two resident copies of the inputs, used alternately, so that no step
-    # finds its logits in the 256 MB Infinity Cache from the step before.
+    # Resident copies of the inputs, used in turn, so that no step finds its
+    # logits in the 256 MB Infinity Cache (MALL) from the steps before: as
+    # many as make the rotation at least 512 MiB (two for the large
+    # workloads, twelve for chain_bf16_peaked's 45 MB), at most 16.
+    per_copy = inp.target.nbytes + (inp.draft.nbytes if getattr(inp, "draft", None) is not None else 0)
+    ncopies = int(min(16, max(2, -(-(512 << 20) // per_copy))))
     copies = []
-    for _ in range(2):
+    for _ in range(ncopies):
         if is_tree:
             copies.append(dict(t=to_dev(inp.target, torch, dev), par=torch.from_numpy(inp.parents).to(dev),
                                dep=torch.from_numpy(inp.depth).to(dev), tok=torch.from_numpy(inp.node_tokens).to(dev)))
@@ -403,7 +433,7 @@ def main():
         positions = B * (N - 1)
 
         def step(k):
-            c = copies[k % 2]
+            c = copies[k % ncopies]
             if sampled_tree:
                 rsv.spec_verify_tree_sample(c["t"], c["d"], c["par"], c["dep"], c["tok"], c["temp"], inp.max_depth,
                                             seed=inp.seed, offset=inp.offset, out_path=out[0], out_path_len=out[1],
@@ -419,7 +449,7 @@ def main():
         positions = B * G
 
         def step(k):
-            c = copies[k % 2]
+            c = copies[k % ncopies]
             rsv.spec_verify_sample(c["t"], c["d"], c["ids"], c["temp"], seed=inp.seed, offset=inp.offset,
                                    out_tokens=out[0], out_num_accepted=out[1], workspace=wbuf)
 
@@ -504,6 +534,8 @@ def main():
         "hbm_read_ceiling_GBps": ceiling,
         "frac_of_read_ceiling": achieved / ceiling,
         "warm_cache_launch_ms": {"p50": float(np.median(warm_ms)), "note": "same input copy every step"},
+        "input_copies": {"count": ncopies, "bytes_each": int(per_copy),
+                         "note": "used in turn, so that the timed steps read their logits from HBM"},
         **extra,
     }
     if not args.no_cpu_baseline:

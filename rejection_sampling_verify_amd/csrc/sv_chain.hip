@@ -209,6 +209,19 @@ struct Chunk {
     }
   }
 
+  // bf16: the vectors past the end of a short chunk become -inf elements
+  // (bit pattern 0xFF80), which neither the packed maximum (it reads them
+  // as f16 NaNs and skips them), nor an exponential sum, nor an argmax
+  // search for a finite maximum can pick up; then the packed whole-chunk
+  // paths serve a short chunk too, as long as it holds whole vectors only.
+  __device__ __forceinline__ void pad_neg_inf() {
+#pragma unroll
+    for (int k = 0; k < kMaxVecsPerThread; ++k) {
+      const int vi = k * kThreads + (int)threadIdx.x;
+      if (vi >= nfull) q[k] = u32x4{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+    }
+  }
+
   // Calls f(value, index) for each element this thread owns, in increasing
   // index order.
   template <typename F>
@@ -488,7 +501,7 @@ __device__ __forceinline__ float key_total(uint32_t k) {
 
 // Writes everything the decision fixes. The token at position n is left to
 // the last pass-2 item when a draw is still pending.
-__device__ void write_decision(const ChainArgs& a, int b, Smem& sm) {
+__device__ __forceinline__ void write_decision(const ChainArgs& a, int b, Smem& sm) {
   const int G = a.gamma, tid = threadIdx.x;
   const Decision& d = sm.dec;
   const int32_t* ids = a.ids + (int64_t)b * G;
@@ -732,10 +745,12 @@ __device__ __forceinline__ void pass1_item(const ChainArgs& a, int b, int r, Sme
   const int lo = c * a.chunk;
   const int hi = min(a.V, lo + a.chunk);
   const uint8_t* row = draft_item ? draft_row(a, b, i) : target_row(a, b, i);
-  // Whole 16-byte-aligned bf16 chunk at the full tile width: fast path.
-  const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && hi - lo == a.chunk;
+  // 16-byte-aligned bf16 chunk at the full tile width holding whole vectors
+  // only (a short last chunk is padded with -inf): fast path.
+  const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && ((hi - lo) & 7) == 0;
   Chunk<BF16, VEC> ch;
   ch.load(row, lo, hi, a.kv);
+  if (fast && hi - lo != a.chunk) ch.pad_neg_inf();
   // w0 belongs to the target item, w1 to the draft item of a dense draft and
   // to the target item otherwise.
   uint64_t w0 = 0u, w1 = 1u;
@@ -791,7 +806,7 @@ __device__ __forceinline__ bool in_list(const int32_t* l, int n, int idx) {
 // elements take no part (sampled trees whose siblings were drawn without
 // replacement).
 template <bool BF16, bool VEC, int MODE, bool EXCL = false>
-__device__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm, P2Slot* out,
+__device__ __forceinline__ void gumbel_chunk(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm, P2Slot* out,
                              const int32_t* excl = nullptr, int nexcl = 0) {
   using E = Elem<BF16>;
   constexpr int EV = E::kPerVec;
@@ -975,20 +990,25 @@ struct PhaseTable {
 };
 
 // One chunk of a Gumbel-max draw over 16-byte-aligned bf16 rows. Each lane
-// takes one 8-element vector per round, loaded two rounds ahead (three
-// vector buffers that rotate by unrolling the loop three times, so that no
-// register move waits for a load in flight), forms the Philox words of its
-// two 4-element blocks and a cheap, conservative pruning test; only the
-// survivors get their exact score and noise. The first round seeds the
-// wave's threshold L with the exact total of its highest-scoring element. L
-// is wave-uniform and rises whenever a survivor beats it, or another wave of
-// the workgroup (through LDS) or another workgroup of the same row (through
-// the sequence record, read once every three rounds) reports a higher total.
-// The residual's bulk test bounds its score by log2 p alone (ln (p - q) <=
-// ln p), reading only the target vector; the tighter bound on log2 (p - q)
-// and the candidacy test p > q are applied only in waves where some element
-// passes the first test (about one wave-round in a hundred at the large
-// workloads).
+// takes one 8-element vector per round, loaded kBufs - 1 rounds ahead (the
+// buffers rotate by unrolling the loop kBufs times, so that no register move
+// waits for a load in flight), forms the Philox words of its two 4-element
+// blocks and a cheap, conservative pruning test; only the survivors get
+// their exact score and noise. Before the first round the workgroup seeds
+// its threshold L with the exact total of each lane's highest-scoring
+// element of its first vector, and hands the seed to the row's other
+// workgroups. L is wave-uniform and rises whenever a survivor beats it, or
+// another wave of the workgroup (through LDS) or another workgroup of the
+// same row (through the sequence record, read once every kBufs rounds)
+// reports a higher total. The residual's bulk test bounds its score by
+// log2 p alone (ln (p - q) <= ln p) and reads only the target vector; the
+// draft vector is loaded, and the candidacy test p > q and the tighter
+// bound on log2 (p - q) applied, only in a wave-round where some element
+// passed the first test (about one in ten at the large chain workload).
+// Target-vector buffers of the bf16 Gumbel loop: its loads run kBufs - 1
+// rounds ahead of the round that uses them.
+constexpr int kBufs = 3;
+
 template <int MODE, bool BETA, bool EXCL = false>
 __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm,
                                   P2Slot* out, const int32_t* excl = nullptr, int nexcl = 0) {
@@ -1052,18 +1072,25 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
   const int vi0 = (int)threadIdx.x;
   // A lane past the last whole vector loads the last one again (discarded),
   // so that every load is issued by the whole wave.
+  // The bulk test reads the target vector only; the residual's draft vector
+  // is loaded on demand, by a wave-round with a survivor (want_beta, the
+  // diagnostics variant, reads it always).
   auto fetch = [&](int vi, u32x4& qt, u32x4& qd) {
     const int v = min(vi, nfull - 1);
     qt = load_vec_stream(rt + (int64_t)(lo + v * 8) * 2);
-    if (residual) qd = load_vec_stream(rd + (int64_t)(lo + v * 8) * 2);
+    if (want_beta) qd = load_vec_stream(rd + (int64_t)(lo + v * 8) * 2);
   };
+  auto draft_vec = [&](int vi) -> u32x4 { return load_vec_stream(rd + (int64_t)(lo + min(vi, nfull - 1) * 8) * 2); };
   const int rounds = (nfull + kThreads - 1) / kThreads;  // same for every lane
-  u32x4 qa, qb, qc, da, db, dc;
-  if (rounds > 0) fetch(vi0, qa, da);
-  if (rounds > 1) fetch(vi0 + kThreads, qb, db);
+  // kBufs vector buffers per row read: the loads run kBufs - 1 rounds ahead
+  // of the round that uses them.
+  u32x4 qv[kBufs], dv[kBufs];
+#pragma unroll
+  for (int j = 0; j < kBufs - 1; ++j)
+    if (j < rounds) fetch(vi0 + j * kThreads, qv[j], dv[j]);
   // The first vectors have landed before the loop (vmcnt(0)): inside it the
   // compiler then waits only for the vectors of the round it works on, not
-  // for the loads of the next two.
+  // for the loads of the rounds after it.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   {
     // Seed L: every lane's highest-scoring element of its first vector gets
@@ -1073,15 +1100,16 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     const int base = lo + vi0 * 8;
     float key = -INFINITY;
     int ke = -1;
+    if (residual && !want_beta && rounds > 0) dv[0] = draft_vec(vi0);
     if (vi0 < nfull) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float k;
         if (residual) {
-          const float lp2 = __builtin_fmaf(el(qa, e), c2, -zt2), lq2 = __builtin_fmaf(el(da, e), c2, -zd2);
+          const float lp2 = __builtin_fmaf(el(qv[0], e), c2, -zt2), lq2 = __builtin_fmaf(el(dv[0], e), c2, -zd2);
           k = lp2 > lq2 ? residual_log2_bound(lp2, lq2) : -INFINITY;
         } else {
-          k = (onehot && base + e == xex) ? -INFINITY : el(qa, e);
+          k = (onehot && base + e == xex) ? -INFINITY : el(qv[0], e);
         }
         if (EXCL && in_list(excl, nexcl, base + e)) k = -INFINITY;
         if (k > key) {
@@ -1096,8 +1124,8 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e == ke) {
-          klt = el(qa, e);
-          if (residual) kld = el(da, e);
+          klt = el(qv[0], e);
+          if (residual) kld = el(dv[0], e);
         }
       const int kidx = base + ke;
       t0 = total(klt, kld, word_at(philox10((uint32_t)kidx >> 2, crow, cseq, ctr3, k0, k1), kidx & 3));
@@ -1112,14 +1140,17 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     if (ls != -INFINITY) {
       set_L(ls);
       set_bounds();
+      // The seed goes to the other workgroups of the row at once.
+      if (threadIdx.x == 0) atomicMax(gkey, order_key(ls));
+      Lpost = ls;
     }
   }
   const PhaseTable phase(rounds);
-  // One round over the vectors qt0 / qd0 (whose loads were issued two rounds
-  // earlier).
+  // One round over the target vector qt0 (its load issued kBufs - 1 rounds
+  // earlier; qd0, the draft vector, only in the diagnostics variant).
   auto round = [&](int rnd, const u32x4& qt0, const u32x4& qd0) __attribute__((always_inline)) {
-    // The three unrolled rounds are scheduled one after the other: left to
-    // interleave them, the compiler would hold three rounds' Philox words
+    // The unrolled rounds are scheduled one after the other: left to
+    // interleave them, the compiler would hold several rounds' Philox words
     // at once and lose occupancy.
     __builtin_amdgcn_sched_barrier(0);
     phase.set(rnd);
@@ -1142,34 +1173,54 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     // the one-hot draft token or ask whether p > q: the survivor path does.
     // Only whether some lane of the wave has a survivor is kept: the
     // verdicts are lane masks OR-ed on the scalar unit.
+    // Each element slot's verdicts stay a wave mask in scalar registers, so
+    // that the tests after it run only for the slots, and in them only for
+    // the lanes, that passed.
+    uint64_t lm[8];
+    const uint64_t have_m = __builtin_amdgcn_ballot_w64(have);
     uint64_t surv = 0ull;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      surv |= lanes_may_win((e < 4) ? wa.w[e & 3] : wb.w[e & 3], __builtin_fmaf(el(qt0, e), c2s, bulk_bias));
-    surv &= __builtin_amdgcn_ballot_w64(have);
-    if (surv != 0ull && have) {
+    for (int e = 0; e < 8; ++e) {
+      lm[e] = lanes_may_win((e < 4) ? wa.w[e & 3] : wb.w[e & 3], __builtin_fmaf(el(qt0, e), c2s, bulk_bias)) & have_m;
+      surv |= lm[e];
+    }
+    if (surv != 0ull) {
       // One-hot: the draft token is excluded (xrel: its place in this vector,
       // if it is there).
       const int xrel = onehot ? xex - base : -1;
+      const u32x4 qd1 = (residual && !want_beta) ? draft_vec(vi) : qd0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        if (lm[e] == 0ull) continue;
+        if (!((lm[e] >> lane) & 1ull)) continue;
         uint32_t w = (e < 4) ? wa.w[e & 3] : wb.w[e & 3];
-        // Tested again on a word the compiler cannot match with the first
-        // test, so that it does not keep the eight verdicts in registers.
+        // A word the compiler cannot match with the bulk test's, so that it
+        // does not keep the bulk test's values in registers for this path.
         asm volatile("" : "+v"(w));
-        bool k;
+        const float lt = el(qt0, e);
+        float tot;
         if (residual) {
-          const float lp2 = __builtin_fmaf(el(qt0, e), c2, -zt2), lq2 = __builtin_fmaf(el(qd0, e), c2, -zd2);
-          k = lp2 > lq2 && may_win_bits(w, __builtin_fmaf(residual_log2_bound(lp2, lq2), 0x1p23f, log_bias));
+          const float lq2 = __builtin_fmaf(el(qd1, e), c2, -zd2), lp2 = __builtin_fmaf(lt, c2, -zt2);
+          if (!(lp2 > lq2)) continue;
+          const float bnd = residual_log2_bound(lp2, lq2);
+          if (!may_win_bits(w, __builtin_fmaf(bnd, 0x1p23f, log_bias))) continue;
+          if (EXCL && in_list(excl, nexcl, base + e)) continue;
+          // The exact noise first: with it, the bound on the score (in log2
+          // units, ln 2 times that in nats) decides most of these elements
+          // before the exact score, which costs several library logarithms.
+          // An element is dropped only below L by more than a margin that
+          // covers this sum's rounding, so every element that could reach L
+          // (ties included) goes on to its exact total.
+          const float g = gumbel(w);
+          if (__builtin_fmaf(bnd, kLn2, g) < L - fmaxf(1.0f, fabsf(L)) * 0x1p-12f) continue;
+          tot = lp2 * kLn2 + log1mexp((lq2 - lp2) * kLn2) + g;  // ln (p - q) + G
         } else {
-          k = (e != xrel) && may_win_bits(w, __builtin_fmaf(el(qt0, e), c2s, log_bias));
+          if (e == xrel || !may_win_bits(w, __builtin_fmaf(lt, c2s, log_bias))) continue;
+          if (EXCL && in_list(excl, nexcl, base + e)) continue;
+          tot = lt * invT + gumbel(w);
         }
-        if (EXCL && k && in_list(excl, nexcl, base + e)) k = false;
-        if (k) {
-          const float tot = total(el(qt0, e), residual ? el(qd0, e) : 0.0f, w);
-          best_push(bst, tot, base + e);
-          mine = fmaxf(mine, tot);
-        }
+        best_push(bst, tot, base + e);
+        mine = fmaxf(mine, tot);
       }
     }
     // Share and collect totals: only a wave with survivors can have a new one.
@@ -1191,8 +1242,8 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     __builtin_amdgcn_sched_barrier(0);
   };
   // The sequence's best total from the other workgroups of the row: loaded
-  // before the first of three rounds' vector loads and read after the third
-  // round, whose vectors were loaded after it (loads complete in order, so it
+  // before the first of kBufs rounds' vector loads and read after the last of
+  // them, whose vectors were loaded after it (loads complete in order, so it
   // costs no wait of its own).
   auto take_global = [&](uint32_t gk) {
     const float g = key_total(__builtin_amdgcn_readfirstlane(gk));
@@ -1202,18 +1253,18 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     }
   };
 #pragma unroll 1
-  for (int rnd = 0; rnd < rounds; rnd += 2) {
+  for (int rnd = 0; rnd < rounds; rnd += kBufs) {
     const uint32_t gk = xload(gkey);
-    if (rnd + 2 < rounds) fetch(vi0 + (rnd + 2) * kThreads, qc, dc);
-    round(rnd, qa, da);
-    if (rnd + 1 >= rounds) break;
-    qa = qb;
-    if (residual) da = db;
-    if (rnd + 3 < rounds) fetch(vi0 + (rnd + 3) * kThreads, qb, db);
-    round(rnd + 1, qa, da);
-    qa = qc;
-    if (residual) da = dc;
-    take_global(gk);
+#pragma unroll
+    for (int j = 0; j < kBufs; ++j) {
+      if (rnd + j >= rounds) break;
+      // The buffer freed by the round before this one takes the load of the
+      // round kBufs - 1 ahead.
+      if (rnd + j + kBufs - 1 < rounds)
+        fetch(vi0 + (rnd + j + kBufs - 1) * kThreads, qv[(j + kBufs - 1) % kBufs], dv[(j + kBufs - 1) % kBufs]);
+      round(rnd + j, qv[j], dv[j]);
+      if (j == kBufs - 1) take_global(gk);
+    }
   }
   // Elements past the last whole vector, one by one.
   const int tail_lo = lo + nfull * 8;
@@ -1255,7 +1306,7 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
 // Greedy bonus draw over [lo, hi): the target row's argmax (lowest index on
 // ties).
 template <bool BF16, bool VEC>
-__device__ void greedy_chunk(const ChainArgs& a, int b, const Decision d, int lo, int hi, Smem& sm, P2Slot* out) {
+__device__ __forceinline__ void greedy_chunk(const ChainArgs& a, int b, const Decision d, int lo, int hi, Smem& sm, P2Slot* out) {
   const uint8_t* rt = target_row(a, b, d.row);
   ArgMax best;
   best.v = -INFINITY;
@@ -1271,7 +1322,7 @@ __device__ void greedy_chunk(const ChainArgs& a, int b, const Decision d, int lo
 }
 
 template <bool BF16, bool VEC, bool BETA>
-__device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo, int hi, Smem& sm, P2Slot* out) {
+__device__ __forceinline__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo, int hi, Smem& sm, P2Slot* out) {
   if (d.mode == P2_GREEDY_BONUS) {
     greedy_chunk<BF16, VEC>(a, b, d, lo, hi, sm, out);
   } else if (BF16 && VEC) {
@@ -1294,7 +1345,7 @@ __device__ void pass2_chunk(const ChainArgs& a, int b, const Decision d, int lo,
 // Last pass-2 item of b: merge the chunk partials, write the last token and
 // return the sequence's scratch to zero.
 template <bool BF16, bool VEC, bool BETA>
-__device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks, Smem& sm) {
+__device__ __forceinline__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks, Smem& sm) {
   const int C2 = p2_nchunks, G = a.gamma;
   const Decision d = sm.dec;
   P2Slot* ps = a.p2 + (int64_t)b * a.p2_stride;
@@ -1391,7 +1442,7 @@ __device__ void finalize(const ChainArgs& a, int b, int p2_chunk, int p2_nchunks
 // Reads the decision record of b (thread 0). The first launch has completed,
 // so the record is complete: its four words in one round trip. Returns false
 // if it was never published (a wait of the first launch gave up).
-__device__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
+__device__ __forceinline__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
   uint64_t* rec = a.seq[b].dec;
   const uint64_t d0 = xget64(&rec[0]);
   const uint64_t d1 = xget64(&rec[1]);
@@ -1878,9 +1929,10 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
         acc.s = 0.0f;
         for (int lo2 = lo; lo2 < hi; lo2 += a.chunk) {
           const int hi2 = min(hi, lo2 + a.chunk);
-          const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && hi2 - lo2 == a.chunk;
+          const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && ((hi2 - lo2) & 7) == 0;
           Chunk<BF16, VEC> ch;
           ch.load(row, lo2, hi2, a.kv);
+          if (fast && hi2 - lo2 != a.chunk) ch.pad_neg_inf();
           acc = lse_merge(acc, block_lse(fast ? lse_packed_bf16(ch.q, c2) : chunk_lse(ch, row, a.kv, c2), c2, sm, kind),
                           c2);
         }
