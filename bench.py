@@ -5,9 +5,11 @@ chain_bf16_llama workload (B=256 sequences, gamma=8 drafts, V=128256, bf16
 logits, temperatures drawn from {0, 0.7, 1.0}), inputs resident in HBM. Prints
 one JSON line: verified positions/s (B * gamma per step) as `value`, the
 logit-read bandwidth against the HBM roofline of one verify call (the kernels
-it launches back to back on one stream, timed with HIP events on that stream),
-and the CPU oracle timed on the host as a baseline (every host thread the
-process may use, and one).
+it launches back to back on one stream, timed with one pair of HIP events on
+that stream around the timed steps), and the CPU oracle timed on the host as a
+baseline (every host thread the process may use, and one). Before the warmup
+steps the GPU reads a buffer for about 50 ms, so that the timed steps do not
+start on idle clocks.
 Beside the roofline it reports the GPU's streaming-read rate measured in the
 same run (the library's read yardstick over a 2 GiB buffer) and the call's
 fraction of it, and a warm-cache launch time (the same input copy every step,
@@ -164,6 +166,72 @@ def copy_calibration(torch, dev, steps: int):
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": steps}), flush=True)
 
 
+def settle(torch, dev, rsv, seconds: float = 0.05):
+    """Untimed, before the warmup steps: plain reads of a 512 MiB buffer for
+    about `seconds` of wall-clock time, so that the timed steps do not begin
+    while the GPU is still leaving its idle clocks (the first tens of calls
+    after an idle spell run several percent slower otherwise)."""
+    buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    nblocks = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(4 * nblocks, dtype=torch.int32, device=dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            rsv.sv_debug_read_stream(buf, nblocks, out=out)
+        torch.cuda.synchronize()
+    del buf
+
+
+def timed_region(torch, step, steps: int, stream, per_call: bool = False):
+    """The timed steps: synchronize, `steps` calls on `stream`, synchronize.
+    Returns (wall-clock seconds, mean ms per call from HIP events on `stream`,
+    per-call ms or None).
+
+    By default one event goes before the first call and one after the last, and
+    nothing else is queued between the calls: an event pair around every call
+    would put its own markers (several microseconds a call) into the timed
+    region. With per_call, an event pair goes around each call instead: for
+    kernels shorter than the host's time to issue a call, where back-to-back
+    calls leave the GPU waiting on the host and the mean of the whole region
+    would time the host."""
+    torch.cuda.synchronize()
+    if per_call:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for k, (a, b) in enumerate(ev):
+            a.record(stream)
+            step(k)
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        each = np.array([a.elapsed_time(b) for a, b in ev])
+        return wall, float(each.mean()), each
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(stream)
+    for k in range(steps):
+        step(k)
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, a.elapsed_time(b) / steps, None
+
+
+def launch_spread(torch, step, steps: int, stream):
+    """Untimed, after a timed region without per-call events: the same calls
+    with an event pair around each one, for the spread of a single call's time
+    (each figure includes the markers of its own pair)."""
+    return timed_region(torch, step, steps, stream, per_call=True)[2]
+
+
+def launch_stats(mean_ms: float, spread, per_call: bool = False):
+    note = ("an event pair around each timed call" if per_call else
+            "mean: two HIP events around the timed calls on the kernels' stream, divided by the calls; "
+            "p10/p50/p90: a second pass with an event pair around each call")
+    return {"mean": mean_ms, "p10": float(np.percentile(spread, 10)), "p50": float(np.median(spread)),
+            "p90": float(np.percentile(spread, 90)), "note": note}
+
+
 def run_kv(args, torch, rsv, workloads, dev):
     """KV-cache rollback after a tree verify step: one sv_kv_rollback call over
     the resident K and V caches of every layer. Successive steps move the root
@@ -183,23 +251,14 @@ def run_kv(args, torch, rsv, workloads, dev):
         rsv.sv_kv_rollback(k, v, roots[j % 16], path, plen, cache_len=out)
 
     stream = torch.cuda.current_stream()
+    settle(torch, dev, rsv)
     for j in range(args.warmup):
         step(j)
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for j in range(args.steps):
-        starts[j].record(stream)
-        step(j)
-        ends[j].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    wall, mean_ms, launch_ms = timed_region(torch, step, args.steps, stream, per_call=True)
     print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
     ms_per_step = wall * 1e3 / args.steps
     alg_bytes = inp.algorithmic_bytes()
-    achieved = alg_bytes / (float(np.mean(launch_ms)) * 1e-3) / 1e9
+    achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
     rec = {
         "metric": "KV-cache rollback sequences/s (every layer's K and V moved to the accepted path)",
         "value": B / (ms_per_step * 1e-3), "unit": "sequences/s", "n_gpus": 1, "steps": args.steps,
@@ -209,8 +268,7 @@ def run_kv(args, torch, rsv, workloads, dev):
                    "paths": "walks in the 65-node tree, 1 to 4 nodes"},
         "moved_rows_per_layer_head": int(inp.moved_rows().sum()),
         "algorithmic_bytes_per_step": int(alg_bytes),
-        "launch_ms": {"mean": float(np.mean(launch_ms)), "p10": float(np.percentile(launch_ms, 10)),
-                      "p50": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "launch_ms": launch_stats(mean_ms, launch_ms, per_call=True),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload)},
     }
@@ -237,24 +295,15 @@ def run_ngram(args, torch, rsv, workloads, dev):
                            out_match=out[2])
 
     stream = torch.cuda.current_stream()
+    settle(torch, dev, rsv)
     for j in range(args.warmup):
         step(j)
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for j in range(args.steps):
-        starts[j].record(stream)
-        step(j)
-        ends[j].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    wall, mean_ms, launch_ms = timed_region(torch, step, args.steps, stream, per_call=True)
     print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
     ms_per_step = wall * 1e3 / args.steps
     match = out[2].cpu().numpy()
     alg_bytes = inp.algorithmic_bytes(match)
-    achieved = alg_bytes / (float(np.mean(launch_ms)) * 1e-3) / 1e9
+    achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
     rec = {
         "metric": "n-gram (prompt-lookup) drafts/s: one-hot gamma-token proposals per second",
         "value": B / (ms_per_step * 1e-3), "unit": "drafts/s", "n_gpus": 1, "steps": args.steps,
@@ -267,8 +316,7 @@ def run_ngram(args, torch, rsv, workloads, dev):
         "algorithmic_bytes_per_step": int(alg_bytes),
         "algorithmic_bytes_note": "each sequence's tokens from its match's start to its end (all of them "
                                   "without a match), plus lengths and outputs",
-        "launch_ms": {"mean": float(np.mean(launch_ms)), "p10": float(np.percentile(launch_ms, 10)),
-                      "p50": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "launch_ms": launch_stats(mean_ms, launch_ms, per_call=True),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload)},
     }
@@ -303,23 +351,14 @@ def run_tree_mask(args, torch, rsv, workloads, dev):
         rsv.sv_tree_mask(par, off, out_mask=out_mask, out_position_ids=out_pos)
 
     stream = torch.cuda.current_stream()
+    settle(torch, dev, rsv)
     for j in range(args.warmup):
         step(j)
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for j in range(args.steps):
-        starts[j].record(stream)
-        step(j)
-        ends[j].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    wall, mean_ms, launch_ms = timed_region(torch, step, args.steps, stream, per_call=True)
     print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
     ms_per_step = wall * 1e3 / args.steps
     alg_bytes = inp.algorithmic_bytes()
-    achieved = alg_bytes / (float(np.mean(launch_ms)) * 1e-3) / 1e9
+    achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
     rec = {
         "metric": "tree attention masks/s (ancestor mask and depth position ids per sequence)",
         "value": B / (ms_per_step * 1e-3), "unit": "masks/s", "n_gpus": 1, "steps": args.steps,
@@ -328,8 +367,7 @@ def run_tree_mask(args, torch, rsv, workloads, dev):
         "config": {"workload": args.workload, "B": B, "nodes": N, "mask": "bool [B, N, N]",
                    "trees": "one per sequence, breadth-first, 1 to 4 children per node"},
         "algorithmic_bytes_per_step": int(alg_bytes),
-        "launch_ms": {"mean": float(np.mean(launch_ms)), "p10": float(np.percentile(launch_ms, 10)),
-                      "p50": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "launch_ms": launch_stats(mean_ms, launch_ms, per_call=True),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload)},
     }
@@ -454,23 +492,15 @@ def main():
                                    out_tokens=out[0], out_num_accepted=out[1], workspace=wbuf)
 
     stream = torch.cuda.current_stream()
+    settle(torch, dev, rsv)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        starts[k].record(stream)
-        step(k)
-        ends[k].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    wall, mean_ms, _ = timed_region(torch, step, args.steps, stream)
     print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
+    launch_ms = launch_spread(torch, step, args.steps, stream)
 
     # Warm cache, labelled as such: the same input copy every step, so that
     # part of it is still in the 256 MB MALL from the step before.
@@ -491,7 +521,7 @@ def main():
         # Data-dependent: the walk reads only the nodes on each sequence's path.
         inp.paths = (out[0].cpu().numpy(), out[1].cpu().numpy())
     alg_bytes = inp.algorithmic_bytes()
-    t_launch = float(np.mean(launch_ms)) * 1e-3
+    t_launch = mean_ms * 1e-3
     achieved = alg_bytes / t_launch / 1e9
     traffic = measured_traffic(args.workload)
 
@@ -527,8 +557,7 @@ def main():
         "logit_read_GBps": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac_of_peak": alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": int(alg_bytes),
-        "launch_ms": {"mean": float(np.mean(launch_ms)), "p10": float(np.percentile(launch_ms, 10)),
-                      "p50": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "launch_ms": launch_stats(mean_ms, launch_ms),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "hbm_read_ceiling_GBps": ceiling,
