@@ -33,7 +33,7 @@ WsLayout ws_layout(int32_t B, int32_t rows, int32_t nchunks) {
   L.tree_slot = off;
   off = round_up(off + (size_t)B * rows * nchunks * sizeof(TreeSlot), 256);
   L.work = off;
-  off = round_up(off + (size_t)B * sizeof(uint32_t), 256);
+  off = round_up(off + (size_t)B * sizeof(WorkRec), 256);
   L.total = off;
   return L;
 }
@@ -235,7 +235,7 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
   a.seq = (SeqState*)(ws + L.seq);
   a.p1 = (P1Slot*)(ws + L.p1);
   a.p2 = (P2Slot*)(ws + L.p2);
-  a.work = (uint32_t*)(ws + L.work);
+  a.work = (WorkRec*)(ws + L.work);
   a.spin_limit = 1u << 22;
   const long long n1 = (long long)gamma * tl.nchunks * (draft ? 2 : 1);
   if ((long long)B * (n1 + 1) >= (1ll << 31)) return SV_ERR_BAD_SHAPE;

@@ -702,23 +702,22 @@ __device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
   }
   __syncthreads();
   write_decision(a, b, sm);
-  // Publish the record for the pass-2 items: the payload, then (once it has
-  // landed) the word that marks it complete. Only a sequence with a pending
-  // draw has pass-2 items; it is appended to the work list.
+  // A sequence with a pending draw is appended to the work list with its
+  // decision record (the pass-2 launch reads them after this one ends).
   if (tid == 0) {
     const Decision& d = sm.dec;
     if (d.mode != P2_NONE) {
-      SeqState* st = a.seq + b;
-      xput64(&st->dec[1], pack(d.zt2, __float_as_uint(d.zd2)));
-      xput64(&st->dec[2], pack(d.c2, __float_as_uint(d.invT)));
-      xput64(&st->dec[3], pack(d.a_row, (uint32_t)d.x));
-      wait_vmem();
-      xput64(&st->dec[0], kRecPublished | ((uint64_t)(uint32_t)d.row << 32) | ((uint32_t)(d.n + 64) << 8) | d.mode);
-    }
-    if (d.mode != P2_NONE) {
       const uint32_t idx = atomicAdd(&a.done[kDoneNWork], 1u);
-      if (idx < (uint32_t)a.B) xput(&a.work[idx], (uint32_t)b);
-      else atomicOr(&a.done[1], 1u);  // a list left over from an aborted call
+      if (idx < (uint32_t)a.B) {
+        WorkRec* w = a.work + idx;
+        xput64(&w->dec[1], pack(d.zt2, __float_as_uint(d.zd2)));
+        xput64(&w->dec[2], pack(d.c2, __float_as_uint(d.invT)));
+        xput64(&w->dec[3], pack(d.a_row, (uint32_t)d.x));
+        xput(&w->b, (uint32_t)b);
+        xput64(&w->dec[0], kRecPublished | ((uint64_t)(uint32_t)d.row << 32) | ((uint32_t)(d.n + 64) << 8) | d.mode);
+      } else {
+        atomicOr(&a.done[1], 1u);  // a list left over from an aborted call
+      }
     }
   }
 }
@@ -1088,6 +1087,8 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
 #pragma unroll
   for (int j = 0; j < kBufs - 1; ++j)
     if (j < rounds) fetch(vi0 + j * kThreads, qv[j], dv[j]);
+  // The seed below needs the first draft vector of a residual draw too.
+  if (residual && !want_beta && rounds > 0) dv[0] = draft_vec(vi0);
   // The first vectors have landed before the loop (vmcnt(0)): inside it the
   // compiler then waits only for the vectors of the round it works on, not
   // for the loads of the rounds after it.
@@ -1100,7 +1101,6 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     const int base = lo + vi0 * 8;
     float key = -INFINITY;
     int ke = -1;
-    if (residual && !want_beta && rounds > 0) dv[0] = draft_vec(vi0);
     if (vi0 < nfull) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -1176,13 +1176,27 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     // Each element slot's verdicts stay a wave mask in scalar registers, so
     // that the tests after it run only for the slots, and in them only for
     // the lanes, that passed.
+    // First the lane's bound: its largest logit against its smallest n (the
+    // complement of its largest word). The test is monotone in both, so a
+    // lane that fails it has no element that passes the per-element test;
+    // at the large workloads about one wave-round in twenty has a lane that
+    // passes, and only then do the eight per-element tests run.
     uint64_t lm[8];
     const uint64_t have_m = __builtin_amdgcn_ballot_w64(have);
-    uint64_t surv = 0ull;
+    float lmax = el(qt0, 0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lm[e] = lanes_may_win((e < 4) ? wa.w[e & 3] : wb.w[e & 3], __builtin_fmaf(el(qt0, e), c2s, bulk_bias)) & have_m;
-      surv |= lm[e];
+    for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, el(qt0, e));
+    uint32_t wmax = wa.w[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) wmax = max(wmax, (e < 4) ? wa.w[e & 3] : wb.w[e & 3]);
+    const uint64_t lane_m = lanes_may_win(wmax, __builtin_fmaf(lmax, c2s, bulk_bias)) & have_m;
+    uint64_t surv = 0ull;
+    if (lane_m != 0ull) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lm[e] = lanes_may_win((e < 4) ? wa.w[e & 3] : wb.w[e & 3], __builtin_fmaf(el(qt0, e), c2s, bulk_bias)) & lane_m;
+        surv |= lm[e];
+      }
     }
     if (surv != 0ull) {
       // One-hot: the draft token is excluded (xrel: its place in this vector,
@@ -1424,13 +1438,14 @@ __device__ __forceinline__ void finalize(const ChainArgs& a, int b, int p2_chunk
     uint64_t* w2 = (uint64_t*)ps;
     for (int k = threadIdx.x; k < C2 * 2; k += kThreads) xput64(&w2[k], 0u);
   }
-  if (threadIdx.x < 4) xput64(&a.seq[b].dec[threadIdx.x], 0u);
+  // Every item of the sequence has read its work entry by now.
+  WorkRec* w = a.work + sm.unit[4];
+  if (threadIdx.x < 4) xput64(&w->dec[threadIdx.x], 0u);
   if (threadIdx.x == 0) {
+    xput(&w->b, 0u);
     xput(&a.seq[b].p2_arrive, 0u);
     xput(&a.seq[b].lbest, 0u);
-    // Every item on the work list has read it once all draws are done: the
-    // last sequence to finish returns the list to empty.
-    xput(&a.work[sm.unit[4]], 0u);
+    // The last sequence to finish returns the list to empty.
     const uint32_t fin = atomicAdd(&a.done[kDoneNFinal], 1u) + 1u;
     if (fin == sm.nwork) {
       xput(&a.done[kDoneNWork], 0u);
@@ -1439,16 +1454,18 @@ __device__ __forceinline__ void finalize(const ChainArgs& a, int b, int p2_chunk
   }
 }
 
-// Reads the decision record of b (thread 0). The first launch has completed,
-// so the record is complete: its four words in one round trip. Returns false
-// if it was never published (a wait of the first launch gave up).
-__device__ __forceinline__ bool read_decision(const ChainArgs& a, int b, Decision* out) {
-  uint64_t* rec = a.seq[b].dec;
-  const uint64_t d0 = xget64(&rec[0]);
-  const uint64_t d1 = xget64(&rec[1]);
-  const uint64_t d2 = xget64(&rec[2]);
-  const uint64_t d3 = xget64(&rec[3]);
-  if (!(d0 & kRecPublished)) {
+// Reads entry li of the work list (thread 0): the sequence and its decision
+// record in one round trip. The first launch has completed, so the entry is
+// complete; returns false if it was never published (a workspace left dirty
+// by an earlier call whose wait gave up).
+__device__ __forceinline__ bool read_work(const ChainArgs& a, int li, int* b, Decision* out) {
+  WorkRec* w = a.work + li;
+  const uint64_t d0 = xget64(&w->dec[0]);
+  const uint64_t d1 = xget64(&w->dec[1]);
+  const uint64_t d2 = xget64(&w->dec[2]);
+  const uint64_t d3 = xget64(&w->dec[3]);
+  const uint32_t wb = xload(&w->b);
+  if (!(d0 & kRecPublished) || wb >= (uint32_t)a.B) {
     atomicOr(&a.done[1], 1u);
     return false;
   }
@@ -1465,25 +1482,15 @@ __device__ __forceinline__ bool read_decision(const ChainArgs& a, int b, Decisio
   d.a_row = hi_f(d3);
   d.x = (int)lo_u(d3);
   d.tok = -1;
+  *b = (int)wb;
   *out = d;
   return true;
 }
 
+// Chunk c of the draw of sequence b, whose decision the launch has read
+// into sm.dec.
 template <bool BF16, bool VEC, bool BETA>
 __device__ __forceinline__ void pass2_item(const ChainArgs& a, int b, int c, int p2_chunk, int p2_nchunks, Smem& sm) {
-  if (threadIdx.x == 0) {
-    Decision d;
-    const bool ok = read_decision(a, b, &d);
-    if (!ok) {
-      d.mode = P2_NONE;
-      d.n = -4;
-      a.out_n[b] = -4;
-    }
-    sm.dec = d;
-    sm.stalled = ok ? 0u : 1u;
-    sm.lkey = 0u;
-  }
-  __syncthreads();
   const Decision d = sm.dec;
   P2Slot part;
   part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
@@ -1549,11 +1556,17 @@ __global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
       const uint32_t u = blockIdx.x;
       if (u < nw * (uint32_t)nc) {
         li = (int)(u / (uint32_t)nc);
-        b = (int)xload(&a.work[li]);
         c = (int)(u % (uint32_t)nc);
-        if (b >= a.B) b = -1;
+        Decision d;
+        if (read_work(a, li, &b, &d)) {
+          sm.dec = d;
+          sm.stalled = 0u;
+        } else {
+          b = -1;  // nothing this workgroup can do: the call reports through done[1]
+        }
       }
     }
+    sm.lkey = 0u;
     sm.nwork = nw;
     sm.unit[0] = b;
     sm.unit[1] = c;

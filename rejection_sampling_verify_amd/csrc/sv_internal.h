@@ -28,17 +28,24 @@ struct SeqState {
   uint32_t p2_arrive;  // pass-2 items finished
   uint32_t lbest;      // pass 2: the largest Gumbel total any item of the
                        // sequence has reached so far, as an order key (0: none)
-  uint32_t pad0[2];
-  // The decision record:
-  //   dec[1] = (zt2 bits << 32) | zd2 bits     (log2-domain normalizers)
-  //   dec[2] = (c2 bits << 32) | invT bits
-  //   dec[3] = (a_row bits << 32) | x
-  //   dec[0] = 2^63 | row << 32 | (n + 64) << 8 | mode, stored last.
-  // Written by the decision item of the sequence, read by its pass-2 items.
-  uint64_t dec[4];
-  uint32_t pad1[20];
+  uint32_t pad0[30];
 };
 static_assert(sizeof(SeqState) == 128, "one line per sequence");
+
+// Entry of the pass-2 work list: a sequence with a pending draw and its
+// decision record, written by its decision item, read by its pass-2 items
+// in one round trip:
+//   dec[1] = (zt2 bits << 32) | zd2 bits     (log2-domain normalizers)
+//   dec[2] = (c2 bits << 32) | invT bits
+//   dec[3] = (a_row bits << 32) | x
+//   dec[0] = 2^63 | row << 32 | (n + 64) << 8 | mode
+//   b      = the sequence
+struct WorkRec {
+  uint64_t dec[4];
+  uint32_t b;
+  uint32_t pad[7];
+};
+static_assert(sizeof(WorkRec) == 64, "half a line per entry");
 constexpr uint64_t kRecPublished = 1ull << 63;
 
 // Words of the workspace's control line (ChainArgs::done), on their own
@@ -101,8 +108,8 @@ struct ChainArgs {
   SeqState* seq;      // [B]
   P1Slot* p1;         // [B, gamma, nchunks]
   P2Slot* p2;         // [B, p2_stride]
-  uint32_t* work;     // [B] sequences with pass-2 work, in the order their
-                      // decisions were taken
+  WorkRec* work;      // [B] sequences with pass-2 work and their decisions, in
+                      // the order the decisions were taken
   uint32_t spin_limit;
 };
 
