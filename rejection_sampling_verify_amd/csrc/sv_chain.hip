@@ -188,11 +188,11 @@ __device__ __forceinline__ uint32_t lo_u(uint64_t w) { return (uint32_t)w; }
 // vector (a ragged tail) are read one by one by the thread owning the next
 // vector index. Without 16-byte alignment every element is read singly.
 // ---------------------------------------------------------------------------
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int KV = kMaxVecsPerThread>
 struct Chunk {
   using E = Elem<BF16>;
   static constexpr int EV = E::kPerVec;
-  u32x4 q[kMaxVecsPerThread];
+  u32x4 q[KV];
   int nfull;  // whole vectors in the chunk
   int lo, hi;
 
@@ -202,7 +202,7 @@ struct Chunk {
     nfull = VEC ? (hi - lo) / EV : 0;
     if (VEC) {
 #pragma unroll
-      for (int k = 0; k < kMaxVecsPerThread; ++k) {
+      for (int k = 0; k < KV; ++k) {
         const int vi = k * kThreads + (int)threadIdx.x;
         if (k < kv && vi < nfull) q[k] = load_vec_stream(row + (int64_t)(lo + vi * EV) * E::kBytes);
       }
@@ -216,7 +216,7 @@ struct Chunk {
   // paths serve a short chunk too, as long as it holds whole vectors only.
   __device__ __forceinline__ void pad_neg_inf() {
 #pragma unroll
-    for (int k = 0; k < kMaxVecsPerThread; ++k) {
+    for (int k = 0; k < KV; ++k) {
       const int vi = k * kThreads + (int)threadIdx.x;
       if (vi >= nfull) q[k] = u32x4{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
     }
@@ -228,7 +228,7 @@ struct Chunk {
   __device__ __forceinline__ void for_each(const uint8_t* row, int kv, F&& f) const {
     if (VEC) {
 #pragma unroll
-      for (int k = 0; k < kMaxVecsPerThread; ++k) {
+      for (int k = 0; k < KV; ++k) {
         const int vi = k * kThreads + (int)threadIdx.x;
         if (k < kv && vi < nfull) {
           float v[EV];
@@ -247,8 +247,8 @@ struct Chunk {
   }
 };
 
-template <bool BF16, bool VEC>
-__device__ __forceinline__ LseState chunk_lse(const Chunk<BF16, VEC>& ch, const uint8_t* row, int kv,
+template <bool BF16, bool VEC, int KV>
+__device__ __forceinline__ LseState chunk_lse(const Chunk<BF16, VEC, KV>& ch, const uint8_t* row, int kv,
                                               float c) {
   float M = -INFINITY;
   ch.for_each(row, kv, [&](float v, int) { M = fmaxf(M, v); });
@@ -263,8 +263,8 @@ __device__ __forceinline__ LseState chunk_lse(const Chunk<BF16, VEC>& ch, const 
   return st;
 }
 
-template <bool BF16, bool VEC>
-__device__ __forceinline__ ArgMax chunk_argmax(const Chunk<BF16, VEC>& ch, const uint8_t* row, int kv) {
+template <bool BF16, bool VEC, int KV>
+__device__ __forceinline__ ArgMax chunk_argmax(const Chunk<BF16, VEC, KV>& ch, const uint8_t* row, int kv) {
   ArgMax best;
   best.v = -INFINITY;
   best.i = -1;
@@ -296,10 +296,11 @@ __device__ __forceinline__ uint32_t pk_max_f16(uint32_t a, uint32_t b) {
   return r;
 }
 
-__device__ __forceinline__ float packed_max_bf16(const u32x4 (&q)[kMaxVecsPerThread]) {
+template <int KV>
+__device__ __forceinline__ float packed_max_bf16(const u32x4 (&q)[KV]) {
   uint32_t m0 = 0xFBFFFBFFu, m1 = 0xFBFFFBFFu;
 #pragma unroll
-  for (int k = 0; k < kMaxVecsPerThread; ++k) {
+  for (int k = 0; k < KV; ++k) {
     m0 = pk_max_f16(m0, q[k][0]);
     m1 = pk_max_f16(m1, q[k][1]);
     m0 = pk_max_f16(m0, q[k][2]);
@@ -314,9 +315,10 @@ __device__ __forceinline__ float packed_max_bf16(const u32x4 (&q)[kMaxVecsPerThr
 
 // Keeps the compiler from holding the unpacked elements of a max pass in
 // registers until a later pass (unpacking again is cheaper than 32 registers).
-__device__ __forceinline__ void opaque(u32x4 (&q)[kMaxVecsPerThread]) {
+template <int KV>
+__device__ __forceinline__ void opaque(u32x4 (&q)[KV]) {
 #pragma unroll
-  for (int k = 0; k < kMaxVecsPerThread; ++k)
+  for (int k = 0; k < KV; ++k)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t w = q[k][j];
@@ -325,7 +327,8 @@ __device__ __forceinline__ void opaque(u32x4 (&q)[kMaxVecsPerThread]) {
     }
 }
 
-__device__ __forceinline__ LseState lse_packed_bf16(u32x4 (&q)[kMaxVecsPerThread], float c) {
+template <int KV>
+__device__ __forceinline__ LseState lse_packed_bf16(u32x4 (&q)[KV], float c, int kvn = KV) {
   LseState st;
   st.M = packed_max_bf16(q);
   st.s = 0.0f;
@@ -333,7 +336,8 @@ __device__ __forceinline__ LseState lse_packed_bf16(u32x4 (&q)[kMaxVecsPerThread
     const float Mc = st.M * c;
     float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kMaxVecsPerThread; ++k) {
+    for (int k = 0; k < KV; ++k) {
+      if (k >= kvn) break;  // padding vectors (all -inf) add nothing
       s0 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][0] << 16), c, -Mc));
       s1 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][0] & 0xFFFF0000u), c, -Mc));
       s2 += fast_exp2(__builtin_fmaf(__uint_as_float(q[k][1] << 16), c, -Mc));
@@ -361,10 +365,11 @@ __device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
 // see: +inf, a NaN with the sign bit clear, or a value of 2^121 or more (bit
 // patterns from 0x7C00 up). Positive bf16 values order like their patterns
 // read as signed 16-bit integers, so one packed integer maximum finds them.
-__device__ __forceinline__ bool has_huge_positive_bf16(const u32x4 (&q)[kMaxVecsPerThread]) {
+template <int KV>
+__device__ __forceinline__ bool has_huge_positive_bf16(const u32x4 (&q)[KV]) {
   uint32_t m0 = 0x80008000u, m1 = 0x80008000u;
 #pragma unroll
-  for (int k = 0; k < kMaxVecsPerThread; ++k) {
+  for (int k = 0; k < KV; ++k) {
     m0 = pk_max_i16(m0, q[k][0]);
     m1 = pk_max_i16(m1, q[k][1]);
     m0 = pk_max_i16(m0, q[k][2]);
@@ -378,7 +383,8 @@ __device__ __forceinline__ bool has_huge_positive_bf16(const u32x4 (&q)[kMaxVecs
 // a positive element it cannot see (see has_huge_positive_bf16), or a chunk
 // whose maximum reads as -inf (every element -inf, or some at or below
 // -2^121). The caller then scans the chunk element by element.
-__device__ __forceinline__ ArgMax argmax_packed_bf16(u32x4 (&q)[kMaxVecsPerThread], int lo, Smem& sm) {
+template <int KV>
+__device__ __forceinline__ ArgMax argmax_packed_bf16(u32x4 (&q)[KV], int lo, Smem& sm) {
   float m = packed_max_bf16(q);
   if (has_huge_positive_bf16(q)) m = INFINITY;
   opaque(q);
@@ -392,7 +398,7 @@ __device__ __forceinline__ ArgMax argmax_packed_bf16(u32x4 (&q)[kMaxVecsPerThrea
   int idx = 0x7FFFFFFF;
   if (m == bm) {
 #pragma unroll
-    for (int k = kMaxVecsPerThread - 1; k >= 0; --k) {
+    for (int k = KV - 1; k >= 0; --k) {
       const int base = lo + (k * kThreads + (int)threadIdx.x) * 8;
 #pragma unroll
       for (int j = 3; j >= 0; --j) {
@@ -763,7 +769,9 @@ __device__ __forceinline__ void pass1_item(const ChainArgs& a, int b, int r, Sme
     w0 = pack(m.v, (uint32_t)(m.i + 1));
   } else {
     const float c2 = kLog2e / T;
-    LseState st = block_lse(fast ? lse_packed_bf16(ch.q, c2) : chunk_lse(ch, row, a.kv, c2), c2, sm, 0);
+    LseState st = block_lse(fast ? lse_packed_bf16(ch.q, c2, (ch.nfull + kThreads - 1) / kThreads)
+                                 : chunk_lse(ch, row, a.kv, c2),
+                            c2, sm, 0);
     // The packed maximum skips elements of magnitude 2^121 or more, +inf and
     // NaN. A skipped element above the maximum overflows the sum (+inf or
     // NaN), and a chunk whose every element is skipped or -inf reads as -inf:
@@ -1668,11 +1676,10 @@ __device__ __forceinline__ void tree_children(int N, const int32_t* par, int v, 
 // for them with their gathered logits).
 template <bool BF16>
 __device__ __forceinline__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, TreeState& s, const int32_t* kids,
-                                int nkids, const uint8_t* haskid, const int32_t* tok_s, const uint64_t (*part)[2],
-                                int tree_bad, int tok_bad, bool writer, const TreeDrawn& dr) {
-  using E = Elem<BF16>;
+                                int nkids, const uint8_t* haskid, const int32_t* tok_s, float merged0, float merged1,
+                                int tree_bad, int tok_bad, bool writer, const TreeDrawn& dr, float T,
+                                float pre_lt = 0.0f, float pre_ld = 0.0f) {
   const ChainArgs& a = ta.c;
-  const float T = a.temperature[b];
   const float c2 = kLog2e / T;
   int32_t* path = ta.out_path + (int64_t)b * (ta.max_depth + 1);
   auto to_node = [&](int v) {
@@ -1704,24 +1711,11 @@ __device__ __forceinline__ uint32_t tree_decide(const TreeSampleArgs& ta, int b,
     return haskid[0] ? TA_STATS : TA_DRAW_BONUS;
   }
   if (prev == TA_STATS) {
-    LseState t, d;
-    t.M = d.M = -INFINITY;
-    t.s = d.s = 0.0f;
-    for (int w = 0; w < ta.W; ++w) {
-      const uint64_t w0 = part[w][0], w1 = part[w][1];
-      LseState o;
-      o.M = hi_f(w0);
-      o.s = __uint_as_float(lo_u(w0));
-      t = lse_merge(t, o, c2);
-      o.M = hi_f(w1);
-      o.s = __uint_as_float(lo_u(w1));
-      d = lse_merge(d, o, c2);
-    }
-    s.zt2 = t.M * c2 + fast_log2(t.s);
-    s.zd2 = d.M * c2 + fast_log2(d.s);
+    // The node's log2 normalizers, merged from the workgroups' parts.
+    s.zt2 = merged0;
+    s.zd2 = merged1;
   } else {
-    float S = 0.0f;
-    for (int w = 0; w < ta.W; ++w) S += __uint_as_float((uint32_t)part[w][0]);
+    float S = merged0;  // the pass's mass, summed over the workgroups' parts
     const int r = s.round;  // the sibling just rejected
     if (ta.wor)
       for (int i = 0; i < r; ++i) S += dr.F[i] - fmaxf(0.0f, dr.p[i] - s.An * dr.q[i]);
@@ -1740,7 +1734,8 @@ __device__ __forceinline__ uint32_t tree_decide(const TreeSampleArgs& ta, int b,
     return (s.round > 0 && s.A > 0.0f) ? TA_DRAW_RESIDUAL : TA_DRAW_BONUS;
   }
   const int x = tok_s[c];
-  const float lt = E::load(target_row(a, b, s.node), x), ld = E::load(draft_row(a, b, s.node), x);
+  // The two logits of the sibling were gathered while the action ran.
+  const float lt = pre_lt, ld = pre_ld;
   const float lp2 = __builtin_fmaf(lt, c2, -s.zt2), lq2 = __builtin_fmaf(ld, c2, -s.zd2);
   const float p = fast_exp2(lp2), q = fast_exp2(lq2);
   const float sfac = (ta.wor && s.qd > 0.0f) ? 1.0f / (1.0f - s.qd) : 1.0f;
@@ -1912,60 +1907,98 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
       for (int k2 = 1; k2 < k; ++k2) dup |= s_par[k2] == s_par[k] && s_tok[k2] == s_tok[k];
     tok_bad |= __syncthreads_or(dup);
   }
+  // The sequence's temperature, read once.
+  const float T = a.temperature[b];
   // The first decisions need no part of any workgroup.
   if (threadIdx.x == 0) {
     TreeState s0;
-    s_action = tree_decide<BF16>(ta, b, TA_NONE, s0, s_kids, 0, s_haskid, s_tok, nullptr, tree_bad, tok_bad, w == 0, dr);
+    s_action = tree_decide<BF16>(ta, b, TA_NONE, s0, s_kids, 0, s_haskid, s_tok, 0.0f, 0.0f, tree_bad, tok_bad, w == 0, dr, T);
     s_state = s0;
     sm.lkey = 0u;
   }
   __syncthreads();
   uint32_t action = s_action;
   if (action == TA_DONE) return;  // a bad input: nothing was touched
-  const float c2 = kLog2e / a.temperature[b];
+  const float c2 = kLog2e / T;
+  // Statistics pieces: four vectors per thread (a slice is usually one piece).
+  constexpr int kPieceVecs = 4;
+  constexpr int piece = kThreads * Elem<BF16>::kPerVec * kPieceVecs;
+  // The first piece of this workgroup's slice of the target and draft rows of
+  // the child the next decision tests (if it has children), loaded while the
+  // parts are exchanged: if the walk enters that child, its statistics start
+  // from them.
+  Chunk<BF16, VEC, kPieceVecs> spec[2];
+  int spec_node = -1;
   for (uint32_t epoch = 0; epoch <= (uint32_t)ta.N + 2u; ++epoch) {
     const TreeState t = s_state;
+    // The node's children, and the two logits at the node of the sibling the
+    // next decision tests (the first child after the statistics, the next one
+    // after a pass), requested now so that they have landed by then.
+    tree_children(ta.N, s_par, t.node, s_kids, &s_nkids, s_wcnt);
+    __syncthreads();
+    float pre_lt = 0.0f, pre_ld = 0.0f;
+    if (threadIdx.x == 0 && (action == TA_STATS || action == TA_PASS)) {
+      const int next = action == TA_STATS ? 0 : t.round + 1;
+      if (next < s_nkids) {
+        const int x = s_tok[s_kids[next]];
+        pre_lt = Elem<BF16>::load(target_row(a, b, t.node), x);
+        pre_ld = Elem<BF16>::load(draft_row(a, b, t.node), x);
+      }
+    }
     float partial = 0.0f;
     P2Slot part;
     part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
     part.w1 = 0u;
+    // The tag of this action's parts (nonzero: slots hold zero between calls).
+    const uint32_t tag = epoch + 1u;
     if (action == TA_STATS) {
-      // (max, sum exp2) of the node's target and draft rows over [lo, hi),
-      // in pieces of the launch's tile.
-      LseState lt, ld;
-      lt.M = ld.M = -INFINITY;
-      lt.s = ld.s = 0.0f;
-      for (int kind = 0; kind < 2; ++kind) {  // the target row, then the draft row
-        const uint8_t* row = kind ? draft_row(a, b, t.node) : target_row(a, b, t.node);
-        LseState acc;
-        acc.M = -INFINITY;
-        acc.s = 0.0f;
-        for (int lo2 = lo; lo2 < hi; lo2 += a.chunk) {
-          const int hi2 = min(hi, lo2 + a.chunk);
-          const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && ((hi2 - lo2) & 7) == 0;
-          Chunk<BF16, VEC> ch;
-          ch.load(row, lo2, hi2, a.kv);
-          if (fast && hi2 - lo2 != a.chunk) ch.pad_neg_inf();
-          acc = lse_merge(acc, block_lse(fast ? lse_packed_bf16(ch.q, c2) : chunk_lse(ch, row, a.kv, c2), c2, sm, kind),
-                          c2);
+      // The log2 normalizers of the node's target and draft rows over
+      // [lo, hi): both slices requested at once, in pieces of the launch's
+      // tile.
+      LseState acc[2];
+      acc[0].M = acc[1].M = -INFINITY;
+      acc[0].s = acc[1].s = 0.0f;
+      const uint8_t* rows[2] = {target_row(a, b, t.node), draft_row(a, b, t.node)};
+      for (int lo2 = lo; lo2 < hi; lo2 += piece) {
+        const int hi2 = min(hi, lo2 + piece);
+        const bool fast = BF16 && VEC && ((hi2 - lo2) & 7) == 0;
+        Chunk<BF16, VEC, kPieceVecs> ch[2];
+        if (lo2 == lo && spec_node == t.node) {
+          ch[0] = spec[0];
+          ch[1] = spec[1];
+        } else {
+          ch[0].load(rows[0], lo2, hi2, kPieceVecs);
+          ch[1].load(rows[1], lo2, hi2, kPieceVecs);
         }
-        if (kind) ld = acc;
-        else lt = acc;
+        const int kvn = (ch[0].nfull + kThreads - 1) / kThreads;
+#pragma unroll
+        for (int kind = 0; kind < 2; ++kind) {
+          if (fast && hi2 - lo2 != piece) ch[kind].pad_neg_inf();
+          acc[kind] = lse_merge(acc[kind],
+                                block_lse(fast ? lse_packed_bf16(ch[kind].q, c2, kvn)
+                                               : chunk_lse(ch[kind], rows[kind], kPieceVecs, c2),
+                                          c2, sm, kind),
+                                c2);
+        }
       }
-      part.w0 = pack(lt.M, __float_as_uint(lt.s));
-      part.w1 = pack(ld.M, __float_as_uint(ld.s));
+      const float zt = acc[0].M == -INFINITY ? -INFINITY : acc[0].M * c2 + fast_log2(acc[0].s);
+      const float zd = acc[1].M == -INFINITY ? -INFINITY : acc[1].M * c2 + fast_log2(acc[1].s);
+      part.w0 = ((uint64_t)__float_as_uint(zt) << 32) | tag;
+      part.w1 = ((uint64_t)__float_as_uint(zd) << 32) | tag;
     } else if (action == TA_PASS) {
       const float zd2s = t.zd2 - fast_log2(t.An);
       partial = block_sum(residual_mass_part<BF16, VEC>(target_row(a, b, t.node), draft_row(a, b, t.node), lo, hi, c2,
                                                         t.zt2, zd2s),
                           sm);
+      part.w0 = ((uint64_t)__float_as_uint(partial) << 32) | tag;
+      part.w1 = tag;
     } else {
       Decision d;
       d.kind = KIND_SAMPLED;
       d.n = 0;
       d.row = t.node;
       d.x = -1;
-      d.T = a.temperature[b];
+      d.T = T;
       d.c2 = c2;
       d.invT = 1.0f / d.T;
       d.zt2 = t.zt2;
@@ -1986,58 +2019,101 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
         else gumbel_chunk<BF16, VEC, P2_BONUS>(a, b, d, lo, hi, sm, &part);
       }
     }
-    // Arrive with this workgroup's part (buffer epoch & 1): the arrival counter
-    // only grows during the walk, W per action.
+    spec_node = -1;
+    if (action == TA_STATS || action == TA_PASS) {
+      const int next = action == TA_STATS ? 0 : t.round + 1;
+      const int c = next < s_nkids ? s_kids[next] : -1;
+      if (c >= 0) {
+        // (A leaf child is drawn from at once, from its target row only: its
+        // statistics are never taken, and the load only brings that slice
+        // into the cache for the draw.)
+        const int hi2 = min(hi, lo + piece);
+        spec[0].load(target_row(a, b, c), lo, hi2, kPieceVecs);
+        if (s_haskid[c]) spec[1].load(draft_row(a, b, c), lo, hi2, kPieceVecs);
+        spec_node = c;
+      }
+    }
+    // This workgroup's part goes to buffer epoch & 1 (a workgroup can start
+    // the next action while another still reads this one's parts).
     P2Slot* parts = ((epoch & 1u) ? ta.slot2 : a.p2) + (int64_t)b * a.p2_stride;
-    const uint32_t want = (uint32_t)ta.W * (epoch + 1u);
-    if (threadIdx.x == 0) {
-      if (action == TA_PASS) {
-        xput64(&parts[w].w0, (uint64_t)__float_as_uint(partial));
-      } else {
+    if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) {
+      // The draw: the last of the W to arrive finishes the sequence (the
+      // arrival counter counts the draw only).
+      if (threadIdx.x == 0) {
         xput64(&parts[w].w0, part.w0);
         xput64(&parts[w].w1, part.w1);
+        wait_vmem();
+        sm.flag_last = (atomicAdd(&st->p2_arrive, 1u) + 1u == (uint32_t)ta.W) ? 1u : 0u;
       }
-      wait_vmem();
-      const uint32_t old = atomicAdd(&st->p2_arrive, 1u);
-      sm.flag_last = (old + 1u == want) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) {
+      __syncthreads();
       if (sm.flag_last) {
         const int nx = (ta.wor && action == TA_DRAW_RESIDUAL) ? t.round - 1 : 0;
         tree_finish<BF16, VEC>(ta, b, t.len, parts, epoch > 0u, t.node, nx > 0 ? nx : 0, dr, sm);
       }
       return;
     }
-    // Wait until all W have arrived (bounded).
+    // Statistics and passes: every word of a part carries the action's tag,
+    // so a part is complete when both its words show it. Thread k reads part
+    // k until it does (a bounded wait), then every workgroup takes the same
+    // decisions from the same parts.
     if (threadIdx.x == 0) {
-      uint32_t spins = 0;
-      sm.stalled = 0u;
-      while (xget(&st->p2_arrive) < want) {
-        if (++spins > a.spin_limit || ((spins & 255u) == 0u && xget(&a.done[1]) != 0u)) {
+      xput64(&parts[w].w0, part.w0);
+      xput64(&parts[w].w1, part.w1);
+    }
+    int stalled = 0;
+    for (int k = threadIdx.x; k < ta.W; k += kThreads) {
+      uint64_t w0 = xget64((uint64_t*)&parts[k].w0), w1 = xget64((uint64_t*)&parts[k].w1);
+      for (uint32_t spins = 0; (uint32_t)w0 != tag || (uint32_t)w1 != tag; ++spins) {
+        if (spins > a.spin_limit || ((spins & 255u) == 255u && xget(&a.done[1]) != 0u)) {
           atomicOr(&a.done[1], 1u);
-          xput(&ta.out_len[b], -4);
-          sm.stalled = 1u;
+          stalled = 1;
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(1);
+        w0 = xget64((uint64_t*)&parts[k].w0);
+        w1 = xget64((uint64_t*)&parts[k].w1);
       }
+      sm.u.slot[k][0] = w0 >> 32;
+      sm.u.slot[k][1] = w1 >> 32;
     }
-    __syncthreads();
-    if (sm.stalled) return;
-    // Every workgroup: the parts (read in parallel), the node's children, and
-    // the same decisions.
-    for (int k = threadIdx.x; k < ta.W; k += kThreads) {
-      sm.u.slot[k][0] = xget64((uint64_t*)&parts[k].w0);
-      sm.u.slot[k][1] = xget64((uint64_t*)&parts[k].w1);
+    if (__syncthreads_or(stalled)) {
+      if (threadIdx.x == 0) xput(&ta.out_len[b], -4);
+      return;
     }
-    tree_children(ta.N, s_par, t.node, s_kids, &s_nkids, s_wcnt);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      TreeState s1 = s_state;
-      s_action = tree_decide<BF16>(ta, b, action, s1, s_kids, s_nkids, s_haskid, s_tok, sm.u.slot, 0, 0, w == 0, dr);
-      s_state = s1;
-      sm.lkey = 0u;
+    // Wave 0 merges the parts, lane k taking parts k, k + 64, ... (a fixed
+    // order): the statistics' log2 normalizers (largest part, then the sum of
+    // exp2 of each part less it), or the pass's mass. Thread 0 then decides.
+    if (threadIdx.x < 64) {
+      float m0, m1 = 0.0f;
+      if (action == TA_STATS) {
+        float lt = -INFINITY, ld = -INFINITY;
+        for (int k = threadIdx.x; k < ta.W; k += 64) {
+          lt = fmaxf(lt, __uint_as_float((uint32_t)sm.u.slot[k][0]));
+          ld = fmaxf(ld, __uint_as_float((uint32_t)sm.u.slot[k][1]));
+        }
+        const float mt = wave_max(lt), md = wave_max(ld);
+        float st = 0.0f, sd = 0.0f;
+        for (int k = threadIdx.x; k < ta.W; k += 64) {
+          const float zt = __uint_as_float((uint32_t)sm.u.slot[k][0]), zd = __uint_as_float((uint32_t)sm.u.slot[k][1]);
+          if (zt != -INFINITY) st += fast_exp2(zt - mt);
+          if (zd != -INFINITY) sd += fast_exp2(zd - md);
+        }
+        st = wave_sum(st);
+        sd = wave_sum(sd);
+        m0 = mt == -INFINITY ? -INFINITY : mt + fast_log2(st);
+        m1 = md == -INFINITY ? -INFINITY : md + fast_log2(sd);
+      } else {
+        float S = 0.0f;
+        for (int k = threadIdx.x; k < ta.W; k += 64) S += __uint_as_float((uint32_t)sm.u.slot[k][0]);
+        m0 = wave_sum(S);
+      }
+      if (threadIdx.x == 0) {
+        TreeState s1 = s_state;
+        s_action = tree_decide<BF16>(ta, b, action, s1, s_kids, s_nkids, s_haskid, s_tok, m0, m1, 0, 0, w == 0, dr, T,
+                                     pre_lt, pre_ld);
+        s_state = s1;
+        sm.lkey = 0u;
+      }
     }
     __syncthreads();
     action = s_action;
