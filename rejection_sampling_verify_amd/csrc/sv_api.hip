@@ -49,9 +49,12 @@ struct Tiling {
   int kv, chunk, nchunks;
 };
 
-// Pass-1 items a launch should hold at least, so that small batches still
-// spread over the whole GPU.
-constexpr long long kTargetItems = 4096;
+// Pass-1 items a launch should hold at least (one per CU), so that small
+// batches still spread over the whole GPU. Above that, longer chunks win: at
+// chain_bf16_peaked (640 row reads of 32000) chunks of eight vectors per
+// thread (1280 items, one resident wave of them) take 31.7 us a call against
+// 36.9 us for two vectors per thread (5120 items).
+constexpr long long kTargetItems = 256;
 
 // Chunk length: as long as possible (8 vectors per thread) while the pass-1
 // item count stays at or above the target. forced_kv (a power of two up to 8)
