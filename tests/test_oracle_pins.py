@@ -313,6 +313,67 @@ def test_one_hot_draft():
     assert _chi2_pvalue(obs, expect, int(rej.sum())) > 1e-4
 
 
+def test_one_hot_residual_over_several_blocks():
+    """Exercise 4's replacement p without x, on a row of three draw blocks: the
+    block is chosen by its share of that mass and the Gumbel-max runs inside
+    it, so every token other than x must still come out with p(v) / (1 - p(x)).
+    Heavy tokens sit in every block (x among them, in block 0) so that a block
+    weighed with x's mass, a block picked without the uniform, or an element
+    drawn outside its block all move the counts."""
+    rng = np.random.default_rng(41)
+    K = oracle.DRAW_BLOCK
+    V, B = 2 * K + 5000, 12000
+    l = (rng.normal(0, 1.0, V) - 6.0).astype(np.float32)
+    heavy = {100: 2.0, 101: 3.0, K + 7: 1.5, K + 9000: 2.2, 2 * K + 4999: 1.8}
+    for v, val in heavy.items():
+        l[v] = val
+    x = 101
+    tgt = np.broadcast_to(np.stack([l, l]), (B, 2, V)).copy()
+    ids = np.full((B, 1), x, np.int32)
+    u = np.full((B, 1), 1.0 - 2.0 ** -24)  # every sequence rejects x
+    r = oracle.verify_sample(tgt, None, ids, np.ones(B, np.float32), seed=17, u_override=u)
+    assert np.all(r["n"] == 0)
+    p = _softmax64(l, 1.0)
+    res = p.copy()
+    res[x] = 0.0
+    res /= res.sum()
+    tok = r["tokens"][:, 0]
+    assert not np.any(tok == x)
+    cats = {}
+    for v in heavy:
+        if v != x:
+            cats[("tok", v)] = res[v]
+    for j in range(3):
+        lo, hi = j * K, min(V, (j + 1) * K)
+        rest = res[lo:hi].sum() - sum(res[v] for v in heavy if lo <= v < hi)
+        cats[("rest", j)] = rest
+    obs = {}
+    for v in tok:
+        key = ("tok", int(v)) if int(v) in heavy else ("rest", int(v) // K)
+        obs[key] = obs.get(key, 0) + 1
+    assert _chi2_pvalue(obs, cats, B) > 1e-4
+    assert np.allclose(r["residual_mass"], 1.0 - p[x], atol=1e-12)
+
+
+def test_one_hot_residual_skips_empty_blocks():
+    """A block holding no mass besides x is never chosen, whatever its uniform:
+    with every entry of block 0 but x at -inf, every replacement lies in the
+    other blocks."""
+    K = oracle.DRAW_BLOCK
+    V, B = 2 * K + 8000, 400
+    l = np.full(V, -np.inf, np.float32)
+    l[5] = 4.0  # x
+    l[K:] = np.random.default_rng(3).normal(0, 1.0, V - K).astype(np.float32)
+    tgt = np.broadcast_to(np.stack([l, l]), (B, 2, V)).copy()
+    ids = np.full((B, 1), 5, np.int32)
+    u = np.full((B, 1), 1.0 - 2.0 ** -24)
+    r = oracle.verify_sample(tgt, None, ids, np.ones(B, np.float32), seed=2, u_override=u)
+    assert np.all(r["n"] == 0)
+    assert np.all(r["tokens"][:, 0] >= K)
+    # both other blocks are reached
+    assert (r["tokens"][:, 0] >= 2 * K).any() and (r["tokens"][:, 0] < 2 * K).any()
+
+
 def test_bonus_draw_follows_p_of_last_row():
     """With q = p every draft is accepted; the bonus token is then a draw from
     p of row gamma (not of any other row)."""
