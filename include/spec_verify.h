@@ -55,8 +55,7 @@
  * Random.   Randomness is counter-based Philox4x32-10 (Salmon et al., SC'11)
  *           with key = (seed low 32 bits, seed high 32 bits) and counter words
  *           (c0, c1, c2, c3) = (c0, position, seq_base + b, 2*offset + stream):
- *             stream 0, c0 = 0       : accept uniform of position i = word 0,
- *                                      block uniform of position i = word 1;
+ *             stream 0, c0 = 0       : accept uniform of position i = word 0;
  *             stream 1, c0 = v / 4   : Gumbel noise of vocab entry v = word v%4.
  *           A word w maps to u = (w >> 8) * 2^-24 (accept test, u in [0,1)) or
  *           to U = ((w >> 8) + 0.5) * 2^-24 in (0,1) and Gumbel noise
@@ -155,13 +154,7 @@ const char* sv_status_string(sv_status_t status);
  *                 position gamma.
  *   If rounding leaves (p_n - q_n)_+ empty, the correction is drawn from p_n
  *   instead (same noise). With draft_logits == NULL the draft is one-hot at x_i
- *   ([SB] Exercise 4): a_i = p_i(x_i) and the residual is p_n without x_n,
- *   drawn in two steps: the row is cut into blocks of 16384 entries, the
- *   first block whose running sum of that residual (in block order) exceeds
- *   u' times its total is chosen (u' = the block uniform of position n, the
- *   last block with mass if rounding carries u' past the end), and the
- *   Gumbel-max runs inside that block only. Each entry v != x_n is emitted
- *   with p_n(v) / (1 - p_n(x_n)), as by one Gumbel-max over the whole row.
+ *   ([SB] Exercise 4): a_i = p_i(x_i) and the residual is p_n without x_n.
  * For T == 0 the sequence is verified greedily ([SB] "Extending to a chain of
  * γ draft tokens", its temperature-0 paragraph): x_i is accepted iff it
  * equals argmax_v of target row i (lowest index on ties); the correction is

@@ -30,7 +30,6 @@ SEQ_BAD_LOGITS = -5
 FLAG_KNIFE_EDGE = 1
 FLAG_FALLBACK = 2
 KNIFE_EDGE = 1e-5
-DRAW_BLOCK = 16384  # one-hot residual draws take place in one block of this many entries
 
 _lib = None
 
@@ -58,8 +57,6 @@ def lib() -> ctypes.CDLL:
         L.or_philox4x32_10.restype = None
         L.or_accept_uniform.argtypes = [u64, u64, i32, i32]
         L.or_accept_uniform.restype = ctypes.c_double
-        L.or_block_uniform.argtypes = [u64, u64, i32, i32]
-        L.or_block_uniform.restype = ctypes.c_double
         L.or_gumbel.argtypes = [u64, u64, i32, i32, i32]
         L.or_gumbel.restype = ctypes.c_double
         L.or_verify_sample.argtypes = [P, i64, P, i64, ctypes.c_int, P, P, i32, i32, i32, u64, u64,
@@ -120,10 +117,6 @@ def philox4x32_10(ctr, key) -> np.ndarray:
 
 def accept_uniform(seed: int, offset: int, b: int, i: int) -> float:
     return lib().or_accept_uniform(seed, offset, b, i)
-
-
-def block_uniform(seed: int, offset: int, b: int, i: int) -> float:
-    return lib().or_block_uniform(seed, offset, b, i)
 
 
 def gumbel(seed: int, offset: int, b: int, pos: int, v: int) -> float:

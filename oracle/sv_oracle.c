@@ -24,14 +24,6 @@
  *  - the accept test is u < a with u = (w >> 8) * 2^-24;
  *  - samples of the residual (p - q)_+ and of the bonus distribution p are
  *    drawn by Gumbel-max with G = -ln(-ln U), U = ((w >> 8) + 0.5) * 2^-24;
- *  - with a one-hot draft the residual is p without the drafted token x
- *    ([SB] Exercise 4), drawn in two steps: the row is cut into blocks of
- *    OR_DRAW_BLOCK entries; the first block whose running sum of that mass
- *    exceeds u' times the whole (u' from word 1 of the accept draw at the
- *    rejected position, mapped as u) is chosen, and the Gumbel-max runs over
- *    that block alone. Block j holds mass m_j, and the Gumbel-max inside it
- *    picks v with p(v) / m_j, so v is emitted with p(v) / sum_j m_j: the same
- *    law as one Gumbel-max over the whole row;
  *  - random words come from Philox4x32-10 with key (seed_lo, seed_hi) and
  *    counter (c0, position, sequence, 2*offset + stream);
  *  - an empty residual (only reachable through rounding) falls back to p;
@@ -97,14 +89,6 @@ double or_accept_uniform(uint64_t seed, uint64_t offset, int32_t b, int32_t i) {
   uint32_t w[4];
   or_words(seed, 0u, (uint32_t)i, (uint32_t)b, (uint32_t)(2u * (uint32_t)offset), w);
   return (double)(w[0] >> 8) * (1.0 / 16777216.0);
-}
-
-/* Block uniform u' of sequence b at position i: stream 0, word 1 (the
- * accept uniform's draw, another of its words). */
-double or_block_uniform(uint64_t seed, uint64_t offset, int32_t b, int32_t i) {
-  uint32_t w[4];
-  or_words(seed, 0u, (uint32_t)i, (uint32_t)b, (uint32_t)(2u * (uint32_t)offset), w);
-  return (double)(w[1] >> 8) * (1.0 / 16777216.0);
 }
 
 /* Gumbel noise of vocab entry v for sequence b at position pos: stream 1. */
@@ -299,51 +283,13 @@ static void or_sample_one(const void* target, int64_t tstride, const void* draft
       for (int32_t v = 0; v < V; ++v) yq[v] /= T;
     }
     beta = 0.0;
-    /* One-hot draft: the block the draw is taken in (all of the row
-     * otherwise). */
-    int32_t vlo = 0, vhi = V;
-    if (one_hot) {
-      const int32_t nb = (V + OR_DRAW_BLOCK - 1) / OR_DRAW_BLOCK;
-      double* mass = (double*)malloc(sizeof(double) * (size_t)nb);
-      /* Masses up to a common factor: relative to the largest entry other
-       * than x, so that W > 0 exactly when some entry other than x is finite. */
-      double mx = -INFINITY;
-      for (int32_t v = 0; v < V; ++v)
-        if (v != x && yp[v] > mx) mx = yp[v];
-      double W = 0.0;
-      for (int32_t j = 0; j < nb; ++j) {
-        mass[j] = 0.0;
-        if (mx > -INFINITY)
-          for (int32_t v = j * OR_DRAW_BLOCK; v < V && v < (j + 1) * OR_DRAW_BLOCK; ++v)
-            if (v != x) mass[j] += exp(yp[v] - mx);
-        W += mass[j];
-      }
-      if (W > 0.0) {
-        const double t = or_block_uniform(seed, offset, b, n) * W;
-        int32_t pick = -1, last = -1;
-        double run = 0.0;
-        for (int32_t j = 0; j < nb; ++j) {
-          run += mass[j];
-          if (mass[j] > 0.0) {
-            last = j;
-            if (fabs(run - t) < OR_BLOCK_KNIFE * W) flags |= OR_FLAG_KNIFE_EDGE;
-            if (pick < 0 && run > t) pick = j;
-          }
-        }
-        if (pick < 0) pick = last; /* t reached the end through rounding */
-        vlo = pick * OR_DRAW_BLOCK;
-        vhi = (pick + 1) * OR_DRAW_BLOCK < V ? (pick + 1) * OR_DRAW_BLOCK : V;
-      }
-      free(mass);
-    }
     for (int32_t v = 0; v < V; ++v) {
       double lp = yp[v] - logzp[n];
       double score;
       if (one_hot) {
         if (v == x) continue; /* (p - delta_x)_+ vanishes at x */
-        beta += exp(lp);
-        if (v < vlo || v >= vhi) continue; /* outside the chosen block */
         score = yp[v];
+        beta += exp(lp);
       } else {
         double lq = yq[v] - logzq[n];
         if (!(lp > lq)) continue; /* outside the support of (p - q)_+ */

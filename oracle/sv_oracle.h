@@ -20,18 +20,13 @@
 #define OR_SEQ_BAD_LOGITS (-5) /* a sampled sequence's row has no probability distribution */
 
 /* flags[b] bits */
-#define OR_FLAG_KNIFE_EDGE 1 /* some tested position had |u - a| < OR_KNIFE_EDGE, or a one-hot
-                              residual's block uniform lay within OR_BLOCK_KNIFE of a block edge */
+#define OR_FLAG_KNIFE_EDGE 1 /* some tested position had |u - a| < OR_KNIFE_EDGE */
 #define OR_FLAG_FALLBACK 2   /* the residual was empty; the correction came from p */
 
 /* An accept decision closer than this to its threshold is excusable in a
  * comparison with an fp32 implementation whose accept probabilities are held
  * to the same absolute tolerance. */
 #define OR_KNIFE_EDGE 1e-5
-/* One-hot residual draws take place in one block of OR_DRAW_BLOCK consecutive
- * vocabulary entries; the block is chosen by its share of the residual mass. */
-#define OR_DRAW_BLOCK 16384
-#define OR_BLOCK_KNIFE 1e-5 /* relative to the residual mass */
 
 /* Optional per-sequence diagnostics (any field may be NULL). */
 typedef struct {
@@ -47,7 +42,6 @@ typedef struct {
 
 void or_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 double or_accept_uniform(uint64_t seed, uint64_t offset, int32_t b, int32_t i);
-double or_block_uniform(uint64_t seed, uint64_t offset, int32_t b, int32_t i);
 double or_gumbel(uint64_t seed, uint64_t offset, int32_t b, int32_t pos, int32_t v);
 
 /* Returns 0 on success, nonzero for invalid arguments. u_override [B, gamma]

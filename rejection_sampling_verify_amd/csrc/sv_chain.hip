@@ -51,7 +51,6 @@ struct Decision {
   float zt2, zd2;  // log2-domain normalizers of target / draft row `row`
   float a_row;     // accept probability at `row` (one-hot draft: p(x) there)
   int tok;         // token at position n when the decision already fixes it
-  int slo, shi;    // the draw runs over entries [slo, shi) of `row`
 };
 
 struct Smem {
@@ -71,7 +70,6 @@ struct Smem {
   LseState rt[kMaxGamma], rd[kMaxGamma];
   ArgMax rg[kMaxGamma];
   int32_t acc[kMaxGamma];
-  float ublk[kMaxGamma];  // decision: block uniform of each position (one-hot drafts)
   Decision dec;
 };
 
@@ -227,24 +225,6 @@ struct Chunk {
     }
   }
 
-  // bf16: element x of the chunk (if it is one of its whole vectors) becomes
-  // -inf, so that the packed paths leave it out. Only the lane holding it
-  // changes anything.
-  __device__ __forceinline__ void mask_index(int x) {
-    const int rel = x - lo;
-    if (!BF16 || !VEC || rel < 0 || rel >= nfull * EV) return;
-    const int vi = rel / EV, e = rel % EV;
-    if ((vi % kThreads) != (int)threadIdx.x) return;
-#pragma unroll
-    for (int k = 0; k < KV; ++k)
-      if (k == vi / kThreads) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (j == (e >> 1))
-            q[k][j] = (e & 1) ? ((q[k][j] & 0x0000FFFFu) | 0xFF800000u) : ((q[k][j] & 0xFFFF0000u) | 0x0000FF80u);
-      }
-  }
-
   // Calls f(value, index) for each element this thread owns, in increasing
   // index order.
   template <typename F>
@@ -270,20 +250,15 @@ struct Chunk {
   }
 };
 
-// skip: an entry left out of the statistics (-1: none).
 template <bool BF16, bool VEC, int KV>
 __device__ __forceinline__ LseState chunk_lse(const Chunk<BF16, VEC, KV>& ch, const uint8_t* row, int kv,
-                                              float c, int skip = -1) {
+                                              float c) {
   float M = -INFINITY;
-  ch.for_each(row, kv, [&](float v, int idx) {
-    if (idx != skip) M = fmaxf(M, v);
-  });
+  ch.for_each(row, kv, [&](float v, int) { M = fmaxf(M, v); });
   float s = 0.0f;
   if (M != -INFINITY) {
     const float Mc = M * c;
-    ch.for_each(row, kv, [&](float v, int idx) {
-      if (idx != skip) s += fast_exp2(__builtin_fmaf(v, c, -Mc));
-    });
+    ch.for_each(row, kv, [&](float v, int) { s += fast_exp2(__builtin_fmaf(v, c, -Mc)); });
   }
   LseState st;
   st.M = M;
@@ -570,79 +545,6 @@ __device__ __forceinline__ void write_decision(const ChainArgs& a, int b, Smem& 
   if (tid == 0 && a.d_beta && d.mode != P2_RESIDUAL && d.mode != P2_RESIDUAL_ONEHOT) a.d_beta[b] = NAN;
 }
 
-// Inclusive prefix sum over a wave, lane order.
-__device__ __forceinline__ float wave_incl_scan(float x) {
-  const int lane = (int)(threadIdx.x & 63);
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float t = __shfl_up(x, d, 64);
-    if (lane >= d) x += t;
-  }
-  return x;
-}
-
-// Wave 0 of a decision whose one-hot draft was rejected at row n = sm.dec.n:
-// the block of kDrawBlock entries the residual draw takes place in. The
-// residual is p without the drafted token, which the chunk statistics already
-// leave out, so block j's share is its merged chunk sums scaled to a common
-// maximum. The first block whose running sum (in block order) exceeds u' times
-// the total is chosen, u' the block uniform of row n (the last block with a
-// share if rounding carries u' past the end). Its entries go to sm.dec.slo and
-// sm.dec.shi; with no share anywhere the draw keeps the whole row. The
-// slots come from LDS when the decision polled them in one batch (in_lds),
-// else from the workspace, which still holds them.
-__device__ __forceinline__ void pick_draw_block(const ChainArgs& a, int b, const P1Slot* slots, bool in_lds, Smem& sm) {
-  const int lane = (int)(threadIdx.x & 63);
-  const int n = sm.dec.n, C = a.nchunks;
-  const int cpb = kDrawBlock / a.chunk, NB = (C + cpb - 1) / cpb;
-  const float c2 = sm.dec.c2, u = sm.ublk[n];
-  auto block = [&](int j) -> LseState {
-    LseState st;
-    st.M = -INFINITY;
-    st.s = 0.0f;
-    if (j < NB) {
-      for (int cc = j * cpb; cc < min(C, (j + 1) * cpb); ++cc) {
-        const uint64_t w0 = in_lds ? sm.u.slot[n * C + cc][0] : xget64((uint64_t*)&slots[n * C + cc].w0);
-        LseState o;
-        o.M = hi_f(w0);
-        o.s = __uint_as_float(lo_u(w0));
-        st = lse_merge(st, o, c2);
-      }
-    }
-    return st;
-  };
-  float Mx = -INFINITY;
-  for (int g = 0; g < NB; g += 64) Mx = fmaxf(Mx, wave_max(block(g + lane).M));
-  if (Mx == -INFINITY) return;  // nothing besides the drafted token
-  auto weight = [&](int j) -> float {
-    const LseState st = block(j);
-    return st.M == -INFINITY ? 0.0f : st.s * fast_exp2((st.M - Mx) * c2);
-  };
-  // The total, as the same running sums reach it below.
-  float W = 0.0f;
-  for (int g = 0; g < NB; g += 64) W += __shfl(wave_incl_scan(weight(g + lane)), 63, 64);
-  const float t = u * W;
-  float carry = 0.0f;
-  int pick = -1, last = -1;
-  for (int g = 0; g < NB; g += 64) {
-    const float w = weight(g + lane);
-    const float incl = wave_incl_scan(w);
-    const uint64_t nz = __ballot(w > 0.0f);
-    const uint64_t hit = __ballot(w > 0.0f && carry + incl > t);
-    if (nz) last = g + 63 - __clzll((long long)nz);
-    if (hit) {
-      pick = g + __ffsll((long long)hit) - 1;
-      break;
-    }
-    carry += __shfl(incl, 63, 64);
-  }
-  if (pick < 0) pick = last;
-  if (lane == 0 && pick >= 0) {
-    sm.dec.slo = pick * kDrawBlock;
-    sm.dec.shi = min(a.V, (pick + 1) * kDrawBlock);
-  }
-}
-
 template <bool BF16>
 __device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
   const int G = a.gamma, C = a.nchunks, tid = threadIdx.x;
@@ -670,13 +572,12 @@ __device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
   // word still set) decides nothing: the sequence reports SV_SEQ_INTERNAL.
   if (tid == 0) sm.stalled = (xload(&a.done[1]) != 0u) ? 1u : 0u;
   __syncthreads();
-  // Every slot is waited for (also when a drafted id turns out to be invalid,
-  // so that no slot can land after they have been cleared), 256 at a time,
-  // and each row's chunks are merged in order. The slots return to zero at
-  // the end (a one-hot residual's draw block is chosen from them first).
-  P1Slot* const slots = a.p1 + (int64_t)b * G * C;
-  const int total = G * C;
   if (kind != KIND_BAD_T) {
+    // Wait for every slot (also when a drafted id turns out to be invalid, so
+    // that no slot can land after they have been cleared), 256 at a time;
+    // return them to zero and merge each row's chunks in order.
+    P1Slot* slots = a.p1 + (int64_t)b * G * C;
+    const int total = G * C;
     for (int base = 0; base < total; base += kThreads) {
       const int k = base + tid;
       if (k < total) {
@@ -698,6 +599,10 @@ __device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
         sm.u.slot[tid][1] = w1;
       }
       __syncthreads();
+      if (k < total) {
+        xput64(&slots[k].w0, 0u);
+        xput64(&slots[k].w1, 0u);
+      }
       if (tid < G) {
         const int r0 = max(tid * C, base), r1 = min(tid * C + C, base + kThreads);
         for (int r = r0; r < r1; ++r) {
@@ -730,13 +635,6 @@ __device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
   if (tid == 0) sm.flag_last = 0u;  // set below if some row has no distribution
   __syncthreads();
   if (tid < G && kind == KIND_SAMPLED) {
-    if (a.draft == nullptr) {
-      // The drafted token was left out of the chunk statistics.
-      LseState ox;
-      ox.M = glt;
-      ox.s = 1.0f;
-      sm.rt[tid] = lse_merge(sm.rt[tid], ox, c2);
-    }
     const float z2t = sm.rt[tid].M * c2 + fast_log2(sm.rt[tid].s);
     const float lp2 = __builtin_fmaf(glt, c2, -z2t);
     float z2d = NAN, lq2 = 0.0f;
@@ -751,7 +649,6 @@ __device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
     const float acc_p = fast_exp2(fminf(0.0f, lp2 - lq2));
     const Words4 w = philox10(0u, (uint32_t)tid, a.seq_base + (uint32_t)b, a.ctr_accept, a.key0, a.key1);
     sm.acc[tid] = (uniform_accept(w.w[0]) < acc_p) ? 1 : 0;
-    sm.ublk[tid] = uniform_accept(w.w[1]);  // a one-hot residual's block uniform
     sm.rt[tid].M = z2t;  // from here on: the row normalizers and a_i
     sm.rd[tid].M = z2d;
     sm.rt[tid].s = acc_p;
@@ -770,8 +667,6 @@ __device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
     d.zt2 = d.zd2 = 0.0f;
     d.a_row = 0.0f;
     d.tok = -1;
-    d.slo = 0;
-    d.shi = a.V;
     if (kind == KIND_BAD_T) {
       d.n = -2;
     } else if (kind == KIND_BAD_ID) {
@@ -815,15 +710,6 @@ __device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
     sm.dec = d;
   }
   __syncthreads();
-  if (sm.dec.mode == P2_RESIDUAL_ONEHOT && tid < 64) pick_draw_block(a, b, slots, total <= kThreads, sm);
-  if (kind != KIND_BAD_T) {
-    __syncthreads();  // the block's slots have been read
-    for (int k = tid; k < total; k += kThreads) {
-      xput64(&slots[k].w0, 0u);
-      xput64(&slots[k].w1, 0u);
-    }
-  }
-  __syncthreads();
   write_decision(a, b, sm);
   // A sequence with a pending draw is appended to the work list with its
   // decision record (the pass-2 launch reads them after this one ends).
@@ -837,8 +723,6 @@ __device__ __forceinline__ void decide(const ChainArgs& a, int b, Smem& sm) {
         xput64(&w->dec[2], pack(d.c2, __float_as_uint(d.invT)));
         xput64(&w->dec[3], pack(d.a_row, (uint32_t)d.x));
         xput(&w->b, (uint32_t)b);
-        xput(&w->slo, (uint32_t)d.slo);
-        xput(&w->shi, (uint32_t)d.shi);
         xput64(&w->dec[0], kRecPublished | ((uint64_t)(uint32_t)d.row << 32) | ((uint32_t)(d.n + 64) << 8) | d.mode);
       } else {
         atomicOr(&a.done[1], 1u);  // a list left over from an aborted call
@@ -869,21 +753,12 @@ __device__ __forceinline__ void pass1_item(const ChainArgs& a, int b, int r, Sme
   const int lo = c * a.chunk;
   const int hi = min(a.V, lo + a.chunk);
   const uint8_t* row = draft_item ? draft_row(a, b, i) : target_row(a, b, i);
-  // A one-hot draft's drafted token is left out of the target statistics:
-  // the decision adds it back from its gathered logit, and the draw blocks'
-  // shares of the residual (p without x) are then sums without cancellation.
-  int skip = -1;
-  if (kind == KIND_SAMPLED && a.draft == nullptr) {
-    const int x = a.ids[(int64_t)b * a.gamma + i];
-    if (x >= lo && x < hi) skip = x;
-  }
   // 16-byte-aligned bf16 chunk at the full tile width holding whole vectors
   // only (a short last chunk is padded with -inf): fast path.
   const bool fast = BF16 && VEC && a.kv == kMaxVecsPerThread && ((hi - lo) & 7) == 0;
   Chunk<BF16, VEC> ch;
   ch.load(row, lo, hi, a.kv);
   if (fast && hi - lo != a.chunk) ch.pad_neg_inf();
-  if (fast && skip >= 0) ch.mask_index(skip);
   // w0 belongs to the target item, w1 to the draft item of a dense draft and
   // to the target item otherwise.
   uint64_t w0 = 0u, w1 = 1u;
@@ -898,7 +773,7 @@ __device__ __forceinline__ void pass1_item(const ChainArgs& a, int b, int r, Sme
   } else {
     const float c2 = kLog2e / T;
     LseState st = block_lse(fast ? lse_packed_bf16(ch.q, c2, (ch.nfull + kThreads - 1) / kThreads)
-                                 : chunk_lse(ch, row, a.kv, c2, skip),
+                                 : chunk_lse(ch, row, a.kv, c2),
                             c2, sm, 0);
     // The packed maximum skips elements of magnitude 2^121 or more, +inf and
     // NaN. A skipped element above the maximum overflows the sum (+inf or
@@ -906,7 +781,7 @@ __device__ __forceinline__ void pass1_item(const ChainArgs& a, int b, int r, Sme
     // in both cases the plain scan takes the chunk again. (If the row has no
     // distribution, its statistics stay non-finite and the decision reports
     // the sequence.)
-    if (fast && (!(st.s <= 3.0e38f) || st.M == -INFINITY)) st = block_lse(chunk_lse(ch, row, a.kv, c2, skip), c2, sm, 0);
+    if (fast && (!(st.s <= 3.0e38f) || st.M == -INFINITY)) st = block_lse(chunk_lse(ch, row, a.kv, c2), c2, sm, 0);
     const uint64_t w = pack(st.M, __float_as_uint(st.s));
     if (draft_item) w1 = w;
     else w0 = w;
@@ -1579,8 +1454,6 @@ __device__ __forceinline__ void finalize(const ChainArgs& a, int b, int p2_chunk
   if (threadIdx.x < 4) xput64(&w->dec[threadIdx.x], 0u);
   if (threadIdx.x == 0) {
     xput(&w->b, 0u);
-    xput(&w->slo, 0u);
-    xput(&w->shi, 0u);
     xput(&a.seq[b].p2_arrive, 0u);
     xput(&a.seq[b].lbest, 0u);
     // The last sequence to finish returns the list to empty.
@@ -1603,8 +1476,7 @@ __device__ __forceinline__ bool read_work(const ChainArgs& a, int li, int* b, De
   const uint64_t d2 = xget64(&w->dec[2]);
   const uint64_t d3 = xget64(&w->dec[3]);
   const uint32_t wb = xload(&w->b);
-  const uint32_t slo = xload(&w->slo), shi = xload(&w->shi);
-  if (!(d0 & kRecPublished) || wb >= (uint32_t)a.B || slo >= shi || shi > (uint32_t)a.V) {
+  if (!(d0 & kRecPublished) || wb >= (uint32_t)a.B) {
     atomicOr(&a.done[1], 1u);
     return false;
   }
@@ -1621,8 +1493,6 @@ __device__ __forceinline__ bool read_work(const ChainArgs& a, int li, int* b, De
   d.a_row = hi_f(d3);
   d.x = (int)lo_u(d3);
   d.tok = -1;
-  d.slo = (int)slo;
-  d.shi = (int)shi;
   *b = (int)wb;
   *out = d;
   return true;
@@ -1637,15 +1507,8 @@ __device__ __forceinline__ void pass2_item(const ChainArgs& a, int b, int c, int
   part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
   part.w1 = 0u;
   if (d.mode != P2_NONE) {
-    // The whole row in the launch's chunks, or a draw block cut into as many
-    // pieces of whole rounds (the last ones may be empty).
-    int lo = c * p2_chunk, hi = min(a.V, lo + p2_chunk);
-    if (d.slo != 0 || d.shi != a.V) {
-      const int len = ((d.shi - d.slo + p2_nchunks - 1) / p2_nchunks + a.p2_unit - 1) / a.p2_unit * a.p2_unit;
-      lo = min(d.shi, d.slo + c * len);
-      hi = min(d.shi, lo + len);
-    }
-    if (lo < hi) pass2_chunk<BF16, VEC, BETA>(a, b, d, lo, hi, sm, &part);
+    const int lo = c * p2_chunk;
+    pass2_chunk<BF16, VEC, BETA>(a, b, d, lo, min(a.V, lo + p2_chunk), sm, &part);
   }
   if (threadIdx.x == 0) {
     sm.flag_last = 0u;
@@ -2152,8 +2015,6 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
       d.zd2 = action == TA_DRAW_RESIDUAL ? t.zd2 - fast_log2(t.A) : t.zd2;
       d.a_row = 0.0f;
       d.tok = -1;
-      d.slo = 0;
-      d.shi = a.V;
       d.mode = action == TA_DRAW_RESIDUAL ? P2_RESIDUAL : P2_BONUS;
       // Without replacement, the siblings drawn before the last one keep
       // their own values: they are drawn apart, at the finish.

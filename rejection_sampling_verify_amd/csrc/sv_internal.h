@@ -10,9 +10,6 @@ namespace sv {
 
 constexpr int kMaxVecsPerThread = 8;  // 16-byte vectors per thread per row chunk
 constexpr int kMaxGamma = 16;
-// A one-hot draft's residual draw takes place in one block of this many
-// consecutive vocabulary entries, chosen by its share of the residual mass.
-constexpr int kDrawBlock = 16384;
 constexpr int kMaxTreeNodes = 1024;
 
 // Pass-2 work of a decided sequence.
@@ -43,13 +40,10 @@ static_assert(sizeof(SeqState) == 128, "one line per sequence");
 //   dec[3] = (a_row bits << 32) | x
 //   dec[0] = 2^63 | row << 32 | (n + 64) << 8 | mode
 //   b      = the sequence
-//   slo, shi = the entries [slo, shi) of the row the draw runs over (the
-//            whole row, or one draw block for a one-hot residual)
 struct WorkRec {
   uint64_t dec[4];
   uint32_t b;
-  uint32_t slo, shi;
-  uint32_t pad[5];
+  uint32_t pad[7];
 };
 static_assert(sizeof(WorkRec) == 64, "half a line per entry");
 constexpr uint64_t kRecPublished = 1ull << 63;

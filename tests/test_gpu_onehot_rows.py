@@ -1,16 +1,14 @@
-"""GPU parity of the one-hot residual draw over several draw blocks, through
-the C ABI, against the CPU oracle.
+"""GPU parity of the one-hot residual draw on long, shaped rows, through the
+C ABI, against the CPU oracle.
 
 With a one-hot draft ([SB] Exercise 4) the replacement is p without the
-drafted token. The library draws it in two steps: a block of 16384 entries is
-chosen by its share of that mass (the block uniform of the rejected position),
-then the Gumbel-max runs inside the block. The cases put the mass in chosen
-blocks, leave blocks empty (every entry -inf), put the drafted token alone in
-its block, use a ragged last block, rows that are not 16-byte aligned (the
-scalar paths), every pass-1 chunk length (a block is then several chunks),
-and a vocabulary of more than 64 blocks with more pass-1 slots than one
-polling batch (the decision then reads the block's slots back from the
-workspace).
+drafted token, drawn by Gumbel-max over the whole row. The cases shape the
+rows in spans of 16384 entries: mass in one span only, spans emptied (every
+entry -inf), the drafted token alone in its span, one span much heavier than
+the rest; with a ragged end, rows that are not 16-byte aligned (the scalar
+paths), fp32, every pass-1 chunk length, and a vocabulary of more than a
+million entries with more pass-1 slots than one polling batch of the
+decision.
 """
 import numpy as np
 import pytest
@@ -24,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-K = oracle.DRAW_BLOCK
+K = 16384  # the span length the rows are shaped in
 
 
 @pytest.fixture(scope="module")
@@ -36,11 +34,11 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _shape_blocks(inp, seed):
-    """Per sequence, one of: mass spread over every block; all blocks but one
-    emptied; the drafted token alone in its block; one block much heavier
-    than the rest. Applied to every target row, so whichever position is
-    rejected has that shape."""
+def _shape_spans(inp, seed):
+    """Per sequence, one of: mass spread over every span; all spans but one
+    emptied; the drafted token alone in its span; one span much heavier than
+    the rest. Applied to every target row, so whichever position is rejected
+    has that shape."""
     rng = np.random.default_rng(seed)
     V = inp.meta["V"]
     nb = (V + K - 1) // K
@@ -76,26 +74,27 @@ def _shape_blocks(inp, seed):
 
 
 @pytest.mark.parametrize("bf16,V", [(True, 3 * K + 776), (True, 3 * K + 777), (False, 2 * K + 3001)])
-def test_onehot_blocks_match_oracle(dev, bf16, V):
-    inp = make_chain("onehot_blocks", 48, 3, V, bf16=bf16, seed=51, target_sigma=3.0,
+def test_onehot_shaped_rows_match_oracle(dev, bf16, V):
+    inp = make_chain("onehot_rows", 48, 3, V, bf16=bf16, seed=51, target_sigma=3.0,
                      temperatures=(0.7, 1.0), one_hot=True, onehot_hit=0.5)
-    _shape_blocks(inp, 52)
+    _shape_spans(inp, 52)
     ref = oracle_sample(inp)
-    # rejections at several positions, and several blocks chosen
+    # rejections at several positions, replacements from several spans
     rej = ref["n"] < 3
     assert rej.sum() >= 24
-    blocks = {int(ref["tokens"][b, ref["n"][b]]) // K for b in np.nonzero(rej)[0]}
-    assert len(blocks) >= 3
+    spans = {int(ref["tokens"][b, ref["n"][b]]) // K for b in np.nonzero(rej)[0]}
+    assert len(spans) >= 3
     for tiling in (None, (8, 0), (4, 0), (1, 0), (0, 3)):
         got = run_sample(inp, torch, dev, tiling=tiling)
-        compare_chain(got, ref, label="onehot blocks %s %d %s" % (bf16, V, tiling))
+        compare_chain(got, ref, label="onehot rows %s %d %s" % (bf16, V, tiling))
 
 
-def test_onehot_many_blocks(dev):
-    """65 blocks (two waves' worth of block shares) and 4 x 65 pass-1 slots
-    per sequence; some sequences hold their mass only past block 63."""
+def test_onehot_long_rows(dev):
+    """V just over 2^20 (65 spans, 4 x 65 pass-1 slots per sequence, more
+    than one polling batch); some sequences hold their mass only in the last
+    two spans."""
     V = 64 * K + 1000
-    inp = make_chain("onehot_many_blocks", 8, 4, V, bf16=True, seed=53, target_sigma=2.0,
+    inp = make_chain("onehot_long_rows", 8, 4, V, bf16=True, seed=53, target_sigma=2.0,
                      temperatures=(1.0,), one_hot=True, onehot_hit=0.3)
     ninf = np.uint16(0xFF80)
     for b in range(0, 8, 2):
@@ -111,4 +110,4 @@ def test_onehot_many_blocks(dev):
     assert all(ref["tokens"][b, ref["n"][b]] >= 63 * K for b in late)
     for tiling in (None, (8, 0), (2, 0)):
         got = run_sample(inp, torch, dev, tiling=tiling)
-        compare_chain(got, ref, label="onehot many blocks %s" % (tiling,))
+        compare_chain(got, ref, label="onehot long rows %s" % (tiling,))

@@ -313,15 +313,13 @@ def test_one_hot_draft():
     assert _chi2_pvalue(obs, expect, int(rej.sum())) > 1e-4
 
 
-def test_one_hot_residual_over_several_blocks():
-    """Exercise 4's replacement p without x, on a row of three draw blocks: the
-    block is chosen by its share of that mass and the Gumbel-max runs inside
-    it, so every token other than x must still come out with p(v) / (1 - p(x)).
-    Heavy tokens sit in every block (x among them, in block 0) so that a block
-    weighed with x's mass, a block picked without the uniform, or an element
-    drawn outside its block all move the counts."""
+def test_one_hot_residual_on_a_long_row():
+    """Exercise 4's replacement p without x on a row of 37768 entries, heavy
+    tokens spread along it (x among them): every token other than x comes out
+    with p(v) / (1 - p(x)), counted per heavy token and per stretch of the
+    rest."""
     rng = np.random.default_rng(41)
-    K = oracle.DRAW_BLOCK
+    K = 16384
     V, B = 2 * K + 5000, 12000
     l = (rng.normal(0, 1.0, V) - 6.0).astype(np.float32)
     heavy = {100: 2.0, 101: 3.0, K + 7: 1.5, K + 9000: 2.2, 2 * K + 4999: 1.8}
@@ -355,11 +353,10 @@ def test_one_hot_residual_over_several_blocks():
     assert np.allclose(r["residual_mass"], 1.0 - p[x], atol=1e-12)
 
 
-def test_one_hot_residual_skips_empty_blocks():
-    """A block holding no mass besides x is never chosen, whatever its uniform:
-    with every entry of block 0 but x at -inf, every replacement lies in the
-    other blocks."""
-    K = oracle.DRAW_BLOCK
+def test_one_hot_residual_with_masked_stretch():
+    """With every entry of the first 16384 but x at -inf, no replacement comes
+    from there, and both later stretches are reached."""
+    K = 16384
     V, B = 2 * K + 8000, 400
     l = np.full(V, -np.inf, np.float32)
     l[5] = 4.0  # x
@@ -370,7 +367,6 @@ def test_one_hot_residual_skips_empty_blocks():
     r = oracle.verify_sample(tgt, None, ids, np.ones(B, np.float32), seed=2, u_override=u)
     assert np.all(r["n"] == 0)
     assert np.all(r["tokens"][:, 0] >= K)
-    # both other blocks are reached
     assert (r["tokens"][:, 0] >= 2 * K).any() and (r["tokens"][:, 0] < 2 * K).any()
 
 
