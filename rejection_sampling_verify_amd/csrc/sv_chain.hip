@@ -1016,8 +1016,10 @@ struct PhaseTable {
 // bound on log2 (p - q) applied, only in a wave-round where some element
 // passed the first test (about one in ten at the large chain workload).
 // Target-vector buffers of the bf16 Gumbel loop: its loads run kBufs - 1
-// rounds ahead of the round that uses them.
-constexpr int kBufs = 3;
+// rounds ahead of the round that uses them. Two buffers keep the pass-2
+// kernel within 80 VGPRs, six waves per SIMD: at three buffers (83 VGPRs,
+// five waves) onehot_bf16_qwen's pass 2 took 58.9 us against 56.7.
+constexpr int kBufs = 2;
 
 template <int MODE, bool BETA, bool EXCL = false>
 __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, const Decision dec, int lo, int hi, Smem& sm,
@@ -1556,7 +1558,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 // as fill the launch's workgroups (one resident wave of them), and workgroup
 // u takes chunk u mod n of list entry u / n; the others have nothing to do.
 template <bool BF16, bool VEC, bool BETA>
-__global__ __launch_bounds__(kThreads) void chain_p2_kernel(ChainArgs a) {
+// Six waves per SIMD (at most 80 VGPRs): see kBufs.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void chain_p2_kernel(ChainArgs a) {
   __shared__ Smem sm;
   // The start (work record, first vectors, seed) at the highest priority:
   // at the default one it waited behind the rounds of workgroups already in
