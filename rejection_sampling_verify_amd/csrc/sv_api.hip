@@ -217,7 +217,10 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
     a.p2_cap = (int32_t)cap;
     a.p2_force = forced_p2 > 0 ? (int32_t)std::min<long long>(forced_p2, cap) : 0;
     const long long resident2 = (long long)cus * p2_occupancy(dev, bf16, vec);
-    const long long grid2 = a.p2_force > 0 ? (long long)B * a.p2_force : std::max<long long>(resident2, B);
+    // No more workgroups than the draws can use (B rows of at most cap
+    // chunks): a small batch launches only those.
+    const long long grid2 = a.p2_force > 0 ? (long long)B * a.p2_force
+                                           : std::max<long long>(B, std::min<long long>(resident2, (long long)B * cap));
     if (grid2 >= (1ll << 31)) return SV_ERR_BAD_SHAPE;
     a.p2_grid = (int32_t)grid2;
   }
