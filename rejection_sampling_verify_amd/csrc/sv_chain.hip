@@ -355,6 +355,42 @@ __device__ __forceinline__ LseState lse_packed_bf16(u32x4 (&q)[KV], float c, int
   return st;
 }
 
+// lse_packed_bf16 that also keeps every element's exp2((l - M) c2) in e
+// (element order; 0 past the kvn vectors that hold data), M being this
+// thread's own maximum; the sum is formed in the same order, so the
+// statistics are bit for bit those of lse_packed_bf16.
+template <int KV>
+__device__ __forceinline__ LseState lse_packed_bf16_keep(u32x4 (&q)[KV], float c, int kvn, float (&e)[KV * 8]) {
+  LseState st;
+  st.M = packed_max_bf16(q);
+  st.s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < KV * 8; ++i) e[i] = 0.0f;
+  if (st.M != -INFINITY) {
+    const float Mc = st.M * c;
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+      if (k >= kvn) break;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[k * 8 + 2 * j] = fast_exp2(__builtin_fmaf(__uint_as_float(q[k][j] << 16), c, -Mc));
+        e[k * 8 + 2 * j + 1] = fast_exp2(__builtin_fmaf(__uint_as_float(q[k][j] & 0xFFFF0000u), c, -Mc));
+      }
+      s0 += e[k * 8 + 0];
+      s1 += e[k * 8 + 1];
+      s2 += e[k * 8 + 2];
+      s3 += e[k * 8 + 3];
+      s0 += e[k * 8 + 4];
+      s1 += e[k * 8 + 5];
+      s2 += e[k * 8 + 6];
+      s3 += e[k * 8 + 7];
+    }
+    st.s = (s0 + s1) + (s2 + s3);
+  }
+  return st;
+}
+
 // Argmax of the chunk [lo, lo + chunk) (lowest index among equal values): the
 // block maximum first, then the lowest index holding it, searched only by the
 // threads that hold it.
@@ -1942,6 +1978,14 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   // from them.
   Chunk<BF16, VEC, kPieceVecs> spec[2];
   int spec_node = -1;
+  // A slice that is one piece of whole vectors keeps, from the statistics
+  // action, every element's exp2((l - M) c2) of the node's target and draft
+  // rows (M: the thread's own maximum of each), so that the residual-mass
+  // passes at that node need neither its rows nor an exponential.
+  float ct[kPieceVecs * 8], cd[kPieceVecs * 8];
+  float cMt = -INFINITY, cMd = -INFINITY;
+  int cnode = -1;
+  const bool keep = BF16 && VEC && hi - lo <= piece && ((hi - lo) & 7) == 0;
   for (uint32_t epoch = 0; epoch <= (uint32_t)ta.N + 2u; ++epoch) {
     const TreeState t = s_state;
     // The node's children, and the two logits at the node of the sibling the
@@ -1987,22 +2031,40 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
 #pragma unroll
         for (int kind = 0; kind < 2; ++kind) {
           if (fast && hi2 - lo2 != piece) ch[kind].pad_neg_inf();
-          acc[kind] = lse_merge(acc[kind],
-                                block_lse(fast ? lse_packed_bf16(ch[kind].q, c2, kvn)
-                                               : chunk_lse(ch[kind], rows[kind], kPieceVecs, c2),
-                                          c2, sm, kind),
-                                c2);
+          LseState mine;
+          if (keep) {
+            mine = lse_packed_bf16_keep(ch[kind].q, c2, kvn, kind ? cd : ct);
+            if (kind) cMd = mine.M;
+            else cMt = mine.M;
+          } else {
+            mine = fast ? lse_packed_bf16(ch[kind].q, c2, kvn) : chunk_lse(ch[kind], rows[kind], kPieceVecs, c2);
+          }
+          acc[kind] = lse_merge(acc[kind], block_lse(mine, c2, sm, kind), c2);
         }
       }
+      cnode = keep ? t.node : -1;
       const float zt = acc[0].M == -INFINITY ? -INFINITY : acc[0].M * c2 + fast_log2(acc[0].s);
       const float zd = acc[1].M == -INFINITY ? -INFINITY : acc[1].M * c2 + fast_log2(acc[1].s);
       part.w0 = ((uint64_t)__float_as_uint(zt) << 32) | tag;
       part.w1 = ((uint64_t)__float_as_uint(zd) << 32) | tag;
     } else if (action == TA_PASS) {
       const float zd2s = t.zd2 - fast_log2(t.An);
-      partial = block_sum(residual_mass_part<BF16, VEC>(target_row(a, b, t.node), draft_row(a, b, t.node), lo, hi, c2,
-                                                        t.zt2, zd2s),
-                          sm);
+      float mass;
+      if (cnode == t.node) {
+        // p = exp2(l c2 - zt2) = exp2(M c2 - zt2) exp2((l - M) c2), and A q
+        // likewise with zd2 - log2 A.
+        const float at = cMt == -INFINITY ? 0.0f : fast_exp2(__builtin_fmaf(cMt, c2, -t.zt2));
+        const float ad = cMd == -INFINITY ? 0.0f : fast_exp2(__builtin_fmaf(cMd, c2, -zd2s));
+        mass = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPieceVecs * 8; ++i) {
+          const float pv = at * ct[i], qv = ad * cd[i];
+          if (pv > qv) mass += pv - qv;
+        }
+      } else {
+        mass = residual_mass_part<BF16, VEC>(target_row(a, b, t.node), draft_row(a, b, t.node), lo, hi, c2, t.zt2, zd2s);
+      }
+      partial = block_sum(mass, sm);
       part.w0 = ((uint64_t)__float_as_uint(partial) << 32) | tag;
       part.w1 = tag;
     } else {
