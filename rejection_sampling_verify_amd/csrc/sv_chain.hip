@@ -77,12 +77,8 @@ struct Smem {
 // lane rescales its sum to it and the sums are added (one exponential per
 // lane); the four wave states are merged through LDS.
 __device__ __forceinline__ LseState block_lse(LseState st, float c, Smem& sm, int slot) {
-  float M = st.M;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
-  float sum = (st.M == -INFINITY) ? 0.0f : st.s * fast_exp2((st.M - M) * c);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) sum += shfl_xor_f(sum, m);
+  const float M = wave_max(st.M);
+  const float sum = wave_sum((st.M == -INFINITY) ? 0.0f : st.s * fast_exp2((st.M - M) * c));
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     sm.lse[slot][w].M = M;
@@ -1986,13 +1982,18 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   float cMt = -INFINITY, cMd = -INFINITY;
   int cnode = -1;
   const bool keep = BF16 && VEC && hi - lo <= piece && ((hi - lo) & 7) == 0;
+  int kids_node = -1;  // the node whose children s_kids holds
   for (uint32_t epoch = 0; epoch <= (uint32_t)ta.N + 2u; ++epoch) {
     const TreeState t = s_state;
     // The node's children, and the two logits at the node of the sibling the
     // next decision tests (the first child after the statistics, the next one
     // after a pass), requested now so that they have landed by then.
-    tree_children(ta.N, s_par, t.node, s_kids, &s_nkids, s_wcnt);
-    __syncthreads();
+    // (Passes stay at the node: its children are already staged.)
+    if (t.node != kids_node) {
+      tree_children(ta.N, s_par, t.node, s_kids, &s_nkids, s_wcnt);
+      __syncthreads();
+      kids_node = t.node;
+    }
     float pre_lt = 0.0f, pre_ld = 0.0f;
     if (threadIdx.x == 0 && (action == TA_STATS || action == TA_PASS)) {
       const int next = action == TA_STATS ? 0 : t.round + 1;

@@ -274,11 +274,20 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(x, fmaxf(a, b));
 }
 
-// Wave-wide sum, in every lane (fixed order).
+// Wave-wide sum, the same value in every lane (fixed order): DPP steps
+// within each 16-lane row (after each step both lanes of a pair hold the same
+// sum, fp32 addition being commutative), then the four row sums read into
+// scalar registers and added in row order.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += shfl_xor_f(x, m);
-  return x;
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ int wave_or(int x) {
