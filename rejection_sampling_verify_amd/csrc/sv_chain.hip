@@ -839,6 +839,34 @@ __device__ __forceinline__ bool in_list(const int32_t* l, int n, int idx) {
   return false;
 }
 
+// The end of a Gumbel chunk: the workgroup's best (value, index), the sum
+// of beta and the OR of any, through one exchange in LDS (each reduced
+// within the wave first, then over the waves in wave order).
+__device__ __forceinline__ void block_draw_result(ArgMax m, float beta, int any, Smem& sm, P2Slot* out) {
+  m = wave_argmax(m);
+  beta = wave_sum(beta);
+  any = wave_or(any);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm.am[w] = m;
+    sm.fsum[w] = beta;
+    sm.ior[w] = any;
+  }
+  __syncthreads();
+  ArgMax r = sm.am[0];
+  float bs = sm.fsum[0];
+  int ba = sm.ior[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) {
+    r = argmax_merge(r, sm.am[k]);
+    bs += sm.fsum[k];
+    ba |= sm.ior[k];
+  }
+  __syncthreads();
+  out->w0 = pack(r.v, (uint32_t)r.i);
+  out->w1 = pack(bs, (uint32_t)ba);
+}
+
 // One chunk of a Gumbel-max draw, specialised on what the score of an element
 // is (MODE = P2_RESIDUAL: ln(p - q) where p > q; P2_RESIDUAL_ONEHOT: l/T for
 // v != x; P2_BONUS: l/T). For each 16-byte vector the lane forms the Philox
@@ -1000,11 +1028,7 @@ __device__ __forceinline__ void gumbel_chunk(const ChainArgs& a, int b, const De
   ArgMax m;
   m.v = bst.s;
   m.i = bst.i;
-  m = block_argmax(m, sm);
-  const float bsum = block_sum(beta, sm);
-  const int bany = block_or(any, sm);
-  out->w0 = pack(m.v, (uint32_t)m.i);
-  out->w1 = pack(bsum, (uint32_t)bany);
+  block_draw_result(m, beta, any, sm, out);
 }
 
 // Wave priority from progress through a chunk: 3 in its first quarter of
@@ -1355,11 +1379,7 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
   ArgMax m;
   m.v = bst.s;
   m.i = bst.i;
-  m = block_argmax(m, sm);
-  const float bsum = block_sum(beta, sm);
-  const int bany = block_or(any, sm);
-  out->w0 = pack(m.v, (uint32_t)m.i);
-  out->w1 = pack(bsum, (uint32_t)bany);
+  block_draw_result(m, beta, any, sm, out);
 }
 
 // Greedy bonus draw over [lo, hi): the target row's argmax (lowest index on

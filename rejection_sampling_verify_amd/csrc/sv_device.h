@@ -230,16 +230,6 @@ __device__ __forceinline__ LseState wave_lse(LseState a, float c) {
   return a;
 }
 
-__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    ArgMax o;
-    o.v = shfl_xor_f(a.v, m);
-    o.i = shfl_xor_i(a.i, m);
-    a = argmax_merge(a, o);
-  }
-  return a;
-}
 
 // Lane exchanges without LDS: DPP within 16-lane rows, then the gfx950 row
 // swaps (16 lanes, then 32). After lane_swaps(v), each lane holds v of the
@@ -290,10 +280,32 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (r0 + r1) + (r2 + r3);
 }
 
-__device__ __forceinline__ int wave_or(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x |= shfl_xor_i(x, m);
-  return x;
+__device__ __forceinline__ int wave_or(int x) { return __builtin_amdgcn_ballot_w64(x != 0) != 0ull ? 1 : 0; }
+
+template <int CTRL>
+__device__ __forceinline__ ArgMax dpp_am(ArgMax a) {
+  ArgMax o;
+  o.v = dpp_f<CTRL>(a.v);
+  o.i = __builtin_amdgcn_update_dpp(0, a.i, CTRL, 0xF, 0xF, false);
+  return o;
+}
+__device__ __forceinline__ ArgMax readlane_am(ArgMax a, int lane) {
+  ArgMax o;
+  o.v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.v), lane));
+  o.i = __builtin_amdgcn_readlane(a.i, lane);
+  return o;
+}
+
+// Wave-wide argmax (larger value, lower index on ties), the same in every
+// lane: the DPP steps of wave_sum within each 16-lane row, then the four row
+// results merged in row order.
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+  a = argmax_merge(a, dpp_am<0xB1>(a));
+  a = argmax_merge(a, dpp_am<0x4E>(a));
+  a = argmax_merge(a, dpp_am<0x141>(a));
+  a = argmax_merge(a, dpp_am<0x140>(a));
+  return argmax_merge(argmax_merge(readlane_am(a, 0), readlane_am(a, 16)),
+                      argmax_merge(readlane_am(a, 32), readlane_am(a, 48)));
 }
 
 // --------------------------------------------------------------------------
