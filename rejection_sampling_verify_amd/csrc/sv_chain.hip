@@ -92,6 +92,30 @@ __device__ __forceinline__ LseState block_lse(LseState st, float c, Smem& sm, in
   return r;
 }
 
+// block_lse of two states at once (one exchange through LDS for both).
+__device__ __forceinline__ void block_lse2(LseState& s0, LseState& s1, float c, Smem& sm) {
+  const float M0 = wave_max(s0.M), M1 = wave_max(s1.M);
+  const float t0 = wave_sum((s0.M == -INFINITY) ? 0.0f : s0.s * fast_exp2((s0.M - M0) * c));
+  const float t1 = wave_sum((s1.M == -INFINITY) ? 0.0f : s1.s * fast_exp2((s1.M - M1) * c));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm.lse[0][w].M = M0;
+    sm.lse[0][w].s = t0;
+    sm.lse[1][w].M = M1;
+    sm.lse[1][w].s = t1;
+  }
+  __syncthreads();
+  LseState r0 = sm.lse[0][0], r1 = sm.lse[1][0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) {
+    r0 = lse_merge(r0, sm.lse[0][k], c);
+    r1 = lse_merge(r1, sm.lse[1][k], c);
+  }
+  __syncthreads();
+  s0 = r0;
+  s1 = r1;
+}
+
 __device__ __forceinline__ ArgMax block_argmax(ArgMax a, Smem& sm) {
   a = wave_argmax(a);
   const int w = threadIdx.x >> 6;
@@ -1743,7 +1767,7 @@ template <bool BF16>
 __device__ __forceinline__ uint32_t tree_decide(const TreeSampleArgs& ta, int b, uint32_t prev, TreeState& s, const int32_t* kids,
                                 int nkids, const uint8_t* haskid, const int32_t* tok_s, float merged0, float merged1,
                                 int tree_bad, int tok_bad, bool writer, const TreeDrawn& dr, float T,
-                                float pre_lt = 0.0f, float pre_ld = 0.0f) {
+                                float pre_lt = 0.0f, float pre_ld = 0.0f, float pre_u = -1.0f) {
   const ChainArgs& a = ta.c;
   const float c2 = kLog2e / T;
   int32_t* path = ta.out_path + (int64_t)b * (ta.max_depth + 1);
@@ -1810,8 +1834,12 @@ __device__ __forceinline__ uint32_t tree_decide(const TreeSampleArgs& ta, int b,
   } else {
     acc = q > 0.0f ? fminf(1.0f, fmaxf(0.0f, p - s.A * q) / (s.Bv * q * sfac)) : 1.0f;
   }
-  const Words4 wu = philox10((uint32_t)s.round, (uint32_t)s.node, a.seq_base + (uint32_t)b, a.ctr_accept, a.key0, a.key1);
-  if (uniform_accept(wu.w[0]) < acc) {
+  // The accept uniform of this sibling (formed by another lane while the
+  // action ran, or here).
+  float u = pre_u;
+  if (u < 0.0f)
+    u = uniform_accept(philox10((uint32_t)s.round, (uint32_t)s.node, a.seq_base + (uint32_t)b, a.ctr_accept, a.key0, a.key1).w[0]);
+  if (u < acc) {
     if (writer && s.len <= ta.max_depth) xput(&path[s.len], c);
     s.len += 1;
     to_node(c);
@@ -1940,6 +1968,7 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   __shared__ int32_t s_nkids, s_wcnt[kThreads / 64];
   __shared__ TreeState s_state;
   __shared__ uint32_t s_action;
+  __shared__ float s_unif;  // the accept uniform of the sibling the next decision tests
   __shared__ int32_t s_dx[kMaxTreeNodes];
   __shared__ float s_dp[kMaxTreeNodes], s_dq[kMaxTreeNodes], s_dF[kMaxTreeNodes];
   TreeDrawn dr;
@@ -2023,6 +2052,14 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
         pre_ld = Elem<BF16>::load(draft_row(a, b, t.node), x);
       }
     }
+    // ... and that sibling's accept uniform, formed on another wave.
+    if (threadIdx.x == 64) {
+      const int next = action == TA_STATS ? 0 : t.round + 1;
+      s_unif = (action == TA_STATS || action == TA_PASS)
+                   ? uniform_accept(philox10((uint32_t)next, (uint32_t)t.node, a.seq_base + (uint32_t)b, a.ctr_accept,
+                                             a.key0, a.key1).w[0])
+                   : -1.0f;
+    }
     float partial = 0.0f;
     P2Slot part;
     part.w0 = pack(-INFINITY, 0xFFFFFFFFu);
@@ -2049,19 +2086,21 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
           ch[1].load(rows[1], lo2, hi2, kPieceVecs);
         }
         const int kvn = (ch[0].nfull + kThreads - 1) / kThreads;
+        LseState mine[2];
 #pragma unroll
         for (int kind = 0; kind < 2; ++kind) {
           if (fast && hi2 - lo2 != piece) ch[kind].pad_neg_inf();
-          LseState mine;
           if (keep) {
-            mine = lse_packed_bf16_keep(ch[kind].q, c2, kvn, kind ? cd : ct);
-            if (kind) cMd = mine.M;
-            else cMt = mine.M;
+            mine[kind] = lse_packed_bf16_keep(ch[kind].q, c2, kvn, kind ? cd : ct);
+            if (kind) cMd = mine[kind].M;
+            else cMt = mine[kind].M;
           } else {
-            mine = fast ? lse_packed_bf16(ch[kind].q, c2, kvn) : chunk_lse(ch[kind], rows[kind], kPieceVecs, c2);
+            mine[kind] = fast ? lse_packed_bf16(ch[kind].q, c2, kvn) : chunk_lse(ch[kind], rows[kind], kPieceVecs, c2);
           }
-          acc[kind] = lse_merge(acc[kind], block_lse(mine, c2, sm, kind), c2);
         }
+        block_lse2(mine[0], mine[1], c2, sm);
+        acc[0] = lse_merge(acc[0], mine[0], c2);
+        acc[1] = lse_merge(acc[1], mine[1], c2);
       }
       cnode = keep ? t.node : -1;
       const float zt = acc[0].M == -INFINITY ? -INFINITY : acc[0].M * c2 + fast_log2(acc[0].s);
@@ -2206,7 +2245,7 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
       if (threadIdx.x == 0) {
         TreeState s1 = s_state;
         s_action = tree_decide<BF16>(ta, b, action, s1, s_kids, s_nkids, s_haskid, s_tok, m0, m1, 0, 0, w == 0, dr, T,
-                                     pre_lt, pre_ld);
+                                     pre_lt, pre_ld, s_unif);
         s_state = s1;
         sm.lkey = 0u;
       }
