@@ -59,6 +59,7 @@ struct Smem {
   float fsum[kWaves];
   int ior[kWaves];
   uint32_t flag_last;
+  uint32_t again;  // sampled trees: the final draw is taken again over the whole row
   uint32_t stalled;
   uint32_t lkey;   // pass 2: order key of the best total the workgroup has reached
   uint32_t nwork;  // second launch: sequences on the pass-2 work list
@@ -1686,7 +1687,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
 // outputs) and carries out the next action on its part of the row: the
 // (max, sum exp2) of a node's target and draft rows when the walk reaches a
 // node with children (only the nodes on the walked path are read), a
-// residual-mass pass, or the final Gumbel-max draw. The parts of successive
+// residual-mass pass before each sibling after the first, or the final
+// Gumbel-max draw. The parts of successive
 // actions alternate between two slot buffers, since a workgroup can start
 // the next action while another still reads the parts of the last.
 // After some rejections at a node the target distribution is
@@ -1750,8 +1752,9 @@ __device__ __forceinline__ void tree_children(int N, const int32_t* par, int v, 
 // (max, sum) pairs are merged in workgroup order into the node's normalizers;
 // after a pass the partial masses are summed in workgroup order and the target
 // distribution is updated. Then the next sibling is tested: an accepted child
-// with children needs its statistics, a rejection the next pass, and the walk
-// otherwise ends in a draw. Only the workgroup with `writer` set writes the
+// with children needs its statistics, a rejection the next pass (or, after
+// the last sibling, the final residual draw at s.An), and the walk otherwise
+// ends in a bonus draw. Only the workgroup with `writer` set writes the
 // outputs.
 // In LDS: kids[0 .. nkids), the children of s.node in index order; haskid,
 // whether each node has children; tok_s, this sequence's node tokens; part,
@@ -1817,10 +1820,11 @@ __device__ __forceinline__ uint32_t tree_decide(const TreeSampleArgs& ta, int b,
   }
   const int c = s.round < nkids ? kids[s.round] : -1;
   if (c < 0) {
-    // A leaf (no child tested) draws the bonus from p; a node whose children
-    // were all rejected draws from its final residual (or from p if no
-    // residual had mass).
-    return (s.round > 0 && s.A > 0.0f) ? TA_DRAW_RESIDUAL : TA_DRAW_BONUS;
+    // (Not reached: a node's statistics are taken only when it has children,
+    // and a pass only when another sibling follows. A draw from the current
+    // target distribution.)
+    s.An = s.A;
+    return s.A > 0.0f ? TA_DRAW_RESIDUAL : TA_DRAW_BONUS;
   }
   const int x = tok_s[c];
   // The two logits of the sibling were gathered while the action ran.
@@ -1832,7 +1836,11 @@ __device__ __forceinline__ uint32_t tree_decide(const TreeSampleArgs& ta, int b,
   if (s.A == 0.0f && s.Bv == 1.0f && sfac == 1.0f) {
     acc = fast_exp2(fminf(0.0f, lp2 - lq2));  // min(1, p/q), as the chains compute it
   } else {
-    acc = q > 0.0f ? fminf(1.0f, fmaxf(0.0f, p - s.A * q) / (s.Bv * q * sfac)) : 1.0f;
+    // (p - A q)_+ / (B q s) in two divisions: B q s alone can underflow
+    // when the residual mass B left is small (B and q near 2^-120), and a
+    // zero numerator rejects outright.
+    const float num = fmaxf(0.0f, p - s.A * q);
+    acc = !(q > 0.0f) ? 1.0f : num > 0.0f ? fminf(1.0f, (num / s.Bv) / (q * sfac)) : 0.0f;
   }
   // The accept uniform of this sibling (formed by another lane while the
   // action ran, or here).
@@ -1854,7 +1862,15 @@ __device__ __forceinline__ uint32_t tree_decide(const TreeSampleArgs& ta, int b,
     s.qd += q;
   }
   s.An = s.A + s.Bv * sfac;
-  return TA_PASS;  // the mass of (p - A' q)_+ at this node, A' = s.An
+  // The next sibling's test needs the mass of (p - A' q)_+, A' = s.An.
+  if (s.round + 1 < nkids) return TA_PASS;
+  // After the last sibling the walk ends with a draw from (p - A' q)_+, whose
+  // scale does not matter: a pass would only tell whether it has mass. The
+  // draw tells that itself (a residual without mass has no candidate), and
+  // then the target distribution stays the one before this rejection
+  // (s.A, unchanged).
+  s.round += 1;
+  return TA_DRAW_RESIDUAL;
 }
 
 // This workgroup's part of sum_v (p(v) - A q(v))_+ over [lo, hi), with the
@@ -1900,48 +1916,117 @@ __device__ __forceinline__ float residual_mass_part(const uint8_t* rt, const uin
   return s;
 }
 
-// The last workgroup to arrive after the draw: the drawn token (workgroup
-// parts merged in workgroup order, lowest index on ties), the outputs, and the
-// sequence's workspace returned to zero. parts: the draw's slot buffer;
-// both_buffers: whether earlier actions used the other one too.
-// ndrawn > 0 (a residual draw without replacement): the siblings drawn before
-// the last one took no part in the row's draw; each competes with its kept
-// value F instead (ln F plus its noise, keyed as the row's).
+// This workgroup's part of a draw at node t.node over [lo, hi): from the
+// residual (p - A q)_+ (A > 0, log2 A folded into the draft normalizer; the
+// siblings excl[0 .. nx) take no part), or from p (A = 0, the bonus).
 template <bool BF16, bool VEC>
-__device__ __forceinline__ void tree_finish(const TreeSampleArgs& ta, int b, int len, const P2Slot* parts, bool both_buffers,
-                            int node, int ndrawn, const TreeDrawn& dr, Smem& sm) {
-  const ChainArgs& a = ta.c;
-  if (threadIdx.x == 0) {
-    ArgMax m;
-    m.v = -INFINITY;
-    m.i = -1;
-    for (int w = 0; w < ta.W; ++w) {
-      const uint64_t w0 = xget64((uint64_t*)&parts[w].w0);
-      ArgMax o;
-      o.v = hi_f(w0);
-      o.i = (int)lo_u(w0);
-      m = argmax_merge(m, o);
-    }
-    for (int i = 0; i < ndrawn; ++i) {
-      if (!(dr.F[i] > 0.0f)) continue;
-      const int x = dr.x[i];
-      ArgMax o;
-      o.v = logf(dr.F[i]) +
-            gumbel(word_at(philox10((uint32_t)x >> 2, (uint32_t)node, a.seq_base + (uint32_t)b, a.ctr_noise, a.key0, a.key1), x & 3));
-      o.i = x;
-      m = argmax_merge(m, o);
-    }
-    xput(&ta.out_token[b], m.i);
-    xput(&ta.out_len[b], len);
+__device__ __forceinline__ P2Slot tree_draw_part(const ChainArgs& a, int b, const TreeState& t, float T, float A, int lo,
+                                                 int hi, const int32_t* excl, int nx, Smem& sm) {
+  const bool res = A > 0.0f;
+  Decision d;
+  d.kind = KIND_SAMPLED;
+  d.n = 0;
+  d.row = t.node;
+  d.x = -1;
+  d.T = T;
+  d.c2 = kLog2e / T;
+  d.invT = 1.0f / T;
+  d.zt2 = t.zt2;
+  d.zd2 = res ? t.zd2 - fast_log2(A) : t.zd2;
+  d.a_row = 0.0f;
+  d.tok = -1;
+  d.mode = res ? P2_RESIDUAL : P2_BONUS;
+  P2Slot part;
+  if (BF16 && VEC) {
+    if (res && nx > 0) gumbel_chunk_bf16<P2_RESIDUAL, false, true>(a, b, d, lo, hi, sm, &part, excl, nx);
+    else if (res) gumbel_chunk_bf16<P2_RESIDUAL, false>(a, b, d, lo, hi, sm, &part);
+    else gumbel_chunk_bf16<P2_BONUS, false>(a, b, d, lo, hi, sm, &part);
+  } else {
+    if (res && nx > 0) gumbel_chunk<BF16, VEC, P2_RESIDUAL, true>(a, b, d, lo, hi, sm, &part, excl, nx);
+    else if (res) gumbel_chunk<BF16, VEC, P2_RESIDUAL>(a, b, d, lo, hi, sm, &part);
+    else gumbel_chunk<BF16, VEC, P2_BONUS>(a, b, d, lo, hi, sm, &part);
   }
-  __syncthreads();
+  return part;
+}
+
+// The walk's last action, the draw (action TA_DRAW_RESIDUAL or TA_DRAW_BONUS),
+// by all threads of workgroup w. Every workgroup draws its part of the row and
+// arrives on the sequence's counter; the last to arrive merges the parts in
+// part order (lowest index on ties), writes the token and length, and returns
+// both part buffers (`parts`, this action's; the other too when
+// both_buffers) and the counter to zero.
+// Without replacement the siblings drawn before the last one take no part in
+// the row's residual draw: each competes at the merge with ln F_i plus its own
+// noise, keyed as the row's.
+// The residual draw after the last sibling's rejection is taken at t.An with
+// no pass before it. If nothing has mass there (no candidate in the row and no
+// F_i > 0), the target distribution is the one before that rejection: the
+// merging workgroup then draws from it alone, over the whole row (the
+// residual at t.A, or p when t.A = 0).
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void tree_draw_finish(const TreeSampleArgs& ta, int b, int w, const TreeState& t, uint32_t action,
+                                                 float T, int lo, int hi, P2Slot* parts, bool both_buffers,
+                                                 const TreeDrawn& dr, Smem& sm) {
+  const ChainArgs& a = ta.c;
+  SeqState* st = a.seq + b;
+  const int nx = (ta.wor && action == TA_DRAW_RESIDUAL) ? t.round - 1 : 0;
+  float A = action == TA_DRAW_RESIDUAL ? t.An : 0.0f;
+  bool whole = false;  // the fallback draw: one workgroup, the whole row
+  for (;;) {
+    const int ndr = A > 0.0f ? nx : 0;
+    const P2Slot part = tree_draw_part<BF16, VEC>(a, b, t, T, A, whole ? 0 : lo, whole ? a.V : hi, dr.x, ndr, sm);
+    if (!whole) {
+      if (threadIdx.x == 0) {
+        xput64(&parts[w].w0, part.w0);
+        xput64(&parts[w].w1, part.w1);
+        wait_vmem();
+        sm.flag_last = (atomicAdd(&st->p2_arrive, 1u) + 1u == (uint32_t)ta.W) ? 1u : 0u;
+      }
+      __syncthreads();
+      if (!sm.flag_last) return;
+    }
+    if (threadIdx.x == 0) {
+      ArgMax m;
+      m.v = -INFINITY;
+      m.i = -1;
+      for (int k = 0; k < (whole ? 1 : ta.W); ++k) {
+        const uint64_t w0 = whole ? part.w0 : xget64((uint64_t*)&parts[k].w0);
+        ArgMax o;
+        o.v = hi_f(w0);
+        o.i = (int)lo_u(w0);
+        m = argmax_merge(m, o);
+      }
+      for (int i = 0; i < ndr; ++i) {
+        if (!(dr.F[i] > 0.0f)) continue;
+        const int x = dr.x[i];
+        ArgMax o;
+        o.v = logf(dr.F[i]) + gumbel(word_at(philox10((uint32_t)x >> 2, (uint32_t)t.node, a.seq_base + (uint32_t)b,
+                                                      a.ctr_noise, a.key0, a.key1), x & 3));
+        o.i = x;
+        m = argmax_merge(m, o);
+      }
+      const bool again = !whole && action == TA_DRAW_RESIDUAL && m.i < 0;
+      if (!again) {
+        xput(&ta.out_token[b], m.i);
+        xput(&ta.out_len[b], t.len);
+      } else {
+        // The fallback draw starts from no threshold.
+        sm.lkey = 0u;
+        xput(&st->lbest, 0u);
+      }
+      sm.again = again ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!sm.again) break;
+    whole = true;
+    A = t.A;
+  }
   uint64_t* s0 = (uint64_t*)(a.p2 + (int64_t)b * a.p2_stride);
   uint64_t* s1 = (uint64_t*)(ta.slot2 + (int64_t)b * a.p2_stride);
   for (int k = threadIdx.x; k < 2 * ta.W; k += kThreads) {
     xput64(&s0[k], 0u);
     if (both_buffers) xput64(&s1[k], 0u);
   }
-  SeqState* st = a.seq + b;
   if (threadIdx.x == 0) {
     xput(&st->lbest, 0u);
     xput(&st->p2_arrive, 0u);
@@ -2034,6 +2119,12 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   int kids_node = -1;  // the node whose children s_kids holds
   for (uint32_t epoch = 0; epoch <= (uint32_t)ta.N + 2u; ++epoch) {
     const TreeState t = s_state;
+    if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) {
+      // The last action: the draw (parts in buffer epoch & 1).
+      P2Slot* parts = ((epoch & 1u) ? ta.slot2 : a.p2) + (int64_t)b * a.p2_stride;
+      tree_draw_finish<BF16, VEC>(ta, b, w, t, action, T, lo, hi, parts, epoch > 0u, dr, sm);
+      return;
+    }
     // The node's children, and the two logits at the node of the sibling the
     // next decision tests (the first child after the statistics, the next one
     // after a pass), requested now so that they have landed by then.
@@ -2127,32 +2218,6 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
       partial = block_sum(mass, sm);
       part.w0 = ((uint64_t)__float_as_uint(partial) << 32) | tag;
       part.w1 = tag;
-    } else {
-      Decision d;
-      d.kind = KIND_SAMPLED;
-      d.n = 0;
-      d.row = t.node;
-      d.x = -1;
-      d.T = T;
-      d.c2 = c2;
-      d.invT = 1.0f / d.T;
-      d.zt2 = t.zt2;
-      d.zd2 = action == TA_DRAW_RESIDUAL ? t.zd2 - fast_log2(t.A) : t.zd2;
-      d.a_row = 0.0f;
-      d.tok = -1;
-      d.mode = action == TA_DRAW_RESIDUAL ? P2_RESIDUAL : P2_BONUS;
-      // Without replacement, the siblings drawn before the last one keep
-      // their own values: they are drawn apart, at the finish.
-      const int nx = (ta.wor && action == TA_DRAW_RESIDUAL) ? t.round - 1 : 0;
-      if (BF16 && VEC) {
-        if (nx > 0) gumbel_chunk_bf16<P2_RESIDUAL, false, true>(a, b, d, lo, hi, sm, &part, s_dx, nx);
-        else if (action == TA_DRAW_RESIDUAL) gumbel_chunk_bf16<P2_RESIDUAL, false>(a, b, d, lo, hi, sm, &part);
-        else gumbel_chunk_bf16<P2_BONUS, false>(a, b, d, lo, hi, sm, &part);
-      } else {
-        if (nx > 0) gumbel_chunk<BF16, VEC, P2_RESIDUAL, true>(a, b, d, lo, hi, sm, &part, s_dx, nx);
-        else if (action == TA_DRAW_RESIDUAL) gumbel_chunk<BF16, VEC, P2_RESIDUAL>(a, b, d, lo, hi, sm, &part);
-        else gumbel_chunk<BF16, VEC, P2_BONUS>(a, b, d, lo, hi, sm, &part);
-      }
     }
     spec_node = -1;
     if (action == TA_STATS || action == TA_PASS) {
@@ -2171,22 +2236,6 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
     // This workgroup's part goes to buffer epoch & 1 (a workgroup can start
     // the next action while another still reads this one's parts).
     P2Slot* parts = ((epoch & 1u) ? ta.slot2 : a.p2) + (int64_t)b * a.p2_stride;
-    if (action == TA_DRAW_RESIDUAL || action == TA_DRAW_BONUS) {
-      // The draw: the last of the W to arrive finishes the sequence (the
-      // arrival counter counts the draw only).
-      if (threadIdx.x == 0) {
-        xput64(&parts[w].w0, part.w0);
-        xput64(&parts[w].w1, part.w1);
-        wait_vmem();
-        sm.flag_last = (atomicAdd(&st->p2_arrive, 1u) + 1u == (uint32_t)ta.W) ? 1u : 0u;
-      }
-      __syncthreads();
-      if (sm.flag_last) {
-        const int nx = (ta.wor && action == TA_DRAW_RESIDUAL) ? t.round - 1 : 0;
-        tree_finish<BF16, VEC>(ta, b, t.len, parts, epoch > 0u, t.node, nx > 0 ? nx : 0, dr, sm);
-      }
-      return;
-    }
     // Statistics and passes: every word of a part carries the action's tag,
     // so a part is complete when both its words show it. Thread k reads part
     // k until it does (a bounded wait), then every workgroup takes the same

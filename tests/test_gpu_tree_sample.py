@@ -286,3 +286,50 @@ def test_deepest_paths(dev, wor):
     got = _run(inp, dev, seed=4, wor=wor)
     _compare(got, _oracle(inp, seed=4, wor=wor), "narrow N=1024 wor=%d" % wor)
     assert got["path_len"].max() >= 4
+
+
+@pytest.mark.parametrize("wor", [False, True])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_residual_without_mass(dev, bf16, wor):
+    """Siblings whose residual has no mass. The root's draft row equals its
+    target row (its one child is accepted); at that child the draft row equals
+    the target row except at the first k of its three children's tokens,
+    where the draft logit is -30 (too small to move any normalizer sum) and
+    the target logit -60 (a about e^-30, never accepted at these seeds). Each
+    such rejection leaves (p - q)_+ with no mass, so the target distribution
+    stays p; a later sibling then has p(x) = q(x) and is accepted. With all
+    three rejected the walk ends in a draw from p itself (i.i.d. siblings).
+    Without replacement, a drawn sibling leaves q, so the second rejection's
+    residual holds the first sibling's own p(x) alone: the target becomes that
+    token, every later sibling is rejected and the walk emits it."""
+    B, V = 12, 20000 if bf16 else 5003
+    parents = np.array([-1, 0, 1, 1, 1, 2, 3], np.int32)
+    depth = oracle.tree_depths(parents)
+    inp = make_tree_sample("no_mass", B, V, parents, depth, bf16=bf16, seed=31, temperatures=(1.0, 0.8),
+                           target_sigma=1.0, zipf=0.0)
+    rng = np.random.default_rng(32)
+    put = (lambda v: workloads.round_bf16(np.float32([v]))[0]) if bf16 else np.float32
+    kk = np.zeros(B, np.int32)
+    for b in range(B):
+        inp.draft[b, 0] = inp.target[b, 0]
+        inp.draft[b, 1] = inp.target[b, 1]
+        xs = rng.choice(V, size=3, replace=False)
+        inp.node_tokens[b, 2:5] = xs
+        kk[b] = b % 3 + 1
+        for x in xs[:kk[b]]:
+            inp.target[b, 1, x] = put(-60.0)
+            inp.draft[b, 1, x] = put(-30.0)
+    ref = _oracle(inp, seed=3, wor=wor)
+    got = _run(inp, dev, seed=3, wor=wor)
+    _compare(got, ref, "no mass bf16=%s wor=%s" % (bf16, wor))
+    assert np.all(got["path"][:, :2] == [0, 1])
+    for b in range(B):
+        k = kk[b]
+        assert ref["rejections"][b] >= k
+        assert ref["flags"][b] & oracle.FLAG_FALLBACK
+        if wor and k >= 2:
+            assert got["path_len"][b] == 2 and got["token"][b] == inp.node_tokens[b, 2]
+        elif k < 3:
+            assert got["path"][b, 2] == 2 + k  # the first sibling with p(x) = q(x)
+        else:
+            assert got["path_len"][b] == 2
