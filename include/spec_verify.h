@@ -212,8 +212,8 @@ sv_status_t spec_verify_sample_noalloc(const void* target_logits, int64_t target
  * caller instead of chosen by the library (for tests that check that results
  * do not depend on the tiling; no operation of the pages). p1_vectors: 16-byte
  * vectors per thread in a pass-1 chunk (1, 2, 4 or 8; 0 = chosen); p2_chunks:
- * pass-2 chunks per drawn row (0 = chosen; capped at one per four streaming
- * rounds). Everything else is as for spec_verify_sample; SV_ERR_BAD_ARG for
+ * pass-2 chunks per drawn row (0 = chosen; capped at one per streaming
+ * round, i.e. at least one vector per thread in a chunk). Everything else is as for spec_verify_sample; SV_ERR_BAD_ARG for
  * other tiling values. */
 sv_status_t sv_debug_sample_tiled(const void* target_logits, int64_t target_row_stride,
                                   const void* draft_logits, int64_t draft_row_stride,

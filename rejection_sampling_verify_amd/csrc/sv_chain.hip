@@ -425,6 +425,19 @@ __device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
 // see: +inf, a NaN with the sign bit clear, or a value of 2^121 or more (bit
 // patterns from 0x7C00 up). Positive bf16 values order like their patterns
 // read as signed 16-bit integers, so one packed integer maximum finds them.
+// An upper bound on the largest of a vector's eight bf16 logits: the largest
+// pattern read as a signed 16-bit integer, clamped at +0. Non-negative values
+// (+inf and values beyond the f16 range included) order as their patterns and
+// every negative pattern reads as a negative integer, so the bound is exact
+// when some element is >= 0, and 0 when all are negative.
+__device__ __forceinline__ float max_bound_bf16(const u32x4& q) {
+  const uint32_t m = pk_max_i16(pk_max_i16(q[0], q[1]), pk_max_i16(q[2], q[3]));
+  // max(low half, high half, 0) as 16-bit integers, in the low half of r.
+  uint32_t r;
+  asm("v_max3_i16 %0, %1, %2, 0" : "=v"(r) : "v"(m), "v"(m >> 16));
+  return __uint_as_float(r << 16);
+}
+
 template <int KV>
 __device__ __forceinline__ bool has_huge_positive_bf16(const u32x4 (&q)[KV]) {
   uint32_t m0 = 0x80008000u, m1 = 0x80008000u;
@@ -527,12 +540,12 @@ __device__ __forceinline__ bool may_win_bits(uint32_t w, float t) {
 
 // may_win_bits over a wave: the mask of active lanes whose element may win,
 // straight from the compare (a ballot of the verdict costs two more vector
-// operations per element). Same test, also true for an unordered compare.
+// operations per element), as a value the compiler knows to be the same on
+// every lane (branches on it stay on the scalar unit). Same test, also true
+// for an unordered compare (predicate 13: unordered or less or equal).
 __device__ __forceinline__ uint64_t lanes_may_win(uint32_t w, float t) {
   const float n = (float)(int)__float_as_uint((float)(~w));
-  uint64_t m;
-  asm("v_cmp_ngt_f32 %0, %1, %2" : "=s"(m) : "v"(n), "v"(t));
-  return m;
+  return __builtin_amdgcn_fcmpf(n, t, 13);
 }
 
 // Upper bound, in log2 units, on log2 (p - q) for log2 p = lp2 > lq2 = log2 q:
@@ -1124,12 +1137,15 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
   float L = -INFINITY, nL2 = INFINITY;  // wave-uniform
   // The residual mass is summed only for the caller's diagnostics (BETA).
   constexpr bool want_beta = residual && BETA;
-  float Lpost = -INFINITY;  // the largest total this wave has reported
   uint32_t* const gkey = &a.seq[b].lbest;
   auto set_L = [&](float l) {
     L = l;
     nL2 = -L * kLog2e;
   };
+  // L and the largest total this wave has reported, also as order keys (0:
+  // none yet), so that the common case (nothing new) is decided on the
+  // scalar unit.
+  uint32_t Lk = 0u, Lpk = 0u;
   auto total = [&](float lt, float ld, uint32_t w) -> float {
     float sc;
     if (residual) {
@@ -1161,19 +1177,32 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
                          : log_bias;
   };
   set_bounds();
+  // L rises to the total of order key k, if that is higher.
+  auto raise = [&](uint32_t k) {
+    if (k > Lk) {
+      Lk = k;
+      set_L(key_total(k));
+      set_bounds();
+    }
+  };
   const int nfull = (hi - lo) / 8;
   const int vi0 = (int)threadIdx.x;
-  // A lane past the last whole vector loads the last one again (discarded),
-  // so that every load is issued by the whole wave.
+  // The chunk's whole vectors as buffers: vector vi is at byte 16 vi, and a
+  // lane past the last whole vector reads zeros (masked out below), so that
+  // every load is issued by the whole wave.
   // The bulk test reads the target vector only; the residual's draft vector
   // is loaded on demand, by a wave-round with a survivor (want_beta, the
   // diagnostics variant, reads it always).
+  const __amdgpu_buffer_rsrc_t rs_t = make_rsrc(rt + (int64_t)lo * 2, (uint32_t)nfull * 16u);
+  const __amdgpu_buffer_rsrc_t rs_d = residual ? make_rsrc(rd + (int64_t)lo * 2, (uint32_t)nfull * 16u) : rs_t;
   auto fetch = [&](int vi, u32x4& qt, u32x4& qd) {
-    const int v = min(vi, nfull - 1);
-    qt = load_vec_stream(rt + (int64_t)(lo + v * 8) * 2);
-    if (want_beta) qd = load_vec_stream(rd + (int64_t)(lo + v * 8) * 2);
+    qt = load_vec_buf(rs_t, (uint32_t)vi * 16u);
+    if (want_beta) qd = load_vec_buf(rs_d, (uint32_t)vi * 16u);
   };
-  auto draft_vec = [&](int vi) -> u32x4 { return load_vec_stream(rd + (int64_t)(lo + min(vi, nfull - 1) * 8) * 2); };
+  auto draft_vec = [&](int vi) -> u32x4 { return load_vec_buf(rs_d, (uint32_t)vi * 16u); };
+  // Word 0 of the lane's first Philox block in round 0 (element index / 4);
+  // each round advances it by kThreads * 8 / 4.
+  const uint32_t cbase = (uint32_t)(lo + vi0 * 8) >> 2;
   const int rounds = (nfull + kThreads - 1) / kThreads;  // same for every lane
   // kBufs vector buffers per row read: the loads run kBufs - 1 rounds ahead
   // of the round that uses them.
@@ -1229,14 +1258,13 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     const float wm = wave_max(t0);
     if (lane == 0 && wm != -INFINITY) atomicMax(&sm.lkey, order_key(wm));
     __syncthreads();
-    const float ls = key_total(__builtin_amdgcn_readfirstlane(
-        __hip_atomic_load(&sm.lkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
-    if (ls != -INFINITY) {
-      set_L(ls);
-      set_bounds();
+    const uint32_t lsk = (uint32_t)__builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(&sm.lkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (lsk != 0u) {
+      raise(lsk);
       // The seed goes to the other workgroups of the row at once.
-      if (threadIdx.x == 0) atomicMax(gkey, order_key(ls));
-      Lpost = ls;
+      if (threadIdx.x == 0) atomicMax(gkey, lsk);
+      Lpk = lsk;
     }
   }
   const PhaseTable phase(rounds);
@@ -1255,7 +1283,8 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     Words4 wa, wb;
     // (Every lane forms them: a lane past the chunk's end costs the wave
     // nothing more, and its words are masked out below.)
-    philox10x2((uint32_t)base >> 2, ((uint32_t)base >> 2) + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
+    const uint32_t cw = cbase + (uint32_t)rnd * (uint32_t)(kThreads * 2);
+    philox10x2(cw, cw + 1u, crow, cseq, ctr3, k0, k1, wa, wb);
     if (want_beta && have) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -1276,10 +1305,9 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
     // at the large workloads about one wave-round in twenty has a lane that
     // passes, and only then do the eight per-element tests run.
     uint64_t lm[8];
-    const uint64_t have_m = __builtin_amdgcn_ballot_w64(have);
-    float lmax = el(qt0, 0);
-#pragma unroll
-    for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, el(qt0, e));
+    // Every lane holds a whole vector except, perhaps, in the last round.
+    const uint64_t have_m = (rnd + 1 < rounds) ? ~0ull : __builtin_amdgcn_ballot_w64(have);
+    const float lmax = max_bound_bf16(qt0);
     uint32_t wmax = wa.w[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) wmax = max(wmax, (e < 4) ? wa.w[e & 3] : wb.w[e & 3]);
@@ -1331,35 +1359,34 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
         mine = fmaxf(mine, tot);
       }
     }
-    // Share and collect totals: only a wave with survivors can have a new one.
-    float Ln = L;
-    if (surv != 0ull) Ln = fmaxf(Ln, wave_max(mine));
-    if (Ln > Lpost) {
-      if (lane == 0) {
-        atomicMax(&sm.lkey, order_key(Ln));
-        atomicMax(gkey, order_key(Ln));
+    // Share and collect totals: only a wave with survivors can have a new
+    // one, and only one above L and above what it reported is shared.
+    uint32_t kn = Lk;
+    if (surv != 0ull) {
+      // (Read from lane 0, so that the compiler knows it is the same on
+      // every lane.)
+      const float wm = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(mine))));
+      if (wm != -INFINITY) {
+        const uint32_t kw = (uint32_t)__builtin_amdgcn_readfirstlane(order_key(wm));
+        if (kw > Lk && kw > Lpk) {
+          if (lane == 0) {
+            atomicMax(&sm.lkey, kw);
+            atomicMax(gkey, kw);
+          }
+          Lpk = kw;
+        }
+        kn = max(kn, kw);
       }
-      Lpost = Ln;
     }
-    const uint32_t lk = __builtin_amdgcn_readfirstlane(__hip_atomic_load(&sm.lkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-    Ln = fmaxf(Ln, key_total(lk));
-    if (Ln > L) {
-      set_L(Ln);
-      set_bounds();
-    }
+    raise(max(kn, (uint32_t)__builtin_amdgcn_readfirstlane(
+                      __hip_atomic_load(&sm.lkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))));
     __builtin_amdgcn_sched_barrier(0);
   };
   // The sequence's best total from the other workgroups of the row: loaded
   // before the first of kBufs rounds' vector loads and read after the last of
   // them, whose vectors were loaded after it (loads complete in order, so it
   // costs no wait of its own).
-  auto take_global = [&](uint32_t gk) {
-    const float g = key_total(__builtin_amdgcn_readfirstlane(gk));
-    if (g > L) {
-      set_L(g);
-      set_bounds();
-    }
-  };
+  auto take_global = [&](uint32_t gk) { raise((uint32_t)__builtin_amdgcn_readfirstlane(gk)); };
 #pragma unroll 1
   for (int rnd = 0; rnd < rounds; rnd += kBufs) {
     const uint32_t gk = xload(gkey);
@@ -1635,8 +1662,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 // as fill the launch's workgroups (one resident wave of them), and workgroup
 // u takes chunk u mod n of list entry u / n; the others have nothing to do.
 template <bool BF16, bool VEC, bool BETA>
-// Six waves per SIMD (at most 80 VGPRs): see kBufs.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void chain_p2_kernel(ChainArgs a) {
+// kP2Resident waves per SIMD (at most 80 VGPRs): see kBufs.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kP2Resident))) void chain_p2_kernel(ChainArgs a) {
   __shared__ Smem sm;
   // The start (work record, first vectors, seed) at the highest priority:
   // at the default one it waited behind the rounds of workgroups already in

@@ -63,6 +63,30 @@ __device__ __forceinline__ void philox10x2(uint32_t a0, uint32_t b0, uint32_t c1
   uint32_t a1 = c1, a2 = c2, a3 = c3, b1 = c1, b2 = c2, b3 = c3;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
+    if (r < 3) {
+      // In the first rounds some operands are still the same on every lane
+      // (c1, c2, c3 and the key; word 0 of both blocks after round 0): plain
+      // two-input xors let the compiler combine those on the scalar unit.
+      const uint64_t pa0 = (uint64_t)0xD2511F53u * a0;
+      const uint64_t pb0 = (uint64_t)0xD2511F53u * b0;
+      const uint64_t pa1 = (uint64_t)0xCD9E8D57u * a2;
+      const uint64_t pb1 = (uint64_t)0xCD9E8D57u * b2;
+      const uint32_t na0 = (uint32_t)(pa1 >> 32) ^ (a1 ^ k0);
+      const uint32_t nb0 = (uint32_t)(pb1 >> 32) ^ (b1 ^ k0);
+      const uint32_t na2 = (uint32_t)(pa0 >> 32) ^ (a3 ^ k1);
+      const uint32_t nb2 = (uint32_t)(pb0 >> 32) ^ (b3 ^ k1);
+      a1 = (uint32_t)pa1;
+      b1 = (uint32_t)pb1;
+      a3 = (uint32_t)pa0;
+      b3 = (uint32_t)pb0;
+      a0 = na0;
+      b0 = nb0;
+      a2 = na2;
+      b2 = nb2;
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+      continue;
+    }
     const uint64_t pa0 = (uint64_t)0xD2511F53u * a0;
     const uint64_t pb0 = (uint64_t)0xD2511F53u * b0;
     const uint64_t pa1 = (uint64_t)0xCD9E8D57u * a2;
@@ -177,6 +201,18 @@ struct Elem<false> {
 
 __device__ __forceinline__ u32x4 load_vec_stream(const uint8_t* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+// A buffer resource over [p, p + bytes): loads through it take their whole
+// offset from one vector register (no 64-bit address arithmetic per load),
+// and a load at or past `bytes` returns zeros instead of reading memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes at byte offset off of a buffer, nontemporal (aux bit 1).
+__device__ __forceinline__ u32x4 load_vec_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
 }
 
 // --------------------------------------------------------------------------

@@ -11,6 +11,9 @@ namespace sv {
 constexpr int kMaxVecsPerThread = 8;  // 16-byte vectors per thread per row chunk
 constexpr int kMaxGamma = 16;
 constexpr int kMaxTreeNodes = 1024;
+// Pass-2 workgroups resident per CU (one wave per SIMD each): the second
+// launch is sized for this many, and its kernel is built for it.
+constexpr int kP2Resident = 6;
 
 // Pass-2 work of a decided sequence.
 enum P2Mode : uint32_t {
