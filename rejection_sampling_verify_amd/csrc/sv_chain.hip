@@ -1106,13 +1106,12 @@ struct PhaseTable {
 // same row (through the sequence record, read once every kBufs rounds)
 // reports a higher total. The residual's bulk test bounds its score by
 // log2 p alone (ln (p - q) <= ln p) and reads only the target vector; the
-// draft vector is loaded, and the candidacy test p > q and the tighter
-// bound on log2 (p - q) applied, only in a wave-round where some element
-// passed the first test (about one in ten at the large chain workload).
-// Target-vector buffers of the bf16 Gumbel loop: its loads run kBufs - 1
-// rounds ahead of the round that uses them. Two buffers keep the pass-2
-// kernel within 80 VGPRs, six waves per SIMD: at three buffers (83 VGPRs,
-// five waves) onehot_bf16_qwen's pass 2 took 58.9 us against 56.7.
+// candidacy test p > q and the tighter bound on log2 (p - q), which read the
+// draft vector (loaded with the target vector), are applied only in a
+// wave-round where some element passed the first test.
+// Vector buffers of the bf16 Gumbel loop: its loads run kBufs - 1 rounds
+// ahead of the round that uses them. Two buffers keep the pass-2 kernel
+// within 80 VGPRs, six waves per SIMD; a third changes nothing measurable.
 constexpr int kBufs = 2;
 
 template <int MODE, bool BETA, bool EXCL = false>
@@ -1190,16 +1189,16 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
   // The chunk's whole vectors as buffers: vector vi is at byte 16 vi, and a
   // lane past the last whole vector reads zeros (masked out below), so that
   // every load is issued by the whole wave.
-  // The bulk test reads the target vector only; the residual's draft vector
-  // is loaded on demand, by a wave-round with a survivor (want_beta, the
-  // diagnostics variant, reads it always).
+  // The bulk test reads the target vector only; a residual draw's draft
+  // vector is loaded with it all the same: most residual wave-rounds have a
+  // survivor that needs it, and a load issued mid-round stalls a wave that
+  // has no other waves to hide it (small batches run one per SIMD).
   const __amdgpu_buffer_rsrc_t rs_t = make_rsrc(rt + (int64_t)lo * 2, (uint32_t)nfull * 16u);
   const __amdgpu_buffer_rsrc_t rs_d = residual ? make_rsrc(rd + (int64_t)lo * 2, (uint32_t)nfull * 16u) : rs_t;
   auto fetch = [&](int vi, u32x4& qt, u32x4& qd) {
     qt = load_vec_buf(rs_t, (uint32_t)vi * 16u);
-    if (want_beta) qd = load_vec_buf(rs_d, (uint32_t)vi * 16u);
+    if (residual) qd = load_vec_buf(rs_d, (uint32_t)vi * 16u);
   };
-  auto draft_vec = [&](int vi) -> u32x4 { return load_vec_buf(rs_d, (uint32_t)vi * 16u); };
   // Word 0 of the lane's first Philox block in round 0 (element index / 4);
   // each round advances it by kThreads * 8 / 4.
   const uint32_t cbase = (uint32_t)(lo + vi0 * 8) >> 2;
@@ -1210,8 +1209,6 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
 #pragma unroll
   for (int j = 0; j < kBufs - 1; ++j)
     if (j < rounds) fetch(vi0 + j * kThreads, qv[j], dv[j]);
-  // The seed below needs the first draft vector of a residual draw too.
-  if (residual && !want_beta && rounds > 0) dv[0] = draft_vec(vi0);
   // The first vectors have landed before the loop (vmcnt(0)): inside it the
   // compiler then waits only for the vectors of the round it works on, not
   // for the loads of the rounds after it.
@@ -1269,7 +1266,7 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
   }
   const PhaseTable phase(rounds);
   // One round over the target vector qt0 (its load issued kBufs - 1 rounds
-  // earlier; qd0, the draft vector, only in the diagnostics variant).
+  // earlier; qd0, the draft vector of a residual draw, loaded with it).
   auto round = [&](int rnd, const u32x4& qt0, const u32x4& qd0) __attribute__((always_inline)) {
     // The unrolled rounds are scheduled one after the other: left to
     // interleave them, the compiler would hold several rounds' Philox words
@@ -1324,7 +1321,7 @@ __device__ __forceinline__ void gumbel_chunk_bf16(const ChainArgs& a, int b, con
       // One-hot: the draft token is excluded (xrel: its place in this vector,
       // if it is there).
       const int xrel = onehot ? xex - base : -1;
-      const u32x4 qd1 = (residual && !want_beta) ? draft_vec(vi) : qd0;
+      const u32x4& qd1 = qd0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (lm[e] == 0ull) continue;
