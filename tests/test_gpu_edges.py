@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import make_chain, make_tree, round_bf16
+from workloads import bf16_to_f32, make_chain, make_tree, round_bf16
 
 from gpu_util import compare_chain, oracle_sample, run_sample, to_dev
 
@@ -121,6 +121,49 @@ def test_masked_and_underflowing_probabilities(dev, bf16):
     ref = oracle_sample(oh)
     for got in _both_tilings(oh, dev):
         compare_chain(got, ref, label="masked one-hot bf16=%s" % bf16)
+
+
+@pytest.mark.parametrize("one_hot", [False, True])
+def test_pruning_bound_on_shifted_rows(dev, one_hot):
+    """The draws' lane-level bound reads a vector's eight bf16 patterns as
+    signed 16-bit integers: exact when some element is >= 0, 0 when all are
+    negative. Rows shifted far below zero (every lane negative), rows shifted
+    far above zero (every lane positive), and sequences whose drafts are all
+    accepted and whose bonus row holds one logit of 2^125 (beyond the f16
+    reading's range) must still draw exactly the oracle's tokens: residual,
+    one-hot residual and bonus draws."""
+    B, G, V = 18, 3, 20000
+    inp = make_chain("shifted", B, G, V, bf16=True, seed=512, target_sigma=2.0, draft_sigma=0.7,
+                     temperatures=(0.7, 1.0, 1.6), one_hot=one_hot)
+    rng = np.random.default_rng(513)
+    t = bf16_to_f32(inp.target)
+    d = bf16_to_f32(inp.draft) if not one_hot else None
+    huge = []
+    for b in range(B):
+        kind = b % 3
+        if kind < 2:
+            shift = np.float32(-80.0 if kind == 0 else 80.0)
+            inp.target[b] = round_bf16(t[b] + shift)
+            if not one_hot:
+                inp.draft[b] = round_bf16(d[b] + shift)
+        else:
+            # Every draft accepted (q = p, or p one-hot at the drafted token),
+            # then the bonus draw meets a logit of 2^125.
+            if one_hot:
+                for i in range(G):
+                    inp.target[b, i, :] = BF16_NINF
+                    inp.target[b, i, int(inp.draft_ids[b, i])] = round_bf16(np.float32([0.5]))[0]
+            else:
+                inp.draft[b] = inp.target[b, :G]
+            h = int(rng.integers(V))
+            inp.target[b, G, h] = BF16_HUGE
+            huge.append((b, h))
+    ref = oracle_sample(inp)
+    for b, h in huge:
+        assert ref["n"][b] == G and ref["tokens"][b, G] == h
+    assert np.any(ref["n"][np.arange(B) % 3 < 2] < G)  # some shifted sequences end in a residual draw
+    for got in _both_tilings(inp, dev):
+        compare_chain(got, ref, check_diag=False, label="shifted rows one_hot=%s" % one_hot)
 
 
 def test_logits_outside_the_packed_range(dev):
