@@ -141,18 +141,6 @@ __device__ __forceinline__ float block_sum(float x, Smem& sm) {
   return r;
 }
 
-__device__ __forceinline__ int block_or(int x, Smem& sm) {
-  x = wave_or(x);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) sm.ior[w] = x;
-  __syncthreads();
-  int r = 0;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) r |= sm.ior[k];
-  __syncthreads();
-  return r;
-}
-
 __device__ __forceinline__ float block_max(float x, Smem& sm) {
   x = wave_max(x);
   const int w = threadIdx.x >> 6;
@@ -1568,35 +1556,46 @@ __device__ __forceinline__ void finalize(const ChainArgs& a, int b, int p2_chunk
   }
 }
 
-// Reads entry li of the work list (thread 0): the sequence and its decision
-// record in one round trip. The first launch has completed, so the entry is
-// complete; returns false if it was never published (a workspace left dirty
-// by an earlier call whose wait gave up).
-__device__ __forceinline__ bool read_work(const ChainArgs& a, int li, int* b, Decision* out) {
+// Entry li of the work list as loaded (thread 0): the sequence and its
+// decision record, requested in one round trip.
+struct WorkRaw {
+  uint64_t d0, d1, d2, d3;
+  uint32_t wb;
+};
+
+__device__ __forceinline__ WorkRaw load_work(const ChainArgs& a, int li) {
   WorkRec* w = a.work + li;
-  const uint64_t d0 = xget64(&w->dec[0]);
-  const uint64_t d1 = xget64(&w->dec[1]);
-  const uint64_t d2 = xget64(&w->dec[2]);
-  const uint64_t d3 = xget64(&w->dec[3]);
-  const uint32_t wb = xload(&w->b);
-  if (!(d0 & kRecPublished) || wb >= (uint32_t)a.B) {
+  WorkRaw r;
+  r.d0 = xget64(&w->dec[0]);
+  r.d1 = xget64(&w->dec[1]);
+  r.d2 = xget64(&w->dec[2]);
+  r.d3 = xget64(&w->dec[3]);
+  r.wb = xload(&w->b);
+  return r;
+}
+
+// The decision of a loaded entry. The first launch has completed, so an entry
+// below the list's length is complete; returns false if it was never
+// published (a workspace left dirty by an earlier call whose wait gave up).
+__device__ __forceinline__ bool decode_work(const ChainArgs& a, const WorkRaw& r, int* b, Decision* out) {
+  if (!(r.d0 & kRecPublished) || r.wb >= (uint32_t)a.B) {
     atomicOr(&a.done[1], 1u);
     return false;
   }
   Decision d;
   d.kind = KIND_SAMPLED;  // not used by pass 2
   d.T = 0.0f;
-  d.mode = (uint32_t)(d0 & 0xFFu);
-  d.n = (int)((d0 >> 8) & 0xFFu) - 64;
-  d.row = (int)((d0 >> 32) & 0x7FFFFFFFu);
-  d.zt2 = hi_f(d1);
-  d.zd2 = __uint_as_float(lo_u(d1));
-  d.c2 = hi_f(d2);
-  d.invT = __uint_as_float(lo_u(d2));
-  d.a_row = hi_f(d3);
-  d.x = (int)lo_u(d3);
+  d.mode = (uint32_t)(r.d0 & 0xFFu);
+  d.n = (int)((r.d0 >> 8) & 0xFFu) - 64;
+  d.row = (int)((r.d0 >> 32) & 0x7FFFFFFFu);
+  d.zt2 = hi_f(r.d1);
+  d.zd2 = __uint_as_float(lo_u(r.d1));
+  d.c2 = hi_f(r.d2);
+  d.invT = __uint_as_float(lo_u(r.d2));
+  d.a_row = hi_f(r.d3);
+  d.x = (int)lo_u(r.d3);
   d.tok = -1;
-  *b = (int)wb;
+  *b = (int)r.wb;
   *out = d;
   return true;
 }
@@ -1667,20 +1666,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kP2Res
   // their first phase, up to 13 us instead of 3.
   __builtin_amdgcn_s_setprio(3);
   if (threadIdx.x == 0) {
-    const uint32_t nw = min(xload(&a.done[kDoneNWork]), (uint32_t)a.B);
-    int b = -1, c = 0, len = 0, nc = 0, li = 0;
-    if (nw > 0) {
+    // Rows of nw listed draws are cut into nc chunks of len elements each.
+    auto geometry = [&](uint32_t nw, int& len, int& nc) {
       int c2 = a.p2_force > 0 ? a.p2_force : a.p2_grid / (int)nw;
       c2 = max(1, min(c2, a.p2_cap));
       len = (a.V + c2 - 1) / c2;
       len = (len + a.p2_unit - 1) / a.p2_unit * a.p2_unit;
       nc = (a.V + len - 1) / len;
-      const uint32_t u = blockIdx.x;
+    };
+    const uint32_t u = blockIdx.x;
+    // The entry this workgroup takes when every sequence has a draw pending
+    // (the usual case) is requested together with the list's length: one
+    // round trip instead of two. Otherwise it is not used.
+    int len_all, nc_all;
+    geometry((uint32_t)a.B, len_all, nc_all);
+    const bool guess = u < (uint32_t)a.B * (uint32_t)nc_all;
+    WorkRaw raw_all;
+    if (guess) raw_all = load_work(a, (int)(u / (uint32_t)nc_all));
+    const uint32_t nw = min(xload(&a.done[kDoneNWork]), (uint32_t)a.B);
+    int b = -1, c = 0, len = 0, nc = 0, li = 0;
+    if (nw > 0) {
+      geometry(nw, len, nc);
       if (u < nw * (uint32_t)nc) {
         li = (int)(u / (uint32_t)nc);
         c = (int)(u % (uint32_t)nc);
+        const WorkRaw raw = (nw == (uint32_t)a.B && guess) ? raw_all : load_work(a, li);
         Decision d;
-        if (read_work(a, li, &b, &d)) {
+        if (decode_work(a, raw, &b, &d)) {
           sm.dec = d;
           sm.stalled = 0u;
         } else {
@@ -2067,7 +2079,6 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(TreeSampleArgs ta) 
   const int b = ta.b_base + (int)(blockIdx.x / (uint32_t)ta.W);
   const int w = (int)(blockIdx.x % (uint32_t)ta.W);
   if (b >= ta.b_base + ta.b_count) return;  // whole sequences only
-  SeqState* st = a.seq + b;
   const int lo = w * ta.wlen, hi = min(a.V, lo + ta.wlen);
   // The tree and this sequence's tokens in LDS, with the checks of the tree
   // (root first at depth 0; every other parent an earlier node, one level
