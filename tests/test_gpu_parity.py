@@ -315,6 +315,19 @@ def test_named_workload_full_size(dev, name):
     print("[parity] %s mean accepted %.3f, emitted/step %.3f" % (name, n.mean(), n.mean() + 1), flush=True)
 
 
+@pytest.mark.parametrize("name", [n for n in workloads.CONFIGS if not n.startswith("tree")])
+def test_named_chains_more_seeds(dev, name):
+    """The chain workloads at full size under four more (seed, offset) pairs:
+    the same logits with other accept uniforms and Gumbel noise, hence other
+    first rejections and other residual, one-hot and bonus draws. Launched as
+    the bench launches them (no diagnostics); nothing is excused."""
+    inp = workloads.make(name)
+    for seed, offset in ((11, 0), (12, 5), ((1 << 40) + 3, 17), (977, 1 << 20)):
+        got = run_sample(inp, torch, dev, seed=seed, offset=offset, diag=False)
+        ref = oracle_sample(inp, seed=seed, offset=offset)
+        compare_chain(got, ref, check_diag=False, label="%s seed %d offset %d" % (name, seed, offset))
+
+
 def test_tree_deepest_paths(dev):
     """1024-node trees at full depth: a chain-shaped tree (depth 1023) whose
     every child carries its parent's argmax, so the accepted path runs to the

@@ -183,6 +183,11 @@ def test_named_workload_full_size(dev):
     ref = _oracle(inp, seed=inp.seed, offset=inp.offset)
     _compare(got, ref, "tree_sample_bf16_llama")
     assert np.all(ref["path_len"] >= 1)
+    # Other accept uniforms and noise over the same logits, both sibling rules.
+    for seed, offset, wor in ((21, 0, False), (22, 9, True), ((1 << 36) + 5, 123, False), (23, 1 << 18, True)):
+        got = _run(inp, dev, seed=seed, offset=offset, wor=wor)
+        _compare(got, _oracle(inp, seed=seed, offset=offset, wor=wor),
+                 "tree_sample_bf16_llama seed %d offset %d wor=%s" % (seed, offset, wor))
 
 
 @pytest.mark.parametrize("N,V", [(1, 1000), (2, 1000), (2, 700), (3, 2048)])
