@@ -274,7 +274,9 @@ sv_status_t spec_verify_tree(const void* target_logits, int64_t target_row_strid
  * becomes the normalized residual (p - q)_+ / ||(p - q)_+||_1 and the next
  * sibling is tested against it; if every child is rejected the replacement
  * token is drawn from the final residual; a leaf ends the path with a bonus
- * token drawn from p there).
+ * token drawn from p there). A residual with no mass (p and q equal wherever
+ * p is not below q, in the arithmetic of the call) leaves the target
+ * distribution as it was.
  *   target_logits: device [B, N, V] (row stride target_row_stride elements):
  *     row v of sequence b scores the token after node v.
  *   draft_logits: device [B, N, V] (row stride draft_row_stride): row v is
