@@ -218,8 +218,8 @@ sv_status_t run_chain(const void* target, int64_t t_stride, const void* draft, i
     const long long cap1 = (V + unit - 1) / unit;
     a.p2_force = forced_p2 > 0 ? (int32_t)std::min<long long>(forced_p2, cap1) : 0;
     a.p2_cap = a.p2_force > 0 ? a.p2_force : (int32_t)cap;
-    // At most kP2Resident per CU even where more would fit: at
-    // chain_bf16_llama, seven per CU (more, shorter chunks) were slower.
+    // At most kP2Resident per CU even where more would fit: seven per CU
+    // measured no faster at either large chain workload.
     const long long resident2 = (long long)cus * std::min(kP2Resident, p2_occupancy(dev, bf16, vec));
     // No more workgroups than the draws can use (B rows of at most cap
     // chunks): a small batch launches only those.
