@@ -418,7 +418,7 @@ def main():
                     help="only run device-to-device copies of a known size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
