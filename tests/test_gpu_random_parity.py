@@ -5,9 +5,9 @@ length, vocabulary (small ones of a few hundred entries or fewer, sizes that
 are not multiples of the 8-element vector, and the full 128256), bf16 or
 fp32 logits, dense or one-hot drafts, a mix of greedy and sampled
 temperatures, the Philox seed and offset, and, for chains, both the
-library's tiling and a forced one. Sampled trees get random trees and both
-sibling rules. Tokens, accepted lengths and paths must match the oracle bit
-for bit ([SB] "The rule", "Extending to a chain of γ draft tokens" and "Tree
+library's tiling and a forced one. Greedy trees get random shapes and
+match rates; sampled trees get random shapes and both sibling rules. Tokens,
+accepted lengths and paths must match the oracle bit for bit ([SB] "The rule", "Extending to a chain of γ draft tokens" and "Tree
 Attention"); at these seeds nothing is excused.
 """
 import numpy as np
@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import workloads
-from workloads import make_chain, make_tree_sample
+from workloads import make_chain, make_tree, make_tree_sample
 
 from gpu_util import compare_chain, oracle_sample, run_sample, to_dev
 
@@ -93,3 +93,26 @@ def test_random_sampled_trees(dev, block):
         assert np.array_equal(plen.cpu().numpy(), ref["path_len"]), label
         assert np.array_equal(path.cpu().numpy(), ref["path"]), label
         assert np.array_equal(token.cpu().numpy(), ref["token"]), label
+
+
+@pytest.mark.parametrize("block", range(2))
+def test_random_greedy_trees(dev, block):
+    import rejection_sampling_verify_amd as rsv
+    rng = np.random.default_rng(9300 + block)
+    for it in range(10):
+        N, B, V = int(rng.integers(1, 300)), int(rng.integers(1, 40)), _vocab(rng)
+        bf16 = bool(rng.random() < 0.7)
+        parents = workloads.random_tree(rng, N, (1, int(rng.integers(1, 7))))
+        depth = np.array(oracle.tree_depths(parents), np.int32)
+        inp = make_tree("random_greedy_%d_%d" % (block, it), B, V, parents, depth, bf16=bf16,
+                        seed=int(rng.integers(1 << 30)), target_sigma=float(rng.choice([1.0, 3.0])),
+                        hit=float(rng.choice([0.3, 0.7, 0.95])))
+        path, plen, bonus = rsv.spec_verify_tree(
+            to_dev(inp.target, torch, dev), torch.from_numpy(inp.parents).to(dev),
+            torch.from_numpy(inp.depth).to(dev), torch.from_numpy(inp.node_tokens).to(dev), inp.max_depth)
+        torch.cuda.synchronize()
+        ref = oracle.verify_tree(inp.target, inp.parents, inp.depth, inp.node_tokens, inp.max_depth)
+        label = "block %d case %d: N=%d B=%d V=%d bf16=%s" % (block, it, N, B, V, bf16)
+        assert np.array_equal(plen.cpu().numpy(), ref["path_len"]), label
+        assert np.array_equal(path.cpu().numpy(), ref["path"]), label
+        assert np.array_equal(bonus.cpu().numpy(), ref["bonus"]), label
